@@ -1,0 +1,25 @@
+"""CPU fp64 oracle for paged-KV attention — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may import this package.  The product path (the HIP
+library and its Python binding) never imports, calls or links it.
+
+Pins: every function here is checked in ``tests/test_oracle_pins.py``
+against closed forms, page values, a separately written dense attention,
+torch's fp64 scaled-dot-product attention, and 50-digit brute force.  No
+function is "parity unpinned".
+"""
+
+from .paged_attention import (  # noqa: F401
+    attention_state,
+    bf16_to_f64,
+    cascade_prefix_attention,
+    causal_visible,
+    default_scale,
+    gather_kv,
+    merge_attn_states,
+    paged_attention,
+    reshape_and_cache,
+    slot_mapping,
+    token_positions,
+)
