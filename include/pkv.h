@@ -1,0 +1,174 @@
+/*
+ * pkv.h — C ABI of libpkv, attention over a paged KV cache on AMD MI355X (gfx950).
+ *
+ * Objects (the names the pages and the vLLM attention metadata use):
+ *   q             bf16 [num_tokens, num_q_heads, head_dim]; the new tokens of every request,
+ *                 concatenated request after request (batched prefill: Tencent Cloud
+ *                 article on vLLM inference acceleration, batched-prefill paragraph).
+ *   k_cache,      bf16 [num_blocks, num_kv_heads, block_size, head_dim]; physical block
+ *   v_cache       pools. Token p of a request lives in physical block block_tables[r][p / bs]
+ *                 at offset p % bs ("11. vLLM principles", section 11.2 PagedAttention).
+ *   block_tables  int32 [num_seqs, bt_stride]; logical block -> physical block per request.
+ *                 Rows may share physical blocks (shared, read-only prefix; same section).
+ *   query_start_loc int32 [num_seqs + 1]; request r owns tokens [qsl[r], qsl[r+1]).
+ *   context_lens  int32 [num_seqs]; tokens of request r already cached before this step
+ *                 (earlier chunks, or a prefix-cache hit: Tencent Cloud article, chunked
+ *                 prefill and prefix caching sections).
+ *   seq_lens      int32 [num_seqs]; keys visible after this step = context_lens + query len.
+ *   slot_mapping  int64 [num_tokens]; flat pool slot (physical_block * bs + offset) of every
+ *                 new token; a negative slot means "do not write".
+ *
+ * Attention: token i of request r sits at position p = context_lens[r] + i and attends to
+ * keys 0..p of its own request (its own key included), with scale 1/sqrt(head_dim) unless
+ * pkv_shape.scale > 0.  q head h reads kv head h / (num_q_heads / num_kv_heads).
+ * LSE outputs are natural-log log-sum-exp of the scaled scores, fp32.
+ *
+ * Conventions for every entry point:
+ *   - all tensor pointers are device pointers owned by the caller, except the h_* arguments
+ *     of pkv_plan_varlen which are host pointers; the library keeps no pointer after return;
+ *   - work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ *     asynchronous; no entry point synchronises the device or allocates device memory;
+ *   - return 0 on success or a negative PKV_E* code; on error nothing was enqueued and
+ *     pkv_last_error() (thread-local) describes the failure;
+ *   - device-resident metadata is trusted: block ids must lie in [0, num_blocks), and the
+ *     device copies must agree with the host copies given to pkv_plan_varlen.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_EINVAL (-1)     /* null pointer, unsupported shape, inconsistent metadata */
+#define PKV_EWORKSPACE (-2) /* workspace too small for the plan */
+#define PKV_EPREFIX (-3)    /* cascade prefix length not a multiple of block_size */
+#define PKV_EHIP (-4)       /* the HIP runtime reported an error (launch or copy) */
+
+#define PKV_DTYPE_BF16 0
+#define PKV_DTYPE_F32 1
+
+/* Static shape of one attention layer's cache.  Supported: head_dim 64 or 128,
+ * block_size 16, num_q_heads / num_kv_heads in {1, 2, 4, 8}. */
+typedef struct pkv_shape {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks; /* physical blocks in each pool */
+  int32_t bt_stride;  /* int32 elements between consecutive block-table rows */
+  float scale;        /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+} pkv_shape;
+
+/* Host-side summary of a varlen plan, filled by pkv_plan_varlen and read by
+ * pkv_paged_attention_varlen.  Plain data; the work list itself lives in the workspace. */
+typedef struct pkv_varlen_plan {
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t num_items;       /* work items (each is launched once per kv head) */
+  int32_t num_prefill_items;
+  int32_t num_decode_items;
+  int32_t num_partials;    /* split-KV partial states per q head */
+  int32_t blocks_per_split;
+  int32_t has_splits;
+  int64_t workspace_used;  /* bytes of the workspace the plan occupies */
+  int32_t head_dim, num_q_heads, num_kv_heads, block_size; /* shape the plan was made for */
+} pkv_varlen_plan;
+
+/* Size in bytes of a workspace that fits any plan with at most these sizes. */
+size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
+                                 const pkv_shape* shape);
+
+/* a1 — slot mapping [Tencent Cloud article, chunked prefill / prefix caching sections, and
+ * "11. vLLM principles" section 11.2]: for token i of request r at position
+ * p = context_lens[r] + i, slot = block_tables[r][p / bs] * bs + p % bs.
+ * Writes slot_mapping[num_tokens] (int64).  A token whose logical block index is
+ * >= bt_stride gets slot -1.  num_tokens == 0 is a no-op. */
+int pkv_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                             const int32_t* query_start_loc, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_tokens, const pkv_shape* shape,
+                             void* stream);
+
+/* a2 — KV caching [2048ai.net vLLM V1 article, "KV Caching"]: copies the bits of k[t] and
+ * v[t] (bf16 [num_tokens, num_kv_heads, head_dim]) into the pools at slot_mapping[t].
+ * Negative slots and slots >= num_blocks * block_size are skipped.  Bit-exact copy. */
+int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                          const int64_t* slot_mapping, int32_t num_tokens,
+                          const pkv_shape* shape, void* stream);
+
+/* Builds the work list of one varlen attention call from host copies of the metadata:
+ * validates seq_lens[r] == context_lens[r] + (qsl[r+1] - qsl[r]) and every length, cuts
+ * query-length-1 rows into split-KV decode items and longer rows into 128-row prefill
+ * tiles, orders them heaviest first, and enqueues a host-to-device copy of the list into
+ * `workspace` on `stream`.  Fills *plan.  The workspace must stay untouched until the
+ * attention call that uses the plan has run. */
+int pkv_plan_varlen(pkv_varlen_plan* plan, void* workspace, size_t workspace_bytes,
+                    const int32_t* h_query_start_loc, const int32_t* h_context_lens,
+                    const int32_t* h_seq_lens, int32_t num_seqs, int32_t num_tokens,
+                    const pkv_shape* shape, void* stream);
+
+/* The same planning into host memory only (no device work): writes up to `max_items`
+ * work items of 8 int32 each {seq, kind (0 decode, 1 prefill), q_begin, q_count,
+ * kv_begin, kv_end, partial_base, split} into `items`.  For inspection and tests. */
+int pkv_plan_varlen_host(pkv_varlen_plan* plan, int32_t* items, int32_t max_items,
+                         const int32_t* h_query_start_loc, const int32_t* h_context_lens,
+                         const int32_t* h_seq_lens, int32_t num_seqs, int32_t num_tokens,
+                         const pkv_shape* shape);
+
+/* a3/a4/a5 — paged attention over a mixed continuous batch [Tencent Cloud article,
+ * continuous batching, chunked prefill and prefix caching sections; "11. vLLM principles"
+ * section 11.3, prefill vs decode]: one kernel launch serves decode rows (one query token;
+ * VALU path with split-KV) and chunked-prefill / prefix-hit rows (MFMA tiles with the causal
+ * mask offset by context_lens), followed by a split-KV reduce when any row was split.
+ * out: [num_tokens, num_q_heads, head_dim], bf16 or fp32 (out_dtype); lse: nullable fp32
+ * [num_tokens, num_q_heads].  The pools must already hold this step's new keys/values
+ * (pkv_reshape_and_cache first).  `plan` must come from pkv_plan_varlen with the same
+ * metadata, shape and workspace. */
+int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* query_start_loc,
+                               const int32_t* context_lens, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_tokens, const pkv_shape* shape,
+                               const pkv_varlen_plan* plan, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for pkv_cascade_prefix_attention with these sizes. */
+size_t pkv_cascade_workspace_size(int32_t num_tokens, int32_t prefix_len, const pkv_shape* shape);
+
+/* a6 — cascade inference, shared-prefix pass [2048ai.net vLLM V1 article, "Cascade
+ * Inference"]: the attention state of every query token over the prefix keys
+ * 0..prefix_len-1 named by prefix_block_table (int32 [prefix_len / block_size]); no mask
+ * (every query lies after the prefix).  Writes out_prefix fp32 [num_tokens, num_q_heads,
+ * head_dim] and lse_prefix fp32 [num_tokens, num_q_heads].  prefix_len must be a positive
+ * multiple of block_size (PKV_EPREFIX otherwise).  The workspace holds per-segment
+ * partial states when the prefix is cut into segments. */
+int pkv_cascade_prefix_attention(float* out_prefix, float* lse_prefix, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* prefix_block_table, int32_t prefix_len,
+                                 int32_t num_tokens, const pkv_shape* shape, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* a8 — merge of two attention states over disjoint key sets [2048ai.net vLLM V1 article,
+ * "Cascade Inference", the associative and commutative merge operator]:
+ * out = (e^lse_a o_a + e^lse_b o_b) / (e^lse_a + e^lse_b), lse_out = ln(e^lse_a + e^lse_b),
+ * computed shifted by max(lse_a, lse_b); (0, -inf) is the identity.  out is bf16 or fp32
+ * [num_tokens, num_heads, head_dim]; lse_out nullable.  head_dim must be a multiple of 4. */
+int pkv_merge_attn_states(void* out, int32_t out_dtype, float* lse_out, const float* out_a,
+                          const float* lse_a, const float* out_b, const float* lse_b,
+                          int32_t num_tokens, int32_t num_heads, int32_t head_dim, void* stream);
+
+/* Thread-local description of the last error returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

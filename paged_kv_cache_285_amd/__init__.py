@@ -1,0 +1,22 @@
+"""Attention over a paged KV cache on AMD MI355X (gfx950): HIP kernels behind a C ABI.
+
+The compute path lives in ``libpkv.so`` (built from ``csrc/`` by ``build.py``); this package
+is its thin Python binding.  Importing it does not load the library; the first call does, and
+raises if the library has not been built.
+"""
+
+from ._lib import PKV_DTYPE_BF16, PKV_DTYPE_F32, PkvError, PkvShape, PkvVarlenPlan, lib  # noqa: F401
+from .ops import (  # noqa: F401
+    alloc_workspace,
+    cascade_prefix_attention,
+    cascade_workspace_size,
+    compute_slot_mapping,
+    make_shape,
+    merge_attn_states,
+    paged_attention_varlen,
+    plan_varlen,
+    plan_varlen_host,
+    reshape_and_cache,
+    varlen_workspace_size,
+    version,
+)

@@ -1,0 +1,542 @@
+// C-ABI front end of libpkv: argument validation, the varlen work plan, and kernel dispatch.
+// Every entry point is declared (with the passage of the pages it follows) in include/pkv.h.
+#include "pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return PKV_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int check_shape(const pkv_shape* s) {
+  if (!s) return fail(PKV_EINVAL, "shape is null");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(PKV_EINVAL, "head_dim %d unsupported (64 or 128)", s->head_dim);
+  if (s->block_size != pkv::kBlockSize)
+    return fail(PKV_EINVAL, "block_size %d unsupported (16)", s->block_size);
+  if (s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->num_q_heads % s->num_kv_heads)
+    return fail(PKV_EINVAL, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                s->num_q_heads, s->num_kv_heads);
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PKV_EINVAL, "q heads per kv head %d unsupported (1, 2, 4, 8)", G);
+  if (s->num_blocks <= 0) return fail(PKV_EINVAL, "num_blocks must be positive");
+  if (s->bt_stride <= 0) return fail(PKV_EINVAL, "bt_stride must be positive");
+  return PKV_OK;
+}
+
+float scale_log2(const pkv_shape* s) {
+  const double sc = s->scale > 0 ? (double)s->scale : 1.0 / std::sqrt((double)s->head_dim);
+  return (float)(sc * 1.4426950408889634);  // log2(e)
+}
+
+// ---------------------------------------------------------------------------------------
+// Workspace layout of a varlen plan.
+// ---------------------------------------------------------------------------------------
+struct VarlenLayout {
+  size_t items_off, split_off, plse_off, po_off, total;
+};
+
+VarlenLayout varlen_layout(int64_t items, int64_t tokens, int64_t partials, int64_t Hq, int64_t D) {
+  VarlenLayout L;
+  L.items_off = 0;
+  L.split_off = align256(L.items_off + (size_t)items * sizeof(pkv::WorkItem));
+  L.plse_off = align256(L.split_off + (size_t)tokens * 2 * sizeof(int32_t));
+  L.po_off = align256(L.plse_off + (size_t)partials * Hq * sizeof(float));
+  L.total = align256(L.po_off + (size_t)partials * Hq * D * sizeof(float));
+  return L;
+}
+
+int decode_target_wgs() {
+  static int v = [] {
+    const char* e = std::getenv("PKV_DECODE_TARGET_WGS");
+    int x = e ? std::atoi(e) : 0;
+    return x > 0 ? x : 8192;
+  }();
+  return v;
+}
+
+struct Plan {
+  std::vector<pkv::WorkItem> items;
+  std::vector<int32_t> token_split;  // per token {partial_base, count}
+  int32_t num_partials = 0;
+  int32_t bps = 0;
+  int32_t n_prefill = 0, n_decode = 0;
+};
+
+int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* seq,
+               int32_t num_seqs, int32_t num_tokens, const pkv_shape* s) {
+  if (num_seqs < 0 || num_tokens < 0) return fail(PKV_EINVAL, "negative num_seqs/num_tokens");
+  if (num_seqs > 0 && (!qsl || !ctx || !seq)) return fail(PKV_EINVAL, "null host metadata");
+  if (num_seqs == 0 && num_tokens != 0) return fail(PKV_EINVAL, "tokens without sequences");
+  if (num_seqs > 0) {
+    if (qsl[0] != 0) return fail(PKV_EINVAL, "query_start_loc[0] must be 0");
+    if (qsl[num_seqs] != num_tokens)
+      return fail(PKV_EINVAL, "query_start_loc[num_seqs]=%d != num_tokens=%d", qsl[num_seqs],
+                  num_tokens);
+  }
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const int tok_per_tile = pkv::kTileRows / G;
+  for (int r = 0; r < num_seqs; ++r) {
+    const int32_t ql = qsl[r + 1] - qsl[r];
+    if (ql < 0) return fail(PKV_EINVAL, "query_start_loc not ascending at %d", r);
+    if (ctx[r] < 0) return fail(PKV_EINVAL, "context_lens[%d] negative", r);
+    if ((int64_t)seq[r] != (int64_t)ctx[r] + ql)
+      return fail(PKV_EINVAL, "seq_lens[%d]=%d != context_lens %d + query len %d", r, seq[r],
+                  ctx[r], ql);
+    if (ceil_div(seq[r], pkv::kBlockSize) > s->bt_stride)
+      return fail(PKV_EINVAL, "seq_lens[%d]=%d needs more than bt_stride=%d blocks", r, seq[r],
+                  s->bt_stride);
+    if (ceil_div(seq[r], pkv::kBlockSize) > s->num_blocks && ql > 0)
+      return fail(PKV_EINVAL, "seq_lens[%d]=%d needs more blocks than the pool has", r, seq[r]);
+  }
+  // Split size for decode rows: the smallest power of two (>= kMinBlocksPerSplit, <= 256
+  // blocks) whose item count times Hkv stays within the target workgroup count.
+  int bps = pkv::kMinBlocksPerSplit;
+  for (; bps < 256; bps *= 2) {
+    int64_t n = 0;
+    for (int r = 0; r < num_seqs; ++r)
+      if (qsl[r + 1] - qsl[r] == 1) n += ceil_div(ceil_div(seq[r], pkv::kBlockSize), bps);
+    if (n * s->num_kv_heads <= decode_target_wgs()) break;
+  }
+  P.bps = bps;
+  P.items.clear();
+  P.token_split.assign((size_t)num_tokens * 2, 0);
+  std::vector<pkv::WorkItem> pre, dec;
+  int32_t partials = 0;
+  for (int r = 0; r < num_seqs; ++r) {
+    const int32_t ql = qsl[r + 1] - qsl[r];
+    if (ql == 0) continue;
+    if (ql == 1) {
+      const int32_t nblk = (int32_t)ceil_div(seq[r], pkv::kBlockSize);
+      const int32_t splits = (int32_t)ceil_div(nblk, bps);
+      const int32_t t = qsl[r];
+      if (splits > 1) {
+        P.token_split[2 * t] = partials;
+        P.token_split[2 * t + 1] = splits;
+      } else {
+        P.token_split[2 * t] = -1;
+        P.token_split[2 * t + 1] = 1;
+      }
+      for (int32_t sidx = 0; sidx < splits; ++sidx) {
+        pkv::WorkItem it;
+        it.seq = r;
+        it.kind = pkv::kDecode;
+        it.q_begin = 0;
+        it.q_count = 1;
+        it.kv_begin = sidx * bps * pkv::kBlockSize;
+        it.kv_end = std::min<int32_t>(seq[r], (sidx + 1) * bps * pkv::kBlockSize);
+        it.partial_base = splits > 1 ? partials : -1;
+        it.split = sidx;
+        dec.push_back(it);
+      }
+      if (splits > 1) partials += splits;
+    } else {
+      const int32_t tiles = (int32_t)ceil_div(ql, tok_per_tile);
+      for (int32_t i = 0; i < tiles; ++i) {
+        pkv::WorkItem it;
+        it.seq = r;
+        it.kind = pkv::kPrefill;
+        it.q_begin = i * tok_per_tile;
+        it.q_count = std::min<int32_t>(tok_per_tile, ql - it.q_begin);
+        it.kv_begin = 0;
+        it.kv_end = std::min<int32_t>(seq[r], ctx[r] + it.q_begin + it.q_count);
+        it.partial_base = -1;
+        it.split = 0;
+        pre.push_back(it);
+      }
+    }
+  }
+  // Heaviest first: prefill tiles by (rows x keys), then decode items by key count.
+  std::stable_sort(pre.begin(), pre.end(), [](const pkv::WorkItem& x, const pkv::WorkItem& y) {
+    return (int64_t)x.q_count * (x.kv_end - x.kv_begin) > (int64_t)y.q_count * (y.kv_end - y.kv_begin);
+  });
+  std::stable_sort(dec.begin(), dec.end(), [](const pkv::WorkItem& x, const pkv::WorkItem& y) {
+    return (x.kv_end - x.kv_begin) > (y.kv_end - y.kv_begin);
+  });
+  P.items = pre;
+  P.items.insert(P.items.end(), dec.begin(), dec.end());
+  P.num_partials = partials;
+  P.n_prefill = (int32_t)pre.size();
+  P.n_decode = (int32_t)dec.size();
+  return PKV_OK;
+}
+
+void fill_plan_struct(pkv_varlen_plan* out, const Plan& P, int32_t num_seqs, int32_t num_tokens,
+                      const pkv_shape* s) {
+  out->num_seqs = num_seqs;
+  out->num_tokens = num_tokens;
+  out->num_items = (int32_t)P.items.size();
+  out->num_prefill_items = P.n_prefill;
+  out->num_decode_items = P.n_decode;
+  out->num_partials = P.num_partials;
+  out->blocks_per_split = P.bps;
+  out->has_splits = P.num_partials > 0;
+  out->head_dim = s->head_dim;
+  out->num_q_heads = s->num_q_heads;
+  out->num_kv_heads = s->num_kv_heads;
+  out->block_size = s->block_size;
+  const VarlenLayout L =
+      varlen_layout(out->num_items, num_tokens, P.num_partials, s->num_q_heads, s->head_dim);
+  out->workspace_used = (int64_t)L.total;
+}
+
+// Pinned host staging for the plan upload: a small ring per device and thread, so a buffer is
+// only refilled after the copy that last read it has completed.
+struct StagingSlot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+struct StagingRing {
+  StagingSlot slot[8];
+  int next = 0;
+};
+thread_local std::unordered_map<int, StagingRing> g_rings;
+
+int stage_and_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return PKV_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  StagingRing& ring = g_rings[dev];
+  StagingSlot& sl = ring.slot[ring.next];
+  ring.next = (ring.next + 1) % 8;
+  if (sl.pending) {
+    e = hipEventSynchronize(sl.ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
+    sl.pending = false;
+  }
+  if (!sl.ev) {
+    e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate(staging)");
+  }
+  if (sl.cap < bytes) {
+    if (sl.host) (void)hipHostFree(sl.host);
+    sl.host = nullptr;
+    sl.cap = 0;
+    const size_t cap = std::max<size_t>(bytes, 64 << 10);
+    e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
+    sl.cap = cap;
+  }
+  std::memcpy(sl.host, src, bytes);
+  e = hipMemcpyAsync(dst, sl.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  e = hipEventRecord(sl.ev, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
+  sl.pending = true;
+  return PKV_OK;
+}
+
+// Cascade segmenting: enough (tile, segment) workgroups to give every CU two, with segments of
+// at least 1024 keys, rounded to whole KV tiles.
+struct CascadeSplit {
+  int32_t tiles, segs, seg_len;
+};
+CascadeSplit cascade_split(int32_t num_tokens, int32_t prefix_len, const pkv_shape* s) {
+  const int G = s->num_q_heads / s->num_kv_heads;
+  CascadeSplit c;
+  c.tiles = (int32_t)ceil_div(num_tokens, pkv::kTileRows / G);
+  const int64_t wgs = std::max<int64_t>(1, (int64_t)c.tiles * s->num_kv_heads);
+  const int64_t want = ceil_div(512, wgs);
+  const int64_t max_segs = std::max<int64_t>(1, prefix_len / 1024);
+  int64_t segs = std::max<int64_t>(1, std::min(want, max_segs));
+  int64_t seg_len = ceil_div(ceil_div(prefix_len, segs), pkv::kKvTile) * pkv::kKvTile;
+  segs = ceil_div(prefix_len, seg_len);
+  c.segs = (int32_t)segs;
+  c.seg_len = (int32_t)seg_len;
+  return c;
+}
+
+size_t cascade_bytes(const CascadeSplit& c, int32_t num_tokens, const pkv_shape* s) {
+  if (c.segs <= 1) return 0;
+  const size_t rows = (size_t)c.segs * num_tokens * s->num_q_heads;
+  return align256(rows * sizeof(float)) + align256(rows * s->head_dim * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_error.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
+
+size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
+                                 const pkv_shape* shape) {
+  if (check_shape(shape) != PKV_OK || num_seqs < 0 || num_tokens < 0 || max_seq_len < 0) return 0;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  const int64_t per_row = ceil_div(ceil_div(max_seq_len, pkv::kBlockSize), pkv::kMinBlocksPerSplit);
+  const int64_t items = ceil_div((int64_t)num_tokens * G, pkv::kTileRows) + num_seqs +
+                        (int64_t)num_seqs * std::max<int64_t>(1, per_row);
+  const int64_t partials = (int64_t)num_seqs * std::max<int64_t>(1, per_row);
+  return varlen_layout(items, num_tokens, partials, shape->num_q_heads, shape->head_dim).total;
+}
+
+int pkv_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                             const int32_t* query_start_loc, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_tokens, const pkv_shape* shape,
+                             void* stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (num_tokens < 0 || num_seqs < 0) return fail(PKV_EINVAL, "negative sizes");
+  if (num_tokens == 0) return ok();
+  if (num_seqs == 0) return fail(PKV_EINVAL, "tokens without sequences");
+  if (!slot_mapping || !block_tables || !query_start_loc || !context_lens)
+    return fail(PKV_EINVAL, "null pointer argument");
+  hipError_t e = pkv::launch_slot_mapping(slot_mapping, block_tables, query_start_loc,
+                                          context_lens, num_seqs, num_tokens, shape->bt_stride,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "slot_mapping launch");
+  return ok();
+}
+
+int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                          const int64_t* slot_mapping, int32_t num_tokens,
+                          const pkv_shape* shape, void* stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (num_tokens < 0) return fail(PKV_EINVAL, "negative num_tokens");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+    return fail(PKV_EINVAL, "null pointer argument");
+  const int64_t num_slots = (int64_t)shape->num_blocks * shape->block_size;
+  hipError_t e = pkv::launch_reshape_and_cache(
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), slot_mapping, num_tokens,
+      shape->num_kv_heads, shape->head_dim, num_slots, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "reshape_and_cache launch");
+  return ok();
+}
+
+int pkv_plan_varlen_host(pkv_varlen_plan* plan, int32_t* items, int32_t max_items,
+                         const int32_t* h_query_start_loc, const int32_t* h_context_lens,
+                         const int32_t* h_seq_lens, int32_t num_seqs, int32_t num_tokens,
+                         const pkv_shape* shape) {
+  if (int rc = check_shape(shape)) return rc;
+  if (!plan) return fail(PKV_EINVAL, "plan is null");
+  Plan P;
+  if (int rc = build_plan(P, h_query_start_loc, h_context_lens, h_seq_lens, num_seqs, num_tokens,
+                          shape))
+    return rc;
+  fill_plan_struct(plan, P, num_seqs, num_tokens, shape);
+  if (items) {
+    if ((int64_t)P.items.size() > max_items)
+      return fail(PKV_EWORKSPACE, "plan has %zu items, buffer holds %d", P.items.size(), max_items);
+    std::memcpy(items, P.items.data(), P.items.size() * sizeof(pkv::WorkItem));
+  }
+  return ok();
+}
+
+int pkv_plan_varlen(pkv_varlen_plan* plan, void* workspace, size_t workspace_bytes,
+                    const int32_t* h_query_start_loc, const int32_t* h_context_lens,
+                    const int32_t* h_seq_lens, int32_t num_seqs, int32_t num_tokens,
+                    const pkv_shape* shape, void* stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (!plan) return fail(PKV_EINVAL, "plan is null");
+  thread_local Plan P;
+  if (int rc = build_plan(P, h_query_start_loc, h_context_lens, h_seq_lens, num_seqs, num_tokens,
+                          shape))
+    return rc;
+  fill_plan_struct(plan, P, num_seqs, num_tokens, shape);
+  if (plan->num_items == 0) return ok();
+  if (!workspace) return fail(PKV_EINVAL, "workspace is null");
+  if ((size_t)plan->workspace_used > workspace_bytes)
+    return fail(PKV_EWORKSPACE, "plan needs %lld workspace bytes, got %zu",
+                (long long)plan->workspace_used, workspace_bytes);
+  const VarlenLayout L =
+      varlen_layout(plan->num_items, num_tokens, P.num_partials, shape->num_q_heads, shape->head_dim);
+  // One upload: the items followed (at split_off) by the per-token split table.
+  thread_local std::vector<char> host;
+  const size_t bytes = P.num_partials > 0 ? L.split_off + P.token_split.size() * sizeof(int32_t)
+                                          : P.items.size() * sizeof(pkv::WorkItem);
+  host.assign(bytes, 0);
+  std::memcpy(host.data(), P.items.data(), P.items.size() * sizeof(pkv::WorkItem));
+  if (P.num_partials > 0)
+    std::memcpy(host.data() + L.split_off, P.token_split.data(),
+                P.token_split.size() * sizeof(int32_t));
+  if (int rc = stage_and_copy(workspace, host.data(), bytes, (hipStream_t)stream)) return rc;
+  return ok();
+}
+
+int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* query_start_loc,
+                               const int32_t* context_lens, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_tokens, const pkv_shape* shape,
+                               const pkv_varlen_plan* plan, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (!plan) return fail(PKV_EINVAL, "plan is null");
+  if (out_dtype != PKV_DTYPE_BF16 && out_dtype != PKV_DTYPE_F32)
+    return fail(PKV_EINVAL, "out_dtype %d unsupported", out_dtype);
+  if (plan->num_seqs != num_seqs || plan->num_tokens != num_tokens ||
+      plan->head_dim != shape->head_dim || plan->num_q_heads != shape->num_q_heads ||
+      plan->num_kv_heads != shape->num_kv_heads)
+    return fail(PKV_EINVAL, "plan was made for different metadata or shape");
+  if (num_tokens == 0 || plan->num_items == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens ||
+      !seq_lens || !workspace)
+    return fail(PKV_EINVAL, "null pointer argument");
+  if ((size_t)plan->workspace_used > workspace_bytes)
+    return fail(PKV_EWORKSPACE, "plan needs %lld workspace bytes, got %zu",
+                (long long)plan->workspace_used, workspace_bytes);
+  const VarlenLayout L = varlen_layout(plan->num_items, num_tokens, plan->num_partials,
+                                       shape->num_q_heads, shape->head_dim);
+  char* ws = static_cast<char*>(workspace);
+  pkv::VarlenArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.query_start_loc = query_start_loc;
+  a.context_lens = context_lens;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.out_f32 = out_dtype == PKV_DTYPE_F32;
+  a.items = reinterpret_cast<const pkv::WorkItem*>(ws + L.items_off);
+  a.num_items = plan->num_items;
+  a.part_o = reinterpret_cast<float*>(ws + L.po_off);
+  a.part_lse = reinterpret_cast<float*>(ws + L.plse_off);
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.bt_stride = shape->bt_stride;
+  a.scale_log2 = scale_log2(shape);
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  hipError_t e = pkv::launch_varlen(a, shape->head_dim, G, plan->num_prefill_items > 0,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "varlen attention launch");
+  if (plan->num_partials > 0) {
+    pkv::ReduceArgs ra;
+    ra.part_o = a.part_o;
+    ra.part_lse = a.part_lse;
+    ra.token_split = reinterpret_cast<const int32_t*>(ws + L.split_off);
+    ra.uniform_count = 0;
+    ra.num_tokens = num_tokens;
+    ra.num_q_heads = shape->num_q_heads;
+    ra.out = out;
+    ra.out_f32 = a.out_f32;
+    ra.lse = lse;
+    e = pkv::launch_reduce(ra, shape->head_dim, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "split-KV reduce launch");
+  }
+  return ok();
+}
+
+size_t pkv_cascade_workspace_size(int32_t num_tokens, int32_t prefix_len, const pkv_shape* shape) {
+  if (check_shape(shape) != PKV_OK || num_tokens < 0 || prefix_len <= 0) return 0;
+  return cascade_bytes(cascade_split(num_tokens, prefix_len, shape), num_tokens, shape);
+}
+
+int pkv_cascade_prefix_attention(float* out_prefix, float* lse_prefix, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* prefix_block_table, int32_t prefix_len,
+                                 int32_t num_tokens, const pkv_shape* shape, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (prefix_len <= 0 || prefix_len % shape->block_size)
+    return fail(PKV_EPREFIX, "prefix_len %d must be a positive multiple of block_size %d",
+                prefix_len, shape->block_size);
+  if (prefix_len / shape->block_size > shape->num_blocks)
+    return fail(PKV_EINVAL, "prefix needs more blocks than the pool has");
+  if (num_tokens < 0) return fail(PKV_EINVAL, "negative num_tokens");
+  if (num_tokens == 0) return ok();
+  if (!out_prefix || !lse_prefix || !q || !k_cache || !v_cache || !prefix_block_table)
+    return fail(PKV_EINVAL, "null pointer argument");
+  const CascadeSplit cs = cascade_split(num_tokens, prefix_len, shape);
+  const size_t need = cascade_bytes(cs, num_tokens, shape);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_EWORKSPACE, "cascade needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  pkv::CascadeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.prefix_bt = prefix_block_table;
+  a.prefix_len = prefix_len;
+  a.num_tokens = num_tokens;
+  a.num_segments = cs.segs;
+  a.seg_len = cs.seg_len;
+  a.num_tiles = cs.tiles;
+  a.out = out_prefix;
+  a.lse = lse_prefix;
+  const size_t rows = (size_t)cs.segs * num_tokens * shape->num_q_heads;
+  a.part_lse = static_cast<float*>(workspace);
+  a.part_o = cs.segs > 1
+                 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)))
+                 : nullptr;
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.scale_log2 = scale_log2(shape);
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  hipError_t e = pkv::launch_cascade(a, shape->head_dim, G, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cascade prefix launch");
+  if (cs.segs > 1) {
+    pkv::ReduceArgs ra;
+    ra.part_o = a.part_o;
+    ra.part_lse = a.part_lse;
+    ra.token_split = nullptr;
+    ra.uniform_count = cs.segs;
+    ra.num_tokens = num_tokens;
+    ra.num_q_heads = shape->num_q_heads;
+    ra.out = out_prefix;
+    ra.out_f32 = 1;
+    ra.lse = lse_prefix;
+    e = pkv::launch_reduce(ra, shape->head_dim, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "cascade segment reduce launch");
+  }
+  return ok();
+}
+
+int pkv_merge_attn_states(void* out, int32_t out_dtype, float* lse_out, const float* out_a,
+                          const float* lse_a, const float* out_b, const float* lse_b,
+                          int32_t num_tokens, int32_t num_heads, int32_t head_dim, void* stream) {
+  if (out_dtype != PKV_DTYPE_BF16 && out_dtype != PKV_DTYPE_F32)
+    return fail(PKV_EINVAL, "out_dtype %d unsupported", out_dtype);
+  if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0 || head_dim % 4)
+    return fail(PKV_EINVAL, "bad sizes (tokens %d, heads %d, head_dim %d)", num_tokens, num_heads,
+                head_dim);
+  if (num_tokens == 0) return ok();
+  if (!out || !out_a || !lse_a || !out_b || !lse_b) return fail(PKV_EINVAL, "null pointer argument");
+  hipError_t e = pkv::launch_merge(out, out_dtype == PKV_DTYPE_F32, lse_out, out_a, lse_a, out_b,
+                                   lse_b, (int64_t)num_tokens * num_heads, head_dim,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
+}  // extern "C"

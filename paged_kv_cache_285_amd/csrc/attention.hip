@@ -1,0 +1,728 @@
+// Attention over a paged KV cache for a mixed continuous batch, on CDNA4 (gfx950).
+//
+// What is computed ["11. vLLM principles", sections 11.2 and 11.3; Tencent Cloud article on
+// vLLM inference acceleration, continuous batching, chunked prefill and prefix caching
+// sections; 2048ai.net vLLM V1 article, "Cascade Inference"]: for token i of request r at
+// position p = context_lens[r] + i and q head h, softmax(scale * q . k_j) over keys
+// j = 0..p of the request, read through its block table, weighting the values v_j.
+//
+// Kernel design (MI355X-first, not a translation of any printed kernel):
+//  * varlen_kernel: one launch serves the whole batch.  The host plan lists work items; each
+//    is run once per kv head (grid = items * Hkv, kv head fastest so that all tiles of one kv
+//    head fall on the same XCD under round-robin dispatch and share its L2).  Each workgroup
+//    branches uniformly on the item kind:
+//      - decode item (query length 1): VALU path.  4 waves stream disjoint 16-token blocks of
+//        the item's key range straight from HBM with 16-byte coalesced loads (one wave load
+//        covers 1 KB of a 4 KB block tile), software-pipelined one block ahead.  All G q heads
+//        of the kv head share every K/V byte.  Q.K uses v_dot2_f32_bf16 on packed bf16 and a
+//        16-lane DPP row reduction; online softmax runs per 16-lane row; P.V is fp32 FMA.
+//        Rows, then waves, are merged with the (o, lse) merge; long rows are cut into
+//        split-KV items whose partial states a small reduce kernel merges.
+//      - prefill tile (query length > 1): 128 packed (token, q head) rows x 64-key tiles on
+//        bf16 MFMA 32x32x16.  S^T = K Q^T puts one query per lane column so the row max and
+//        row sum stay inside a lane (plus one cross-half exchange); O^T = V^T P^T reuses the
+//        S^T accumulator registers as the B operand.  K tiles are staged in LDS row-major,
+//        V tiles transposed, both double-buffered; the causal mask (offset by the cached
+//        length) is only evaluated on tiles that straddle the diagonal or the sequence end.
+//  * cascade_kernel: the shared-prefix pass, the same MFMA tile with no mask over the prefix
+//    block table, optionally cut into key segments whose states are merged afterwards.
+//  * reduce_kernel: merges split-KV / segment partial states into the final output.
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         c, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LANES (8 or 16) lanes; every lane of a group gets the same bits.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror: pairs the two quads of each 8-lane half
+  if constexpr (LANES == 16) x += dpp_f32<0x140>(x);  // row_mirror: pairs the two halves
+  return x;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Merge state (m2, l2, o2) into (m, l, o); m in log2 units of scaled scores.
+template <int N>
+__device__ __forceinline__ void merge_state(float& m, float& l, float (&o)[N], float m2, float l2,
+                                            const float (&o2)[N]) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  const float f1 = fast_exp2(m - mn), f2 = fast_exp2(m2 - mn);
+  l = l * f1 + l2 * f2;
+#pragma unroll
+  for (int e = 0; e < N; ++e) o[e] = o[e] * f1 + o2[e] * f2;
+  m = mn;
+}
+
+// Store 8 consecutive output values of one (token, head) row at element offset `off`.
+__device__ __forceinline__ void store8(void* out, int out_f32, int64_t off, const float (&v)[8]) {
+  if (out_f32) {
+    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + off);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint4 w;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    w.z = pack_bf16x2(v[4], v[5]);
+    w.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + off) = w;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode item: one query token, G q heads sharing kv head g, keys [kv_begin, kv_end).
+// Lane layout: LPT lanes own one token row of a block (8 dims = 16 bytes each); a wave load
+// covers TPL token rows; a 16-token block takes LPB loads per lane for K and LPB for V.
+// ------------------------------------------------------------------------------------------
+template <int D, int G>
+__device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char* smem_raw) {
+  constexpr int LPT = D / 8;
+  constexpr int TPL = 64 / LPT;
+  constexpr int LPB = kBlockSize / TPL;
+  constexpr int CH = D / 8;  // uint4 chunks per token row
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane / LPT;
+  const int c = lane % LPT;
+  const int r = it.seq;
+  const int token = a.query_start_loc[r] + it.q_begin;
+  const int kv_end = it.kv_end;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const float sl = a.scale_log2;
+
+  uint4 qv[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+    qv[hh] = reinterpret_cast<const uint4*>(a.q + ((int64_t)token * Hq + g * G + hh) * D)[c];
+
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+  }
+
+  const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
+  const int b_begin = it.kv_begin / kBlockSize;
+  const int b_end = (kv_end + kBlockSize - 1) / kBlockSize;
+  const int64_t blk_stride = (int64_t)Hkv * kBlockSize * CH;  // uint4 per physical block
+  const uint4* kb = reinterpret_cast<const uint4*>(a.k_cache) + (int64_t)g * kBlockSize * CH;
+  const uint4* vb = reinterpret_cast<const uint4*>(a.v_cache) + (int64_t)g * kBlockSize * CH;
+  const int lane_off = j * CH + c;
+
+  auto load = [&](int b, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
+    const int64_t phys = __builtin_amdgcn_readfirstlane(bt[b]);
+    const uint4* kp = kb + phys * blk_stride + lane_off;
+    const uint4* vp = vb + phys * blk_stride + lane_off;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) kr[i] = kp[i * TPL * CH];
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) vr[i] = vp[i * TPL * CH];
+  };
+
+  auto process = [&](int b, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
+    const int t0 = b * kBlockSize;
+    const bool partial = t0 + kBlockSize > kv_end;  // only the last block can be partial
+    float s[LPB][G];
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float acc = dot2(qv[hh].x, kr[i].x, 0.f);
+        acc = dot2(qv[hh].y, kr[i].y, acc);
+        acc = dot2(qv[hh].z, kr[i].z, acc);
+        acc = dot2(qv[hh].w, kr[i].w, acc);
+        s[i][hh] = group_sum<LPT>(acc) * sl;  // scaled, in log2 units
+      }
+    }
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) {
+        if (t0 + j + TPL * i >= kv_end) {
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) s[i][hh] = -INFINITY;
+          vr[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
+    float vf[LPB][8];
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      vf[i][0] = bf16_lo(vr[i].x);
+      vf[i][1] = bf16_hi(vr[i].x);
+      vf[i][2] = bf16_lo(vr[i].y);
+      vf[i][3] = bf16_hi(vr[i].y);
+      vf[i][4] = bf16_lo(vr[i].z);
+      vf[i][5] = bf16_hi(vr[i].z);
+      vf[i][6] = bf16_lo(vr[i].w);
+      vf[i][7] = bf16_hi(vr[i].w);
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float mx = s[0][hh];
+#pragma unroll
+      for (int i = 1; i < LPB; ++i) mx = fmaxf(mx, s[i][hh]);
+      const float mn = fmaxf(m[hh], mx);
+      const float mref = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(m[hh] - mref);
+      float p[LPB];
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) {
+        p[i] = fast_exp2(s[i][hh] - mref);  // exactly 1 for the running maximum
+        ps += p[i];
+      }
+      l[hh] = l[hh] * alpha + ps;
+      m[hh] = mn;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float acc = o[hh][e] * alpha;
+#pragma unroll
+        for (int i = 0; i < LPB; ++i) acc = fmaf(p[i], vf[i][e], acc);
+        o[hh][e] = acc;
+      }
+    }
+  };
+
+  // Software pipeline: the next block's loads are in flight while the current one computes.
+  int b = b_begin + wave;
+  if (b < b_end) {
+    uint4 ka[LPB], va[LPB], kn[LPB], vn[LPB];
+    load(b, ka, va);
+    while (true) {
+      const int bn = b + 4;
+      if (bn < b_end) load(bn, kn, vn);
+      process(b, ka, va);
+      if (bn >= b_end) break;
+      const int bnn = bn + 4;
+      if (bnn < b_end) load(bnn, ka, va);
+      process(bn, kn, vn);
+      if (bnn >= b_end) break;
+      b = bnn;
+    }
+  }
+
+  // Merge the token rows of the wave (lanes with equal c, different j).
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float m2 = __shfl_xor(m[hh], off);
+      const float l2 = __shfl_xor(l[hh], off);
+      float o2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[hh][e], off);
+      merge_state<8>(m[hh], l[hh], o[hh], m2, l2, o2);
+    }
+  }
+
+  // Merge the 4 waves through LDS.
+  float* s_o = reinterpret_cast<float*>(smem_raw);  // [4][G][D]
+  float* s_m = s_o + 4 * G * D;                     // [4][G]
+  float* s_l = s_m + 4 * G;                         // [4][G]
+  if (j == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float4* dst = reinterpret_cast<float4*>(s_o + (wave * G + hh) * D + c * 8);
+      dst[0] = make_float4(o[hh][0], o[hh][1], o[hh][2], o[hh][3]);
+      dst[1] = make_float4(o[hh][4], o[hh][5], o[hh][6], o[hh][7]);
+      if (c == 0) {
+        s_m[wave * G + hh] = m[hh];
+        s_l[wave * G + hh] = l[hh];
+      }
+    }
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < G * LPT) {
+    const int hh = t / LPT, cc = t % LPT;
+    float mm = -INFINITY, ll = 0.f, oo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oo[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* src = s_o + (w * G + hh) * D + cc * 8;
+      float o2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o2[e] = src[e];
+      merge_state<8>(mm, ll, oo, s_m[w * G + hh], s_l[w * G + hh], o2);
+    }
+    const float inv = (ll > 0.f) ? 1.f / ll : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oo[e] *= inv;
+    const float lse = (ll > 0.f) ? (mm + __log2f(ll)) * kLn2 : -INFINITY;
+    const int head = g * G + hh;
+    if (it.partial_base < 0) {
+      store8(a.out, a.out_f32, ((int64_t)token * Hq + head) * D + cc * 8, oo);
+      if (a.lse && cc == 0) a.lse[(int64_t)token * Hq + head] = lse;
+    } else {
+      const int64_t prow = (int64_t)(it.partial_base + it.split) * Hq + head;
+      store8(a.part_o, 1, prow * D + cc * 8, oo);
+      if (cc == 0) a.part_lse[prow] = lse;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// MFMA tile: 128 packed rows (TOK tokens x G q heads of kv head g) over keys [kv_begin,
+// kv_end).  Wave w owns rows 32w..32w+31; lane (n = lane % 32, h = lane / 32) owns query
+// column n.  Rows beyond ntok tokens are padding (computed, never stored).
+// ------------------------------------------------------------------------------------------
+template <int D>
+struct TileSmem {
+  static constexpr int KP = D + 8;          // K row pitch (bf16): conflict-free 16-byte reads
+  static constexpr int VP = kKvTile + 8;    // V^T row pitch (bf16)
+  static constexpr int K_ELEMS = kKvTile * KP;
+  static constexpr int V_ELEMS = D * VP;
+  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+  static constexpr int BYTES = 2 * BUF_ELEMS * 2;
+};
+
+template <int D, int G, bool CAUSAL>
+__device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t* __restrict__ k_cache,
+                          const uint16_t* __restrict__ v_cache, int Hkv, int g,
+                          const int32_t* __restrict__ bt, int tok0, int ntok, int pos0, int kv_begin,
+                          int kv_end, float sl, void* out, int out_f32, float* lse_out,
+                          char* smem_raw) {
+  using S = TileSmem<D>;
+  constexpr int KSTEPS = D / 16;  // QK^T contraction steps
+  constexpr int DT = D / 32;      // output d tiles
+  constexpr int LPT = D / 8;      // lanes per key row when staging
+  constexpr int KPI = 64 / LPT;   // key rows per wave load
+  constexpr int NI = kBlockSize / KPI;  // loads per lane per block (K and V each)
+  constexpr int CH = D / 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int pr = wave * 32 + n;
+  const int tq = pr / G;
+  const int hh = pr % G;
+  const bool row_valid = tq < ntok;
+  const int qpos = row_valid ? pos0 + tq : 0x7fffffff;
+
+  uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
+
+  // Q^T operand (B of S^T = K Q^T): lane holds dims 16s + 8h .. +7 of its query row.
+  bf16x8 qb[KSTEPS];
+  {
+    const uint4* qrow =
+        reinterpret_cast<const uint4*>(q + ((int64_t)(tok0 + (row_valid ? tq : 0)) * Hq + g * G + hh) * D);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      uint4 v = row_valid ? qrow[2 * s + h] : make_uint4(0u, 0u, 0u, 0u);
+      qb[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  floatx16 oacc[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
+
+  // Staging: wave w loads logical block (tile/16 + w); K rows key = KPI*i + lane/LPT,
+  // V rows key = NI*(lane/LPT) + i (consecutive keys per lane for the transposed write).
+  const int sc = lane % LPT;
+  const int sr = lane / LPT;
+  const int64_t blk_stride = (int64_t)Hkv * kBlockSize * CH;
+  const uint4* kbase = reinterpret_cast<const uint4*>(k_cache) + (int64_t)g * kBlockSize * CH;
+  const uint4* vbase = reinterpret_cast<const uint4*>(v_cache) + (int64_t)g * kBlockSize * CH;
+  uint4 kst[NI], vst[NI];
+
+  auto stage_load = [&](int k0) {
+    const int lb = k0 / kBlockSize + wave;
+    const int key0 = lb * kBlockSize;
+    if (key0 < kv_end) {
+      const int64_t phys = __builtin_amdgcn_readfirstlane(bt[lb]);
+      const uint4* kp = kbase + phys * blk_stride;
+      const uint4* vp = vbase + phys * blk_stride;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int kk = KPI * i + sr;
+        kst[i] = (key0 + kk < kv_end) ? kp[kk * CH + sc] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int kk = NI * sr + i;
+        vst[i] = (key0 + kk < kv_end) ? vp[kk * CH + sc] : make_uint4(0u, 0u, 0u, 0u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        kst[i] = make_uint4(0u, 0u, 0u, 0u);
+        vst[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+
+  auto stage_store = [&](int buf) {
+    uint16_t* ks = smem + buf * S::BUF_ELEMS;
+    uint16_t* vs = ks + S::K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int kk = wave * kBlockSize + KPI * i + sr;
+      *reinterpret_cast<uint4*>(ks + kk * S::KP + sc * 8) = kst[i];
+    }
+    const int kcol = wave * kBlockSize + NI * sr;
+    const uint32_t* w[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) w[i] = reinterpret_cast<const uint32_t*>(&vst[i]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d0 = sc * 8 + 2 * u;
+      if constexpr (NI == 4) {
+        uint2 lo, hi;
+        lo.x = __builtin_amdgcn_perm(w[1][u], w[0][u], 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(w[3][u], w[2][u], 0x05040100u);
+        hi.x = __builtin_amdgcn_perm(w[1][u], w[0][u], 0x07060302u);
+        hi.y = __builtin_amdgcn_perm(w[3][u], w[2][u], 0x07060302u);
+        *reinterpret_cast<uint2*>(vs + d0 * S::VP + kcol) = lo;
+        *reinterpret_cast<uint2*>(vs + (d0 + 1) * S::VP + kcol) = hi;
+      } else {
+        static_assert(NI == 2, "staging layout");
+        *reinterpret_cast<uint32_t*>(vs + d0 * S::VP + kcol) =
+            __builtin_amdgcn_perm(w[1][u], w[0][u], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(vs + (d0 + 1) * S::VP + kcol) =
+            __builtin_amdgcn_perm(w[1][u], w[0][u], 0x07060302u);
+      }
+    }
+  };
+
+  const int ntiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
+  const int min_pos = pos0;  // first token of the tile has the smallest position
+
+  stage_load(kv_begin);
+  stage_store(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = kv_begin + t * kKvTile;
+    const int buf = t & 1;
+    if (t + 1 < ntiles) stage_load(k0 + kKvTile);
+
+    const uint16_t* ks = smem + buf * S::BUF_ELEMS;
+    const uint16_t* vs = ks + S::K_ELEMS;
+
+    // S^T = K Q^T: two 32-key row tiles.
+    floatx16 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(ks + (32 * mt + n) * S::KP + 16 * s + 8 * h);
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sacc[mt], 0, 0, 0);
+      }
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[mt][e] *= sl;  // scaled, in log2 units
+
+    // Mask: only tiles reaching past the first row's position or the sequence end.
+    const bool need_mask = (k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > min_pos);
+    if (need_mask) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+          const bool vis = key < kv_end && (!CAUSAL || key <= qpos);
+          sacc[mt][e] = vis ? sacc[mt][e] : -INFINITY;
+        }
+    }
+
+    // Online softmax for this lane's query column.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float mref = (mn == -INFINITY) ? 0.f : mn;
+    const float alpha = fast_exp2(m - mref);
+    m = mn;
+    float ps = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(sacc[mt][e] - mref);
+        sacc[mt][e] = p;
+        ps += p;
+      }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+
+    // P^T operands: K-step ks covers keys 32*(ks/2) + 8*jj0 + 0..15, jj0 = 2*(ks%2).
+    bf16x8 pb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int mt = ks >> 1, b0 = 8 * (ks & 1);
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (__bf16)sacc[mt][b0 + e];
+      pb[ks] = v;
+    }
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int mt = ks >> 1, jj0 = 2 * (ks & 1);
+        const uint16_t* row = vs + (32 * d + n) * S::VP + 32 * mt + 8 * jj0 + 4 * h;
+        const uint2 x0 = *reinterpret_cast<const uint2*>(row);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(row + 8);
+        const uint4 xv = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv), pb[ks],
+                                                          oacc[d], 0, 0, 0);
+      }
+    }
+
+    if (t + 1 < ntiles) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  lsum += __shfl_xor(lsum, 32);
+  if (!row_valid) return;
+  const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+  const int64_t orow = (int64_t)(tok0 + tq) * Hq + g * G + hh;
+#pragma unroll
+  for (int d = 0; d < DT; ++d) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int dim = 32 * d + 8 * jj + 4 * h;
+      const float v0 = oacc[d][4 * jj] * inv, v1 = oacc[d][4 * jj + 1] * inv;
+      const float v2 = oacc[d][4 * jj + 2] * inv, v3 = oacc[d][4 * jj + 3] * inv;
+      if (out_f32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + orow * D + dim) =
+            make_float4(v0, v1, v2, v3);
+      } else {
+        uint2 w;
+        w.x = pack_bf16x2(v0, v1);
+        w.y = pack_bf16x2(v2, v3);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + orow * D + dim) = w;
+      }
+    }
+  }
+  if (lse_out && h == 0) lse_out[orow] = (lsum > 0.f) ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int x = blockIdx.x;
+  const int g = x % a.num_kv_heads;
+  const WorkItem it = a.items[x / a.num_kv_heads];
+  if (it.kind == kDecode) {
+    decode_item<D, G>(a, it, g, smem);
+  } else {
+    const int r = it.seq;
+    const int ctx = a.context_lens[r];
+    const int tok0 = a.query_start_loc[r] + it.q_begin;
+    const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
+    mfma_tile<D, G, true>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g, bt, tok0,
+                          it.q_count, ctx + it.q_begin, it.kv_begin, it.kv_end, a.scale_log2, a.out,
+                          a.out_f32, a.lse, smem);
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void cascade_kernel(CascadeArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int x = blockIdx.x;
+  const int g = x % a.num_kv_heads;
+  const int rest = x / a.num_kv_heads;
+  const int tile = rest % a.num_tiles;
+  const int seg = rest / a.num_tiles;
+  constexpr int TOK = kTileRows / G;
+  const int tok0 = tile * TOK;
+  const int ntok = min(TOK, a.num_tokens - tok0);
+  const int kv_begin = seg * a.seg_len;
+  const int kv_end = min(a.prefix_len, kv_begin + a.seg_len);
+  float* out = a.out;
+  float* lse = a.lse;
+  if (a.num_segments > 1) {
+    out = a.part_o + (int64_t)seg * a.num_tokens * a.num_q_heads * D;
+    lse = a.part_lse + (int64_t)seg * a.num_tokens * a.num_q_heads;
+  }
+  mfma_tile<D, G, false>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g, a.prefix_bt,
+                         tok0, ntok, 0, kv_begin, kv_end, a.scale_log2, out, 1, lse, smem);
+}
+
+// One wave per (token, head) row; lane holds D/64 consecutive dims.
+template <int D>
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+  constexpr int V = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int Hq = a.num_q_heads;
+  const int64_t token = row / Hq;
+  if (token >= a.num_tokens) return;
+  const int head = (int)(row - token * Hq);
+  int64_t base, stride;
+  int count;
+  if (a.token_split) {
+    base = a.token_split[2 * token];
+    count = a.token_split[2 * token + 1];
+    stride = 1;
+    if (count <= 1) return;  // written directly by the attention kernel
+  } else {
+    base = token;
+    count = a.uniform_count;
+    stride = a.num_tokens;
+  }
+  float mx = -INFINITY;
+  for (int s = 0; s < count; ++s) mx = fmaxf(mx, a.part_lse[(base + s * stride) * Hq + head]);
+  float acc[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = 0.f;
+  float z = 0.f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < count; ++s) {
+      const int64_t prow = (base + s * stride) * Hq + head;
+      const float ls = a.part_lse[prow];
+      const float w = (ls == -INFINITY) ? 0.f : __expf(ls - mx);
+      z += w;
+      const float* src = a.part_o + prow * D + lane * V;
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+    }
+  }
+  const float inv = (z > 0.f) ? 1.f / z : 0.f;
+  const int64_t orow = token * Hq + head;
+  if (a.out_f32) {
+    float* dst = reinterpret_cast<float*>(a.out) + orow * D + lane * V;
+#pragma unroll
+    for (int e = 0; e < V; ++e) dst[e] = acc[e] * inv;
+  } else {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + orow * D + lane * V;
+    if constexpr (V == 1) {
+      const __bf16 b = (__bf16)(acc[0] * inv);
+      dst[0] = __builtin_bit_cast(uint16_t, b);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; e += 2)
+        *reinterpret_cast<uint32_t*>(dst + e) = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
+    }
+  }
+  if (a.lse && lane == 0) a.lse[orow] = (z > 0.f) ? mx + __logf(z) : -INFINITY;
+}
+
+template <int D, int G>
+size_t varlen_smem(bool has_prefill) {
+  const size_t dec = (size_t)4 * G * (D + 2) * sizeof(float);
+  const size_t pre = has_prefill ? (size_t)TileSmem<D>::BYTES : 0;
+  return dec > pre ? dec : pre;
+}
+
+template <int D, int G>
+hipError_t launch_varlen_t(const VarlenArgs& a, bool has_prefill, hipStream_t stream) {
+  const size_t smem = varlen_smem<D, G>(has_prefill);
+  const int64_t grid = (int64_t)a.num_items * a.num_kv_heads;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((varlen_kernel<D, G>), dim3((unsigned)grid), dim3(kThreads), smem, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.num_tiles * a.num_segments * a.num_kv_heads;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((cascade_kernel<D, G>), dim3((unsigned)grid), dim3(kThreads),
+                     (size_t)TileSmem<D>::BYTES, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+#define PKV_DISPATCH_DG(D_, G_, CALL)                 \
+  switch (D_) {                                       \
+    case 64:                                          \
+      switch (G_) {                                   \
+        case 1: return CALL(64, 1);                   \
+        case 2: return CALL(64, 2);                   \
+        case 4: return CALL(64, 4);                   \
+        case 8: return CALL(64, 8);                   \
+      }                                               \
+      break;                                          \
+    case 128:                                         \
+      switch (G_) {                                   \
+        case 1: return CALL(128, 1);                  \
+        case 2: return CALL(128, 2);                  \
+        case 4: return CALL(128, 4);                  \
+        case 8: return CALL(128, 8);                  \
+      }                                               \
+      break;                                          \
+  }                                                   \
+  return hipErrorInvalidValue;
+
+hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, bool has_prefill,
+                         hipStream_t stream) {
+#define CALL_V(D, G) launch_varlen_t<D, G>(a, has_prefill, stream)
+  PKV_DISPATCH_DG(head_dim, group, CALL_V)
+#undef CALL_V
+}
+
+hipError_t launch_cascade(const CascadeArgs& a, int head_dim, int group, hipStream_t stream) {
+#define CALL_C(D, G) launch_cascade_t<D, G>(a, stream)
+  PKV_DISPATCH_DG(head_dim, group, CALL_C)
+#undef CALL_C
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.num_tokens * a.num_q_heads;
+  if (rows == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((rows + 3) / 4);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(reduce_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL(reduce_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pkv

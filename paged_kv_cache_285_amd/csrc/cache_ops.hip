@@ -1,0 +1,90 @@
+// Slot mapping and the paged cache write.
+//
+// Paging ["11. vLLM principles", section 11.2 PagedAttention]: the cache is cut into blocks of
+// 16 tokens; a request's block table maps logical block p / 16 to a physical block anywhere in
+// the pool.  New tokens follow the cached ones [Tencent Cloud article on vLLM inference
+// acceleration, chunked prefill and prefix caching sections], so token i of request r is at
+// position context_lens[r] + i.  KV caching [2048ai.net vLLM V1 article, "KV Caching"] stores
+// each new token's K and V at its slot.
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+// One thread per new token.  The owning request is found by binary search over
+// query_start_loc (num_seqs + 1 ascending entries).
+__global__ void slot_mapping_kernel(int64_t* __restrict__ slots, const int32_t* __restrict__ bt,
+                                    const int32_t* __restrict__ qsl,
+                                    const int32_t* __restrict__ ctx, int32_t num_seqs,
+                                    int32_t num_tokens, int32_t bt_stride) {
+  const int32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= num_tokens) return;
+  int32_t lo = 0, hi = num_seqs - 1;  // largest r with qsl[r] <= t
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int32_t r = lo;
+  const int32_t pos = ctx[r] + (t - qsl[r]);
+  const int32_t logical = pos / kBlockSize;
+  if (pos < 0 || logical >= bt_stride) {
+    slots[t] = -1;
+    return;
+  }
+  const int64_t phys = bt[(int64_t)r * bt_stride + logical];
+  slots[t] = phys * kBlockSize + (pos % kBlockSize);
+}
+
+// One thread per 16-byte chunk (8 bf16) of one token's K and V for one kv head.
+// Pools are [num_blocks, Hkv, 16, D]; a slot names (block, offset).
+__global__ void reshape_and_cache_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
+                                         uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                         const int64_t* __restrict__ slots, int32_t num_tokens,
+                                         int32_t num_kv_heads, int32_t chunks_per_head,
+                                         int64_t num_slots) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)num_kv_heads * chunks_per_head;
+  const int64_t t = gid / per_token;
+  if (t >= num_tokens) return;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t within = gid - t * per_token;
+  const int64_t h = within / chunks_per_head;
+  const int64_t c = within - h * chunks_per_head;
+  const int64_t blk = slot / kBlockSize;
+  const int64_t off = slot - blk * kBlockSize;
+  const int64_t dst = ((blk * num_kv_heads + h) * kBlockSize + off) * chunks_per_head + c;
+  k_cache[dst] = k[gid];
+  v_cache[dst] = v[gid];
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                               const int32_t* qsl, const int32_t* ctx, int32_t num_seqs,
+                               int32_t num_tokens, int32_t bt_stride, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int threads = 256;
+  const int blocks = (num_tokens + threads - 1) / threads;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(blocks), dim3(threads), 0, stream, slot_mapping,
+                     block_tables, qsl, ctx, num_seqs, num_tokens, bt_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v, uint16_t* k_cache,
+                                    uint16_t* v_cache, const int64_t* slots, int32_t num_tokens,
+                                    int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
+                                    hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int32_t chunks = head_dim / 8;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
+                     reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache), slots,
+                     num_tokens, num_kv_heads, chunks, num_slots);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

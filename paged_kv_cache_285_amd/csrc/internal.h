@@ -1,0 +1,100 @@
+// Internal declarations shared by the host front end (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlockSize = 16;       // tokens per cache block (the only supported size)
+constexpr int kTileRows = 128;       // packed (token, q head) rows per MFMA attention tile
+constexpr int kKvTile = 64;          // keys per MFMA KV tile (4 cache blocks)
+constexpr int kThreads = 256;        // threads per attention workgroup (4 waves)
+constexpr int kMinBlocksPerSplit = 16;
+
+enum ItemKind : int32_t { kDecode = 0, kPrefill = 1 };
+
+// One unit of work of the varlen kernel; it is run once per kv head.
+struct WorkItem {
+  int32_t seq;           // request index
+  int32_t kind;          // ItemKind
+  int32_t q_begin;       // first query token of the tile, relative to the request
+  int32_t q_count;       // query tokens in the tile
+  int32_t kv_begin;      // first key (token index) of this item
+  int32_t kv_end;        // one past the last key
+  int32_t partial_base;  // decode: partial row base of the request (-1: write the output)
+  int32_t split;         // decode: split index within the request
+};
+static_assert(sizeof(WorkItem) == 32, "work item layout");
+
+struct VarlenArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* query_start_loc;
+  const int32_t* context_lens;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  int32_t out_f32;
+  const WorkItem* items;
+  int32_t num_items;
+  float* part_o;    // [num_partials * Hq, D]
+  float* part_lse;  // [num_partials * Hq]
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t bt_stride;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+struct CascadeArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* prefix_bt;
+  int32_t prefix_len;
+  int32_t num_tokens;
+  int32_t num_segments;
+  int32_t seg_len;     // keys per segment (multiple of the KV tile)
+  int32_t num_tiles;   // query tiles per kv head
+  float* out;          // final fp32 output when num_segments == 1
+  float* lse;
+  float* part_o;       // [num_segments, T, Hq, D] when num_segments > 1
+  float* part_lse;     // [num_segments, T, Hq]
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  float scale_log2;
+};
+
+// Split-KV reduce: row (token, head) merges `count` partial states.
+struct ReduceArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* token_split;  // per token {partial_base, count}; nullptr: uniform layout
+  int32_t uniform_count;       // uniform layout: partial row of split s = (s * T + token)
+  int32_t num_tokens;
+  int32_t num_q_heads;
+  void* out;
+  int32_t out_f32;
+  float* lse;
+};
+
+// Launchers (defined in the .hip files); return the hipError_t of the launch.
+hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                               const int32_t* qsl, const int32_t* ctx, int32_t num_seqs,
+                               int32_t num_tokens, int32_t bt_stride, hipStream_t stream);
+hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v, uint16_t* k_cache,
+                                    uint16_t* v_cache, const int64_t* slots, int32_t num_tokens,
+                                    int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
+                                    hipStream_t stream);
+hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, bool has_prefill,
+                         hipStream_t stream);
+hipError_t launch_cascade(const CascadeArgs& a, int head_dim, int group, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_merge(void* out, int32_t out_f32, float* lse_out, const float* oa,
+                        const float* la, const float* ob, const float* lb, int64_t rows,
+                        int32_t head_dim, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,288 @@
+"""Python face of libpkv: one function per C entry point, same names, torch tensors in and out.
+
+Only argument marshalling happens here (dtype/device/contiguity checks, pointer extraction,
+the current HIP stream).  Every step of the attention path runs in the HIP kernels of
+libpkv.so.  bf16 tensors may be passed as torch.bfloat16 or as raw 16-bit views.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+from ._lib import PKV_DTYPE_BF16, PKV_DTYPE_F32, PkvShape, PkvVarlenPlan, check, lib
+
+_16BIT = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def make_shape(
+    num_q_heads: int,
+    num_kv_heads: int,
+    head_dim: int,
+    num_blocks: int,
+    bt_stride: int,
+    block_size: int = 16,
+    scale: float = 0.0,
+) -> PkvShape:
+    return PkvShape(num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, bt_stride, scale)
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes=None) -> ctypes.c_void_p:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt(t: Optional[torch.Tensor], name: str, dtypes=None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0) if t is None else _dev(t, name, dtypes)
+
+
+def _host_i32(x, name: str) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(x), dtype=np.int32)
+    if a.ndim != 1:
+        raise ValueError(f"{name} must be one-dimensional")
+    return a
+
+
+def version() -> str:
+    return lib().pkv_version().decode()
+
+
+def compute_slot_mapping(
+    block_tables: torch.Tensor,
+    query_start_loc: torch.Tensor,
+    context_lens: torch.Tensor,
+    shape: PkvShape,
+    num_tokens: int,
+    out: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """Slot of every new token (int64 [num_tokens]) from the block tables."""
+    num_seqs = int(context_lens.numel())
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int64, device=block_tables.device)
+    check(
+        lib().pkv_compute_slot_mapping(
+            _dev(out, "slot_mapping", (torch.int64,)),
+            _dev(block_tables, "block_tables", (torch.int32,)),
+            _dev(query_start_loc, "query_start_loc", (torch.int32,)),
+            _dev(context_lens, "context_lens", (torch.int32,)),
+            num_seqs,
+            num_tokens,
+            ctypes.byref(shape),
+            _stream(),
+        )
+    )
+    return out
+
+
+def reshape_and_cache(
+    k: torch.Tensor,
+    v: torch.Tensor,
+    k_cache: torch.Tensor,
+    v_cache: torch.Tensor,
+    slot_mapping: torch.Tensor,
+    shape: PkvShape,
+) -> None:
+    """Write the new tokens' K/V bits into the paged pools at their slots (in place)."""
+    num_tokens = int(k.shape[0])
+    check(
+        lib().pkv_reshape_and_cache(
+            _dev(k, "k", _16BIT),
+            _dev(v, "v", _16BIT),
+            _dev(k_cache, "k_cache", _16BIT),
+            _dev(v_cache, "v_cache", _16BIT),
+            _dev(slot_mapping, "slot_mapping", (torch.int64,)),
+            num_tokens,
+            ctypes.byref(shape),
+            _stream(),
+        )
+    )
+
+
+def varlen_workspace_size(num_seqs: int, num_tokens: int, max_seq_len: int, shape: PkvShape) -> int:
+    return int(lib().pkv_varlen_workspace_size(num_seqs, num_tokens, max_seq_len, ctypes.byref(shape)))
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def plan_varlen(
+    workspace: torch.Tensor,
+    query_start_loc,
+    context_lens,
+    seq_lens,
+    shape: PkvShape,
+) -> PkvVarlenPlan:
+    """Build the work list from host copies of the metadata and upload it into ``workspace``."""
+    qsl = _host_i32(query_start_loc, "query_start_loc")
+    ctx = _host_i32(context_lens, "context_lens")
+    sl = _host_i32(seq_lens, "seq_lens")
+    plan = PkvVarlenPlan()
+    check(
+        lib().pkv_plan_varlen(
+            ctypes.byref(plan),
+            _dev(workspace, "workspace", (torch.uint8,)),
+            workspace.numel(),
+            qsl.ctypes.data_as(ctypes.c_void_p),
+            ctx.ctypes.data_as(ctypes.c_void_p),
+            sl.ctypes.data_as(ctypes.c_void_p),
+            int(ctx.shape[0]),
+            int(qsl[-1]) if qsl.size else 0,
+            ctypes.byref(shape),
+            _stream(),
+        )
+    )
+    return plan
+
+
+def plan_varlen_host(query_start_loc, context_lens, seq_lens, shape: PkvShape) -> Tuple[PkvVarlenPlan, np.ndarray]:
+    """Host-only planning (no device work): the plan summary and the work items [n, 8] int32."""
+    qsl = _host_i32(query_start_loc, "query_start_loc")
+    ctx = _host_i32(context_lens, "context_lens")
+    sl = _host_i32(seq_lens, "seq_lens")
+    plan = PkvVarlenPlan()
+    args = (
+        qsl.ctypes.data_as(ctypes.c_void_p),
+        ctx.ctypes.data_as(ctypes.c_void_p),
+        sl.ctypes.data_as(ctypes.c_void_p),
+        int(ctx.shape[0]),
+        int(qsl[-1]) if qsl.size else 0,
+        ctypes.byref(shape),
+    )
+    check(lib().pkv_plan_varlen_host(ctypes.byref(plan), None, 0, *args))
+    items = np.zeros((max(plan.num_items, 1), 8), dtype=np.int32)
+    check(lib().pkv_plan_varlen_host(ctypes.byref(plan), items.ctypes.data_as(ctypes.c_void_p), items.shape[0], *args))
+    return plan, items[: plan.num_items]
+
+
+def paged_attention_varlen(
+    q: torch.Tensor,
+    k_cache: torch.Tensor,
+    v_cache: torch.Tensor,
+    block_tables: torch.Tensor,
+    query_start_loc: torch.Tensor,
+    context_lens: torch.Tensor,
+    seq_lens: torch.Tensor,
+    shape: PkvShape,
+    plan: PkvVarlenPlan,
+    workspace: torch.Tensor,
+    out: Optional[torch.Tensor] = None,
+    out_dtype: torch.dtype = torch.bfloat16,
+    lse: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """Attention of every new token over its paged keys for a mixed decode/prefill batch."""
+    num_tokens = int(q.shape[0])
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    code = PKV_DTYPE_F32 if out.dtype == torch.float32 else PKV_DTYPE_BF16
+    check(
+        lib().pkv_paged_attention_varlen(
+            _dev(out, "out", _16BIT + (torch.float32,)),
+            code,
+            _opt(lse, "lse", (torch.float32,)),
+            _dev(q, "q", _16BIT),
+            _dev(k_cache, "k_cache", _16BIT),
+            _dev(v_cache, "v_cache", _16BIT),
+            _dev(block_tables, "block_tables", (torch.int32,)),
+            _dev(query_start_loc, "query_start_loc", (torch.int32,)),
+            _dev(context_lens, "context_lens", (torch.int32,)),
+            _dev(seq_lens, "seq_lens", (torch.int32,)),
+            int(context_lens.numel()),
+            num_tokens,
+            ctypes.byref(shape),
+            ctypes.byref(plan),
+            _dev(workspace, "workspace", (torch.uint8,)),
+            workspace.numel(),
+            _stream(),
+        )
+    )
+    return out
+
+
+def cascade_workspace_size(num_tokens: int, prefix_len: int, shape: PkvShape) -> int:
+    return int(lib().pkv_cascade_workspace_size(num_tokens, prefix_len, ctypes.byref(shape)))
+
+
+def cascade_prefix_attention(
+    q: torch.Tensor,
+    k_cache: torch.Tensor,
+    v_cache: torch.Tensor,
+    prefix_block_table: torch.Tensor,
+    prefix_len: int,
+    shape: PkvShape,
+    workspace: Optional[torch.Tensor] = None,
+    out: Optional[torch.Tensor] = None,
+    lse: Optional[torch.Tensor] = None,
+) -> Tuple[torch.Tensor, torch.Tensor]:
+    """State (fp32 output, LSE) of every query over the shared prefix keys."""
+    T, Hq = int(q.shape[0]), int(q.shape[1])
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    ws = workspace
+    check(
+        lib().pkv_cascade_prefix_attention(
+            _dev(out, "out_prefix", (torch.float32,)),
+            _dev(lse, "lse_prefix", (torch.float32,)),
+            _dev(q, "q", _16BIT),
+            _dev(k_cache, "k_cache", _16BIT),
+            _dev(v_cache, "v_cache", _16BIT),
+            _dev(prefix_block_table, "prefix_block_table", (torch.int32,)),
+            int(prefix_len),
+            T,
+            ctypes.byref(shape),
+            _opt(ws, "workspace", (torch.uint8,)),
+            0 if ws is None else ws.numel(),
+            _stream(),
+        )
+    )
+    return out, lse
+
+
+def merge_attn_states(
+    out_a: torch.Tensor,
+    lse_a: torch.Tensor,
+    out_b: torch.Tensor,
+    lse_b: torch.Tensor,
+    out: Optional[torch.Tensor] = None,
+    out_dtype: torch.dtype = torch.bfloat16,
+    lse_out: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """Merge two attention states over disjoint key sets into the state of their union."""
+    T, H, D = (int(x) for x in out_a.shape)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=out_dtype, device=out_a.device)
+    code = PKV_DTYPE_F32 if out.dtype == torch.float32 else PKV_DTYPE_BF16
+    check(
+        lib().pkv_merge_attn_states(
+            _dev(out, "out", _16BIT + (torch.float32,)),
+            code,
+            _opt(lse_out, "lse_out", (torch.float32,)),
+            _dev(out_a, "out_a", (torch.float32,)),
+            _dev(lse_a, "lse_a", (torch.float32,)),
+            _dev(out_b, "out_b", (torch.float32,)),
+            _dev(lse_b, "lse_b", (torch.float32,)),
+            T,
+            H,
+            D,
+            _stream(),
+        )
+    )
+    return out
