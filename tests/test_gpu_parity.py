@@ -68,10 +68,11 @@ def run_and_check(wl, rows_per_step=None, check_pools=True, want_lse=True, out_d
         )
         o_gpu = bf16_out_to_f64(out_g)
         sel = slice(None) if rows is None else rows
-        stats.append(check_attention(o_gpu[sel], o_ref[sel], f"{wl.name} step {si}", bf16_out=out_dtype != torch.float32))
+        r = check_attention(o_gpu[sel], o_ref[sel], f"{wl.name} step {si}", bf16_out=out_dtype != torch.float32)
         if want_lse:
-            stats.append({"lse": check_lse(lse_g.cpu().numpy()[sel], l_ref[sel], f"{wl.name} step {si} lse")})
-        say(f"    plan items={plan.num_items} partials={plan.num_partials} bps={plan.blocks_per_split} {stats[-2]}")
+            r["lse_max_abs"] = check_lse(lse_g.cpu().numpy()[sel], l_ref[sel], f"{wl.name} step {si} lse")
+        stats.append(r)
+        say(f"    plan items={plan.num_items} partials={plan.num_partials} bps={plan.blocks_per_split} {r}")
     return stats
 
 
