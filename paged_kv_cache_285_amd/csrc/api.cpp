@@ -81,13 +81,11 @@ VarlenLayout varlen_layout(int64_t items, int64_t tokens, int64_t partials, int6
   return L;
 }
 
+// Workgroups the decode split size aims for; PKV_DECODE_TARGET_WGS overrides it (tuning).
 int decode_target_wgs() {
-  static int v = [] {
-    const char* e = std::getenv("PKV_DECODE_TARGET_WGS");
-    int x = e ? std::atoi(e) : 0;
-    return x > 0 ? x : 8192;
-  }();
-  return v;
+  const char* e = std::getenv("PKV_DECODE_TARGET_WGS");
+  const int x = e ? std::atoi(e) : 0;
+  return x > 0 ? x : 2048;
 }
 
 struct Plan {
@@ -125,7 +123,8 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
       return fail(PKV_EINVAL, "seq_lens[%d]=%d needs more blocks than the pool has", r, seq[r]);
   }
   // Split size for decode rows: the smallest power of two (>= kMinBlocksPerSplit, <= 256
-  // blocks) whose item count times Hkv stays within the target workgroup count.
+  // blocks, i.e. at most 64 per wave, which the decode kernel relies on) whose item count
+  // times Hkv stays within the target workgroup count.
   int bps = pkv::kMinBlocksPerSplit;
   for (; bps < 256; bps *= 2) {
     int64_t n = 0;

@@ -39,6 +39,14 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Waves per SIMD the decode-only kernel is register-budgeted for (by q heads per kv head).
+#ifndef PKV_DECODE_WAVES_G8
+#define PKV_DECODE_WAVES_G8 2
+#endif
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 3
+#endif
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
@@ -111,7 +119,7 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   constexpr int LPB = kBlockSize / TPL;
   constexpr int CH = D / 8;  // uint4 chunks per token row
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int j = lane / LPT;
   const int c = lane % LPT;
   const int r = it.seq;
@@ -142,8 +150,15 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   const uint4* vb = reinterpret_cast<const uint4*>(a.v_cache) + (int64_t)g * kBlockSize * CH;
   const int lane_off = j * CH + c;
 
-  auto load = [&](int b, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
-    const int64_t phys = __builtin_amdgcn_readfirstlane(bt[b]);
+  // This wave takes blocks b_begin + wave + 4k, k < nk (nk <= 64 since a split has at most
+  // 256 blocks).  Their physical ids are fetched once, one per lane, and read back with
+  // v_readlane so the block loop issues no dependent table loads.
+  const int nb = b_end - b_begin;
+  const int nk = nb > wave ? (nb - wave + 3) / 4 : 0;
+  const int my_id = lane < nk ? bt[b_begin + wave + 4 * lane] : 0;
+
+  auto load = [&](int k, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
+    const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
     const uint4* kp = kb + phys * blk_stride + lane_off;
     const uint4* vp = vb + phys * blk_stride + lane_off;
 #pragma unroll
@@ -152,8 +167,8 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
     for (int i = 0; i < LPB; ++i) vr[i] = vp[i * TPL * CH];
   };
 
-  auto process = [&](int b, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
-    const int t0 = b * kBlockSize;
+  auto process = [&](int k, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
+    const int t0 = (b_begin + wave + 4 * k) * kBlockSize;
     const bool partial = t0 + kBlockSize > kv_end;  // only the last block can be partial
     float s[LPB][G];
 #pragma unroll
@@ -177,18 +192,6 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
         }
       }
     }
-    float vf[LPB][8];
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) {
-      vf[i][0] = bf16_lo(vr[i].x);
-      vf[i][1] = bf16_hi(vr[i].x);
-      vf[i][2] = bf16_lo(vr[i].y);
-      vf[i][3] = bf16_hi(vr[i].y);
-      vf[i][4] = bf16_lo(vr[i].z);
-      vf[i][5] = bf16_hi(vr[i].z);
-      vf[i][6] = bf16_lo(vr[i].w);
-      vf[i][7] = bf16_hi(vr[i].w);
-    }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       float mx = s[0][hh];
@@ -197,40 +200,55 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
       const float mn = fmaxf(m[hh], mx);
       const float mref = (mn == -INFINITY) ? 0.f : mn;
       const float alpha = fast_exp2(m[hh] - mref);
-      float p[LPB];
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < LPB; ++i) {
-        p[i] = fast_exp2(s[i][hh] - mref);  // exactly 1 for the running maximum
-        ps += p[i];
+        s[i][hh] = fast_exp2(s[i][hh] - mref);  // now p; exactly 1 for the running maximum
+        ps += s[i][hh];
       }
       l[hh] = l[hh] * alpha + ps;
       m[hh] = mn;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float acc = o[hh][e] * alpha;
+      for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
+    }
+    // P.V one token row at a time, converting each bf16 value once for all G heads.
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) acc = fmaf(p[i], vf[i][e], acc);
-        o[hh][e] = acc;
-      }
+    for (int i = 0; i < LPB; ++i) {
+      float v[8];
+      v[0] = bf16_lo(vr[i].x);
+      v[1] = bf16_hi(vr[i].x);
+      v[2] = bf16_lo(vr[i].y);
+      v[3] = bf16_hi(vr[i].y);
+      v[4] = bf16_lo(vr[i].z);
+      v[5] = bf16_hi(vr[i].z);
+      v[6] = bf16_lo(vr[i].w);
+      v[7] = bf16_hi(vr[i].w);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(s[i][hh], v[e], o[hh][e]);
     }
   };
 
   // Software pipeline: the next block's loads are in flight while the current one computes.
-  int b = b_begin + wave;
-  if (b < b_end) {
+  // The steady-state loads are unconditional so the compiler's wait counts only ever wait
+  // for the block about to be used (a conditional load would make it wait for both).
+  if (nk > 0) {
     uint4 ka[LPB], va[LPB], kn[LPB], vn[LPB];
-    load(b, ka, va);
-    while (true) {
-      const int bn = b + 4;
-      if (bn < b_end) load(bn, kn, vn);
-      process(b, ka, va);
-      if (bn >= b_end) break;
-      const int bnn = bn + 4;
-      if (bnn < b_end) load(bnn, ka, va);
-      process(bn, kn, vn);
-      if (bnn >= b_end) break;
-      b = bnn;
+    load(0, ka, va);
+    int k = 0;
+    for (; k + 2 < nk; k += 2) {
+      load(k + 1, kn, vn);
+      process(k, ka, va);
+      load(k + 2, ka, va);
+      process(k + 1, kn, vn);
+    }
+    if (k + 1 < nk) {
+      load(k + 1, kn, vn);
+      process(k, ka, va);
+      process(k + 1, kn, vn);
+    } else {
+      process(k, ka, va);
     }
   }
 
@@ -324,7 +342,7 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
   constexpr int NI = kBlockSize / KPI;  // loads per lane per block (K and V each)
   constexpr int CH = D / 8;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 31;
   const int h = lane >> 5;
   const int pr = wave * 32 + n;
@@ -550,13 +568,17 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
   if (lse_out && h == 0) lse_out[orow] = (lsum > 0.f) ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
+// DECODE_ONLY instantiations carry no MFMA path, so they need far fewer registers and run
+// more waves per SIMD; a plan with any prefill tile uses the full kernel.
+template <int D, int G, bool DECODE_ONLY>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(DECODE_ONLY ? (G >= 8 ? PKV_DECODE_WAVES_G8 : PKV_DECODE_WAVES) : 2)))
+void varlen_kernel(VarlenArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int x = blockIdx.x;
   const int g = x % a.num_kv_heads;
   const WorkItem it = a.items[x / a.num_kv_heads];
-  if (it.kind == kDecode) {
+  if (DECODE_ONLY || it.kind == kDecode) {
     decode_item<D, G>(a, it, g, smem);
   } else {
     const int r = it.seq;
@@ -570,7 +592,8 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void cascade_kernel(CascadeArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
+void cascade_kernel(CascadeArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int x = blockIdx.x;
   const int g = x % a.num_kv_heads;
@@ -663,7 +686,10 @@ hipError_t launch_varlen_t(const VarlenArgs& a, bool has_prefill, hipStream_t st
   const size_t smem = varlen_smem<D, G>(has_prefill);
   const int64_t grid = (int64_t)a.num_items * a.num_kv_heads;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((varlen_kernel<D, G>), dim3((unsigned)grid), dim3(kThreads), smem, stream, a);
+  if (has_prefill)
+    hipLaunchKernelGGL((varlen_kernel<D, G, false>), dim3((unsigned)grid), dim3(kThreads), smem, stream, a);
+  else
+    hipLaunchKernelGGL((varlen_kernel<D, G, true>), dim3((unsigned)grid), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
 }
 
