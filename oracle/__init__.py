@@ -16,7 +16,8 @@ from .paged_attention import (  # noqa: F401
     cascade_prefix_attention,
     causal_visible,
     default_scale,
-    gather_kv,
+    gather_keys,
+    gather_values,
     merge_attn_states,
     paged_attention,
     reshape_and_cache,

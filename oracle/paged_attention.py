@@ -29,8 +29,9 @@ on purpose so that it can be checked against the pages by eye:
   commutative merge of (output, log-sum-exp) states.
 
 Readings where the pages are silent (each one is listed in the design doc):
-softmax scale 1/sqrt(head_dim); q head h reads kv head h // (Hq/Hkv); pools
-laid out [num_blocks, Hkv, block_size, head_dim]; a new token at position
+softmax scale 1/sqrt(head_dim); q head h reads kv head h // (Hq/Hkv); the key
+pool is laid out [num_blocks, Hkv, block_size, head_dim] (token-major) and the
+value pool [num_blocks, Hkv, head_dim, block_size] (dim-major); a new token at position
 p = context_len + i sees keys 0..p (its own key included, written to the
 cache before attention); LSE is the natural log of the scaled scores; an
 empty key set has state (o = 0, lse = -inf); slot = -1 means "do not write".
@@ -86,7 +87,9 @@ def slot_mapping(block_tables, query_start_loc, context_lens, block_size: int) -
 def reshape_and_cache(k, v, k_cache, v_cache, slots, block_size: int) -> Tuple[np.ndarray, np.ndarray]:
     """Return copies of the pools with token t's K/V stored at its slot (bitwise; slot < 0 skipped).
 
-    Pools are [num_blocks, Hkv, block_size, D]; a slot names (block, offset).
+    A slot names (block, offset).  The key pool is [num_blocks, Hkv, block_size, D]
+    (token t's key is one row); the value pool is [num_blocks, Hkv, D, block_size]
+    (token t's value is one column).
     """
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
@@ -94,20 +97,25 @@ def reshape_and_cache(k, v, k_cache, v_cache, slots, block_size: int) -> Tuple[n
         if s < 0:
             continue
         kc[s // block_size, :, s % block_size, :] = k[t]
-        vc[s // block_size, :, s % block_size, :] = v[t]
+        vc[s // block_size, :, :, s % block_size] = v[t]
     return kc, vc
 
 
 # ---------------------------------------------------------------------------
 # Gathering keys/values through a block table.
 # ---------------------------------------------------------------------------
-def gather_kv(cache, block_table_row, num_keys: int, kv_head: int, block_size: int) -> np.ndarray:
-    """Keys (or values) 0..num_keys-1 of one kv head, in logical order, as fp64 [num_keys, D]."""
-    if num_keys == 0:
-        return np.zeros((0, cache.shape[-1]), dtype=np.float64)
+def gather_keys(k_cache, block_table_row, num_keys: int, kv_head: int, block_size: int) -> np.ndarray:
+    """Keys 0..num_keys-1 of one kv head, in logical order, as fp64 [num_keys, D]."""
     j = np.arange(num_keys)
     phys = np.asarray(block_table_row, dtype=np.int64)[j // block_size]
-    return bf16_to_f64(cache[phys, kv_head, j % block_size, :])
+    return bf16_to_f64(k_cache[phys, kv_head, j % block_size, :]).reshape(num_keys, k_cache.shape[-1])
+
+
+def gather_values(v_cache, block_table_row, num_keys: int, kv_head: int, block_size: int) -> np.ndarray:
+    """Values 0..num_keys-1 of one kv head, in logical order, as fp64 [num_keys, D]."""
+    j = np.arange(num_keys)
+    phys = np.asarray(block_table_row, dtype=np.int64)[j // block_size]
+    return bf16_to_f64(v_cache[phys, kv_head, :, j % block_size]).reshape(num_keys, v_cache.shape[2])
 
 
 # ---------------------------------------------------------------------------
@@ -198,8 +206,8 @@ def paged_attention(
         n = int(sl[r])
         vis_all = causal_visible(int(ctx[r]), ql, n)
         for g in range(Hkv):
-            K = gather_kv(k_cache, block_tables[r], n, g, block_size)
-            V = gather_kv(v_cache, block_tables[r], n, g, block_size)
+            K = gather_keys(k_cache, block_tables[r], n, g, block_size)
+            V = gather_values(v_cache, block_tables[r], n, g, block_size)
             for a in range(0, toks.size, row_tile):
                 tt = toks[a : a + row_tile]
                 vis = vis_all[tt - t0]
@@ -230,8 +238,8 @@ def cascade_prefix_attention(
     o = np.zeros((T, Hq, D), dtype=np.float64)
     lse = np.full((T, Hq), -np.inf, dtype=np.float64)
     for g in range(Hkv):
-        K = gather_kv(k_cache, prefix_block_table, prefix_len, g, block_size)
-        V = gather_kv(v_cache, prefix_block_table, prefix_len, g, block_size)
+        K = gather_keys(k_cache, prefix_block_table, prefix_len, g, block_size)
+        V = gather_values(v_cache, prefix_block_table, prefix_len, g, block_size)
         for hh in range(G):
             h = g * G + hh
             s = sc * (bf16_to_f64(q[:, h, :]) @ K.T)

@@ -109,124 +109,230 @@ __device__ __forceinline__ void store8(void* out, int out_f32, int64_t off, cons
 
 // ------------------------------------------------------------------------------------------
 // Decode item: one query token, G q heads sharing kv head g, keys [kv_begin, kv_end).
-// Lane layout: LPT lanes own one token row of a block (8 dims = 16 bytes each); a wave load
-// covers TPL token rows; a 16-token block takes LPB loads per lane for K and LPB for V.
+//
+// Each wave streams whole 16-token blocks (4 KB of K, 4 KB of V^T at D=128).
+//  * Q.K: 8 lanes per key; lane group a (= lane / 8) takes tokens a and a+8, lane c (= lane % 8)
+//    the dims 8c + 64k.  Partial dot products (v_dot2_f32_bf16) for the 2 tokens x G heads are
+//    reduced over the 8 lanes by a transpose-reduce: three DPP exchange stages that halve the
+//    values each lane keeps, so every lane ends with distinct, fully reduced scores
+//    (score n = 2*head + token-of-pair, lane c keeps n = c*NK .. c*NK+NK-1) and the softmax
+//    exponentials are not repeated across lanes.
+//  * softmax: the running maximum per head is wave-uniform and only raised when a score
+//    exceeds it by more than kLazy (log2 units), so p = exp2(s - m) <= 2^kLazy and the
+//    rescale of the accumulators is rare; the block's p go to LDS as bf16.
+//  * P.V on the dim-major value tile: lane l holds rows l/2 + 32i of V^T for the token half
+//    l%2 (8 tokens = 4 packed pairs) and accumulates with v_dot2_f32_bf16 against the packed
+//    (p_t, p_t+1) pairs read back from LDS.
 // ------------------------------------------------------------------------------------------
+constexpr float kLazy = 8.0f;
+
+template <int N, int CTRL, int BIT>
+__device__ __forceinline__ void transpose_stage(const float (&in)[N], float (&out)[N / 2], int c) {
+  const bool up = (c >> BIT) & 1;
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const float keep = up ? in[k + N / 2] : in[k];
+    const float send = up ? in[k] : in[k + N / 2];
+    out[k] = keep + dpp_f32<CTRL>(send);
+  }
+}
+
+template <int D, int G>
+struct DecodeSmem {
+  static constexpr int O_FLOATS = 4 * G * D;                 // per-wave output states
+  static constexpr int ML_FLOATS = 8 * G;                     // per-wave m and l
+  static constexpr int SCR_BYTES = G * 16 * 4 + G * 16 * 2;   // per-wave scores + bf16 p
+  static constexpr int BYTES = (O_FLOATS + ML_FLOATS) * 4 + 4 * SCR_BYTES;
+};
+
 template <int D, int G>
 __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char* smem_raw) {
-  constexpr int LPT = D / 8;
-  constexpr int TPL = 64 / LPT;
-  constexpr int LPB = kBlockSize / TPL;
-  constexpr int CH = D / 8;  // uint4 chunks per token row
+  constexpr int CH = D / 8;    // 16-byte chunks per key row
+  constexpr int CPT = D / 64;  // chunks of one key a lane holds
+  constexpr int RPL = D / 32;  // V^T rows a lane holds
+  constexpr int NV = 2 * G;    // scores per lane before the reduction
+  constexpr int NS = NV >= 8 ? 3 : (NV == 4 ? 2 : 1);  // transpose stages (rest: plain adds)
+  constexpr int NK = NV >= 8 ? NV / 8 : 1;            // scores per lane after the reduction
+  constexpr int DUP = 3 - NS;                          // low lane bits holding duplicates
+  using SM = DecodeSmem<D, G>;
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int j = lane / LPT;
-  const int c = lane % LPT;
+  const int grp = lane >> 3;
+  const int c = lane & 7;
   const int r = it.seq;
   const int token = a.query_start_loc[r] + it.q_begin;
   const int kv_end = it.kv_end;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const float sl = a.scale_log2;
 
-  uint4 qv[G];
+  // Scores this lane owns after the reduction: index n = 2*hh + tsel, token grp + 8*tsel.
+  const int n0 = (c >> DUP) * NK;
+  const int my_hh = n0 >> 1;  // the same head for both scores when NK == 2
+  const bool owner = (c & ((1 << DUP) - 1)) == 0;
+
+  uint4 qv[G][CPT];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
-    qv[hh] = reinterpret_cast<const uint4*>(a.q + ((int64_t)token * Hq + g * G + hh) * D)[c];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+      qv[hh][k] = reinterpret_cast<const uint4*>(a.q + ((int64_t)token * Hq + g * G + hh) * D)[c + 8 * k];
 
-  float m[G], l[G], o[G][8];
+  float m[G];        // wave-uniform running max per head (log2 units of scaled scores)
+  float o[G][RPL];   // P.V accumulators: head hh, V^T row (lane >> 1) + 32 i, token half
+  float l_own = 0.f; // sum of p over the scores this lane owns (head my_hh)
+  float m_own = -INFINITY;
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     m[hh] = -INFINITY;
-    l[hh] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+    for (int i = 0; i < RPL; ++i) o[hh][i] = 0.f;
   }
+
+  char* scr = smem_raw + (SM::O_FLOATS + SM::ML_FLOATS) * 4 + wave * SM::SCR_BYTES;
+  float* sbuf = reinterpret_cast<float*>(scr);                  // [G][16] scaled scores
+  uint16_t* pbuf = reinterpret_cast<uint16_t*>(scr + G * 64);   // [G][16] bf16 p
 
   const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
   const int b_begin = it.kv_begin / kBlockSize;
   const int b_end = (kv_end + kBlockSize - 1) / kBlockSize;
-  const int64_t blk_stride = (int64_t)Hkv * kBlockSize * CH;  // uint4 per physical block
-  const uint4* kb = reinterpret_cast<const uint4*>(a.k_cache) + (int64_t)g * kBlockSize * CH;
-  const uint4* vb = reinterpret_cast<const uint4*>(a.v_cache) + (int64_t)g * kBlockSize * CH;
-  const int lane_off = j * CH + c;
+  const int64_t tile_stride = (int64_t)kBlockSize * CH;  // uint4 per (block, head) tile
+  const int64_t blk_stride = (int64_t)Hkv * tile_stride;
+  const uint4* kb = reinterpret_cast<const uint4*>(a.k_cache) + (int64_t)g * tile_stride;
+  const uint4* vb = reinterpret_cast<const uint4*>(a.v_cache) + (int64_t)g * tile_stride;
+  const int th = lane & 1;  // token half of the V^T rows this lane holds
 
-  // This wave takes blocks b_begin + wave + 4k, k < nk (nk <= 64 since a split has at most
-  // 256 blocks).  Their physical ids are fetched once, one per lane, and read back with
-  // v_readlane so the block loop issues no dependent table loads.
+  // Blocks b_begin + wave + 4k, k < nk (nk <= 64: a split has at most 256 blocks); their
+  // physical ids are fetched once, one per lane, and read back with v_readlane.
   const int nb = b_end - b_begin;
   const int nk = nb > wave ? (nb - wave + 3) / 4 : 0;
   const int my_id = lane < nk ? bt[b_begin + wave + 4 * lane] : 0;
 
-  auto load = [&](int k, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
+  constexpr int NKR = 2 * CPT;  // key chunks per lane per block
+  auto load = [&](int k, uint4 (&kr)[NKR], uint4 (&vr)[RPL]) {
     const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
-    const uint4* kp = kb + phys * blk_stride + lane_off;
-    const uint4* vp = vb + phys * blk_stride + lane_off;
+    const uint4* kp = kb + phys * blk_stride;
+    const uint4* vp = vb + phys * blk_stride;
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) kr[i] = kp[i * TPL * CH];
+    for (int ts = 0; ts < 2; ++ts)
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) vr[i] = vp[i * TPL * CH];
+      for (int cc = 0; cc < CPT; ++cc) kr[ts * CPT + cc] = kp[(grp + 8 * ts) * CH + c + 8 * cc];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) vr[i] = vp[lane + 64 * i];
   };
 
-  auto process = [&](int k, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
+  auto process = [&](int k, uint4 (&kr)[NKR], uint4 (&vr)[RPL]) {
     const int t0 = (b_begin + wave + 4 * k) * kBlockSize;
-    const bool partial = t0 + kBlockSize > kv_end;  // only the last block can be partial
-    float s[LPB][G];
+    const int nvalid = kv_end - t0;  // < 16 only in the last block
+    // Q.K partial dot products: v[2*hh + ts].
+    float v[NV];
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) {
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts) {
+        float acc = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+          const uint4 kk = kr[ts * CPT + cc];
+          acc = dot2(qv[hh][cc].x, kk.x, acc);
+          acc = dot2(qv[hh][cc].y, kk.y, acc);
+          acc = dot2(qv[hh][cc].z, kk.z, acc);
+          acc = dot2(qv[hh][cc].w, kk.w, acc);
+        }
+        v[2 * hh + ts] = acc;
+      }
+    // Transpose-reduce over the 8 lanes of the group (partners 7-c, c^2, c^1).
+    float sc[NK];
+    if constexpr (NV == 16) {
+      float s1[8], s2[4];
+      transpose_stage<16, 0x141, 2>(v, s1, c);
+      transpose_stage<8, 0x4E, 1>(s1, s2, c);
+      transpose_stage<4, 0xB1, 0>(s2, sc, c);
+    } else if constexpr (NV == 8) {
+      float s1[4], s2[2];
+      transpose_stage<8, 0x141, 2>(v, s1, c);
+      transpose_stage<4, 0x4E, 1>(s1, s2, c);
+      transpose_stage<2, 0xB1, 0>(s2, sc, c);
+    } else if constexpr (NV == 4) {
+      float s1[2];
+      transpose_stage<4, 0x141, 2>(v, s1, c);
+      transpose_stage<2, 0x4E, 1>(s1, sc, c);
+      sc[0] += dpp_f32<0xB1>(sc[0]);
+    } else {
+      transpose_stage<2, 0x141, 2>(v, sc, c);
+      sc[0] += dpp_f32<0x4E>(sc[0]);
+      sc[0] += dpp_f32<0xB1>(sc[0]);
+    }
+    int tok[NK];
+    bool over = false;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      tok[kk] = grp + 8 * ((n0 + kk) & 1);
+      sc[kk] = (tok[kk] < nvalid) ? sc[kk] * sl : -INFINITY;
+      over |= sc[kk] > m_own + kLazy;
+    }
+    if (__ballot(over) != 0) {
+      // Raise the running max to this block's max (rare after the first block).
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) sbuf[my_hh * 16 + tok[kk]] = sc[kk];
+      __builtin_amdgcn_wave_barrier();  // LDS ops of one wave run in order; keep them so
+      const float4* row = reinterpret_cast<const float4*>(sbuf + my_hh * 16);
+      float bm = -INFINITY;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 x = row[q4];
+        bm = fmaxf(fmaxf(bm, fmaxf(x.x, x.y)), fmaxf(x.z, x.w));
+      }
+      const float mn_own = fmaxf(m_own, bm);
+      l_own *= fast_exp2(m_own - ((mn_own == -INFINITY) ? 0.f : mn_own));
+      m_own = mn_own;
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        float acc = dot2(qv[hh].x, kr[i].x, 0.f);
-        acc = dot2(qv[hh].y, kr[i].y, acc);
-        acc = dot2(qv[hh].z, kr[i].z, acc);
-        acc = dot2(qv[hh].w, kr[i].w, acc);
-        s[i][hh] = group_sum<LPT>(acc) * sl;  // scaled, in log2 units
+        // lane hh * (8 / G) owns head hh
+        const float mn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_own), hh * (8 / G)));
+        const float alpha = fast_exp2(m[hh] - ((mn == -INFINITY) ? 0.f : mn));
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) o[hh][i] *= alpha;
+        m[hh] = mn;
       }
     }
-    if (partial) {
+    const float mref = (m_own == -INFINITY) ? 0.f : m_own;
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        if (t0 + j + TPL * i >= kv_end) {
+    for (int kk = 0; kk < NK; ++kk) {
+      const float p = fast_exp2(sc[kk] - mref);
+      if (owner) l_own += p;
+      pbuf[my_hh * 16 + tok[kk]] = __builtin_bit_cast(uint16_t, (__bf16)p);
+    }
+    if (nvalid < kBlockSize) {
+      // Zero the V^T entries of tokens past the end (the cache may hold NaN there).
+      uint32_t msk[4];
 #pragma unroll
-          for (int hh = 0; hh < G; ++hh) s[i][hh] = -INFINITY;
-          vr[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
+      for (int u = 0; u < 4; ++u) {
+        const int t = 8 * th + 2 * u;
+        msk[u] = (t < nvalid ? 0x0000ffffu : 0u) | (t + 1 < nvalid ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        vr[i].x &= msk[0];
+        vr[i].y &= msk[1];
+        vr[i].z &= msk[2];
+        vr[i].w &= msk[3];
       }
     }
+    // P.V: packed (p_t, p_t+1) pairs of this lane's token half, for every head.
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      float mx = s[0][hh];
+      const uint4 pp = *reinterpret_cast<const uint4*>(pbuf + hh * 16 + 8 * th);
 #pragma unroll
-      for (int i = 1; i < LPB; ++i) mx = fmaxf(mx, s[i][hh]);
-      const float mn = fmaxf(m[hh], mx);
-      const float mref = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = fast_exp2(m[hh] - mref);
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        s[i][hh] = fast_exp2(s[i][hh] - mref);  // now p; exactly 1 for the running maximum
-        ps += s[i][hh];
+      for (int i = 0; i < RPL; ++i) {
+        float acc = o[hh][i];
+        acc = dot2(pp.x, vr[i].x, acc);
+        acc = dot2(pp.y, vr[i].y, acc);
+        acc = dot2(pp.z, vr[i].z, acc);
+        acc = dot2(pp.w, vr[i].w, acc);
+        o[hh][i] = acc;
       }
-      l[hh] = l[hh] * alpha + ps;
-      m[hh] = mn;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
-    }
-    // P.V one token row at a time, converting each bf16 value once for all G heads.
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) {
-      float v[8];
-      v[0] = bf16_lo(vr[i].x);
-      v[1] = bf16_hi(vr[i].x);
-      v[2] = bf16_lo(vr[i].y);
-      v[3] = bf16_hi(vr[i].y);
-      v[4] = bf16_lo(vr[i].z);
-      v[5] = bf16_hi(vr[i].z);
-      v[6] = bf16_lo(vr[i].w);
-      v[7] = bf16_hi(vr[i].w);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(s[i][hh], v[e], o[hh][e]);
     }
   };
 
@@ -234,7 +340,7 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   // The steady-state loads are unconditional so the compiler's wait counts only ever wait
   // for the block about to be used (a conditional load would make it wait for both).
   if (nk > 0) {
-    uint4 ka[LPB], va[LPB], kn[LPB], vn[LPB];
+    uint4 ka[NKR], va[RPL], kn[NKR], vn[RPL];
     load(0, ka, va);
     int k = 0;
     for (; k + 2 < nk; k += 2) {
@@ -252,40 +358,41 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
     }
   }
 
-  // Merge the token rows of the wave (lanes with equal c, different j).
+  // Wave epilogue: add the two token halves, sum l over the lanes owning each head.
 #pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) {
+  for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float m2 = __shfl_xor(m[hh], off);
-      const float l2 = __shfl_xor(l[hh], off);
-      float o2[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[hh][e], off);
-      merge_state<8>(m[hh], l[hh], o[hh], m2, l2, o2);
-    }
-  }
+    for (int i = 0; i < RPL; ++i) o[hh][i] += dpp_f32<0xB1>(o[hh][i]);
+  float lsum = owner ? l_own : 0.f;
+  if constexpr (G <= 4) lsum += __shfl_xor(lsum, 1);
+  if constexpr (G <= 2) lsum += __shfl_xor(lsum, 2);
+  if constexpr (G <= 1) lsum += __shfl_xor(lsum, 4);
+  lsum += __shfl_xor(lsum, 8);
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
 
-  // Merge the 4 waves through LDS.
   float* s_o = reinterpret_cast<float*>(smem_raw);  // [4][G][D]
-  float* s_m = s_o + 4 * G * D;                     // [4][G]
-  float* s_l = s_m + 4 * G;                         // [4][G]
-  if (j == 0) {
+  float* s_m = s_o + SM::O_FLOATS;                   // [4][G]
+  float* s_l = s_m + 4 * G;                          // [4][G]
+  if (th == 0) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float4* dst = reinterpret_cast<float4*>(s_o + (wave * G + hh) * D + c * 8);
-      dst[0] = make_float4(o[hh][0], o[hh][1], o[hh][2], o[hh][3]);
-      dst[1] = make_float4(o[hh][4], o[hh][5], o[hh][6], o[hh][7]);
-      if (c == 0) {
-        s_m[wave * G + hh] = m[hh];
-        s_l[wave * G + hh] = l[hh];
-      }
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) s_o[(wave * G + hh) * D + (lane >> 1) + 32 * i] = o[hh][i];
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const int src = hh * (8 / G);
+    const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsum), src));
+    if (lane == 0) {
+      s_m[wave * G + hh] = m[hh];
+      s_l[wave * G + hh] = lh;
     }
   }
   __syncthreads();
   const int t = threadIdx.x;
-  if (t < G * LPT) {
-    const int hh = t / LPT, cc = t % LPT;
+  if (t < G * CH) {
+    const int hh = t / CH, cc = t % CH;
     float mm = -INFINITY, ll = 0.f, oo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) oo[e] = 0.f;
@@ -372,14 +479,17 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
     for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
   float m = -INFINITY, lsum = 0.f;
 
-  // Staging: wave w loads logical block (tile/16 + w); K rows key = KPI*i + lane/LPT,
-  // V rows key = NI*(lane/LPT) + i (consecutive keys per lane for the transposed write).
+  // Staging: wave w copies logical block (tile/16 + w).  K rows are token-major: key
+  // kk = KPI*i + lane/LPT, chunk lane%LPT.  The value pool is dim-major, so the V^T tile is a
+  // plain copy: chunk lane + 64i is row (lane >> 1) + 32i, token half lane & 1.
+  constexpr int NIV = D / 32;
   const int sc = lane % LPT;
   const int sr = lane / LPT;
-  const int64_t blk_stride = (int64_t)Hkv * kBlockSize * CH;
-  const uint4* kbase = reinterpret_cast<const uint4*>(k_cache) + (int64_t)g * kBlockSize * CH;
-  const uint4* vbase = reinterpret_cast<const uint4*>(v_cache) + (int64_t)g * kBlockSize * CH;
-  uint4 kst[NI], vst[NI];
+  const int64_t tile_stride = (int64_t)kBlockSize * CH;
+  const int64_t blk_stride = (int64_t)Hkv * tile_stride;
+  const uint4* kbase = reinterpret_cast<const uint4*>(k_cache) + (int64_t)g * tile_stride;
+  const uint4* vbase = reinterpret_cast<const uint4*>(v_cache) + (int64_t)g * tile_stride;
+  uint4 kst[NI], vst[NIV];
 
   auto stage_load = [&](int k0) {
     const int lb = k0 / kBlockSize + wave;
@@ -394,16 +504,28 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
         kst[i] = (key0 + kk < kv_end) ? kp[kk * CH + sc] : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int kk = NI * sr + i;
-        vst[i] = (key0 + kk < kv_end) ? vp[kk * CH + sc] : make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < NIV; ++i) vst[i] = vp[lane + 64 * i];
+      const int nvalid = kv_end - key0;
+      if (nvalid < kBlockSize) {
+        // Zero the values of keys past the end (the cache may hold NaN there).
+        const int t = 8 * (lane & 1);
+        uint32_t msk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          msk[u] = (t + 2 * u < nvalid ? 0x0000ffffu : 0u) | (t + 2 * u + 1 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int i = 0; i < NIV; ++i) {
+          vst[i].x &= msk[0];
+          vst[i].y &= msk[1];
+          vst[i].z &= msk[2];
+          vst[i].w &= msk[3];
+        }
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        kst[i] = make_uint4(0u, 0u, 0u, 0u);
-        vst[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int i = 0; i < NI; ++i) kst[i] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int i = 0; i < NIV; ++i) vst[i] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
 
@@ -415,28 +537,10 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
       const int kk = wave * kBlockSize + KPI * i + sr;
       *reinterpret_cast<uint4*>(ks + kk * S::KP + sc * 8) = kst[i];
     }
-    const int kcol = wave * kBlockSize + NI * sr;
-    const uint32_t* w[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) w[i] = reinterpret_cast<const uint32_t*>(&vst[i]);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int d0 = sc * 8 + 2 * u;
-      if constexpr (NI == 4) {
-        uint2 lo, hi;
-        lo.x = __builtin_amdgcn_perm(w[1][u], w[0][u], 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(w[3][u], w[2][u], 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(w[1][u], w[0][u], 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(w[3][u], w[2][u], 0x07060302u);
-        *reinterpret_cast<uint2*>(vs + d0 * S::VP + kcol) = lo;
-        *reinterpret_cast<uint2*>(vs + (d0 + 1) * S::VP + kcol) = hi;
-      } else {
-        static_assert(NI == 2, "staging layout");
-        *reinterpret_cast<uint32_t*>(vs + d0 * S::VP + kcol) =
-            __builtin_amdgcn_perm(w[1][u], w[0][u], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(vs + (d0 + 1) * S::VP + kcol) =
-            __builtin_amdgcn_perm(w[1][u], w[0][u], 0x07060302u);
-      }
+    for (int i = 0; i < NIV; ++i) {
+      const int row = (lane >> 1) + 32 * i;
+      *reinterpret_cast<uint4*>(vs + row * S::VP + wave * kBlockSize + 8 * (lane & 1)) = vst[i];
     }
   };
 
@@ -676,7 +780,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
 
 template <int D, int G>
 size_t varlen_smem(bool has_prefill) {
-  const size_t dec = (size_t)4 * G * (D + 2) * sizeof(float);
+  const size_t dec = (size_t)DecodeSmem<D, G>::BYTES;
   const size_t pre = has_prefill ? (size_t)TileSmem<D>::BYTES : 0;
   return dec > pre ? dec : pre;
 }

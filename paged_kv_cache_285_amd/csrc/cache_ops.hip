@@ -35,10 +35,12 @@ __global__ void slot_mapping_kernel(int64_t* __restrict__ slots, const int32_t* 
   slots[t] = phys * kBlockSize + (pos % kBlockSize);
 }
 
-// One thread per 16-byte chunk (8 bf16) of one token's K and V for one kv head.
-// Pools are [num_blocks, Hkv, 16, D]; a slot names (block, offset).
+// One thread per 16-byte chunk (8 bf16) of one token's K and V for one kv head.  A slot names
+// (block, offset).  The key pool is [num_blocks, Hkv, 16, D]: the token's key is one 16-byte
+// store.  The value pool is [num_blocks, Hkv, D, 16] (dim-major, so attention can read
+// 16-token rows of one dimension): the token's 8 values go to 8 rows, 2 bytes each.
 __global__ void reshape_and_cache_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
-                                         uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                         uint4* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
                                          const int64_t* __restrict__ slots, int32_t num_tokens,
                                          int32_t num_kv_heads, int32_t chunks_per_head,
                                          int64_t num_slots) {
@@ -53,9 +55,16 @@ __global__ void reshape_and_cache_kernel(const uint4* __restrict__ k, const uint
   const int64_t c = within - h * chunks_per_head;
   const int64_t blk = slot / kBlockSize;
   const int64_t off = slot - blk * kBlockSize;
-  const int64_t dst = ((blk * num_kv_heads + h) * kBlockSize + off) * chunks_per_head + c;
-  k_cache[dst] = k[gid];
-  v_cache[dst] = v[gid];
+  const int64_t tile = blk * num_kv_heads + h;  // (block, head) tile index
+  k_cache[(tile * kBlockSize + off) * chunks_per_head + c] = k[gid];
+  const uint4 x = v[gid];
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint16_t* vt = v_cache + (tile * chunks_per_head * 8 + c * 8) * kBlockSize + off;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vt[(2 * e) * kBlockSize] = (uint16_t)(w[e] & 0xffffu);
+    vt[(2 * e + 1) * kBlockSize] = (uint16_t)(w[e] >> 16);
+  }
 }
 
 }  // namespace
@@ -82,7 +91,7 @@ hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v, uint16
   const int64_t blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
                      reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
-                     reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache), slots,
+                     reinterpret_cast<uint4*>(k_cache), v_cache, slots,
                      num_tokens, num_kv_heads, chunks, num_slots);
   return hipGetLastError();
 }

@@ -35,10 +35,20 @@ def empty_pool(nb, hkv, bs, d):
     return np.full((nb, hkv, bs, d), W.BF16_NAN, dtype=np.uint16)
 
 
+def empty_vpool(nb, hkv, bs, d):
+    return np.full((nb, hkv, d, bs), W.BF16_NAN, dtype=np.uint16)
+
+
 def token_view(pool):
-    """[NB, H, bs, D] -> [NB*bs, H, D]: flat token slots (an independent way to address a slot)."""
+    """Key pool [NB, H, bs, D] -> [NB*bs, H, D]: flat token slots (an independent way to address a slot)."""
     nb, h, bs, d = pool.shape
     return pool.transpose(0, 2, 1, 3).reshape(nb * bs, h, d)
+
+
+def vtoken_view(pool):
+    """Value pool [NB, H, D, bs] -> [NB*bs, H, D]."""
+    nb, h, d, bs = pool.shape
+    return pool.transpose(0, 3, 1, 2).reshape(nb * bs, h, d)
 
 
 # ---------------------------------------------------------------------------
@@ -123,7 +133,7 @@ def test_prefix_hit_visible_keys_closed_form(page):
     nblk = -(-total // bs)
     bt = rng.permutation(20)[:nblk].astype(np.int32)[None, :]
     kp = empty_pool(20, hkv, bs, d)
-    vp = empty_pool(20, hkv, bs, d)
+    vp = empty_vpool(20, hkv, bs, d)
     # V_j = (j, 1, 0, 0), exact in bf16 for j < 256; keys arbitrary
     vals = np.zeros((total, hkv, d), np.float32)
     vals[:, 0, 0] = np.arange(total)
@@ -145,7 +155,7 @@ def test_shared_block_tables_give_identical_prefix_states(page):
     bs, hkv, hq, d = 16, 2, 4, 8
     rng = np.random.default_rng(11)
     kp = rand_bf16(rng, 16, hkv, bs, d)
-    vp = rand_bf16(rng, 16, hkv, bs, d)
+    vp = rand_bf16(rng, 16, hkv, d, bs)
     ta = np.array(ex["table_a"], np.int32)
     tb = np.array(ex["table_b"], np.int32)
     q = rand_bf16(rng, 3, hq, d)
@@ -166,14 +176,14 @@ def test_reshape_and_cache_bitwise():
     rng = np.random.default_rng(3)
     nb, h, bs, d, t = 12, 3, 16, 8, 40
     kp = rng.integers(0, 1 << 16, size=(nb, h, bs, d), dtype=np.uint16)
-    vp = rng.integers(0, 1 << 16, size=(nb, h, bs, d), dtype=np.uint16)
+    vp = rng.integers(0, 1 << 16, size=(nb, h, d, bs), dtype=np.uint16)
     k = rng.integers(0, 1 << 16, size=(t, h, d), dtype=np.uint16)
     v = rng.integers(0, 1 << 16, size=(t, h, d), dtype=np.uint16)
     slots = rng.choice(nb * bs, size=t, replace=False).astype(np.int64)
     slots[::7] = -1
     k2, v2 = O.reshape_and_cache(k, v, kp, vp, slots, bs)
-    fk, fv = token_view(k2), token_view(v2)
-    fk0, fv0 = token_view(kp), token_view(vp)
+    fk, fv = token_view(k2), vtoken_view(v2)
+    fk0, fv0 = token_view(kp), vtoken_view(vp)
     written = np.zeros(nb * bs, bool)
     for i, s in enumerate(slots):
         if s >= 0:
@@ -244,7 +254,7 @@ def test_mixed_batch_matches_dense_contiguous_attention():
             c = int(st.context_lens[r])
             if rid not in hist_k:
                 # cached history before the first step: read it through the flat token view
-                tv_k, tv_v = token_view(wl.k_cache), token_view(wl.v_cache)
+                tv_k, tv_v = token_view(wl.k_cache), vtoken_view(wl.v_cache)
                 phys = [int(st.block_tables[r][j // bs]) * bs + j % bs for j in range(c)]
                 hist_k[rid] = [O.bf16_to_f64(tv_k[s]) for s in phys]
                 hist_v[rid] = [O.bf16_to_f64(tv_v[s]) for s in phys]
@@ -306,7 +316,7 @@ def test_chunked_equals_unchunked(total, chunks):
     v = rand_bf16(rng, total, hkv, d)
     nb = 12
     bt = rng.permutation(nb)[None, :].astype(np.int32)
-    pools = (empty_pool(nb, hkv, bs, d), empty_pool(nb, hkv, bs, d))
+    pools = (empty_pool(nb, hkv, bs, d), empty_vpool(nb, hkv, bs, d))
     o1, l1, p1 = _run_steps(q, k, v, [total], 0, bt, pools, bs)
     o2, l2, p2 = _run_steps(q, k, v, chunks, 0, bt, pools, bs)
     assert np.max(np.abs(o1 - o2)) < 1e-12 and np.max(np.abs(l1 - l2)) < 1e-12
@@ -323,7 +333,7 @@ def test_prefix_cached_equals_suffix_of_full(page):
     v = rand_bf16(rng, total, hkv, d)
     nb = 10
     bt = rng.permutation(nb)[None, :7].astype(np.int32)
-    pools = (empty_pool(nb, hkv, bs, d), empty_pool(nb, hkv, bs, d))
+    pools = (empty_pool(nb, hkv, bs, d), empty_vpool(nb, hkv, bs, d))
     full_o, full_l, _ = _run_steps(q, k, v, [total], 0, bt, pools, bs)
     # the cache already holds tokens 0..47 (written by an earlier request)
     slots = O.slot_mapping(bt, [0, c], [0], bs)
@@ -393,7 +403,7 @@ def _single_request(q, k, v, bs=4, ctx=0):
     n, hkv, d = k.shape
     nb = -(-n // bs) + 3
     bt = np.random.default_rng(n).permutation(nb)[None, :].astype(np.int32)
-    kp, vp = empty_pool(nb, hkv, bs, d), empty_pool(nb, hkv, bs, d)
+    kp, vp = empty_pool(nb, hkv, bs, d), empty_vpool(nb, hkv, bs, d)
     slots = O.slot_mapping(bt, [0, n], [0], bs)
     kp, vp = O.reshape_and_cache(k, v, kp, vp, slots, bs)
     L = q.shape[0]
@@ -493,10 +503,10 @@ def test_workload_poison_covers_unwritten_slots():
     wl = W.mixed_llama8b(seed=0, num_decode=3, ctx_range=(20, 40))
     st = wl.steps[0]
     bs = wl.block_size
-    tv = token_view(wl.k_cache)
-    for r in range(st.num_seqs):
-        c = int(st.context_lens[r])
-        cached = [int(st.block_tables[r][j // bs]) * bs + j % bs for j in range(c)]
-        assert np.isfinite(W.bf16_bits_to_f32(tv[cached])).all()
-        fut = [int(st.block_tables[r][j // bs]) * bs + j % bs for j in range(c, int(st.seq_lens[r]))]
-        assert np.isnan(W.bf16_bits_to_f32(tv[fut])).all()
+    for tv in (token_view(wl.k_cache), vtoken_view(wl.v_cache)):
+        for r in range(st.num_seqs):
+            c = int(st.context_lens[r])
+            cached = [int(st.block_tables[r][j // bs]) * bs + j % bs for j in range(c)]
+            assert np.isfinite(W.bf16_bits_to_f32(tv[cached])).all()
+            fut = [int(st.block_tables[r][j // bs]) * bs + j % bs for j in range(c, int(st.seq_lens[r]))]
+            assert np.isnan(W.bf16_bits_to_f32(tv[fut])).all()

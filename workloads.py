@@ -16,6 +16,8 @@ Value recipe (used by every workload):
   * large arrays are drawn in fixed 4 Mi-element chunks, each from its own
     PCG64 stream keyed by (seed, array tag, chunk index), so the values do not
     depend on how many threads draw them;
+  * pools: keys [num_blocks, Hkv, 16, D] (token-major), values
+    [num_blocks, Hkv, D, 16] (dim-major);
   * every pool slot that holds no cached token (unreferenced blocks, block
     table padding and the not-yet-written tail of each request) is set to
     bf16 NaN so that a kernel reading outside the visible keys shows up.
@@ -152,8 +154,8 @@ class Workload:
     block_size: int
     num_blocks: int
     bt_stride: int
-    k_cache: np.ndarray  # bf16 bits [NB, Hkv, bs, D] (initial contents)
-    v_cache: np.ndarray
+    k_cache: np.ndarray  # bf16 bits [NB, Hkv, bs, D] (initial contents; token-major)
+    v_cache: np.ndarray  # bf16 bits [NB, Hkv, D, bs] (dim-major)
     steps: List[Step]
     cascade: Optional[CascadeView] = None
     notes: dict = field(default_factory=dict)
@@ -239,10 +241,9 @@ def build(
             tables[r, nblk[r] :] = spare
 
     H, D = num_kv_heads, head_dim
-    pool_shape = (num_blocks, H, bs, D)
-    nelem = int(np.prod(pool_shape))
-    k_cache = normal_bf16(nelem, seed, _TAGS["pool_k"]).reshape(pool_shape)
-    v_cache = normal_bf16(nelem, seed, _TAGS["pool_v"]).reshape(pool_shape)
+    nelem = num_blocks * H * bs * D
+    k_cache = normal_bf16(nelem, seed, _TAGS["pool_k"]).reshape(num_blocks, H, bs, D)
+    v_cache = normal_bf16(nelem, seed, _TAGS["pool_v"]).reshape(num_blocks, H, D, bs)
     if poison:
         referenced = np.zeros(num_blocks, dtype=bool)
         for r in range(nreq):
@@ -256,7 +257,7 @@ def build(
                 lo = max(start - pos_blk * bs, 0)
                 phys = tables[r, pos_blk]
                 k_cache[phys, :, lo:, :] = BF16_NAN
-                v_cache[phys, :, lo:, :] = BF16_NAN
+                v_cache[phys, :, :, lo:] = BF16_NAN
 
     steps: List[Step] = []
     done = [r.context for r in requests]
