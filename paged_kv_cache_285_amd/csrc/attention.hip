@@ -537,10 +537,15 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
       const int kk = wave * kBlockSize + KPI * i + sr;
       *reinterpret_cast<uint4*>(ks + kk * S::KP + sc * 8) = kst[i];
     }
+    // Within each block the four 4-key groups are stored in the order 0, 2, 1, 3 (key t goes
+    // to column 8*((t>>2)&1) + 4*(t>>3) + (t&3)), so the 8 keys one lane feeds a PV K-step
+    // (t = 4h..4h+3 and 8+4h..8+4h+3) are one conflict-free 16-byte read.
 #pragma unroll
     for (int i = 0; i < NIV; ++i) {
       const int row = (lane >> 1) + 32 * i;
-      *reinterpret_cast<uint4*>(vs + row * S::VP + wave * kBlockSize + 8 * (lane & 1)) = vst[i];
+      uint16_t* dst = vs + row * S::VP + wave * kBlockSize + 4 * (lane & 1);
+      *reinterpret_cast<uint2*>(dst) = make_uint2(vst[i].x, vst[i].y);
+      *reinterpret_cast<uint2*>(dst + 8) = make_uint2(vst[i].z, vst[i].w);
     }
   };
 
@@ -559,26 +564,22 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
     const uint16_t* ks = smem + buf * S::BUF_ELEMS;
     const uint16_t* vs = ks + S::K_ELEMS;
 
-    // S^T = K Q^T: two 32-key row tiles.
+    // S^T = K Q^T: two 32-key row tiles, their MFMA chains interleaved.
     floatx16 sacc[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
         const bf16x8 ka =
             *reinterpret_cast<const bf16x8*>(ks + (32 * mt + n) * S::KP + 16 * s + 8 * h);
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sacc[mt], 0, 0, 0);
       }
-    }
 
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[mt][e] *= sl;  // scaled, in log2 units
-
-    // Mask: only tiles reaching past the first row's position or the sequence end.
+    // Mask (raw scores): only tiles reaching past the first row's position or the sequence end.
     const bool need_mask = (k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > min_pos);
     if (need_mask) {
 #pragma unroll
@@ -591,40 +592,40 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
         }
     }
 
-    // Online softmax for this lane's query column.
+    // Online softmax for this lane's query column.  The running max m (log2 units of scaled
+    // scores) is only raised when a score exceeds it by more than kLazy, for every lane at
+    // once, so the 64-register rescale of the output is rare; p stays <= 2^kLazy.
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float mref = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = fast_exp2(m - mref);
-    m = mn;
-    float ps = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl;
+    if (__ballot(mx > m + kLazy) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
+      lsum *= alpha;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int d = 0; d < DT; ++d)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(sacc[mt][e] - mref);
-        sacc[mt][e] = p;
-        ps += p;
-      }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int d = 0; d < DT; ++d)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+        for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+      m = mn;
+    }
+    const float mref = (m == -INFINITY) ? 0.f : m;
 
-    // P^T operands: K-step ks covers keys 32*(ks/2) + 8*jj0 + 0..15, jj0 = 2*(ks%2).
+    // P^T operands: K-step ks covers keys 32*(ks/2) + 8*jj0 + 0..15, jj0 = 2*(ks%2).  The row
+    // sum is accumulated in fp32 (a sum of the bf16-rounded p would cost ~1e-3 in the LSE).
     bf16x8 pb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int mt = ks >> 1, b0 = 8 * (ks & 1);
       bf16x8 v;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (__bf16)sacc[mt][b0 + e];
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(fmaf(sacc[mt][b0 + e], sl, -mref));
+        lsum += p;
+        v[e] = (__bf16)p;
+      }
       pb[ks] = v;
     }
 
@@ -633,13 +634,8 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
     for (int d = 0; d < DT; ++d) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int mt = ks >> 1, jj0 = 2 * (ks & 1);
-        const uint16_t* row = vs + (32 * d + n) * S::VP + 32 * mt + 8 * jj0 + 4 * h;
-        const uint2 x0 = *reinterpret_cast<const uint2*>(row);
-        const uint2 x1 = *reinterpret_cast<const uint2*>(row + 8);
-        const uint4 xv = make_uint4(x0.x, x0.y, x1.x, x1.y);
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv), pb[ks],
-                                                          oacc[d], 0, 0, 0);
+        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(vs + (32 * d + n) * S::VP + 16 * ks + 8 * h);
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xv, pb[ks], oacc[d], 0, 0, 0);
       }
     }
 
