@@ -93,6 +93,7 @@ struct Plan {
   std::vector<int32_t> token_split;  // per token {partial_base, count}
   int32_t num_partials = 0;
   int32_t bps = 0;
+  int32_t waves = 4;
   int32_t n_prefill = 0, n_decode = 0;
 };
 
@@ -108,7 +109,6 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
                   num_tokens);
   }
   const int G = s->num_q_heads / s->num_kv_heads;
-  const int tok_per_tile = pkv::kTileRows / G;
   for (int r = 0; r < num_seqs; ++r) {
     const int32_t ql = qsl[r + 1] - qsl[r];
     if (ql < 0) return fail(PKV_EINVAL, "query_start_loc not ascending at %d", r);
@@ -133,6 +133,13 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
     if (n * s->num_kv_heads <= decode_target_wgs()) break;
   }
   P.bps = bps;
+  // Prefill tiles hold 32 packed (token, q head) rows per wave: 8-wave (256-row) tiles when the
+  // batch has enough prefill rows to fill them, else 4-wave (128-row) tiles.
+  int64_t prefill_rows = 0;
+  for (int r = 0; r < num_seqs; ++r)
+    if (qsl[r + 1] - qsl[r] > 1) prefill_rows += (int64_t)(qsl[r + 1] - qsl[r]) * G;
+  P.waves = prefill_rows >= pkv::kPrefillRowsFor8Waves ? 8 : 4;
+  const int tok_per_tile = 32 * P.waves / G;
   P.items.clear();
   P.token_split.assign((size_t)num_tokens * 2, 0);
   std::vector<pkv::WorkItem> pre, dec;
@@ -209,6 +216,7 @@ void fill_plan_struct(pkv_varlen_plan* out, const Plan& P, int32_t num_seqs, int
   out->num_q_heads = s->num_q_heads;
   out->num_kv_heads = s->num_kv_heads;
   out->block_size = s->block_size;
+  out->waves_per_group = P.waves;
   const VarlenLayout L =
       varlen_layout(out->num_items, num_tokens, P.num_partials, s->num_q_heads, s->head_dim);
   out->workspace_used = (int64_t)L.total;
@@ -263,17 +271,17 @@ int stage_and_copy(void* dst, const void* src, size_t bytes, hipStream_t stream)
   return PKV_OK;
 }
 
-// Cascade segmenting: enough (tile, segment) workgroups to give every CU two, with segments of
-// at least 1024 keys, rounded to whole KV tiles.
+// Cascade segmenting: enough (tile, segment) workgroups to give every CU one 8-wave workgroup,
+// with segments of at least 1024 keys, rounded to whole KV tiles.
 struct CascadeSplit {
   int32_t tiles, segs, seg_len;
 };
 CascadeSplit cascade_split(int32_t num_tokens, int32_t prefix_len, const pkv_shape* s) {
   const int G = s->num_q_heads / s->num_kv_heads;
   CascadeSplit c;
-  c.tiles = (int32_t)ceil_div(num_tokens, pkv::kTileRows / G);
+  c.tiles = (int32_t)ceil_div(num_tokens, 32 * pkv::kCascadeWaves / G);
   const int64_t wgs = std::max<int64_t>(1, (int64_t)c.tiles * s->num_kv_heads);
-  const int64_t want = ceil_div(512, wgs);
+  const int64_t want = ceil_div(256, wgs);  // one 8-wave workgroup per CU
   const int64_t max_segs = std::max<int64_t>(1, prefix_len / 1024);
   int64_t segs = std::max<int64_t>(1, std::min(want, max_segs));
   int64_t seg_len = ceil_div(ceil_div(prefix_len, segs), pkv::kKvTile) * pkv::kKvTile;
@@ -302,7 +310,7 @@ size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t m
   if (check_shape(shape) != PKV_OK || num_seqs < 0 || num_tokens < 0 || max_seq_len < 0) return 0;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   const int64_t per_row = ceil_div(ceil_div(max_seq_len, pkv::kBlockSize), pkv::kMinBlocksPerSplit);
-  const int64_t items = ceil_div((int64_t)num_tokens * G, pkv::kTileRows) + num_seqs +
+  const int64_t items = ceil_div((int64_t)num_tokens * G, 128) + num_seqs +
                         (int64_t)num_seqs * std::max<int64_t>(1, per_row);
   const int64_t partials = (int64_t)num_seqs * std::max<int64_t>(1, per_row);
   return varlen_layout(items, num_tokens, partials, shape->num_q_heads, shape->head_dim).total;
@@ -438,7 +446,7 @@ int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const v
   a.scale_log2 = scale_log2(shape);
   const int G = shape->num_q_heads / shape->num_kv_heads;
   hipError_t e = pkv::launch_varlen(a, shape->head_dim, G, plan->num_prefill_items > 0,
-                                    (hipStream_t)stream);
+                                    plan->waves_per_group, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "varlen attention launch");
   if (plan->num_partials > 0) {
     pkv::ReduceArgs ra;

@@ -137,15 +137,15 @@ __device__ __forceinline__ void transpose_stage(const float (&in)[N], float (&ou
   }
 }
 
-template <int D, int G>
+template <int D, int G, int NW>
 struct DecodeSmem {
-  static constexpr int O_FLOATS = 4 * G * D;                 // per-wave output states
-  static constexpr int ML_FLOATS = 8 * G;                     // per-wave m and l
+  static constexpr int O_FLOATS = NW * G * D;                 // per-wave output states
+  static constexpr int ML_FLOATS = 2 * NW * G;                // per-wave m and l
   static constexpr int SCR_BYTES = G * 16 * 4 + G * 16 * 2;   // per-wave scores + bf16 p
-  static constexpr int BYTES = (O_FLOATS + ML_FLOATS) * 4 + 4 * SCR_BYTES;
+  static constexpr int BYTES = (O_FLOATS + ML_FLOATS) * 4 + NW * SCR_BYTES;
 };
 
-template <int D, int G>
+template <int D, int G, int NW>
 __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char* smem_raw) {
   constexpr int CH = D / 8;    // 16-byte chunks per key row
   constexpr int CPT = D / 64;  // chunks of one key a lane holds
@@ -154,7 +154,7 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   constexpr int NS = NV >= 8 ? 3 : (NV == 4 ? 2 : 1);  // transpose stages (rest: plain adds)
   constexpr int NK = NV >= 8 ? NV / 8 : 1;            // scores per lane after the reduction
   constexpr int DUP = 3 - NS;                          // low lane bits holding duplicates
-  using SM = DecodeSmem<D, G>;
+  using SM = DecodeSmem<D, G, NW>;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -202,11 +202,11 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   const uint4* vb = reinterpret_cast<const uint4*>(a.v_cache) + (int64_t)g * tile_stride;
   const int th = lane & 1;  // token half of the V^T rows this lane holds
 
-  // Blocks b_begin + wave + 4k, k < nk (nk <= 64: a split has at most 256 blocks); their
+  // Blocks b_begin + wave + NW*k, k < nk (nk <= 64: a split has at most 256 blocks); their
   // physical ids are fetched once, one per lane, and read back with v_readlane.
   const int nb = b_end - b_begin;
-  const int nk = nb > wave ? (nb - wave + 3) / 4 : 0;
-  const int my_id = lane < nk ? bt[b_begin + wave + 4 * lane] : 0;
+  const int nk = nb > wave ? (nb - wave + NW - 1) / NW : 0;
+  const int my_id = lane < nk ? bt[b_begin + wave + NW * lane] : 0;
 
   constexpr int NKR = 2 * CPT;  // key chunks per lane per block
   auto load = [&](int k, uint4 (&kr)[NKR], uint4 (&vr)[RPL]) {
@@ -222,7 +222,7 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   };
 
   auto process = [&](int k, uint4 (&kr)[NKR], uint4 (&vr)[RPL]) {
-    const int t0 = (b_begin + wave + 4 * k) * kBlockSize;
+    const int t0 = (b_begin + wave + NW * k) * kBlockSize;
     const int nvalid = kv_end - t0;  // < 16 only in the last block
     // Q.K partial dot products: v[2*hh + ts].
     float v[NV];
@@ -371,9 +371,9 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
 
-  float* s_o = reinterpret_cast<float*>(smem_raw);  // [4][G][D]
-  float* s_m = s_o + SM::O_FLOATS;                   // [4][G]
-  float* s_l = s_m + 4 * G;                          // [4][G]
+  float* s_o = reinterpret_cast<float*>(smem_raw);  // [NW][G][D]
+  float* s_m = s_o + SM::O_FLOATS;                   // [NW][G]
+  float* s_l = s_m + NW * G;                         // [NW][G]
   if (th == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
@@ -397,7 +397,7 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
 #pragma unroll
     for (int e = 0; e < 8; ++e) oo[e] = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float* src = s_o + (w * G + hh) * D + cc * 8;
       float o2[8];
 #pragma unroll
@@ -421,9 +421,10 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
 }
 
 // ------------------------------------------------------------------------------------------
-// MFMA tile: 128 packed rows (TOK tokens x G q heads of kv head g) over keys [kv_begin,
-// kv_end).  Wave w owns rows 32w..32w+31; lane (n = lane % 32, h = lane / 32) owns query
-// column n.  Rows beyond ntok tokens are padding (computed, never stored).
+// MFMA tile: 32*NW packed rows (32*NW/G tokens x G q heads of kv head g) over keys
+// [kv_begin, kv_end).  Wave w owns rows 32w..32w+31; lane (n = lane % 32, h = lane / 32) owns
+// query column n.  Rows beyond ntok tokens are padding (computed, never stored).  With 8 waves
+// the 64-key K/V tile staged in LDS serves 256 rows, halving staging traffic per flop.
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct TileSmem {
@@ -435,7 +436,7 @@ struct TileSmem {
   static constexpr int BYTES = 2 * BUF_ELEMS * 2;
 };
 
-template <int D, int G, bool CAUSAL>
+template <int D, int G, bool CAUSAL, int NW>
 __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t* __restrict__ k_cache,
                           const uint16_t* __restrict__ v_cache, int Hkv, int g,
                           const int32_t* __restrict__ bt, int tok0, int ntok, int pos0, int kv_begin,
@@ -479,87 +480,101 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
     for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
   float m = -INFINITY, lsum = 0.f;
 
-  // Staging: wave w copies logical block (tile/16 + w).  K rows are token-major: key
+  // Staging of the 64-key tile (4 cache blocks).  K rows are token-major: key
   // kk = KPI*i + lane/LPT, chunk lane%LPT.  The value pool is dim-major, so the V^T tile is a
-  // plain copy: chunk lane + 64i is row (lane >> 1) + 32i, token half lane & 1.
+  // plain copy: chunk lane + 64i is row (lane >> 1) + 32i, token half lane & 1.  With 4 waves,
+  // wave w copies K and V of block w; with 8 waves, waves 0-3 copy K and waves 4-7 copy V, and
+  // the loads run two tiles ahead of the compute (two register sets).  The loads are
+  // unconditional (past the end they re-read the last block and are zeroed) so the compiler's
+  // wait counts never wait for a later tile; block ids are scalar loads through the constant
+  // address space, so they do not drain the vector-load counter either.
   constexpr int NIV = D / 32;
+  static_assert(NI == NIV, "staging layout");
+  constexpr bool SPLIT = NW == 8;
+  constexpr int PD = SPLIT ? 2 : 1;           // prefetch distance in tiles
+  constexpr int RS = SPLIT ? NI : 2 * NI;     // staging registers (uint4) per tile
+  const int sblk = SPLIT ? (wave & 3) : wave;
+  const bool does_k = !SPLIT || wave < 4;
+  const bool does_v = !SPLIT || wave >= 4;
   const int sc = lane % LPT;
   const int sr = lane / LPT;
   const int64_t tile_stride = (int64_t)kBlockSize * CH;
   const int64_t blk_stride = (int64_t)Hkv * tile_stride;
   const uint4* kbase = reinterpret_cast<const uint4*>(k_cache) + (int64_t)g * tile_stride;
   const uint4* vbase = reinterpret_cast<const uint4*>(v_cache) + (int64_t)g * tile_stride;
-  uint4 kst[NI], vst[NIV];
+  typedef __attribute__((address_space(4))) const int32_t cint32;
+  const cint32* cbt = (const cint32*)bt;
+  const int last_blk = (kv_end - 1) / kBlockSize;
+  uint4 st[PD][RS];
 
-  auto stage_load = [&](int k0) {
-    const int lb = k0 / kBlockSize + wave;
-    const int key0 = lb * kBlockSize;
-    if (key0 < kv_end) {
-      const int64_t phys = __builtin_amdgcn_readfirstlane(bt[lb]);
-      const uint4* kp = kbase + phys * blk_stride;
-      const uint4* vp = vbase + phys * blk_stride;
+  // Loads only: the masking of keys past the end happens at store time, so nothing here
+  // waits for the data.  Returns how many of the block's keys are valid (<= 0: none).
+  auto stage_load = [&](int tile, uint4 (&r)[RS]) -> int {
+    const int lb = kv_begin / kBlockSize + 4 * tile + sblk;
+    const int64_t phys = cbt[min(lb, last_blk)];
+    const uint4* kp = kbase + phys * blk_stride;
+    const uint4* vp = vbase + phys * blk_stride;
+    if constexpr (SPLIT) {
+      // One unconditional load stream per wave: K rows for waves 0-3, V^T chunks for 4-7.
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        r[i] = does_k ? kp[(KPI * i + sr) * CH + sc] : vp[lane + 64 * i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) r[i] = kp[(KPI * i + sr) * CH + sc];
+#pragma unroll
+      for (int i = 0; i < NIV; ++i) r[NI + i] = vp[lane + 64 * i];
+    }
+    return kv_end - lb * kBlockSize;
+  };
+
+  auto stage_store = [&](int buf, const uint4 (&r)[RS], int nvalid) {
+    uint16_t* ks = smem + buf * S::BUF_ELEMS;
+    uint16_t* vs = ks + S::K_ELEMS;
+    if (does_k) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int kk = KPI * i + sr;
-        kst[i] = (key0 + kk < kv_end) ? kp[kk * CH + sc] : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 x = (kk < nvalid) ? r[i] : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(ks + (sblk * kBlockSize + kk) * S::KP + sc * 8) = x;
       }
-#pragma unroll
-      for (int i = 0; i < NIV; ++i) vst[i] = vp[lane + 64 * i];
-      const int nvalid = kv_end - key0;
-      if (nvalid < kBlockSize) {
-        // Zero the values of keys past the end (the cache may hold NaN there).
-        const int t = 8 * (lane & 1);
-        uint32_t msk[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          msk[u] = (t + 2 * u < nvalid ? 0x0000ffffu : 0u) | (t + 2 * u + 1 < nvalid ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int i = 0; i < NIV; ++i) {
-          vst[i].x &= msk[0];
-          vst[i].y &= msk[1];
-          vst[i].z &= msk[2];
-          vst[i].w &= msk[3];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) kst[i] = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-      for (int i = 0; i < NIV; ++i) vst[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-
-  auto stage_store = [&](int buf) {
-    uint16_t* ks = smem + buf * S::BUF_ELEMS;
-    uint16_t* vs = ks + S::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int kk = wave * kBlockSize + KPI * i + sr;
-      *reinterpret_cast<uint4*>(ks + kk * S::KP + sc * 8) = kst[i];
     }
     // Within each block the four 4-key groups are stored in the order 0, 2, 1, 3 (key t goes
     // to column 8*((t>>2)&1) + 4*(t>>3) + (t&3)), so the 8 keys one lane feeds a PV K-step
-    // (t = 4h..4h+3 and 8+4h..8+4h+3) are one conflict-free 16-byte read.
+    // (t = 4h..4h+3 and 8+4h..8+4h+3) are one conflict-free 16-byte read.  Values of keys past
+    // the end are zeroed (the cache may hold NaN there).
+    if (does_v) {
+      constexpr int vo = SPLIT ? 0 : NI;
+      const int t = 8 * (lane & 1);
+      uint32_t msk[4];
 #pragma unroll
-    for (int i = 0; i < NIV; ++i) {
-      const int row = (lane >> 1) + 32 * i;
-      uint16_t* dst = vs + row * S::VP + wave * kBlockSize + 4 * (lane & 1);
-      *reinterpret_cast<uint2*>(dst) = make_uint2(vst[i].x, vst[i].y);
-      *reinterpret_cast<uint2*>(dst + 8) = make_uint2(vst[i].z, vst[i].w);
+      for (int u = 0; u < 4; ++u)
+        msk[u] = (t + 2 * u < nvalid ? 0x0000ffffu : 0u) | (t + 2 * u + 1 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int i = 0; i < NIV; ++i) {
+        const int row = (lane >> 1) + 32 * i;
+        uint16_t* dst = vs + row * S::VP + sblk * kBlockSize + 4 * (lane & 1);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(r[vo + i].x & msk[0], r[vo + i].y & msk[1]);
+        *reinterpret_cast<uint2*>(dst + 8) = make_uint2(r[vo + i].z & msk[2], r[vo + i].w & msk[3]);
+      }
     }
   };
 
   const int ntiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
   const int min_pos = pos0;  // first token of the tile has the smallest position
 
-  stage_load(kv_begin);
-  stage_store(0);
+  int nv[PD];
+  nv[0] = stage_load(0, st[0]);
+  if constexpr (PD == 2) nv[1] = stage_load(1, st[1]);
+  stage_store(0, st[0], nv[0]);
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  // One KV tile: prefetch tile t+PD into `ld`, compute tile t from LDS, then store tile t+1
+  // (held in `sto`) into the other LDS buffer.
+  auto body = [&](int t, uint4 (&ld)[RS], int& nld, uint4 (&sto)[RS], int& nsto) {
     const int k0 = kv_begin + t * kKvTile;
     const int buf = t & 1;
-    if (t + 1 < ntiles) stage_load(k0 + kKvTile);
+    nld = stage_load(t + PD, ld);
 
     const uint16_t* ks = smem + buf * S::BUF_ELEMS;
     const uint16_t* vs = ks + S::K_ELEMS;
@@ -639,9 +654,16 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
       }
     }
 
-    if (t + 1 < ntiles) stage_store(buf ^ 1);
+    if (t + 1 < ntiles) stage_store(buf ^ 1, sto, nsto);
     __syncthreads();
+  };
+
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    body(t, st[0], nv[0], st[PD - 1], nv[PD - 1]);
+    body(t + 1, st[PD - 1], nv[PD - 1], st[0], nv[0]);
   }
+  if (t < ntiles) body(t, st[0], nv[0], st[PD - 1], nv[PD - 1]);
 
   lsum += __shfl_xor(lsum, 32);
   if (!row_valid) return;
@@ -669,9 +691,10 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
 }
 
 // DECODE_ONLY instantiations carry no MFMA path, so they need far fewer registers and run
-// more waves per SIMD; a plan with any prefill tile uses the full kernel.
-template <int D, int G, bool DECODE_ONLY>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+// more waves per SIMD; a plan with any prefill tile uses the full kernel, with 4 or 8 waves
+// per workgroup (8 when the batch carries enough prefill rows to fill 256-row tiles).
+template <int D, int G, bool DECODE_ONLY, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu(DECODE_ONLY ? (G >= 8 ? PKV_DECODE_WAVES_G8 : PKV_DECODE_WAVES) : 2)))
 void varlen_kernel(VarlenArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -679,20 +702,21 @@ void varlen_kernel(VarlenArgs a) {
   const int g = x % a.num_kv_heads;
   const WorkItem it = a.items[x / a.num_kv_heads];
   if (DECODE_ONLY || it.kind == kDecode) {
-    decode_item<D, G>(a, it, g, smem);
+    decode_item<D, G, NW>(a, it, g, smem);
   } else {
     const int r = it.seq;
     const int ctx = a.context_lens[r];
     const int tok0 = a.query_start_loc[r] + it.q_begin;
     const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
-    mfma_tile<D, G, true>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g, bt, tok0,
-                          it.q_count, ctx + it.q_begin, it.kv_begin, it.kv_end, a.scale_log2, a.out,
-                          a.out_f32, a.lse, smem);
+    mfma_tile<D, G, true, NW>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g, bt, tok0,
+                              it.q_count, ctx + it.q_begin, it.kv_begin, it.kv_end, a.scale_log2,
+                              a.out, a.out_f32, a.lse, smem);
   }
 }
 
 template <int D, int G>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kCascadeWaves, 64 * kCascadeWaves),
+                          amdgpu_waves_per_eu(2)))
 void cascade_kernel(CascadeArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int x = blockIdx.x;
@@ -700,7 +724,7 @@ void cascade_kernel(CascadeArgs a) {
   const int rest = x / a.num_kv_heads;
   const int tile = rest % a.num_tiles;
   const int seg = rest / a.num_tiles;
-  constexpr int TOK = kTileRows / G;
+  constexpr int TOK = 32 * kCascadeWaves / G;
   const int tok0 = tile * TOK;
   const int ntok = min(TOK, a.num_tokens - tok0);
   const int kv_begin = seg * a.seg_len;
@@ -711,8 +735,9 @@ void cascade_kernel(CascadeArgs a) {
     out = a.part_o + (int64_t)seg * a.num_tokens * a.num_q_heads * D;
     lse = a.part_lse + (int64_t)seg * a.num_tokens * a.num_q_heads;
   }
-  mfma_tile<D, G, false>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g, a.prefix_bt,
-                         tok0, ntok, 0, kv_begin, kv_end, a.scale_log2, out, 1, lse, smem);
+  mfma_tile<D, G, false, kCascadeWaves>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g,
+                                        a.prefix_bt, tok0, ntok, 0, kv_begin, kv_end, a.scale_log2,
+                                        out, 1, lse, smem);
 }
 
 // One wave per (token, head) row; lane holds D/64 consecutive dims.
@@ -774,22 +799,30 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   if (a.lse && lane == 0) a.lse[orow] = (z > 0.f) ? mx + __logf(z) : -INFINITY;
 }
 
-template <int D, int G>
+template <int D, int G, int NW>
 size_t varlen_smem(bool has_prefill) {
-  const size_t dec = (size_t)DecodeSmem<D, G>::BYTES;
+  const size_t dec = (size_t)DecodeSmem<D, G, NW>::BYTES;
   const size_t pre = has_prefill ? (size_t)TileSmem<D>::BYTES : 0;
   return dec > pre ? dec : pre;
 }
 
 template <int D, int G>
-hipError_t launch_varlen_t(const VarlenArgs& a, bool has_prefill, hipStream_t stream) {
-  const size_t smem = varlen_smem<D, G>(has_prefill);
+hipError_t launch_varlen_t(const VarlenArgs& a, bool has_prefill, int waves, hipStream_t stream) {
   const int64_t grid = (int64_t)a.num_items * a.num_kv_heads;
   if (grid == 0) return hipSuccess;
-  if (has_prefill)
-    hipLaunchKernelGGL((varlen_kernel<D, G, false>), dim3((unsigned)grid), dim3(kThreads), smem, stream, a);
-  else
-    hipLaunchKernelGGL((varlen_kernel<D, G, true>), dim3((unsigned)grid), dim3(kThreads), smem, stream, a);
+  if (!has_prefill) {
+    auto kern = varlen_kernel<D, G, true, 4>;
+    const size_t smem = varlen_smem<D, G, 4>(false);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), smem, stream, a);
+  } else if (waves == 8) {
+    auto kern = varlen_kernel<D, G, false, 8>;
+    const size_t smem = varlen_smem<D, G, 8>(true);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), smem, stream, a);
+  } else {
+    auto kern = varlen_kernel<D, G, false, 4>;
+    const size_t smem = varlen_smem<D, G, 4>(true);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), smem, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -797,7 +830,7 @@ template <int D, int G>
 hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.num_tiles * a.num_segments * a.num_kv_heads;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((cascade_kernel<D, G>), dim3((unsigned)grid), dim3(kThreads),
+  hipLaunchKernelGGL((cascade_kernel<D, G>), dim3((unsigned)grid), dim3(64 * kCascadeWaves),
                      (size_t)TileSmem<D>::BYTES, stream, a);
   return hipGetLastError();
 }
@@ -825,9 +858,9 @@ hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
   }                                                   \
   return hipErrorInvalidValue;
 
-hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, bool has_prefill,
+hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, bool has_prefill, int waves,
                          hipStream_t stream) {
-#define CALL_V(D, G) launch_varlen_t<D, G>(a, has_prefill, stream)
+#define CALL_V(D, G) launch_varlen_t<D, G>(a, has_prefill, waves, stream)
   PKV_DISPATCH_DG(head_dim, group, CALL_V)
 #undef CALL_V
 }

@@ -72,7 +72,7 @@ def run_and_check(wl, rows_per_step=None, check_pools=True, want_lse=True, out_d
         if want_lse:
             r["lse_max_abs"] = check_lse(lse_g.cpu().numpy()[sel], l_ref[sel], f"{wl.name} step {si} lse")
         stats.append(r)
-        say(f"    plan items={plan.num_items} partials={plan.num_partials} bps={plan.blocks_per_split} {r}")
+        say(f"    plan items={plan.num_items} waves={plan.waves_per_group} partials={plan.num_partials} bps={plan.blocks_per_split} {r}")
     return stats
 
 
@@ -105,6 +105,13 @@ def test_decode_group8_parity():
 def test_long_chunked_prefill_small_parity():
     say("long_chunked_prefill small: 1024-token prompt in 4 chunks of 256, 6 decode rows")
     run_and_check(W.long_chunked_prefill(seed=1, prompt=1024, chunk=256, num_decode=6, decode_ctx=333))
+
+
+def test_long_chunked_prefill_8wave_tiles_parity():
+    """512-token chunks x 4 q heads per kv head = 2048 packed rows: the plan picks 256-row tiles."""
+    say("long_chunked_prefill small with 8-wave tiles: 1536-token prompt in 3 chunks of 512")
+    stats = run_and_check(W.long_chunked_prefill(seed=2, prompt=1536, chunk=512, num_decode=5, decode_ctx=700))
+    assert stats
 
 
 def test_single_key_rows_are_exact():
