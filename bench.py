@@ -1,9 +1,10 @@
 """Benchmark: mixed continuous-batch paged attention on one MI355X.
 
 One step = one pass of the whole hot path over the mixed Llama-3-8B-shaped batch (32 q / 8 kv
-heads, head_dim 128, block 16): for each of its three scheduler iterations — slot mapping,
-reshape_and_cache, the varlen plan and one paged_attention_varlen launch (decode rows on the
-VALU path, chunked-prefill / prefix-hit rows on MFMA, split-KV reduce).  The 330 query tokens of
+heads, head_dim 128, block 16): for each of its three scheduler iterations — slot mapping and
+cache write (one fused launch), the varlen plan upload and one paged_attention_varlen launch
+(decode rows on the VALU path with the split-KV merge fused in, chunked-prefill / prefix-hit
+rows on MFMA).  The 330 query tokens of
 the pass give the headline attention tokens/s per layer.  Inputs are synthetic (seeded N(0,1)
 bf16) and resident in HBM before timing starts.
 
@@ -90,8 +91,9 @@ class Runner:
         P = self.P
         for i, s in enumerate(self.steps):
             st = s["st"]
-            P.compute_slot_mapping(s["bt"], s["qsl"], s["ctx"], self.shape, st.num_tokens, out=s["slots"])
-            P.reshape_and_cache(s["k"], s["v"], self.k_cache, self.v_cache, s["slots"], self.shape)
+            # slot mapping + cache write (one launch), plan upload, attention (one launch)
+            P.append_kv(s["k"], s["v"], self.k_cache, self.v_cache, s["bt"], s["qsl"], s["ctx"], self.shape,
+                        slot_mapping=s["slots"])
             plan = P.plan_varlen(self.ws, st.query_start_loc, st.context_lens, st.seq_lens, self.shape)
             if events is not None:
                 events[i][0].record()
@@ -104,9 +106,13 @@ class Runner:
 
 
 def time_passes(runner, torch, steps, warmup):
+    import gc
+
     for _ in range(warmup):
         runner.run_pass()
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()  # no collector pauses inside the timed region
     n = len(runner.steps)
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(n)] for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -116,6 +122,7 @@ def time_passes(runner, torch, steps, warmup):
         runner.run_pass(ev[k])
     stop.record()
     torch.cuda.synchronize()
+    gc.enable()
     total_ms = start.elapsed_time(stop)
     per_step_kernel_ms = [float(np.mean([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(steps)])) for i in range(n)]
     return total_ms, per_step_kernel_ms

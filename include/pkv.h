@@ -5,9 +5,12 @@
  *   q             bf16 [num_tokens, num_q_heads, head_dim]; the new tokens of every request,
  *                 concatenated request after request (batched prefill: Tencent Cloud
  *                 article on vLLM inference acceleration, batched-prefill paragraph).
- *   k_cache,      bf16 [num_blocks, num_kv_heads, block_size, head_dim]; physical block
- *   v_cache       pools. Token p of a request lives in physical block block_tables[r][p / bs]
- *                 at offset p % bs ("11. vLLM principles", section 11.2 PagedAttention).
+ *   k_cache       bf16 [num_blocks, num_kv_heads, block_size, head_dim]: physical key blocks,
+ *                 token-major (a key is one contiguous row).
+ *   v_cache       bf16 [num_blocks, num_kv_heads, head_dim, block_size]: physical value blocks,
+ *                 dim-major (16 tokens of one dimension are contiguous).
+ *                 Token p of a request lives in physical block block_tables[r][p / bs] at
+ *                 offset p % bs ("11. vLLM principles", section 11.2 PagedAttention).
  *   block_tables  int32 [num_seqs, bt_stride]; logical block -> physical block per request.
  *                 Rows may share physical blocks (shared, read-only prefix; same section).
  *   query_start_loc int32 [num_seqs + 1]; request r owns tokens [qsl[r], qsl[r+1]).
@@ -95,11 +98,21 @@ int pkv_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
                              void* stream);
 
 /* a2 — KV caching [2048ai.net vLLM V1 article, "KV Caching"]: copies the bits of k[t] and
- * v[t] (bf16 [num_tokens, num_kv_heads, head_dim]) into the pools at slot_mapping[t].
+ * v[t] (bf16 [num_tokens, num_kv_heads, head_dim]) into the pools at slot_mapping[t]
+ * (keys token-major [num_blocks, Hkv, bs, D]; values dim-major [num_blocks, Hkv, D, bs]).
  * Negative slots and slots >= num_blocks * block_size are skipped.  Bit-exact copy. */
 int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                           const int64_t* slot_mapping, int32_t num_tokens,
                           const pkv_shape* shape, void* stream);
+
+/* a1 + a2 in one launch, for callers that do not need the slots separately: computes every
+ * new token's slot from block_tables / query_start_loc / context_lens exactly as
+ * pkv_compute_slot_mapping does, stores the token's K and V there as pkv_reshape_and_cache
+ * does, and also writes the slots to slot_mapping when it is not NULL. */
+int pkv_append_kv(int64_t* slot_mapping, const void* k, const void* v, void* k_cache,
+                  void* v_cache, const int32_t* block_tables, const int32_t* query_start_loc,
+                  const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
+                  const pkv_shape* shape, void* stream);
 
 /* Builds the work list of one varlen attention call from host copies of the metadata:
  * validates seq_lens[r] == context_lens[r] + (qsl[r+1] - qsl[r]) and every length, cuts
@@ -113,8 +126,9 @@ int pkv_plan_varlen(pkv_varlen_plan* plan, void* workspace, size_t workspace_byt
                     const pkv_shape* shape, void* stream);
 
 /* The same planning into host memory only (no device work): writes up to `max_items`
- * work items of 8 int32 each {seq, kind (0 decode, 1 prefill), q_begin, q_count,
- * kv_begin, kv_end, partial_base, split} into `items`.  For inspection and tests. */
+ * work items of 8 int32 each {seq, kind (0 decode, 1 prefill), q_begin, q_count (prefill:
+ * tokens of the tile; decode: splits of the row), kv_begin, kv_end, partial_base, split}
+ * into `items`.  For inspection and tests. */
 int pkv_plan_varlen_host(pkv_varlen_plan* plan, int32_t* items, int32_t max_items,
                          const int32_t* h_query_start_loc, const int32_t* h_context_lens,
                          const int32_t* h_seq_lens, int32_t num_seqs, int32_t num_tokens,

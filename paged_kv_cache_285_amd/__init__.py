@@ -8,6 +8,7 @@ raises if the library has not been built.
 from ._lib import PKV_DTYPE_BF16, PKV_DTYPE_F32, PkvError, PkvShape, PkvVarlenPlan, lib  # noqa: F401
 from .ops import (  # noqa: F401
     alloc_workspace,
+    append_kv,
     cascade_prefix_attention,
     cascade_workspace_size,
     compute_slot_mapping,

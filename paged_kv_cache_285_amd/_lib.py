@@ -21,6 +21,7 @@ EXPORTS = (
     "pkv_varlen_workspace_size",
     "pkv_compute_slot_mapping",
     "pkv_reshape_and_cache",
+    "pkv_append_kv",
     "pkv_plan_varlen",
     "pkv_plan_varlen_host",
     "pkv_paged_attention_varlen",
@@ -81,6 +82,7 @@ _SIGS = {
     "pkv_varlen_workspace_size": (_SZ, [_I32, _I32, _I32, _SHAPE]),
     "pkv_compute_slot_mapping": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _SHAPE, _P]),
     "pkv_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _SHAPE, _P]),
+    "pkv_append_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _P]),
     "pkv_plan_varlen": (ctypes.c_int, [_PLAN, _P, _SZ, _P, _P, _P, _I32, _I32, _SHAPE, _P]),
     "pkv_plan_varlen_host": (ctypes.c_int, [_PLAN, _P, _I32, _P, _P, _P, _I32, _I32, _SHAPE]),
     "pkv_paged_attention_varlen": (

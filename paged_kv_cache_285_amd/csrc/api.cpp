@@ -163,7 +163,7 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
         it.seq = r;
         it.kind = pkv::kDecode;
         it.q_begin = 0;
-        it.q_count = 1;
+        it.q_count = splits;
         it.kv_begin = sidx * bps * pkv::kBlockSize;
         it.kv_end = std::min<int32_t>(seq[r], (sidx + 1) * bps * pkv::kBlockSize);
         it.partial_base = splits > 1 ? partials : -1;
@@ -230,8 +230,9 @@ struct StagingSlot {
   hipEvent_t ev = nullptr;
   bool pending = false;
 };
+constexpr int kStagingSlots = 32;
 struct StagingRing {
-  StagingSlot slot[8];
+  StagingSlot slot[kStagingSlots];
   int next = 0;
 };
 thread_local std::unordered_map<int, StagingRing> g_rings;
@@ -243,10 +244,13 @@ int stage_and_copy(void* dst, const void* src, size_t bytes, hipStream_t stream)
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   StagingRing& ring = g_rings[dev];
   StagingSlot& sl = ring.slot[ring.next];
-  ring.next = (ring.next + 1) % 8;
+  ring.next = (ring.next + 1) % kStagingSlots;
   if (sl.pending) {
-    e = hipEventSynchronize(sl.ev);
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
+    // The copy that last read this buffer was enqueued kStagingSlots uploads ago; poll rather
+    // than sleep so a host running ahead of the device resumes as soon as it completes.
+    while ((e = hipEventQuery(sl.ev)) == hipErrorNotReady) {
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipEventQuery(staging)");
     sl.pending = false;
   }
   if (!sl.ev) {
@@ -330,6 +334,26 @@ int pkv_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
                                           context_lens, num_seqs, num_tokens, shape->bt_stride,
                                           (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "slot_mapping launch");
+  return ok();
+}
+
+int pkv_append_kv(int64_t* slot_mapping, const void* k, const void* v, void* k_cache,
+                  void* v_cache, const int32_t* block_tables, const int32_t* query_start_loc,
+                  const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
+                  const pkv_shape* shape, void* stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (num_tokens < 0 || num_seqs < 0) return fail(PKV_EINVAL, "negative sizes");
+  if (num_tokens == 0) return ok();
+  if (num_seqs == 0) return fail(PKV_EINVAL, "tokens without sequences");
+  if (!k || !v || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)
+    return fail(PKV_EINVAL, "null pointer argument");
+  const int64_t num_slots = (int64_t)shape->num_blocks * shape->block_size;
+  hipError_t e = pkv::launch_append_kv(
+      slot_mapping, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_tables,
+      query_start_loc, context_lens, num_seqs, num_tokens, shape->num_kv_heads, shape->head_dim,
+      shape->bt_stride, num_slots, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append_kv launch");
   return ok();
 }
 

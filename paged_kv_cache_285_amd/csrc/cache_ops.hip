@@ -67,7 +67,67 @@ __global__ void reshape_and_cache_kernel(const uint4* __restrict__ k, const uint
   }
 }
 
+// Slot mapping and cache write in one launch: one thread per 16-byte chunk of one token's K
+// and V for one kv head computes the token's slot from the block table (as above) and stores
+// the chunk; the (head 0, chunk 0) thread also records the slot when slot_mapping is given.
+__global__ void append_kv_kernel(int64_t* __restrict__ slot_out, const uint4* __restrict__ k,
+                                 const uint4* __restrict__ v, uint4* __restrict__ k_cache,
+                                 uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt,
+                                 const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
+                                 int32_t num_seqs, int32_t num_tokens, int32_t num_kv_heads,
+                                 int32_t chunks_per_head, int32_t bt_stride, int64_t num_slots) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)num_kv_heads * chunks_per_head;
+  const int64_t t = gid / per_token;
+  if (t >= num_tokens) return;
+  int32_t lo = 0, hi = num_seqs - 1;  // largest r with qsl[r] <= t
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int32_t pos = ctx[lo] + (int32_t)(t - qsl[lo]);
+  const int32_t logical = pos / kBlockSize;
+  int64_t slot = -1;
+  if (pos >= 0 && logical < bt_stride)
+    slot = (int64_t)bt[(int64_t)lo * bt_stride + logical] * kBlockSize + (pos % kBlockSize);
+  const int64_t within = gid - t * per_token;
+  if (slot_out && within == 0) slot_out[t] = slot;
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t h = within / chunks_per_head;
+  const int64_t c = within - h * chunks_per_head;
+  const int64_t blk = slot / kBlockSize;
+  const int64_t off = slot - blk * kBlockSize;
+  const int64_t tile = blk * num_kv_heads + h;
+  k_cache[(tile * kBlockSize + off) * chunks_per_head + c] = k[gid];
+  const uint4 x = v[gid];
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint16_t* vt = v_cache + (tile * chunks_per_head * 8 + c * 8) * kBlockSize + off;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vt[(2 * e) * kBlockSize] = (uint16_t)(w[e] & 0xffffu);
+    vt[(2 * e + 1) * kBlockSize] = (uint16_t)(w[e] >> 16);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append_kv(int64_t* slot_mapping, const uint16_t* k, const uint16_t* v,
+                            uint16_t* k_cache, uint16_t* v_cache, const int32_t* block_tables,
+                            const int32_t* qsl, const int32_t* ctx, int32_t num_seqs,
+                            int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t bt_stride, int64_t num_slots, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int32_t chunks = head_dim / 8;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     slot_mapping, reinterpret_cast<const uint4*>(k),
+                     reinterpret_cast<const uint4*>(v), reinterpret_cast<uint4*>(k_cache), v_cache,
+                     block_tables, qsl, ctx, num_seqs, num_tokens, num_kv_heads, chunks, bt_stride,
+                     num_slots);
+  return hipGetLastError();
+}
 
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
                                const int32_t* qsl, const int32_t* ctx, int32_t num_seqs,

@@ -20,7 +20,7 @@ struct WorkItem {
   int32_t seq;           // request index
   int32_t kind;          // ItemKind
   int32_t q_begin;       // first query token of the tile, relative to the request
-  int32_t q_count;       // query tokens in the tile
+  int32_t q_count;       // prefill: query tokens in the tile; decode: splits of the row
   int32_t kv_begin;      // first key (token index) of this item
   int32_t kv_end;        // one past the last key
   int32_t partial_base;  // decode: partial row base of the request (-1: write the output)
@@ -85,6 +85,11 @@ struct ReduceArgs {
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
                                const int32_t* qsl, const int32_t* ctx, int32_t num_seqs,
                                int32_t num_tokens, int32_t bt_stride, hipStream_t stream);
+hipError_t launch_append_kv(int64_t* slot_mapping, const uint16_t* k, const uint16_t* v,
+                            uint16_t* k_cache, uint16_t* v_cache, const int32_t* block_tables,
+                            const int32_t* qsl, const int32_t* ctx, int32_t num_seqs,
+                            int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t bt_stride, int64_t num_slots, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v, uint16_t* k_cache,
                                     uint16_t* v_cache, const int64_t* slots, int32_t num_tokens,
                                     int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,

@@ -114,6 +114,37 @@ def reshape_and_cache(
     )
 
 
+def append_kv(
+    k: torch.Tensor,
+    v: torch.Tensor,
+    k_cache: torch.Tensor,
+    v_cache: torch.Tensor,
+    block_tables: torch.Tensor,
+    query_start_loc: torch.Tensor,
+    context_lens: torch.Tensor,
+    shape: PkvShape,
+    slot_mapping: Optional[torch.Tensor] = None,
+) -> Optional[torch.Tensor]:
+    """Slot mapping and cache write in one launch; also fills ``slot_mapping`` when given."""
+    check(
+        lib().pkv_append_kv(
+            _opt(slot_mapping, "slot_mapping", (torch.int64,)),
+            _dev(k, "k", _16BIT),
+            _dev(v, "v", _16BIT),
+            _dev(k_cache, "k_cache", _16BIT),
+            _dev(v_cache, "v_cache", _16BIT),
+            _dev(block_tables, "block_tables", (torch.int32,)),
+            _dev(query_start_loc, "query_start_loc", (torch.int32,)),
+            _dev(context_lens, "context_lens", (torch.int32,)),
+            int(context_lens.numel()),
+            int(k.shape[0]),
+            ctypes.byref(shape),
+            _stream(),
+        )
+    )
+    return slot_mapping
+
+
 def varlen_workspace_size(num_seqs: int, num_tokens: int, max_seq_len: int, shape: PkvShape) -> int:
     return int(lib().pkv_varlen_workspace_size(num_seqs, num_tokens, max_seq_len, ctypes.byref(shape)))
 

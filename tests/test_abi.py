@@ -94,16 +94,16 @@ def test_plan_covers_every_row_exactly_once(P):
             cover_tok[qsl[seqi] + qb : qsl[seqi] + qb + qc] += 1
             assert kb == 0 and ke == min(seq[seqi], ctx[seqi] + qb + qc)
         else:
-            assert ql[seqi] == 1 and qc == 1
+            assert ql[seqi] == 1
             cover_tok[qsl[seqi]] += split == 0
-            dec_keys.setdefault(seqi, []).append((kb, ke, pbase, split))
+            dec_keys.setdefault(seqi, []).append((kb, ke, pbase, split, qc))
     assert (cover_tok == 1).all()
     for r, ranges in dec_keys.items():
         ranges.sort()
         assert ranges[0][0] == 0 and ranges[-1][1] == seq[r]
         for a, b in zip(ranges, ranges[1:]):
             assert a[1] == b[0] and a[1] % 16 == 0
-        assert all(x[3] == i for i, x in enumerate(ranges))
+        assert all(x[3] == i and x[4] == len(ranges) for i, x in enumerate(ranges))
         if len(ranges) == 1:
             assert ranges[0][2] == -1
     # heaviest first within each kind

@@ -125,6 +125,49 @@ def test_single_key_rows_are_exact():
     assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), np.repeat(st.v, wl.group, axis=1))
 
 
+def test_append_kv_matches_oracle_bitwise():
+    """Slot mapping and cache write fused in one launch: slots and pool bits equal the oracle's."""
+    say("append_kv (fused slot mapping + cache write)")
+    wl = W.mixed_llama8b(seed=4, num_decode=9, ctx_range=(5, 300))
+    dw = DeviceWorkload(wl)
+    kp, vp = wl.k_cache, wl.v_cache
+    for st in wl.steps:
+        t = dw.step_tensors(st)
+        slots = torch.empty(st.num_tokens, dtype=torch.int64, device="cuda")
+        P.append_kv(t["k"], t["v"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], t["ctx"], dw.shape, slot_mapping=slots)
+        torch.cuda.synchronize()
+        ref = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, wl.block_size)
+        assert np.array_equal(slots.cpu().numpy(), ref)
+        kp, vp = O.reshape_and_cache(st.k, st.v, kp, vp, ref, wl.block_size)
+        assert np.array_equal(host16(dw.k_cache), kp) and np.array_equal(host16(dw.v_cache), vp)
+
+
+def test_plan_reuse_is_bit_identical():
+    """The same plan run three times over split-KV rows gives identical bits and matches the oracle."""
+    say("plan reuse with split-KV rows")
+    wl = W.decode_only(seed=8, num_seqs=12, ctx_range=(3000, 9000))
+    st = wl.steps[0]
+    dw = DeviceWorkload(wl)
+    t = dw.step_tensors(st)
+    P.append_kv(t["k"], t["v"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], t["ctx"], dw.shape)
+    plan = P.plan_varlen(dw.ws, st.query_start_loc, st.context_lens, st.seq_lens, dw.shape)
+    assert plan.num_partials > 0
+    outs = []
+    for _ in range(3):
+        outs.append(
+            P.paged_attention_varlen(
+                t["q"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], t["ctx"], t["seq"], dw.shape, plan, dw.ws
+            )
+        )
+    torch.cuda.synchronize()
+    a = [o.view(torch.int16).cpu().numpy() for o in outs]
+    assert np.array_equal(a[0], a[1]) and np.array_equal(a[0], a[2])
+    slots = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, wl.block_size)
+    kp, vp = O.reshape_and_cache(st.k, st.v, wl.k_cache, wl.v_cache, slots, wl.block_size)
+    ref, _ = O.paged_attention(st.q, kp, vp, st.block_tables, st.query_start_loc, st.context_lens, st.seq_lens, wl.block_size)
+    check_attention(bf16_out_to_f64(outs[2]), ref, "plan reuse")
+
+
 def test_permutation_invariance_and_rerun_bit_identical():
     say("physical permutation invariance")
     wl = W.decode_only(seed=5, num_seqs=10, ctx_range=(30, 900))
