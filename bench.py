@@ -106,26 +106,51 @@ class Runner:
 
 
 def time_passes(runner, torch, steps, warmup):
+    """Time `steps` passes bracketed by device syncs; the library's launch timing brackets each
+    varlen attention kernel with HIP events on its stream.  Returns (total ms, kernel ms per
+    launch, launches)."""
     import gc
 
+    P = runner.P
     for _ in range(warmup):
         runner.run_pass()
     torch.cuda.synchronize()
     gc.collect()
     gc.disable()  # no collector pauses inside the timed region
-    n = len(runner.steps)
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(n)] for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    P.timing_begin()
     start.record()
-    for k in range(steps):
-        runner.run_pass(ev[k])
+    for _ in range(steps):
+        runner.run_pass()
     stop.record()
     torch.cuda.synchronize()
+    kern_total, launches = P.timing_end()
     gc.enable()
-    total_ms = start.elapsed_time(stop)
-    per_step_kernel_ms = [float(np.mean([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(steps)])) for i in range(n)]
-    return total_ms, per_step_kernel_ms
+    return start.elapsed_time(stop), kern_total / max(launches, 1), launches
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "varlen_kernel_mixed_llama8b_hbm_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by a
+    plain-copy calibration), or None when the kernel sources changed since they were taken."""
+    import hashlib
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            doc = json.load(f)
+        h = hashlib.sha256()
+        for p in doc["kernel_sources"]:
+            with open(os.path.join(HERE, p), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != doc["kernel_sources_sha256"]:
+            return None
+        return float(doc["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, budget_s=15.0):
@@ -167,8 +192,7 @@ def decode_hbm(torch, P, steps=10, warmup=3):
     r = Runner(wl, torch, P)
     st = wl.steps[0]
     s = r.steps[0]
-    P.compute_slot_mapping(s["bt"], s["qsl"], s["ctx"], r.shape, st.num_tokens, out=s["slots"])
-    P.reshape_and_cache(s["k"], s["v"], r.k_cache, r.v_cache, s["slots"], r.shape)
+    P.append_kv(s["k"], s["v"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"], r.shape)
     plan = P.plan_varlen(r.ws, st.query_start_loc, st.context_lens, st.seq_lens, r.shape)
 
     def call():
@@ -179,18 +203,16 @@ def decode_hbm(torch, P, steps=10, warmup=3):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
+    P.timing_begin()
     for _ in range(steps):
         call()
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+    total, n = P.timing_end()
+    ms = total / n
     nbytes = step_bytes(st, wl)
     gbs = nbytes / (ms * 1e-3) / 1e9
     res = {
         "workload": "decode_only: 256 seqs, ctx U[1024,8192], 32q/8kv, D128, bs16",
-        "ms_per_call": ms,
+        "kernel_ms": ms,
         "algorithmic_bytes": nbytes,
         "GB/s": gbs,
         "frac_of_peak": gbs / HBM_PEAK_GBS,
@@ -203,6 +225,86 @@ def decode_hbm(torch, P, steps=10, warmup=3):
     return res
 
 
+def mfma_paths(torch, P, reps=5):
+    """MFMA-bound paths: the cascade shared-prefix pass (512 queries x 64 q heads over a
+    16384-token prefix) and the long chunked prefill (one 32768-token prompt in 16 chunks of
+    2048, no decode rows), as TFLOP/s against the 2.5 PFLOP/s bf16 dense peak."""
+    import workloads as W
+
+    out = {}
+    wl = W.cascade_shared_prefix(seed=0)
+    r = Runner(wl, torch, P)
+    st, s, cv = wl.steps[0], r.steps[0], wl.cascade
+    P.append_kv(s["k"], s["v"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"], r.shape)
+    pbt = torch.from_numpy(cv.prefix_block_table).cuda()
+    cws = P.alloc_workspace(P.cascade_workspace_size(st.num_tokens, cv.prefix_len, r.shape))
+    o = torch.empty(st.q.shape, dtype=torch.float32, device="cuda")
+    l = torch.empty(st.q.shape[:2], dtype=torch.float32, device="cuda")
+    pb = cv.prefix_len // wl.block_size
+    sbt = torch.from_numpy(np.ascontiguousarray(st.block_tables[:, pb:])).cuda()
+    sshape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, sbt.shape[1])
+    sctx, sseq = torch.from_numpy(cv.suffix_context_lens).cuda(), torch.from_numpy(cv.suffix_seq_lens).cuda()
+    splan = P.plan_varlen(r.ws, st.query_start_loc, cv.suffix_context_lens, cv.suffix_seq_lens, sshape)
+    os_, ls_ = torch.empty_like(o), torch.empty_like(l)
+    merged = torch.empty(st.q.shape, dtype=torch.bfloat16, device="cuda")
+
+    def cascade():
+        P.cascade_prefix_attention(s["q"], r.k_cache, r.v_cache, pbt, cv.prefix_len, r.shape, cws, out=o, lse=l)
+        P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, sbt, s["qsl"], sctx, sseq, sshape, splan, r.ws,
+                                 out=os_, lse=ls_)
+        P.merge_attn_states(o, l, os_, ls_, out=merged)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    prefix_ms = timed(lambda: P.cascade_prefix_attention(s["q"], r.k_cache, r.v_cache, pbt, cv.prefix_len,
+                                                         r.shape, cws, out=o, lse=l), reps)
+    cascade_ms = timed(cascade, reps)
+    fplan = P.plan_varlen(r.ws, st.query_start_loc, st.context_lens, st.seq_lens, r.shape)
+    single_ms = timed(lambda: P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"],
+                                                       s["seq"], r.shape, fplan, r.ws, out=s["out"]), reps)
+    flops = st.num_tokens * wl.num_q_heads * cv.prefix_len * 4 * wl.head_dim
+    out["cascade_prefix"] = {
+        "workload": "512 queries, 64 q / 8 kv heads, D128, shared 16384-token prefix",
+        "ms": prefix_ms,
+        "TFLOP/s": flops / (prefix_ms * 1e-3) / 1e12,
+        "frac_of_bf16_peak": flops / (prefix_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        "cascade_total_ms": cascade_ms,
+        "single_pass_ms": single_ms,
+        "cascade_speedup": single_ms / cascade_ms,
+    }
+    del r
+    torch.cuda.empty_cache()
+
+    wl = W.long_chunked_prefill(seed=0, num_decode=0)
+    r = Runner(wl, torch, P)
+    tot_ms, tot_fl = 0.0, 0
+    for s in r.steps:
+        st = s["st"]
+        P.append_kv(s["k"], s["v"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"], r.shape)
+        plan = P.plan_varlen(r.ws, st.query_start_loc, st.context_lens, st.seq_lens, r.shape)
+        tot_ms += timed(lambda: P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"],
+                                                         s["seq"], r.shape, plan, r.ws, out=s["out"]), 2)
+        tot_fl += step_flops(st, wl)
+    out["long_chunked_prefill"] = {
+        "workload": "one 32768-token prompt in 16 chunks of 2048 against its growing paged context, 32 q / 8 kv heads",
+        "ms_all_chunks": tot_ms,
+        "TFLOP/s": tot_fl / (tot_ms * 1e-3) / 1e12,
+        "frac_of_bf16_peak": tot_fl / (tot_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+    }
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +312,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--mfma", action="store_true", help="also time the MFMA-bound cascade prefix and long prefill")
+    ap.add_argument(
+        "--copy-calibration",
+        type=int,
+        default=0,
+        metavar="BYTES",
+        help="only run one plain device-to-device copy of BYTES (to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)",
+    )
     args = ap.parse_args()
     if args.gpus != 1:
         print(
@@ -221,6 +331,16 @@ def main():
 
     import torch
 
+    if args.copy_calibration:
+        n = args.copy_calibration // 2
+        src = torch.ones(n, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 2 * n}), flush=True)
+        return
+
     import paged_kv_cache_285_amd as P
     import workloads as W
 
@@ -228,15 +348,16 @@ def main():
     wl = W.mixed_llama8b(seed=0)
     runner = Runner(wl, torch, P)
     log(f"bench: timing {args.steps} steps after {args.warmup} warmup")
-    total_ms, kern_ms = time_passes(runner, torch, args.steps, args.warmup)
+    total_ms, kern_ms, launches = time_passes(runner, torch, args.steps, args.warmup)
     ms_per_step = total_ms / args.steps
     tokens = sum(st.num_tokens for st in wl.steps)
     value = tokens / (ms_per_step * 1e-3)
 
-    bytes_per_pass = [step_bytes(st, wl) for st in wl.steps]
-    flops_per_pass = [step_flops(st, wl) for st in wl.steps]
-    kern_total_ms = sum(kern_ms)
-    achieved = sum(bytes_per_pass) / (kern_total_ms * 1e-3) / 1e9
+    bytes_per_launch = [step_bytes(st, wl) for st in wl.steps]
+    flops_per_launch = [step_flops(st, wl) for st in wl.steps]
+    mean_bytes = float(np.mean(bytes_per_launch))
+    achieved = mean_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
     line = {
         "metric": "paged-attn decode HBM GB/s (% peak) + mixed-batch attn tokens/s per layer",
         "value": value,
@@ -264,15 +385,19 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
-            "algorithmic_bytes_per_launch": [int(b) for b in bytes_per_pass],
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": mean_bytes,
             "avg_launch_ms": kern_ms,
-            "flops_per_launch": flops_per_pass,
+            "launches_timed": launches,
+            "flops_per_launch": float(np.mean(flops_per_launch)),
         },
     }
     if not args.no_decode:
         log("bench: decode-only batch")
         line["decode_hbm"] = decode_hbm(torch, P)
+    if args.mfma:
+        log("bench: MFMA paths (cascade prefix, long chunked prefill)")
+        line["mfma_paths"] = mfma_paths(torch, P)
     if not args.no_cpu:
         log("bench: cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(wl)

@@ -176,6 +176,14 @@ int pkv_merge_attn_states(void* out, int32_t out_dtype, float* lse_out, const fl
                           const float* lse_a, const float* out_b, const float* lse_b,
                           int32_t num_tokens, int32_t num_heads, int32_t head_dim, void* stream);
 
+/* Launch timing (measurement aid, per calling thread): after pkv_timing_begin(), every
+ * varlen attention kernel launched by pkv_paged_attention_varlen is bracketed by two HIP
+ * events recorded on its stream (the split-KV reduce falls outside them).  pkv_timing_end()
+ * stops recording, waits for the last event and returns the summed kernel milliseconds and
+ * the number of launches.  Creates HIP events on first use; not for graph capture. */
+int pkv_timing_begin(void);
+int pkv_timing_end(double* total_ms, int32_t* launches);
+
 /* Thread-local description of the last error returned on this thread ("" if none). */
 const char* pkv_last_error(void);
 

@@ -18,6 +18,8 @@ from .ops import (  # noqa: F401
     plan_varlen,
     plan_varlen_host,
     reshape_and_cache,
+    timing_begin,
+    timing_end,
     varlen_workspace_size,
     version,
 )

@@ -28,6 +28,8 @@ EXPORTS = (
     "pkv_cascade_workspace_size",
     "pkv_cascade_prefix_attention",
     "pkv_merge_attn_states",
+    "pkv_timing_begin",
+    "pkv_timing_end",
     "pkv_last_error",
     "pkv_version",
 )
@@ -95,6 +97,8 @@ _SIGS = {
         [_P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _P, _SZ, _P],
     ),
     "pkv_merge_attn_states": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "pkv_timing_begin": (ctypes.c_int, []),
+    "pkv_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }

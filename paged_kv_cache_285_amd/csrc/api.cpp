@@ -275,6 +275,37 @@ int stage_and_copy(void* dst, const void* src, size_t bytes, hipStream_t stream)
   return PKV_OK;
 }
 
+// Launch timing of the varlen attention kernel: while enabled (per thread), every varlen launch
+// is bracketed by a pair of HIP events recorded on the caller's stream immediately before and
+// after the kernel (the split-KV reduce is outside the pair).
+struct LaunchTiming {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  size_t used = 0;
+};
+thread_local LaunchTiming g_timing;
+
+int timing_mark(hipStream_t stream, bool before) {
+  if (!g_timing.on) return PKV_OK;
+  if (before) {
+    if (g_timing.used == g_timing.pool.size()) {
+      hipEvent_t a, b;
+      hipError_t e = hipEventCreate(&a);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate(timing)");
+      e = hipEventCreate(&b);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate(timing)");
+      g_timing.pool.emplace_back(a, b);
+    }
+    hipError_t e = hipEventRecord(g_timing.pool[g_timing.used].first, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(timing)");
+  } else {
+    hipError_t e = hipEventRecord(g_timing.pool[g_timing.used].second, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(timing)");
+    ++g_timing.used;
+  }
+  return PKV_OK;
+}
+
 // Cascade segmenting: enough (tile, segment) workgroups to give every CU one 8-wave workgroup,
 // with segments of at least 1024 keys, rounded to whole KV tiles.
 struct CascadeSplit {
@@ -308,6 +339,30 @@ extern "C" {
 const char* pkv_last_error(void) { return g_error.c_str(); }
 
 const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
+
+int pkv_timing_begin(void) {
+  g_timing.on = true;
+  g_timing.used = 0;
+  return ok();
+}
+
+int pkv_timing_end(double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return fail(PKV_EINVAL, "null pointer argument");
+  g_timing.on = false;
+  double sum = 0.0;
+  for (size_t i = 0; i < g_timing.used; ++i) {
+    hipError_t e = hipEventSynchronize(g_timing.pool[i].second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(timing)");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_timing.pool[i].first, g_timing.pool[i].second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime(timing)");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int32_t)g_timing.used;
+  g_timing.used = 0;
+  return ok();
+}
 
 size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
                                  const pkv_shape* shape) {
@@ -469,9 +524,11 @@ int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const v
   a.bt_stride = shape->bt_stride;
   a.scale_log2 = scale_log2(shape);
   const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (int rc = timing_mark((hipStream_t)stream, true)) return rc;
   hipError_t e = pkv::launch_varlen(a, shape->head_dim, G, plan->num_prefill_items > 0,
                                     plan->waves_per_group, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "varlen attention launch");
+  if (int rc = timing_mark((hipStream_t)stream, false)) return rc;
   if (plan->num_partials > 0) {
     pkv::ReduceArgs ra;
     ra.part_o = a.part_o;

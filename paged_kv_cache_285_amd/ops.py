@@ -317,3 +317,16 @@ def merge_attn_states(
         )
     )
     return out
+
+
+def timing_begin() -> None:
+    """Start bracketing every varlen attention kernel launch with HIP events (this thread)."""
+    check(lib().pkv_timing_begin())
+
+
+def timing_end() -> Tuple[float, int]:
+    """Stop timing; return (summed kernel milliseconds, number of varlen launches)."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int32()
+    check(lib().pkv_timing_end(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
