@@ -28,7 +28,7 @@ on purpose so that it can be checked against the pages by eye:
   unique suffix are computed separately and combined by an associative,
   commutative merge of (output, log-sum-exp) states.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 softmax scale 1/sqrt(head_dim); q head h reads kv head h // (Hq/Hkv); the key
 pool is laid out [num_blocks, Hkv, block_size, head_dim] (token-major) and the
 value pool [num_blocks, Hkv, head_dim, block_size] (dim-major); a new token at position
