@@ -2,17 +2,16 @@
 
 One step = one pass of the whole hot path over the mixed Llama-3-8B-shaped batch (32 q / 8 kv
 heads, head_dim 128, block 16): for each of its three scheduler iterations — slot mapping and
-cache write (one fused launch), the varlen plan upload and one paged_attention_varlen launch
-(decode rows on the VALU path with the split-KV merge fused in, chunked-prefill / prefix-hit
-rows on MFMA).  The 330 query tokens of
-the pass give the headline attention tokens/s per layer.  Inputs are synthetic (seeded N(0,1)
+cache write (one fused launch), the varlen plan upload and one paged_attention_varlen call
+(decode rows on the VALU path, chunked-prefill / prefix-hit rows on MFMA, then the split-KV
+reduce).  The 330 query tokens of the pass give the headline attention tokens/s per layer.  Inputs are synthetic (seeded N(0,1)
 bf16) and resident in HBM before timing starts.
 
 Also reported: the dominant kernel's roofline (algorithmic bytes / HIP-event-timed launch
 duration against 8 TB/s), the decode-only batch's HBM GB/s, and the CPU fp64 oracle timed on a
 bounded sample of the same workload (``cpu_baseline``).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--mfma]
 """
 
 from __future__ import annotations

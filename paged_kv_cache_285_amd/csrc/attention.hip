@@ -14,18 +14,22 @@
 //      - decode item (query length 1): VALU path.  4 waves stream disjoint 16-token blocks of
 //        the item's key range straight from HBM with 16-byte coalesced loads (one wave load
 //        covers 1 KB of a 4 KB block tile), software-pipelined one block ahead.  All G q heads
-//        of the kv head share every K/V byte.  Q.K uses v_dot2_f32_bf16 on packed bf16 and a
-//        16-lane DPP row reduction; online softmax runs per 16-lane row; P.V is fp32 FMA.
-//        Rows, then waves, are merged with the (o, lse) merge; long rows are cut into
-//        split-KV items whose partial states a small reduce kernel merges.
-//      - prefill tile (query length > 1): 128 packed (token, q head) rows x 64-key tiles on
-//        bf16 MFMA 32x32x16.  S^T = K Q^T puts one query per lane column so the row max and
-//        row sum stay inside a lane (plus one cross-half exchange); O^T = V^T P^T reuses the
-//        S^T accumulator registers as the B operand.  K tiles are staged in LDS row-major,
-//        V tiles transposed, both double-buffered; the causal mask (offset by the cached
-//        length) is only evaluated on tiles that straddle the diagonal or the sequence end.
-//  * cascade_kernel: the shared-prefix pass, the same MFMA tile with no mask over the prefix
-//    block table, optionally cut into key segments whose states are merged afterwards.
+//        of the kv head share every K/V byte.  Q.K: 8 lanes per key with v_dot2_f32_bf16 and
+//        a DPP transpose-reduce; a wave-uniform, lazily raised running max; P.V on the
+//        dim-major value tile with v_dot2_f32_bf16 against bf16 p pairs.  Waves are merged
+//        with the (o, lse) merge in LDS; long rows are cut into split-KV items whose partial
+//        states reduce_kernel merges.  A decode-only batch uses a specialisation with no
+//        prefill branch and a tighter register budget.
+//      - prefill tile (query length > 1): 32 packed (token, q head) rows per wave (4 or 8
+//        waves) x 64-key tiles on bf16 MFMA 32x32x16.  S^T = K Q^T puts one query per lane
+//        column so the row max and row sum stay inside a lane (plus one cross-half exchange);
+//        O^T = V^T P^T feeds P from the S^T accumulator registers.  K tiles are staged in LDS
+//        row-major, V^T tiles key-permuted so every MFMA operand is one conflict-free 16-byte
+//        read, both double-buffered; the causal mask (offset by the cached length) is only
+//        evaluated on tiles that straddle the diagonal or the sequence end.
+//  * cascade_kernel: the shared-prefix pass, the same 8-wave MFMA tile with no mask over the
+//    prefix block table, cut into key segments when there are too few query tiles to fill
+//    the chip; the segment states are merged afterwards.
 //  * reduce_kernel: merges split-KV / segment partial states into the final output.
 #include "internal.h"
 
