@@ -80,7 +80,7 @@ typedef struct pkv_varlen_plan {
   int32_t has_splits;
   int64_t workspace_used;  /* bytes of the workspace the plan occupies */
   int32_t head_dim, num_q_heads, num_kv_heads, block_size; /* shape the plan was made for */
-  int32_t waves_per_group; /* 4 or 8: prefill tiles hold 32 packed rows per wave */
+  int32_t tile_rows;       /* packed (token, q head) rows per prefill tile: 128 or 256 */
 } pkv_varlen_plan;
 
 /* Size in bytes of a workspace that fits any plan with at most these sizes. */
@@ -117,7 +117,8 @@ int pkv_append_kv(int64_t* slot_mapping, const void* k, const void* v, void* k_c
 /* Builds the work list of one varlen attention call from host copies of the metadata:
  * validates seq_lens[r] == context_lens[r] + (qsl[r+1] - qsl[r]) and every length, cuts
  * query-length-1 rows into split-KV decode items and longer rows into prefill tiles of
- * 128 or 256 packed (token, q head) rows, orders them heaviest first, and enqueues a host-to-device copy of the list into
+ * 128 or 256 packed (token, q head) rows (256 once the batch holds at least 2048 prefill
+ * rows), orders them heaviest first, and enqueues a host-to-device copy of the list into
  * `workspace` on `stream`.  Fills *plan.  The workspace must stay untouched until the
  * attention call that uses the plan has run. */
 int pkv_plan_varlen(pkv_varlen_plan* plan, void* workspace, size_t workspace_bytes,

@@ -62,7 +62,7 @@ class PkvVarlenPlan(ctypes.Structure):
         ("num_q_heads", ctypes.c_int32),
         ("num_kv_heads", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
-        ("waves_per_group", ctypes.c_int32),
+        ("tile_rows", ctypes.c_int32),
     ]
 
 

@@ -93,7 +93,7 @@ struct Plan {
   std::vector<int32_t> token_split;  // per token {partial_base, count}
   int32_t num_partials = 0;
   int32_t bps = 0;
-  int32_t waves = 4;
+  int32_t tile_rows = pkv::kTileRows;
   int32_t n_prefill = 0, n_decode = 0;
 };
 
@@ -133,13 +133,13 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
     if (n * s->num_kv_heads <= decode_target_wgs()) break;
   }
   P.bps = bps;
-  // Prefill tiles hold 32 packed (token, q head) rows per wave: 8-wave (256-row) tiles when the
-  // batch has enough prefill rows to fill them, else 4-wave (128-row) tiles.
+  // Prefill tiles hold 256 packed (token, q head) rows (wide tiles) when the batch has enough
+  // prefill rows to fill them, else 128.
   int64_t prefill_rows = 0;
   for (int r = 0; r < num_seqs; ++r)
     if (qsl[r + 1] - qsl[r] > 1) prefill_rows += (int64_t)(qsl[r + 1] - qsl[r]) * G;
-  P.waves = prefill_rows >= pkv::kPrefillRowsFor8Waves ? 8 : 4;
-  const int tok_per_tile = 32 * P.waves / G;
+  P.tile_rows = prefill_rows >= pkv::kPrefillRowsForWideTiles ? pkv::kWideTileRows : pkv::kTileRows;
+  const int tok_per_tile = P.tile_rows / G;
   P.items.clear();
   P.token_split.assign((size_t)num_tokens * 2, 0);
   std::vector<pkv::WorkItem> pre, dec;
@@ -216,7 +216,7 @@ void fill_plan_struct(pkv_varlen_plan* out, const Plan& P, int32_t num_seqs, int
   out->num_q_heads = s->num_q_heads;
   out->num_kv_heads = s->num_kv_heads;
   out->block_size = s->block_size;
-  out->waves_per_group = P.waves;
+  out->tile_rows = P.tile_rows;
   const VarlenLayout L =
       varlen_layout(out->num_items, num_tokens, P.num_partials, s->num_q_heads, s->head_dim);
   out->workspace_used = (int64_t)L.total;
@@ -314,9 +314,9 @@ struct CascadeSplit {
 CascadeSplit cascade_split(int32_t num_tokens, int32_t prefix_len, const pkv_shape* s) {
   const int G = s->num_q_heads / s->num_kv_heads;
   CascadeSplit c;
-  c.tiles = (int32_t)ceil_div(num_tokens, 32 * pkv::kCascadeWaves / G);
+  c.tiles = (int32_t)ceil_div(num_tokens, pkv::kWideTileRows / G);
   const int64_t wgs = std::max<int64_t>(1, (int64_t)c.tiles * s->num_kv_heads);
-  const int64_t want = ceil_div(256, wgs);  // one 8-wave workgroup per CU
+  const int64_t want = ceil_div(256, wgs);  // one wide-tile workgroup per CU
   const int64_t max_segs = std::max<int64_t>(1, prefix_len / 1024);
   int64_t segs = std::max<int64_t>(1, std::min(want, max_segs));
   int64_t seg_len = ceil_div(ceil_div(prefix_len, segs), pkv::kKvTile) * pkv::kKvTile;
@@ -525,8 +525,8 @@ int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const v
   a.scale_log2 = scale_log2(shape);
   const int G = shape->num_q_heads / shape->num_kv_heads;
   if (int rc = timing_mark((hipStream_t)stream, true)) return rc;
-  hipError_t e = pkv::launch_varlen(a, shape->head_dim, G, plan->num_prefill_items > 0,
-                                    plan->waves_per_group, (hipStream_t)stream);
+  hipError_t e = pkv::launch_varlen(a, shape->head_dim, G, plan->num_prefill_items,
+                                    plan->num_decode_items, plan->tile_rows, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "varlen attention launch");
   if (int rc = timing_mark((hipStream_t)stream, false)) return rc;
   if (plan->num_partials > 0) {

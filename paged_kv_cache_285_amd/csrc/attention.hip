@@ -33,6 +33,8 @@
 //  * reduce_kernel: merges split-KV / segment partial states into the final output.
 #include "internal.h"
 
+#include <type_traits>
+
 namespace pkv {
 namespace {
 
@@ -40,6 +42,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -694,6 +697,343 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
   if (lse_out && h == 0) lse_out[orow] = (lsum > 0.f) ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
 }
 
+// ------------------------------------------------------------------------------------------
+// Pipelined MFMA tile: 256 packed rows on 8 waves (32 rows per wave, two waves per SIMD).  The
+// tile loop is software-pipelined so that one wave's instruction stream mixes matrix and vector
+// work: step t issues the MFMAs of S^T(t+1) = K(t+1) Q^T and O^T += V(t-1)^T P^T(t-1) while the
+// VALU computes the softmax of tile t (whose S^T the previous step produced).  K tiles are
+// staged two ahead of their use and V tiles one behind, each in two LDS buffers (waves 0-3 copy
+// K, waves 4-7 copy V), with one barrier per step.  P^T is built from the S^T accumulator with
+// two lane-half swaps per K-step so that a lane holds 8 consecutive keys; the V^T operand is
+// then one 16-byte read of the value tile in its natural dim-major order.
+// ------------------------------------------------------------------------------------------
+template <int D>
+struct PipeRegs {
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DT = D / 32;
+  bf16x8 qb[KSTEPS];    // Q^T operand: dims 16s + 8h .. +7 of the lane's query row
+  floatx16 oacc[DT];    // O^T accumulators
+  floatx16 sacc[2][2];  // two S^T sets (tile t and t+1), each two 32-key halves
+  bf16x8 pb[2][4];      // two P^T sets (tile t-1 and t), four 16-key steps each
+  float m, lsum;        // running max (log2 units of scaled scores) and row sum
+  int qpos;             // position of the lane's query row
+};
+
+// x of lane l ^ 32 (the other half of the wave).
+__device__ __forceinline__ float other_half(float x, int h) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(h ? r[0] : r[1]);
+}
+
+// Masks the scores of S^T set SET for the tile starting at key k0: keys past kv_end and, for
+// causal rows, keys after the row's position get -inf.
+template <int D, int SET, bool CAUSAL>
+__device__ __forceinline__ void pipe_mask(PipeRegs<D>& R, int h, int k0, int kv_end) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = k0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+      const bool vis = key < kv_end && (!CAUSAL || key <= R.qpos);
+      R.sacc[SET][mt][e] = vis ? R.sacc[SET][mt][e] : -INFINITY;
+    }
+}
+
+// O^T += V^T P^T(SET) over the V buffer `vb`.
+template <int D, int SET>
+__device__ __forceinline__ void pipe_pv(PipeRegs<D>& R, const uint16_t* __restrict__ vb, int n, int h) {
+  using S = TileSmem<D>;
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 xv = *reinterpret_cast<const bf16x8*>(vb + (32 * d + n) * S::VP + 16 * ks + 8 * h);
+      R.oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xv, R.pb[SET][ks], R.oacc[d], 0, 0, 0);
+    }
+}
+
+// One pipeline step.  CUR holds S^T(t) (already masked) and receives P^T(t); the other set
+// receives S^T(t+1) from K buffer `kb` and supplies P^T(t-1) to the P.V over V buffer `vb`.
+// Straight-line code, so that the scheduler can interleave the MFMA and VALU streams.  Returns
+// in `need` whether the running max moved, with the new max and the tile's row sum.
+template <int D, int CUR>
+__device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __restrict__ kb,
+                                          const uint16_t* __restrict__ vb, int n, int h, float sl,
+                                          bool& need, float& mnew, float& ts) {
+  constexpr int NXT = 1 - CUR;
+  constexpr int KSTEPS = D / 16;
+  using S = TileSmem<D>;
+  const floatx16 zero = {};
+
+  // Softmax, part 1: tile max and the lazy max update (raised only past kLazy, for every lane
+  // of the wave at once, so that the output rescale stays rare).
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, R.sacc[CUR][mt][e]);
+  mx = fmaxf(mx, other_half(mx, h)) * sl;
+  need = __ballot(mx > R.m + kLazy) != 0;
+  mnew = need ? fmaxf(R.m, mx) : R.m;
+  const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+
+  // S^T(t+1) = K Q^T.
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + (32 * mt + n) * S::KP + 16 * s + 8 * h);
+      R.sacc[NXT][mt] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, R.qb[s], s == 0 ? zero : R.sacc[NXT][mt], 0, 0, 0);
+    }
+
+  // Softmax, part 2: p = exp2(s * scale - m), fp32 row sum, bf16 pairs.
+  uint32_t pk[2][8];
+  ts = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = fast_exp2(fmaf(R.sacc[CUR][mt][e], sl, -mref));
+      const float p1 = fast_exp2(fmaf(R.sacc[CUR][mt][e + 1], sl, -mref));
+      ts += p0;
+      ts += p1;
+      pk[mt][e >> 1] = pack_bf16x2(p0, p1);
+    }
+
+  // O^T += V^T P^T(t-1).
+  pipe_pv<D, NXT>(R, vb, n, h);
+
+  // Softmax, part 3: the P^T operand of tile t.  K-step ks covers keys 16ks..16ks+15; in the
+  // accumulator layout a lane of half h holds keys 4h..4h+3 and 8+4h..8+4h+3 of them as dwords
+  // d0..d3, and swapping d0<->d2 and d1<->d3 across the halves leaves it keys 8h..8h+7.
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int mt = ks >> 1, b = 4 * (ks & 1);
+    const auto s02 = __builtin_amdgcn_permlane32_swap(pk[mt][b], pk[mt][b + 2], false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(pk[mt][b + 1], pk[mt][b + 3], false, false);
+    u32x4 w;
+    w[0] = s02[0];
+    w[1] = s13[0];
+    w[2] = s02[1];
+    w[3] = s13[1];
+    R.pb[CUR][ks] = __builtin_bit_cast(bf16x8, w);
+  }
+#ifdef PKV_SCHED
+  // Issue order: operand reads PKV_SCHED ahead of their MFMA, VALU work spread between MFMAs.
+  __builtin_amdgcn_sched_group_barrier(0x100, PKV_SCHED, 0);
+#pragma unroll
+  for (int i = 0; i < 32 - PKV_SCHED; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < PKV_SCHED; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+  }
+#endif
+}
+
+// After a step: apply a moved running max to the output (which now holds tiles up to t-1) and
+// the row sum, then add the tile's row sum.
+template <int D>
+__device__ __forceinline__ void pipe_commit(PipeRegs<D>& R, bool need, float mnew, float ts) {
+  if (need) {
+    const float alpha = fast_exp2(R.m - mnew);
+    R.lsum *= alpha;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) R.oacc[d][e] *= alpha;
+  }
+  R.m = mnew;
+  R.lsum += ts;
+}
+
+template <int D, int G, bool CAUSAL>
+__device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t* __restrict__ k_cache,
+                          const uint16_t* __restrict__ v_cache, int Hkv, int g,
+                          const int32_t* __restrict__ bt, int tok0, int ntok, int pos0, int kv_begin,
+                          int kv_end, float sl, void* out, int out_f32, float* lse_out,
+                          char* smem_raw) {
+  using S = TileSmem<D>;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int CH = D / 8;             // 16-byte chunks per key row
+  constexpr int LPT = CH;               // lanes per key row when staging
+  constexpr int KPI = 64 / LPT;         // key rows per wave load
+  constexpr int NI = kBlockSize / KPI;  // loads per lane per block (K rows; V^T chunks alike)
+  static_assert(NI == D / 32, "staging layout");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
+  uint16_t* kbuf0 = smem;
+  uint16_t* vbuf0 = smem + 2 * S::K_ELEMS;
+
+  PipeRegs<D> R;
+#ifdef PKV_AGPR_FORM
+  asm volatile("" ::: "a0");
+#endif
+  const int pr = 32 * wave + n;
+  const int tq = pr / G;
+  const int hh = pr % G;
+  const bool row_valid = tq < ntok;
+  R.qpos = row_valid ? pos0 + tq : 0x7fffffff;
+  {
+    const u32x4* qrow =
+        reinterpret_cast<const u32x4*>(q + ((int64_t)(tok0 + (row_valid ? tq : 0)) * Hq + g * G + hh) * D);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const u32x4 v = row_valid ? qrow[2 * s + h] : u32x4{0u, 0u, 0u, 0u};
+      R.qb[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < DT; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) R.oacc[d][e] = 0.f;
+  R.m = -INFINITY;
+  R.lsum = 0.f;
+
+  const int ntiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
+  if (ntiles > 0) {
+    // Staging: waves 0-3 copy the K rows of cache block (wave & 3) of a tile (key KPI*i +
+    // lane/LPT, chunk lane % LPT), waves 4-7 its V^T chunks (chunk lane + 64i of the dim-major
+    // block tile is dim (lane >> 1) + 32i, tokens 8*(lane & 1)..+7).  Loads are unconditional
+    // (past the end they re-read the last block); values of keys past the end are zeroed at
+    // store time.
+    const bool does_k = wave < 4;
+    const int sblk = wave & 3;
+    const int sc = lane % LPT;
+    const int sr = lane / LPT;
+    const int64_t tile_stride = (int64_t)kBlockSize * CH;
+    const int64_t blk_stride = (int64_t)Hkv * tile_stride;
+    const u32x4* base = reinterpret_cast<const u32x4*>(does_k ? k_cache : v_cache) + (int64_t)g * tile_stride;
+    typedef __attribute__((address_space(4))) const int32_t cint32;
+    const cint32* cbt = (const cint32*)bt;
+    const int last_blk = (kv_end - 1) / kBlockSize;
+    const int blk0 = kv_begin / kBlockSize + sblk;
+    // Per-lane offsets (u32x4 units) of the staged chunks in the block tile and (bf16 units) in LDS.
+    int goff[NI], soff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      goff[i] = does_k ? (KPI * i + sr) * CH + sc : lane + 64 * i;
+      soff[i] = does_k ? (kBlockSize * sblk + KPI * i + sr) * S::KP + sc * 8
+                       : 2 * S::K_ELEMS + ((lane >> 1) + 32 * i) * S::VP + kBlockSize * sblk + 8 * (lane & 1);
+    }
+    // Buffer of tile t: K tiles alternate between the two K buffers, V tiles between the two V
+    // buffers; `tile` is the K tile index for waves 0-3 and the V tile index for waves 4-7.
+    auto load = [&](int tile, u32x4 (&r)[NI]) __attribute__((always_inline)) -> int {
+      const int lb = blk0 + 4 * tile;
+      const u32x4* p = base + (int64_t)cbt[min(lb, last_blk)] * blk_stride;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) r[i] = p[goff[i]];
+      return does_k ? kBlockSize : kv_end - lb * kBlockSize;
+    };
+    auto store = [&](int buf, const u32x4 (&r)[NI], int nvalid) __attribute__((always_inline)) {
+      uint16_t* dst = smem + buf * (does_k ? S::K_ELEMS : S::V_ELEMS);
+      if (nvalid >= kBlockSize) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + soff[i]) = r[i];
+      } else {
+        const int t0 = 8 * (lane & 1);
+        u32x4 msk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          msk[u] = (t0 + 2 * u < nvalid ? 0x0000ffffu : 0u) | (t0 + 2 * u + 1 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + soff[i]) = r[i] & msk;
+      }
+    };
+
+    // Prologue: K(0) and K(1) in LDS, V(-1) = 0 (no tile before the first), K(2) / V(0) in
+    // flight, S^T(0) computed.
+    u32x4 st[NI];
+    int nv;
+    if (does_k) {
+      nv = load(0, st);
+      store(0, st, nv);
+      nv = load(1, st);
+      store(1, st, nv);
+      nv = load(2, st);
+    } else {
+      u32x4* z = reinterpret_cast<u32x4*>(vbuf0 + S::V_ELEMS);
+      for (int i = threadIdx.x - 256; i < S::V_ELEMS / 8; i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
+      nv = load(0, st);
+    }
+    __syncthreads();
+    {
+      const floatx16 zero = {};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kbuf0 + (32 * mt + n) * S::KP + 16 * s + 8 * h);
+          R.sacc[0][mt] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, R.qb[s], s == 0 ? zero : R.sacc[0][mt], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) R.pb[1][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+
+    // Step t: store K(t+2) / V(t), load K(t+3) / V(t+1), then S^T(t+1), P.V(t-1) and softmax(t).
+    auto step = [&](auto cur, int t) __attribute__((always_inline)) {
+      constexpr int CUR = decltype(cur)::value;
+      __syncthreads();
+      store(t & 1, st, nv);
+      nv = load(does_k ? t + 3 : t + 1, st);
+      const int k0 = kv_begin + t * kKvTile;
+      if ((k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > pos0))
+        pipe_mask<D, CUR, CAUSAL>(R, h, k0, kv_end);
+      bool need;
+      float mnew, ts;
+      pipe_step<D, CUR>(R, kbuf0 + ((t + 1) & 1) * S::K_ELEMS, vbuf0 + ((t + 1) & 1) * S::V_ELEMS, n, h, sl,
+                        need, mnew, ts);
+      pipe_commit<D>(R, need, mnew, ts);
+    };
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      step(std::integral_constant<int, 0>(), t);
+      step(std::integral_constant<int, 1>(), t + 1);
+    }
+    if (t < ntiles) step(std::integral_constant<int, 0>(), t);
+    // The last P.V (tile ntiles - 1, stored by the last step).
+    __syncthreads();
+    const uint16_t* vlast = vbuf0 + ((ntiles - 1) & 1) * S::V_ELEMS;
+    if ((ntiles - 1) & 1)
+      pipe_pv<D, 1>(R, vlast, n, h);
+    else
+      pipe_pv<D, 0>(R, vlast, n, h);
+  }
+
+  const float lsum = R.lsum + other_half(R.lsum, h);
+  if (!row_valid) return;
+  const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+  const int64_t orow = (int64_t)(tok0 + tq) * Hq + g * G + hh;
+#pragma unroll
+  for (int d = 0; d < DT; ++d) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int dim = 32 * d + 8 * jj + 4 * h;
+      const float v0 = R.oacc[d][4 * jj] * inv, v1 = R.oacc[d][4 * jj + 1] * inv;
+      const float v2 = R.oacc[d][4 * jj + 2] * inv, v3 = R.oacc[d][4 * jj + 3] * inv;
+      if (out_f32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + orow * D + dim) = make_float4(v0, v1, v2, v3);
+      } else {
+        uint2 w;
+        w.x = pack_bf16x2(v0, v1);
+        w.y = pack_bf16x2(v2, v3);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + orow * D + dim) = w;
+      }
+    }
+  }
+  if (lse_out && h == 0) lse_out[orow] = (lsum > 0.f) ? (R.m + __log2f(lsum)) * kLn2 : -INFINITY;
+}
+
 // DECODE_ONLY instantiations carry no MFMA path, so they need far fewer registers and run
 // more waves per SIMD; a plan with any prefill tile uses the full kernel, with 4 or 8 waves
 // per workgroup (8 when the batch carries enough prefill rows to fill 256-row tiles).
@@ -718,9 +1058,24 @@ void varlen_kernel(VarlenArgs a) {
   }
 }
 
+// Wide-tile kernels: 256-row pipelined tiles on 8 waves.
 template <int D, int G>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kCascadeWaves, 64 * kCascadeWaves),
-                          amdgpu_waves_per_eu(2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void prefill_wide_kernel(VarlenArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int x = blockIdx.x;
+  const int g = x % a.num_kv_heads;
+  const WorkItem it = a.items[x / a.num_kv_heads];
+  const int r = it.seq;
+  const int ctx = a.context_lens[r];
+  const int tok0 = a.query_start_loc[r] + it.q_begin;
+  const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
+  pipe_tile<D, G, true>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g, bt, tok0, it.q_count,
+                        ctx + it.q_begin, it.kv_begin, it.kv_end, a.scale_log2, a.out, a.out_f32, a.lse, smem);
+}
+
+template <int D, int G>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void cascade_kernel(CascadeArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int x = blockIdx.x;
@@ -728,7 +1083,7 @@ void cascade_kernel(CascadeArgs a) {
   const int rest = x / a.num_kv_heads;
   const int tile = rest % a.num_tiles;
   const int seg = rest / a.num_tiles;
-  constexpr int TOK = 32 * kCascadeWaves / G;
+  constexpr int TOK = kWideTileRows / G;
   const int tok0 = tile * TOK;
   const int ntok = min(TOK, a.num_tokens - tok0);
   const int kv_begin = seg * a.seg_len;
@@ -739,9 +1094,8 @@ void cascade_kernel(CascadeArgs a) {
     out = a.part_o + (int64_t)seg * a.num_tokens * a.num_q_heads * D;
     lse = a.part_lse + (int64_t)seg * a.num_tokens * a.num_q_heads;
   }
-  mfma_tile<D, G, false, kCascadeWaves>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g,
-                                        a.prefix_bt, tok0, ntok, 0, kv_begin, kv_end, a.scale_log2,
-                                        out, 1, lse, smem);
+  pipe_tile<D, G, false>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g, a.prefix_bt, tok0,
+                         ntok, 0, kv_begin, kv_end, a.scale_log2, out, 1, lse, smem);
 }
 
 // One wave per (token, head) row; lane holds D/64 consecutive dims.
@@ -811,21 +1165,33 @@ size_t varlen_smem(bool has_prefill) {
 }
 
 template <int D, int G>
-hipError_t launch_varlen_t(const VarlenArgs& a, bool has_prefill, int waves, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.num_items * a.num_kv_heads;
-  if (grid == 0) return hipSuccess;
-  if (!has_prefill) {
+hipError_t launch_varlen_t(const VarlenArgs& a, int n_prefill, int n_decode, int tile_rows,
+                           hipStream_t stream) {
+  const int Hkv = a.num_kv_heads;
+  if (n_prefill + n_decode == 0) return hipSuccess;
+  if (n_prefill == 0) {
     auto kern = varlen_kernel<D, G, true, 4>;
     const size_t smem = varlen_smem<D, G, 4>(false);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), smem, stream, a);
-  } else if (waves == 8) {
-    auto kern = varlen_kernel<D, G, false, 8>;
-    const size_t smem = varlen_smem<D, G, 8>(true);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), smem, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_decode * Hkv)), dim3(256), smem, stream, a);
+  } else if (tile_rows == kWideTileRows) {
+    // Wide prefill tiles, then the decode items in a kernel of their own (the wide tile's
+    // register budget allows two waves per SIMD, too few for the decode path).
+    auto kern = prefill_wide_kernel<D, G>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_prefill * Hkv)), dim3(512),
+                       (size_t)TileSmem<D>::BYTES, stream, a);
+    if (n_decode > 0) {
+      VarlenArgs b = a;
+      b.items = a.items + n_prefill;
+      b.num_items = n_decode;
+      auto dk = varlen_kernel<D, G, true, 4>;
+      const size_t smem = varlen_smem<D, G, 4>(false);
+      hipLaunchKernelGGL(dk, dim3((unsigned)((int64_t)n_decode * Hkv)), dim3(256), smem, stream, b);
+    }
   } else {
     auto kern = varlen_kernel<D, G, false, 4>;
     const size_t smem = varlen_smem<D, G, 4>(true);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), smem, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)(n_prefill + n_decode) * Hkv)), dim3(256), smem,
+                       stream, a);
   }
   return hipGetLastError();
 }
@@ -834,8 +1200,8 @@ template <int D, int G>
 hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.num_tiles * a.num_segments * a.num_kv_heads;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((cascade_kernel<D, G>), dim3((unsigned)grid), dim3(64 * kCascadeWaves),
-                     (size_t)TileSmem<D>::BYTES, stream, a);
+  hipLaunchKernelGGL((cascade_kernel<D, G>), dim3((unsigned)grid), dim3(512), (size_t)TileSmem<D>::BYTES,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -862,9 +1228,9 @@ hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
   }                                                   \
   return hipErrorInvalidValue;
 
-hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, bool has_prefill, int waves,
-                         hipStream_t stream) {
-#define CALL_V(D, G) launch_varlen_t<D, G>(a, has_prefill, waves, stream)
+hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, int n_prefill, int n_decode,
+                         int tile_rows, hipStream_t stream) {
+#define CALL_V(D, G) launch_varlen_t<D, G>(a, n_prefill, n_decode, tile_rows, stream)
   PKV_DISPATCH_DG(head_dim, group, CALL_V)
 #undef CALL_V
 }

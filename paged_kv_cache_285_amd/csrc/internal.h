@@ -9,8 +9,9 @@ namespace pkv {
 
 constexpr int kBlockSize = 16;       // tokens per cache block (the only supported size)
 constexpr int kKvTile = 64;          // keys per MFMA KV tile (4 cache blocks)
-constexpr int kCascadeWaves = 8;     // waves per cascade-prefix workgroup (256-row tiles)
-constexpr int kPrefillRowsFor8Waves = 2048;  // packed prefill rows from which 8-wave tiles pay
+constexpr int kTileRows = 128;       // packed (token, q head) rows of a varlen prefill tile
+constexpr int kWideTileRows = 256;   // rows of a wide tile (prefill-heavy batches, cascade)
+constexpr int kPrefillRowsForWideTiles = 2048;  // packed prefill rows from which wide tiles pay
 constexpr int kMinBlocksPerSplit = 16;
 
 enum ItemKind : int32_t { kDecode = 0, kPrefill = 1 };
@@ -94,8 +95,10 @@ hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v, uint16
                                     uint16_t* v_cache, const int64_t* slots, int32_t num_tokens,
                                     int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
                                     hipStream_t stream);
-hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, bool has_prefill, int waves,
-                         hipStream_t stream);
+// Launches the attention kernels of a varlen plan whose items list n_prefill prefill tiles of
+// tile_rows rows first, then n_decode decode items.
+hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, int n_prefill, int n_decode,
+                         int tile_rows, hipStream_t stream);
 hipError_t launch_cascade(const CascadeArgs& a, int head_dim, int group, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_merge(void* out, int32_t out_f32, float* lse_out, const float* oa,

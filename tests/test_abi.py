@@ -85,7 +85,7 @@ def test_plan_covers_every_row_exactly_once(P):
     plan, items = P.plan_varlen_host(qsl, ctx, seq, s)
     assert plan.num_items == len(items) == plan.num_prefill_items + plan.num_decode_items
     G = 4
-    tok_per_tile = 32 * plan.waves_per_group // G
+    tok_per_tile = plan.tile_rows // G
     cover_tok = np.zeros(int(qsl[-1]), int)
     dec_keys = {}
     for seqi, kind, qb, qc, kb, ke, pbase, split in items:

@@ -72,7 +72,7 @@ def run_and_check(wl, rows_per_step=None, check_pools=True, want_lse=True, out_d
         if want_lse:
             r["lse_max_abs"] = check_lse(lse_g.cpu().numpy()[sel], l_ref[sel], f"{wl.name} step {si} lse")
         stats.append(r)
-        say(f"    plan items={plan.num_items} waves={plan.waves_per_group} partials={plan.num_partials} bps={plan.blocks_per_split} {r}")
+        say(f"    plan items={plan.num_items} tile_rows={plan.tile_rows} partials={plan.num_partials} bps={plan.blocks_per_split} {r}")
     return stats
 
 
