@@ -913,10 +913,12 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
     const int64_t tile_stride = (int64_t)kBlockSize * CH;
     const int64_t blk_stride = (int64_t)Hkv * tile_stride;
     const u32x4* base = reinterpret_cast<const u32x4*>(does_k ? k_cache : v_cache) + (int64_t)g * tile_stride;
-    typedef __attribute__((address_space(4))) const int32_t cint32;
-    const cint32* cbt = (const cint32*)bt;
     const int last_blk = (kv_end - 1) / kBlockSize;
     const int blk0 = kv_begin / kBlockSize + sblk;
+    // Physical ids of the wave's blocks of 64 consecutive tiles, one per lane (read back with
+    // readlane, so the per-tile address needs no memory wait); refreshed every 64 tiles.
+    int bid_base = 0;
+    int bid = bt[min(blk0 + 4 * lane, last_blk)];
     // Per-lane offsets (u32x4 units) of the staged chunks in the block tile and (bf16 units) in LDS.
     int goff[NI], soff[NI];
 #pragma unroll
@@ -929,7 +931,12 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
     // buffers; `tile` is the K tile index for waves 0-3 and the V tile index for waves 4-7.
     auto load = [&](int tile, u32x4 (&r)[NI]) __attribute__((always_inline)) -> int {
       const int lb = blk0 + 4 * tile;
-      const u32x4* p = base + (int64_t)cbt[min(lb, last_blk)] * blk_stride;
+      if (tile - bid_base >= 64) {
+        bid_base = tile;
+        bid = bt[min(blk0 + 4 * (tile + lane), last_blk)];
+      }
+      const int phys = __builtin_amdgcn_readlane(bid, tile - bid_base);
+      const u32x4* p = base + (int64_t)phys * blk_stride;
 #pragma unroll
       for (int i = 0; i < NI; ++i) r[i] = p[goff[i]];
       return does_k ? kBlockSize : kv_end - lb * kBlockSize;

@@ -35,7 +35,8 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_and_check(wl, rows_per_step=None, check_pools=True, want_lse=True, out_dtype=torch.bfloat16, seed=0):
+def run_and_check(wl, rows_per_step=None, check_pools=True, want_lse=True, out_dtype=torch.bfloat16, seed=0,
+                  expect_tile_rows=None):
     """Run every step of ``wl`` on the GPU and compare with the oracle (optionally on sampled rows)."""
     bs = wl.block_size
     dw = DeviceWorkload(wl)
@@ -46,6 +47,8 @@ def run_and_check(wl, rows_per_step=None, check_pools=True, want_lse=True, out_d
         say(f"  step {si}: B={st.num_seqs} T={st.num_tokens}")
         slots_g, out_g, lse_g, plan = dw.run_step(st, out_dtype=out_dtype, want_lse=want_lse)
         torch.cuda.synchronize()
+        if expect_tile_rows is not None:
+            assert plan.tile_rows == expect_tile_rows, plan.tile_rows
         slots_o = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, bs)
         assert np.array_equal(slots_g.cpu().numpy(), slots_o), "slot mapping differs"
         kp, vp = O.reshape_and_cache(st.k, st.v, kp, vp, slots_o, bs)
@@ -112,6 +115,29 @@ def test_long_chunked_prefill_8wave_tiles_parity():
     say("long_chunked_prefill small with 8-wave tiles: 1536-token prompt in 3 chunks of 512")
     stats = run_and_check(W.long_chunked_prefill(seed=2, prompt=1536, chunk=512, num_decode=5, decode_ctx=700))
     assert stats
+
+
+WIDE_SHAPES = [(64, 1), (64, 2), (64, 4), (64, 8), (128, 1), (128, 2), (128, 4), (128, 8)]
+
+
+@pytest.mark.parametrize("head_dim,group", WIDE_SHAPES)
+def test_wide_tiles_every_shape(head_dim, group):
+    """A batch with >= 2048 packed prefill rows (256-row tiles, launched apart from its decode
+    rows) at every supported (head_dim, q heads per kv head): a ragged chunk over a cached
+    context, a short prompt and three decode rows."""
+    say(f"wide tiles D={head_dim} G={group}")
+    reqs = [W.RequestSpec(300, [2048 // group + 37]), W.RequestSpec(0, [100])]
+    reqs += [W.RequestSpec(c, [1]) for c in (1, 700, 1500)]
+    wl = W.build("wide", reqs, num_q_heads=2 * group, num_kv_heads=2, head_dim=head_dim, seed=11)
+    run_and_check(wl, expect_tile_rows=256)
+
+
+@pytest.mark.parametrize("head_dim,group", [(64, 1), (64, 8), (128, 1), (128, 2)])
+def test_cascade_every_shape(head_dim, group):
+    say(f"cascade D={head_dim} G={group}")
+    wl = W.cascade_shared_prefix(seed=5, num_queries=70, prefix=1040, suffix_range=(1, 200),
+                                 num_q_heads=2 * group, num_kv_heads=2, head_dim=head_dim)
+    _cascade_check(wl)
 
 
 def test_single_key_rows_are_exact():

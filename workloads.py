@@ -372,11 +372,17 @@ def long_chunked_prefill(
 
 
 def cascade_shared_prefix(
-    seed: int = 0, num_queries: int = 512, prefix: int = 16384, suffix_range=(64, 1024), num_q_heads: int = 64
+    seed: int = 0,
+    num_queries: int = 512,
+    prefix: int = 16384,
+    suffix_range=(64, 1024),
+    num_q_heads: int = 64,
+    num_kv_heads: int = 8,
+    head_dim: int = 128,
 ) -> Workload:
     """Decode queries that all share one physical prefix, plus unique suffixes (which include the new token).
 
-    70B-shaped head slice: 64 q / 8 kv heads, D=128.
+    Default: the 70B-shaped head slice, 64 q / 8 kv heads, D=128.
     """
     rng = _rng(seed, 4)
     suf = rng.integers(suffix_range[0], suffix_range[1] + 1, size=num_queries)
@@ -385,8 +391,8 @@ def cascade_shared_prefix(
         "cascade_shared_prefix",
         reqs,
         num_q_heads=num_q_heads,
-        num_kv_heads=8,
-        head_dim=128,
+        num_kv_heads=num_kv_heads,
+        head_dim=head_dim,
         seed=seed,
         rng=rng,
         shared_prefix=prefix,
