@@ -64,6 +64,19 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte load with the streaming (non-temporal) cache policy: for K/V bytes read once.
+#ifndef PKV_DECODE_NT
+#define PKV_DECODE_NT 1
+#endif
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+#if PKV_DECODE_NT
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+#else
+  return *p;
+#endif
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __builtin_bit_cast(
@@ -223,9 +236,9 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
 #pragma unroll
     for (int ts = 0; ts < 2; ++ts)
 #pragma unroll
-      for (int cc = 0; cc < CPT; ++cc) kr[ts * CPT + cc] = kp[(grp + 8 * ts) * CH + c + 8 * cc];
+      for (int cc = 0; cc < CPT; ++cc) kr[ts * CPT + cc] = ld_stream(kp + (grp + 8 * ts) * CH + c + 8 * cc);
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) vr[i] = vp[lane + 64 * i];
+    for (int i = 0; i < RPL; ++i) vr[i] = ld_stream(vp + lane + 64 * i);
   };
 
   auto process = [&](int k, uint4 (&kr)[NKR], uint4 (&vr)[RPL]) {
@@ -701,9 +714,9 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
 // Pipelined MFMA tile: 256 packed rows on 8 waves (32 rows per wave, two waves per SIMD).  The
 // tile loop is software-pipelined so that one wave's instruction stream mixes matrix and vector
 // work: step t issues the MFMAs of S^T(t+1) = K(t+1) Q^T and O^T += V(t-1)^T P^T(t-1) while the
-// VALU computes the softmax of tile t (whose S^T the previous step produced).  K tiles are
-// staged two ahead of their use and V tiles one behind, each in two LDS buffers (waves 0-3 copy
-// K, waves 4-7 copy V), with one barrier per step.  P^T is built from the S^T accumulator with
+// VALU computes the softmax of tile t (whose S^T the previous step produced).  Step t also
+// loads K(t+2) and V(t) at its start and stores them into LDS at its end (waves 0-3 copy K,
+// waves 4-7 copy V; two buffers each), with one barrier per step.  P^T is built from the S^T accumulator with
 // two lane-half swaps per K-step so that a lane holds 8 consecutive keys; the V^T operand is
 // then one 16-byte read of the value tile in its natural dim-major order.
 // ------------------------------------------------------------------------------------------
@@ -957,8 +970,7 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
       }
     };
 
-    // Prologue: K(0) and K(1) in LDS, V(-1) = 0 (no tile before the first), K(2) / V(0) in
-    // flight, S^T(0) computed.
+    // Prologue: K(0) and K(1) in LDS, V(-1) = 0 (no tile before the first), S^T(0) computed.
     u32x4 st[NI];
     int nv;
     if (does_k) {
@@ -966,11 +978,9 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
       store(0, st, nv);
       nv = load(1, st);
       store(1, st, nv);
-      nv = load(2, st);
     } else {
       u32x4* z = reinterpret_cast<u32x4*>(vbuf0 + S::V_ELEMS);
       for (int i = threadIdx.x - 256; i < S::V_ELEMS / 8; i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
-      nv = load(0, st);
     }
     __syncthreads();
     {
@@ -987,12 +997,12 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) R.pb[1][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 
-    // Step t: store K(t+2) / V(t), load K(t+3) / V(t+1), then S^T(t+1), P.V(t-1) and softmax(t).
+    // Step t: load K(t+2) / V(t), compute S^T(t+1), P.V(t-1) and softmax(t), then store the
+    // loaded tile (its buffer was last read in step t-1), so the whole step covers the load.
     auto step = [&](auto cur, int t) __attribute__((always_inline)) {
       constexpr int CUR = decltype(cur)::value;
       __syncthreads();
-      store(t & 1, st, nv);
-      nv = load(does_k ? t + 3 : t + 1, st);
+      nv = load(does_k ? t + 2 : t, st);
       const int k0 = kv_begin + t * kKvTile;
       if ((k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > pos0))
         pipe_mask<D, CUR, CAUSAL>(R, h, k0, kv_end);
@@ -1001,6 +1011,7 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
       pipe_step<D, CUR>(R, kbuf0 + ((t + 1) & 1) * S::K_ELEMS, vbuf0 + ((t + 1) & 1) * S::V_ELEMS, n, h, sl,
                         need, mnew, ts);
       pipe_commit<D>(R, need, mnew, ts);
+      store(t & 1, st, nv);
     };
     int t = 0;
     for (; t + 1 < ntiles; t += 2) {
