@@ -727,7 +727,7 @@ struct PipeRegs {
   bf16x8 qb[KSTEPS];    // Q^T operand: dims 16s + 8h .. +7 of the lane's query row
   floatx16 oacc[DT];    // O^T accumulators
   floatx16 sacc[2][2];  // two S^T sets (tile t and t+1), each two 32-key halves
-  bf16x8 pb[2][4];      // two P^T sets (tile t-1 and t), four 16-key steps each
+  bf16x8 pb[4];         // P^T (four 16-key steps): tile t-1 until its P.V step, then tile t
   float m, lsum;        // running max (log2 units of scaled scores) and row sum
   int qpos;             // position of the lane's query row
 };
@@ -752,23 +752,22 @@ __device__ __forceinline__ void pipe_mask(PipeRegs<D>& R, int h, int k0, int kv_
     }
 }
 
-// O^T += V^T P^T(SET) over the V buffer `vb`.
-template <int D, int SET>
-__device__ __forceinline__ void pipe_pv(PipeRegs<D>& R, const uint16_t* __restrict__ vb, int n, int h) {
+// O^T += V^T P^T over the V buffer `vb`, 16-key step ks.
+template <int D>
+__device__ __forceinline__ void pipe_pv_step(PipeRegs<D>& R, const uint16_t* __restrict__ vb, int n, int h, int ks) {
   using S = TileSmem<D>;
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 xv = *reinterpret_cast<const bf16x8*>(vb + (32 * d + n) * S::VP + 16 * ks + 8 * h);
-      R.oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xv, R.pb[SET][ks], R.oacc[d], 0, 0, 0);
-    }
+  for (int d = 0; d < D / 32; ++d) {
+    const bf16x8 xv = *reinterpret_cast<const bf16x8*>(vb + (32 * d + n) * S::VP + 16 * ks + 8 * h);
+    R.oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xv, R.pb[ks], R.oacc[d], 0, 0, 0);
+  }
 }
 
-// One pipeline step.  CUR holds S^T(t) (already masked) and receives P^T(t); the other set
-// receives S^T(t+1) from K buffer `kb` and supplies P^T(t-1) to the P.V over V buffer `vb`.
-// Straight-line code, so that the scheduler can interleave the MFMA and VALU streams.  Returns
-// in `need` whether the running max moved, with the new max and the tile's row sum.
+// One pipeline step.  CUR holds S^T(t) (already masked); the other set receives S^T(t+1) from
+// K buffer `kb`; P^T holds tile t-1 for the P.V over V buffer `vb` and is overwritten, one
+// 16-key step after its P.V, with tile t.  Straight-line code, so that the scheduler can
+// interleave the MFMA and VALU streams.  Returns in `need` whether the running max moved, with
+// the new max and the tile's row sum.
 template <int D, int CUR>
 __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __restrict__ kb,
                                           const uint16_t* __restrict__ vb, int n, int h, float sl,
@@ -800,53 +799,33 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
           __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, R.qb[s], s == 0 ? zero : R.sacc[NXT][mt], 0, 0, 0);
     }
 
-  // Softmax, part 2: p = exp2(s * scale - m), fp32 row sum, bf16 pairs.
-  uint32_t pk[2][8];
+  // Per 16-key step ks: O^T += V^T P^T(t-1) for those keys, then the softmax of tile t for them
+  // (p = exp2(s * scale - m), fp32 row sum, bf16 pairs) becomes the new P^T step.  In the
+  // accumulator layout a lane of half h holds keys 4h..4h+3 and 8+4h..8+4h+3 of the step as
+  // dwords d0..d3; swapping d0<->d2 and d1<->d3 across the halves leaves it keys 8h..8h+7.
   ts = 0.f;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int ks = 0; ks < 4; ++ks) {
+    pipe_pv_step<D>(R, vb, n, h, ks);
+    const int mt = ks >> 1, b0 = 8 * (ks & 1);
+    uint32_t pk[4];
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const float p0 = fast_exp2(fmaf(R.sacc[CUR][mt][e], sl, -mref));
-      const float p1 = fast_exp2(fmaf(R.sacc[CUR][mt][e + 1], sl, -mref));
+    for (int u = 0; u < 4; ++u) {
+      const float p0 = fast_exp2(fmaf(R.sacc[CUR][mt][b0 + 2 * u], sl, -mref));
+      const float p1 = fast_exp2(fmaf(R.sacc[CUR][mt][b0 + 2 * u + 1], sl, -mref));
       ts += p0;
       ts += p1;
-      pk[mt][e >> 1] = pack_bf16x2(p0, p1);
+      pk[u] = pack_bf16x2(p0, p1);
     }
-
-  // O^T += V^T P^T(t-1).
-  pipe_pv<D, NXT>(R, vb, n, h);
-
-  // Softmax, part 3: the P^T operand of tile t.  K-step ks covers keys 16ks..16ks+15; in the
-  // accumulator layout a lane of half h holds keys 4h..4h+3 and 8+4h..8+4h+3 of them as dwords
-  // d0..d3, and swapping d0<->d2 and d1<->d3 across the halves leaves it keys 8h..8h+7.
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int mt = ks >> 1, b = 4 * (ks & 1);
-    const auto s02 = __builtin_amdgcn_permlane32_swap(pk[mt][b], pk[mt][b + 2], false, false);
-    const auto s13 = __builtin_amdgcn_permlane32_swap(pk[mt][b + 1], pk[mt][b + 3], false, false);
+    const auto s02 = __builtin_amdgcn_permlane32_swap(pk[0], pk[2], false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(pk[1], pk[3], false, false);
     u32x4 w;
     w[0] = s02[0];
     w[1] = s13[0];
     w[2] = s02[1];
     w[3] = s13[1];
-    R.pb[CUR][ks] = __builtin_bit_cast(bf16x8, w);
+    R.pb[ks] = __builtin_bit_cast(bf16x8, w);
   }
-#ifdef PKV_SCHED
-  // Issue order: operand reads PKV_SCHED ahead of their MFMA, VALU work spread between MFMAs.
-  __builtin_amdgcn_sched_group_barrier(0x100, PKV_SCHED, 0);
-#pragma unroll
-  for (int i = 0; i < 32 - PKV_SCHED; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < PKV_SCHED; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-  }
-#endif
 }
 
 // After a step: apply a moved running max to the output (which now holds tiles up to t-1) and
@@ -888,9 +867,6 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
   uint16_t* vbuf0 = smem + 2 * S::K_ELEMS;
 
   PipeRegs<D> R;
-#ifdef PKV_AGPR_FORM
-  asm volatile("" ::: "a0");
-#endif
   const int pr = 32 * wave + n;
   const int tq = pr / G;
   const int hh = pr % G;
@@ -914,51 +890,55 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
 
   const int ntiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
   if (ntiles > 0) {
-    // Staging: waves 0-3 copy the K rows of cache block (wave & 3) of a tile (key KPI*i +
-    // lane/LPT, chunk lane % LPT), waves 4-7 its V^T chunks (chunk lane + 64i of the dim-major
-    // block tile is dim (lane >> 1) + 32i, tokens 8*(lane & 1)..+7).  Loads are unconditional
+    // Staging: waves 0-3 copy the K rows (key KPI*i + lane/LPT, chunk lane % LPT) and waves 4-7
+    // the V^T chunks (chunk lane + 64i of the dim-major block tile is dim (lane >> 1) + 32i,
+    // tokens 8*(lane & 1)..+7) of cache block (wave & 3) of a tile.  Loads are unconditional
     // (past the end they re-read the last block); values of keys past the end are zeroed at
-    // store time.
-    const bool does_k = wave < 4;
+    // store time.  The staging code is written per job (J = 1 job per wave).
+    constexpr int J = 1;
     const int sblk = wave & 3;
     const int sc = lane % LPT;
     const int sr = lane / LPT;
     const int64_t tile_stride = (int64_t)kBlockSize * CH;
     const int64_t blk_stride = (int64_t)Hkv * tile_stride;
-    const u32x4* base = reinterpret_cast<const u32x4*>(does_k ? k_cache : v_cache) + (int64_t)g * tile_stride;
     const int last_blk = (kv_end - 1) / kBlockSize;
     const int blk0 = kv_begin / kBlockSize + sblk;
     // Physical ids of the wave's blocks of 64 consecutive tiles, one per lane (read back with
     // readlane, so the per-tile address needs no memory wait); refreshed every 64 tiles.
     int bid_base = 0;
     int bid = bt[min(blk0 + 4 * lane, last_blk)];
-    // Per-lane offsets (u32x4 units) of the staged chunks in the block tile and (bf16 units) in LDS.
-    int goff[NI], soff[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      goff[i] = does_k ? (KPI * i + sr) * CH + sc : lane + 64 * i;
-      soff[i] = does_k ? (kBlockSize * sblk + KPI * i + sr) * S::KP + sc * 8
-                       : 2 * S::K_ELEMS + ((lane >> 1) + 32 * i) * S::VP + kBlockSize * sblk + 8 * (lane & 1);
-    }
-    // Buffer of tile t: K tiles alternate between the two K buffers, V tiles between the two V
-    // buffers; `tile` is the K tile index for waves 0-3 and the V tile index for waves 4-7.
-    auto load = [&](int tile, u32x4 (&r)[NI]) __attribute__((always_inline)) -> int {
-      const int lb = blk0 + 4 * tile;
+    auto block_id = [&](int tile) __attribute__((always_inline)) -> int {
       if (tile - bid_base >= 64) {
         bid_base = tile;
         bid = bt[min(blk0 + 4 * (tile + lane), last_blk)];
       }
-      const int phys = __builtin_amdgcn_readlane(bid, tile - bid_base);
-      const u32x4* p = base + (int64_t)phys * blk_stride;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) r[i] = p[goff[i]];
-      return does_k ? kBlockSize : kv_end - lb * kBlockSize;
+      return __builtin_amdgcn_readlane(bid, tile - bid_base);
     };
-    auto store = [&](int buf, const u32x4 (&r)[NI], int nvalid) __attribute__((always_inline)) {
-      uint16_t* dst = smem + buf * (does_k ? S::K_ELEMS : S::V_ELEMS);
+    bool jv[J];                // the job copies V
+    const u32x4* jbase[J];     // pool base of the job's kv head
+    int soff[J], sstep[J];     // LDS offset (bf16 units) of chunk i: soff + i * sstep
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      jv[j] = wave >= 4;
+      jbase[j] = reinterpret_cast<const u32x4*>(jv[j] ? v_cache : k_cache) + (int64_t)g * tile_stride;
+      // Chunk lane + 64i of the block tile: ((KPI*i + sr)*CH + sc) is that same index for K rows.
+      soff[j] = jv[j] ? 2 * S::K_ELEMS + (lane >> 1) * S::VP + kBlockSize * sblk + 8 * (lane & 1)
+                      : (kBlockSize * sblk + sr) * S::KP + sc * 8;
+      sstep[j] = jv[j] ? 32 * S::VP : KPI * S::KP;
+    }
+    // K tiles alternate between the two K buffers, V tiles between the two V buffers.
+    auto load = [&](int j, int tile, u32x4 (&r)[NI]) __attribute__((always_inline)) -> int {
+      const int lb = blk0 + 4 * tile;
+      const u32x4* p = jbase[j] + (int64_t)block_id(tile) * blk_stride;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) r[i] = p[lane + 64 * i];
+      return jv[j] ? kv_end - lb * kBlockSize : kBlockSize;
+    };
+    auto store = [&](int j, int buf, const u32x4 (&r)[NI], int nvalid) __attribute__((always_inline)) {
+      uint16_t* dst = smem + buf * (jv[j] ? S::V_ELEMS : S::K_ELEMS);
       if (nvalid >= kBlockSize) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + soff[i]) = r[i];
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + soff[j] + i * sstep[j]) = r[i];
       } else {
         const int t0 = 8 * (lane & 1);
         u32x4 msk;
@@ -966,21 +946,25 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
         for (int u = 0; u < 4; ++u)
           msk[u] = (t0 + 2 * u < nvalid ? 0x0000ffffu : 0u) | (t0 + 2 * u + 1 < nvalid ? 0xffff0000u : 0u);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + soff[i]) = r[i] & msk;
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + soff[j] + i * sstep[j]) = r[i] & msk;
       }
     };
 
     // Prologue: K(0) and K(1) in LDS, V(-1) = 0 (no tile before the first), S^T(0) computed.
-    u32x4 st[NI];
-    int nv;
-    if (does_k) {
-      nv = load(0, st);
-      store(0, st, nv);
-      nv = load(1, st);
-      store(1, st, nv);
-    } else {
+    u32x4 st[J][NI];
+    int nv[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (!jv[j]) {
+        nv[j] = load(j, 0, st[j]);
+        store(j, 0, st[j], nv[j]);
+        nv[j] = load(j, 1, st[j]);
+        store(j, 1, st[j], nv[j]);
+      }
+    }
+    {
       u32x4* z = reinterpret_cast<u32x4*>(vbuf0 + S::V_ELEMS);
-      for (int i = threadIdx.x - 256; i < S::V_ELEMS / 8; i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = threadIdx.x; i < S::V_ELEMS / 8; i += 512) z[i] = u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
     {
@@ -995,14 +979,15 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
         }
     }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) R.pb[1][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int ks = 0; ks < 4; ++ks) R.pb[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 
     // Step t: load K(t+2) / V(t), compute S^T(t+1), P.V(t-1) and softmax(t), then store the
-    // loaded tile (its buffer was last read in step t-1), so the whole step covers the load.
+    // loaded tiles (their buffers were last read in step t-1), so the whole step covers the load.
     auto step = [&](auto cur, int t) __attribute__((always_inline)) {
       constexpr int CUR = decltype(cur)::value;
       __syncthreads();
-      nv = load(does_k ? t + 2 : t, st);
+#pragma unroll
+      for (int j = 0; j < J; ++j) nv[j] = load(j, jv[j] ? t : t + 2, st[j]);
       const int k0 = kv_begin + t * kKvTile;
       if ((k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > pos0))
         pipe_mask<D, CUR, CAUSAL>(R, h, k0, kv_end);
@@ -1011,7 +996,8 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
       pipe_step<D, CUR>(R, kbuf0 + ((t + 1) & 1) * S::K_ELEMS, vbuf0 + ((t + 1) & 1) * S::V_ELEMS, n, h, sl,
                         need, mnew, ts);
       pipe_commit<D>(R, need, mnew, ts);
-      store(t & 1, st, nv);
+#pragma unroll
+      for (int j = 0; j < J; ++j) store(j, t & 1, st[j], nv[j]);
     };
     int t = 0;
     for (; t + 1 < ntiles; t += 2) {
@@ -1022,10 +1008,8 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
     // The last P.V (tile ntiles - 1, stored by the last step).
     __syncthreads();
     const uint16_t* vlast = vbuf0 + ((ntiles - 1) & 1) * S::V_ELEMS;
-    if ((ntiles - 1) & 1)
-      pipe_pv<D, 1>(R, vlast, n, h);
-    else
-      pipe_pv<D, 0>(R, vlast, n, h);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pipe_pv_step<D>(R, vlast, n, h, ks);
   }
 
   const float lsum = R.lsum + other_half(R.lsum, h);
@@ -1076,7 +1060,7 @@ void varlen_kernel(VarlenArgs a) {
   }
 }
 
-// Wide-tile kernels: 256-row pipelined tiles on 8 waves.
+// Wide-tile kernels: 256-row pipelined tiles on 8 waves (two per SIMD).
 template <int D, int G>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void prefill_wide_kernel(VarlenArgs a) {
