@@ -764,67 +764,100 @@ __device__ __forceinline__ void pipe_pv_step(PipeRegs<D>& R, const uint16_t* __r
 }
 
 // One pipeline step.  CUR holds S^T(t) (already masked); the other set receives S^T(t+1) from
-// K buffer `kb`; P^T holds tile t-1 for the P.V over V buffer `vb` and is overwritten, one
-// 16-key step after its P.V, with tile t.  Straight-line code, so that the scheduler can
-// interleave the MFMA and VALU streams.  Returns in `need` whether the running max moved, with
-// the new max and the tile's row sum.
+// K buffer `kb`; P^T holds tile t-1 for the P.V over V buffer `vb` and is overwritten, 16-key
+// step by 16-key step after its last P.V use, with tile t.  The step is issued in a fixed
+// order, one slot per MFMA: slot i reads the operand of MFMA i + 2 from LDS, issues MFMA i
+// (first the P.V MFMAs, then the S MFMAs) and then a slice of the softmax of tile t, so that
+// every MFMA runs under VALU work and its operand has been in flight for two MFMAs.  The
+// softmax slices: the tile max and lazy max update over the first NMAX slots, then 16
+// pieces, each the p = exp2(s * scale - m) of 4 keys with their fp32 row sum and bf16 pairs,
+// the fourth piece of a 16-key step also swapping the pairs across the wave halves into the
+// new P^T step (a lane of half h holds keys 4h..4h+3 and 8+4h..8+4h+3 of the step as dwords
+// d0..d3; swapping d0<->d2 and d1<->d3 leaves it keys 8h..8h+7).  Returns in `need` whether
+// the running max moved, with the new max and the tile's row sum.
 template <int D, int CUR>
 __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __restrict__ kb,
                                           const uint16_t* __restrict__ vb, int n, int h, float sl,
                                           bool& need, float& mnew, float& ts) {
   constexpr int NXT = 1 - CUR;
   constexpr int KSTEPS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int NPV = 4 * DT;        // P.V MFMAs (16-key step ks, d tile d: index DT*ks + d)
+  constexpr int NM = NPV + 2 * KSTEPS;  // then S MFMAs (K-step s, key half mt: 2*s + mt)
+  constexpr int PF = 2;              // operand reads in flight
+  constexpr int NMAX = NM / 8;       // slots of the tile max
+  constexpr int SPAN = NM - NMAX - 2;  // slots over which the 16 exp pieces are spread
   using S = TileSmem<D>;
   const floatx16 zero = {};
 
-  // Softmax, part 1: tile max and the lazy max update (raised only past kLazy, for every lane
-  // of the wave at once, so that the output rescale stays rare).
-  float mx = -INFINITY;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, R.sacc[CUR][mt][e]);
-  mx = fmaxf(mx, other_half(mx, h)) * sl;
-  need = __ballot(mx > R.m + kLazy) != 0;
-  mnew = need ? fmaxf(R.m, mx) : R.m;
-  const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-
-  // S^T(t+1) = K Q^T.
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + (32 * mt + n) * S::KP + 16 * s + 8 * h);
-      R.sacc[NXT][mt] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, R.qb[s], s == 0 ? zero : R.sacc[NXT][mt], 0, 0, 0);
+  auto operand = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+    if (i < NPV) {
+      const int ks = i / DT, d = i % DT;
+      return *reinterpret_cast<const bf16x8*>(vb + (32 * d + n) * S::VP + 16 * ks + 8 * h);
     }
+    const int j = i - NPV, s = j / 2, mt = j % 2;
+    return *reinterpret_cast<const bf16x8*>(kb + (32 * mt + n) * S::KP + 16 * s + 8 * h);
+  };
 
-  // Per 16-key step ks: O^T += V^T P^T(t-1) for those keys, then the softmax of tile t for them
-  // (p = exp2(s * scale - m), fp32 row sum, bf16 pairs) becomes the new P^T step.  In the
-  // accumulator layout a lane of half h holds keys 4h..4h+3 and 8+4h..8+4h+3 of the step as
-  // dwords d0..d3; swapping d0<->d2 and d1<->d3 across the halves leaves it keys 8h..8h+7.
+  bf16x8 op[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) op[i] = operand(i);
+  float mx = -INFINITY, mref = 0.f;
+  uint32_t pk[4][4];
   ts = 0.f;
+  need = false;
+  mnew = R.m;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    pipe_pv_step<D>(R, vb, n, h, ks);
-    const int mt = ks >> 1, b0 = 8 * (ks & 1);
-    uint32_t pk[4];
+  for (int i = 0; i < NM; ++i) {
+    const bf16x8 a = op[i % PF];
+    if (i + PF < NM) op[i % PF] = operand(i + PF);
+    if (i < NPV) {
+      const int ks = i / DT, d = i % DT;
+      R.oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, R.pb[ks], R.oacc[d], 0, 0, 0);
+    } else {
+      const int j = i - NPV, s = j / 2, mt = j % 2;
+      R.sacc[NXT][mt] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, R.qb[s], s == 0 ? zero : R.sacc[NXT][mt], 0, 0, 0);
+    }
+    // Softmax slices of this slot.
+    if (i < NMAX) {
+      constexpr int PER = 32 / NMAX;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float p0 = fast_exp2(fmaf(R.sacc[CUR][mt][b0 + 2 * u], sl, -mref));
-      const float p1 = fast_exp2(fmaf(R.sacc[CUR][mt][b0 + 2 * u + 1], sl, -mref));
+      for (int e = 0; e < PER; ++e) {
+        const int x = i * PER + e;
+        mx = fmaxf(mx, R.sacc[CUR][x >> 4][x & 15]);
+      }
+      if (i == NMAX - 1) {
+        // Lazy max: raised only past kLazy, for every lane of the wave at once, so that the
+        // output rescale stays rare.
+        mx = fmaxf(mx, other_half(mx, h)) * sl;
+        need = __ballot(mx > R.m + kLazy) != 0;
+        mnew = need ? fmaxf(R.m, mx) : R.m;
+        mref = (mnew == -INFINITY) ? 0.f : mnew;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (NMAX + (q * SPAN) / 16 != i) continue;
+      const int ks = q >> 2, u = q & 3, mt = ks >> 1, e0 = 8 * (ks & 1) + 2 * u;
+      const float p0 = fast_exp2(fmaf(R.sacc[CUR][mt][e0], sl, -mref));
+      const float p1 = fast_exp2(fmaf(R.sacc[CUR][mt][e0 + 1], sl, -mref));
       ts += p0;
       ts += p1;
-      pk[u] = pack_bf16x2(p0, p1);
+      pk[ks][u] = pack_bf16x2(p0, p1);
+      if (u == 3) {
+        // P^T(t-1) of this 16-key step had its last use in slot DT*ks + DT - 1 < i.
+        const auto s02 = __builtin_amdgcn_permlane32_swap(pk[ks][0], pk[ks][2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(pk[ks][1], pk[ks][3], false, false);
+        u32x4 w;
+        w[0] = s02[0];
+        w[1] = s13[0];
+        w[2] = s02[1];
+        w[3] = s13[1];
+        R.pb[ks] = __builtin_bit_cast(bf16x8, w);
+      }
     }
-    const auto s02 = __builtin_amdgcn_permlane32_swap(pk[0], pk[2], false, false);
-    const auto s13 = __builtin_amdgcn_permlane32_swap(pk[1], pk[3], false, false);
-    u32x4 w;
-    w[0] = s02[0];
-    w[1] = s13[0];
-    w[2] = s02[1];
-    w[3] = s13[1];
-    R.pb[ks] = __builtin_bit_cast(bf16x8, w);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
