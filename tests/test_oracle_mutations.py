@@ -1,0 +1,149 @@
+"""The oracle pins catch plausible mistakes.
+
+Each case below plants one mistake in a step of the CPU oracle: an off-by-one causal mask, a
+wrong scale, the wrong kv head, shifted positions, a transposed value operand, a missing
+softmax normalisation, an LSE in the wrong base, a merge with its weights swapped, and a cache
+write at the wrong offset.  For each, the pins of test_oracle_pins.py run against the mutated
+oracle, and at least one must fail.  The mutations live here, on the CPU, and are undone
+after each case.
+"""
+
+import inspect
+import json
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle  # noqa: F401  (the package; its functions are what the pins call)
+import test_oracle_pins as pins
+
+OM = sys.modules["oracle.paged_attention"]  # the module whose globals the oracle's calls resolve
+
+
+def _pin_calls():
+    """Every pin as a zero-argument callable (fixtures and parameters filled in)."""
+    with open(pins.GOLDEN) as f:
+        page = json.load(f)
+    calls = []
+    for name, fn in sorted(vars(pins).items()):
+        if not name.startswith("test_") or not callable(fn):
+            continue
+        params = list(inspect.signature(fn).parameters)
+        marks = getattr(fn, "pytestmark", [])
+        grids = [m for m in marks if m.name == "parametrize"]
+        if grids:
+            names = [s.strip() for s in grids[0].args[0].split(",")]
+            for values in grids[0].args[1]:
+                kw = dict(zip(names, values if len(names) > 1 else [values]))
+                calls.append((f"{name}{values}", lambda fn=fn, kw=kw: fn(**kw)))
+        elif params == ["page"]:
+            calls.append((name, lambda fn=fn: fn(page)))
+        elif not params:
+            calls.append((name, fn))
+    return calls
+
+
+def _patch(attr, fn):
+    """Replace `attr` in the oracle module and in the package namespace."""
+    saved = [(OM, attr, getattr(OM, attr))]
+    if hasattr(oracle, attr) and callable(getattr(oracle, attr)):
+        saved.append((oracle, attr, getattr(oracle, attr)))
+        setattr(oracle, attr, fn)
+    setattr(OM, attr, fn)
+    return saved
+
+
+def _restore(saved):
+    for mod, attr, fn in saved:
+        setattr(mod, attr, fn)
+
+
+ORIG = {name: getattr(OM, name) for name in (
+    "causal_visible", "default_scale", "gather_keys", "gather_values", "token_positions",
+    "attention_state", "merge_attn_states", "reshape_and_cache")}
+
+
+def causal_strict(context_len, query_len, num_keys):
+    p = ORIG["token_positions"](context_len, query_len)
+    return np.arange(num_keys)[None, :] < p[:, None]  # a row no longer sees its own key
+
+
+def scale_one_over_d(head_dim):
+    return 1.0 / head_dim
+
+
+def keys_of_next_head(k_cache, row, num_keys, kv_head, block_size):
+    return ORIG["gather_keys"](k_cache, row, num_keys, (kv_head + 1) % k_cache.shape[1], block_size)
+
+
+def values_token_major(v_cache, row, num_keys, kv_head, block_size):
+    j = np.arange(num_keys)
+    phys = np.asarray(row, dtype=np.int64)[j // block_size]
+    x = OM.bf16_to_f64(v_cache[phys, kv_head, j % block_size, :])  # reads a dim-major pool as token-major
+    return x.reshape(num_keys, -1)[:, : v_cache.shape[2]]
+
+
+def positions_shifted(context_len, query_len):
+    return np.arange(context_len + 1, context_len + query_len + 1, dtype=np.int64)
+
+
+def state_unnormalised(scores, values):
+    o, lse = ORIG["attention_state"](scores, values)
+    z = np.exp(np.where(np.isfinite(lse), lse - np.max(np.where(np.isfinite(scores), scores, -np.inf), axis=1,
+                                                        initial=-np.inf), 0.0))
+    return o * z[:, None], lse
+
+
+def state_lse_base2(scores, values):
+    o, lse = ORIG["attention_state"](scores, values)
+    m = np.max(scores, axis=1, initial=-np.inf) if scores.shape[1] else lse
+    return o, np.where(np.isfinite(lse), m + (lse - m) / math.log(2.0), lse)
+
+
+def merge_swapped(o_a, lse_a, o_b, lse_b):
+    o, lse = ORIG["merge_attn_states"](o_a, lse_a, o_b, lse_b)
+    o2, _ = ORIG["merge_attn_states"](o_a, lse_b, o_b, lse_a)  # weights of a and b exchanged
+    return o2, lse
+
+
+def cache_write_next_offset(k, v, k_cache, v_cache, slots, block_size):
+    s = np.asarray(slots, dtype=np.int64)
+    shifted = np.where(s < 0, s, (s // block_size) * block_size + (s % block_size + 1) % block_size)
+    return ORIG["reshape_and_cache"](k, v, k_cache, v_cache, shifted, block_size)
+
+
+MUTATIONS = [
+    ("causal_visible", causal_strict),
+    ("default_scale", scale_one_over_d),
+    ("gather_keys", keys_of_next_head),
+    ("gather_values", values_token_major),
+    ("token_positions", positions_shifted),
+    ("attention_state", state_unnormalised),
+    ("attention_state", state_lse_base2),
+    ("merge_attn_states", merge_swapped),
+    ("reshape_and_cache", cache_write_next_offset),
+]
+
+
+@pytest.mark.parametrize("attr,mutant", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
+def test_pins_catch_planted_mistake(attr, mutant):
+    saved = _patch(attr, mutant)
+    failed = []
+    try:
+        with np.errstate(all="ignore"):
+            for name, call in _pin_calls():
+                try:
+                    call()
+                except Exception:  # an assertion or any error the mistake provokes
+                    failed.append(name)
+    finally:
+        _restore(saved)
+    assert failed, f"no pin fails when {attr} is replaced by {mutant.__name__}"
+
+
+def test_pins_pass_on_the_unmutated_oracle():
+    for name, call in _pin_calls():
+        call()
