@@ -227,6 +227,44 @@ def decode_hbm(torch, P, steps=10, warmup=3):
     return res
 
 
+def spec_verify_hbm(torch, P, reps=10):
+    """Speculative-verify batch (64 rows of 1 + 4 tokens, context 1024..4096): varlen launch
+    GB/s against 8 TB/s (the five query tokens of a row share every K/V byte)."""
+    import workloads as W
+
+    wl = W.spec_verify(seed=0)
+    r = Runner(wl, torch, P)
+    st, s = wl.steps[0], r.steps[0]
+    P.append_kv(s["k"], s["v"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"], r.shape)
+    plan = P.plan_varlen(r.ws, st.query_start_loc, st.context_lens, st.seq_lens, r.shape)
+
+    def call():
+        P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"], s["seq"], r.shape, plan,
+                                 r.ws, out=s["out"])
+
+    call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    byts = step_bytes(st, wl)
+    out = {
+        "workload": "spec_verify: 64 rows x (1 + 4 drafted) tokens, ctx U[1024,4096], 32q/8kv, D128",
+        "ms": ms,
+        "algorithmic_bytes": byts,
+        "GB/s": byts / (ms * 1e-3) / 1e9,
+        "frac_of_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "tokens/s/layer": st.num_tokens / (ms * 1e-3),
+    }
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
 def mfma_paths(torch, P, reps=5):
     """MFMA-bound paths: the cascade shared-prefix pass (512 queries x 64 q heads over a
     16384-token prefix) and the long chunked prefill (one 32768-token prompt in 16 chunks of
@@ -397,6 +435,9 @@ def main():
     if not args.no_decode:
         log("bench: decode-only batch")
         line["decode_hbm"] = decode_hbm(torch, P)
+    if not args.no_decode:
+        log("bench: speculative-verify batch")
+        line["spec_verify_hbm"] = spec_verify_hbm(torch, P)
     if args.mfma:
         log("bench: MFMA paths (cascade prefix, long chunked prefill)")
         line["mfma_paths"] = mfma_paths(torch, P)

@@ -114,6 +114,16 @@ int pkv_append_kv(int64_t* slot_mapping, const void* k, const void* v, void* k_c
                   const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
                   const pkv_shape* shape, void* stream);
 
+/* Copy-on-write of shared blocks ["11. vLLM principles", section 11.2: requests with a common
+ * prefix point their block tables at the same physical blocks]: for each of num_pairs pairs
+ * {src, dst} in block_pairs (device int32 [num_pairs, 2]), copies physical block src to dst in
+ * both pools, every kv head, bit for bit, so that a request can take a private copy of a
+ * shared block before writing into it.  Pairs naming a block outside [0, num_blocks), or
+ * src == dst, are skipped.  No destination may also appear as another pair's source or
+ * destination (the copies run concurrently).  num_pairs == 0 is a no-op. */
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
+                    const pkv_shape* shape, void* stream);
+
 /* Builds the work list of one varlen attention call from host copies of the metadata:
  * validates seq_lens[r] == context_lens[r] + (qsl[r+1] - qsl[r]) and every length, cuts
  * query-length-1 rows into split-KV decode items and longer rows into prefill tiles of

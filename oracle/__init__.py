@@ -15,6 +15,7 @@ from .paged_attention import (  # noqa: F401
     bf16_to_f64,
     cascade_prefix_attention,
     causal_visible,
+    copy_blocks,
     default_scale,
     gather_keys,
     gather_values,

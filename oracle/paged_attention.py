@@ -101,6 +101,21 @@ def reshape_and_cache(k, v, k_cache, v_cache, slots, block_size: int) -> Tuple[n
     return kc, vc
 
 
+def copy_blocks(k_cache, v_cache, block_pairs) -> Tuple[np.ndarray, np.ndarray]:
+    """Return copies of the pools where every physical block dst of a pair (src, dst) holds the
+    bits of block src, in both pools and every kv head (the copy-on-write of a shared block
+    ["11. vLLM principles", section 11.2]).  Pairs outside the pool, or with src == dst, are
+    skipped; all copies read the pools as they were before the call."""
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    nb = k_cache.shape[0]
+    for src, dst in np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2):
+        if 0 <= src < nb and 0 <= dst < nb and src != dst:
+            kc[dst] = k_cache[src]
+            vc[dst] = v_cache[src]
+    return kc, vc
+
+
 # ---------------------------------------------------------------------------
 # Gathering keys/values through a block table.
 # ---------------------------------------------------------------------------

@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     cascade_prefix_attention,
     cascade_workspace_size,
     compute_slot_mapping,
+    copy_blocks,
     make_shape,
     merge_attn_states,
     paged_attention_varlen,

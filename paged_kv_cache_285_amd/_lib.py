@@ -22,6 +22,7 @@ EXPORTS = (
     "pkv_compute_slot_mapping",
     "pkv_reshape_and_cache",
     "pkv_append_kv",
+    "pkv_copy_blocks",
     "pkv_plan_varlen",
     "pkv_plan_varlen_host",
     "pkv_paged_attention_varlen",
@@ -85,6 +86,7 @@ _SIGS = {
     "pkv_compute_slot_mapping": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _SHAPE, _P]),
     "pkv_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _SHAPE, _P]),
     "pkv_append_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _P]),
+    "pkv_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _SHAPE, _P]),
     "pkv_plan_varlen": (ctypes.c_int, [_PLAN, _P, _SZ, _P, _P, _P, _I32, _I32, _SHAPE, _P]),
     "pkv_plan_varlen_host": (ctypes.c_int, [_PLAN, _P, _I32, _P, _P, _P, _I32, _I32, _SHAPE]),
     "pkv_paged_attention_varlen": (

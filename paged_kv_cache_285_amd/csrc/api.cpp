@@ -125,6 +125,15 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
   // Split size for decode rows: the smallest power of two (>= kMinBlocksPerSplit, <= 256
   // blocks, i.e. at most 64 per wave, which the decode kernel relies on) whose item count
   // times Hkv stays within the target workgroup count.
+  // Prefill tiles hold 256 packed (token, q head) rows (wide tiles) when the batch has enough
+  // rows in requests long enough to fill them, else 128.
+  int64_t wide_rows = 0;
+  for (int r = 0; r < num_seqs; ++r) {
+    const int64_t rows = (int64_t)(qsl[r + 1] - qsl[r]) * G;
+    if (qsl[r + 1] - qsl[r] > 1 && rows >= pkv::kWideTileRows) wide_rows += rows;
+  }
+  P.tile_rows = wide_rows >= pkv::kPrefillRowsForWideTiles ? pkv::kWideTileRows : pkv::kTileRows;
+  const int tok_per_tile = P.tile_rows / G;
   int bps = pkv::kMinBlocksPerSplit;
   for (; bps < 256; bps *= 2) {
     int64_t n = 0;
@@ -133,13 +142,6 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
     if (n * s->num_kv_heads <= decode_target_wgs()) break;
   }
   P.bps = bps;
-  // Prefill tiles hold 256 packed (token, q head) rows (wide tiles) when the batch has enough
-  // prefill rows to fill them, else 128.
-  int64_t prefill_rows = 0;
-  for (int r = 0; r < num_seqs; ++r)
-    if (qsl[r + 1] - qsl[r] > 1) prefill_rows += (int64_t)(qsl[r + 1] - qsl[r]) * G;
-  P.tile_rows = prefill_rows >= pkv::kPrefillRowsForWideTiles ? pkv::kWideTileRows : pkv::kTileRows;
-  const int tok_per_tile = P.tile_rows / G;
   P.items.clear();
   P.token_split.assign((size_t)num_tokens * 2, 0);
   std::vector<pkv::WorkItem> pre, dec;
@@ -426,6 +428,19 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), slot_mapping, num_tokens,
       shape->num_kv_heads, shape->head_dim, num_slots, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "reshape_and_cache launch");
+  return ok();
+}
+
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
+                    const pkv_shape* shape, void* stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (num_pairs < 0) return fail(PKV_EINVAL, "negative num_pairs");
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !block_pairs) return fail(PKV_EINVAL, "null pointer argument");
+  hipError_t e = pkv::launch_copy_blocks(static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                                         block_pairs, num_pairs, shape->num_blocks, shape->num_kv_heads,
+                                         shape->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
   return ok();
 }
 

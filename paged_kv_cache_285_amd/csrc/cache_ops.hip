@@ -109,6 +109,25 @@ __global__ void append_kv_kernel(int64_t* __restrict__ slot_out, const uint4* __
   }
 }
 
+
+// Copy-on-write support ["11. vLLM principles", section 11.2: requests that share a prefix
+// point their block tables at the same physical blocks]: before one of them writes into a
+// shared block, the block is copied to a fresh one.  Workgroup (pair, pool) copies the whole
+// physical block src -> dst of one pool (K for pool 0, V for pool 1; every kv head), 16 bytes
+// per thread and step.  Pairs naming a block outside [0, num_blocks) are skipped.
+__global__ void copy_blocks_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                   const int32_t* __restrict__ pairs, int32_t num_blocks,
+                                   int64_t chunks_per_block) {
+  const int32_t p = blockIdx.x;
+  const int32_t src = pairs[2 * p];
+  const int32_t dst = pairs[2 * p + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+  uint4* pool = blockIdx.y == 0 ? k_cache : v_cache;
+  const uint4* from = pool + (int64_t)src * chunks_per_block;
+  uint4* to = pool + (int64_t)dst * chunks_per_block;
+  for (int64_t c = threadIdx.x; c < chunks_per_block; c += blockDim.x) to[c] = from[c];
+}
+
 }  // namespace
 
 hipError_t launch_append_kv(int64_t* slot_mapping, const uint16_t* k, const uint16_t* v,
@@ -153,6 +172,17 @@ hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v, uint16
                      reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
                      reinterpret_cast<uint4*>(k_cache), v_cache, slots,
                      num_tokens, num_kv_heads, chunks, num_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(uint16_t* k_cache, uint16_t* v_cache, const int32_t* pairs,
+                              int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                              int32_t head_dim, hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const int64_t chunks = (int64_t)num_kv_heads * kBlockSize * head_dim / 8;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, 2), dim3(256), 0, stream,
+                     reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache), pairs,
+                     num_blocks, chunks);
   return hipGetLastError();
 }
 

@@ -95,6 +95,9 @@ hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v, uint16
                                     uint16_t* v_cache, const int64_t* slots, int32_t num_tokens,
                                     int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
                                     hipStream_t stream);
+hipError_t launch_copy_blocks(uint16_t* k_cache, uint16_t* v_cache, const int32_t* pairs,
+                              int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                              int32_t head_dim, hipStream_t stream);
 // Launches the attention kernels of a varlen plan whose items list n_prefill prefill tiles of
 // tile_rows rows first, then n_decode decode items.
 hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, int n_prefill, int n_decode,

@@ -114,6 +114,20 @@ def reshape_and_cache(
     )
 
 
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: torch.Tensor, shape: PkvShape) -> None:
+    """Copy physical blocks src -> dst in both pools (rows {src, dst} of int32 ``block_pairs``)."""
+    check(
+        lib().pkv_copy_blocks(
+            _dev(k_cache, "k_cache", _16BIT),
+            _dev(v_cache, "v_cache", _16BIT),
+            _dev(block_pairs, "block_pairs", (torch.int32,)),
+            int(block_pairs.shape[0]),
+            ctypes.byref(shape),
+            _stream(),
+        )
+    )
+
+
 def append_kv(
     k: torch.Tensor,
     v: torch.Tensor,

@@ -62,6 +62,9 @@ def test_shape_validation_errors(P):
     assert lib.pkv_cascade_prefix_attention(None, None, None, None, None, None, 100, 4, ctypes.byref(s), None, 0, None) == -3
     assert lib.pkv_merge_attn_states(None, 0, None, None, None, None, None, 4, 8, 6, None) == -1
     assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, None, None) == -1
+    assert lib.pkv_copy_blocks(None, None, None, 0, ctypes.byref(s), None) == 0
+    assert lib.pkv_copy_blocks(None, None, None, -2, ctypes.byref(s), None) == -1
+    assert lib.pkv_copy_blocks(None, None, None, 3, ctypes.byref(s), None) == -1
 
 
 def test_plan_rejects_inconsistent_metadata(P):
@@ -74,11 +77,12 @@ def test_plan_rejects_inconsistent_metadata(P):
         P.plan_varlen_host([0, 1], [64 * 16], [64 * 16 + 1], s)
 
 
-def test_plan_covers_every_row_exactly_once(P):
+@pytest.mark.parametrize("lengths", [(1, 1, 1, 2, 5, 17, 100, 300), (1, 1, 2, 5, 8, 17)])
+def test_plan_covers_every_row_exactly_once(P, lengths):
     s = shape(P, bt_stride=600)
     rng = np.random.default_rng(0)
     B = 40
-    ql = rng.choice([1, 1, 1, 2, 17, 100, 300], size=B)
+    ql = rng.choice(lengths, size=B)
     ctx = rng.integers(0, 5000, size=B)
     qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
     seq = (ctx + ql).astype(np.int32)

@@ -117,6 +117,63 @@ def test_long_chunked_prefill_8wave_tiles_parity():
     assert stats
 
 
+def test_spec_verify_small_parity():
+    """Query length 1 + 4 drafted tokens over cached contexts: small causal-offset MFMA tiles."""
+    say("spec_verify small: 12 rows of 5 tokens, ctx U[1, 700]")
+    run_and_check(W.spec_verify(seed=1, num_seqs=12, ctx_range=(1, 700)))
+    say("spec_verify: 6 rows of 5 tokens and 4 of 8, ctx U[1100, 3000]")
+    run_and_check(W.spec_verify(seed=2, num_seqs=6, ctx_range=(1100, 3000)))
+    run_and_check(W.spec_verify(seed=3, num_seqs=4, draft=7, ctx_range=(1100, 3000)))
+
+
+def test_spec_verify_full_size_sampled():
+    say("spec_verify full: 64 rows of 5 tokens, ctx U[1024, 4096], sampled rows")
+    run_and_check(W.spec_verify(seed=0), rows_per_step=48, check_pools=False)
+
+
+def test_graph_capture_replays_match_eager():
+    """The step's cache write and attention (decode splits with their reduce, and prefill tiles)
+    captured in a HIP graph: every replay, with eager work and synchronisation in between,
+    gives the eager result bit for bit.  The plan is uploaded before capture."""
+    say("graph capture: mixed batch step 0")
+    wl = W.mixed_llama8b(seed=6, num_decode=24, ctx_range=(100, 3000))
+    st = wl.steps[0]
+    dw = DeviceWorkload(wl)
+    t = dw.step_tensors(st)
+    plan = P.plan_varlen(dw.ws, st.query_start_loc, st.context_lens, st.seq_lens, dw.shape)
+    assert plan.num_partials > 0 and plan.num_prefill_items > 0
+    out = torch.empty(st.q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(st.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def step():
+        P.append_kv(t["k"], t["v"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], t["ctx"], dw.shape)
+        P.paged_attention_varlen(t["q"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], t["ctx"], t["seq"], dw.shape,
+                                 plan, dw.ws, out=out, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        step()  # warm the side stream before capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.synchronize()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for rep in range(3):
+        out.zero_()
+        lse.zero_()
+        scratch.add_(1.0)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}: output differs"
+        assert torch.equal(lse, ref_l), f"replay {rep}: lse differs"
+
+
 WIDE_SHAPES = [(64, 1), (64, 2), (64, 4), (64, 8), (128, 1), (128, 2), (128, 4), (128, 8)]
 
 
@@ -166,6 +223,21 @@ def test_append_kv_matches_oracle_bitwise():
         assert np.array_equal(slots.cpu().numpy(), ref)
         kp, vp = O.reshape_and_cache(st.k, st.v, kp, vp, ref, wl.block_size)
         assert np.array_equal(host16(dw.k_cache), kp) and np.array_equal(host16(dw.v_cache), vp)
+
+
+def test_copy_blocks_matches_oracle_bitwise():
+    say("copy_blocks: 40 pairs over the mixed batch pools, plus skipped pairs")
+    wl = W.mixed_llama8b(seed=7, num_decode=8)
+    dw = DeviceWorkload(wl)
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(wl.num_blocks)
+    pairs = np.stack([perm[:40], perm[40:80]], axis=1).astype(np.int32)  # no block in two pairs
+    pairs = np.concatenate([pairs, [[-1, 3], [5, wl.num_blocks], [9, 9]]]).astype(np.int32)
+    P.copy_blocks(dw.k_cache, dw.v_cache, dev32(pairs), dw.shape)
+    torch.cuda.synchronize()
+    kc, vc = O.copy_blocks(wl.k_cache, wl.v_cache, pairs)
+    assert np.array_equal(host16(dw.k_cache), kc), "k_cache bits differ"
+    assert np.array_equal(host16(dw.v_cache), vc), "v_cache bits differ"
 
 
 def test_plan_reuse_is_bit_identical():

@@ -3,7 +3,7 @@
 Each case below plants one mistake in a step of the CPU oracle: an off-by-one causal mask, a
 wrong scale, the wrong kv head, shifted positions, a transposed value operand, a missing
 softmax normalisation, an LSE in the wrong base, a merge with its weights swapped, and a cache
-write at the wrong offset.  For each, the pins of test_oracle_pins.py run against the mutated
+write at the wrong offset, a block copy that forgets the values.  For each, the pins of test_oracle_pins.py run against the mutated
 oracle, and at least one must fail.  The mutations live here, on the CPU, and are undone
 after each case.
 """
@@ -11,7 +11,6 @@ after each case.
 import inspect
 import json
 import math
-import os
 import sys
 
 import numpy as np
@@ -63,7 +62,7 @@ def _restore(saved):
 
 ORIG = {name: getattr(OM, name) for name in (
     "causal_visible", "default_scale", "gather_keys", "gather_values", "token_positions",
-    "attention_state", "merge_attn_states", "reshape_and_cache")}
+    "attention_state", "merge_attn_states", "reshape_and_cache", "copy_blocks")}
 
 
 def causal_strict(context_len, query_len, num_keys):
@@ -115,6 +114,11 @@ def cache_write_next_offset(k, v, k_cache, v_cache, slots, block_size):
     return ORIG["reshape_and_cache"](k, v, k_cache, v_cache, shifted, block_size)
 
 
+def copy_keys_only(k_cache, v_cache, block_pairs):
+    kc, _ = ORIG["copy_blocks"](k_cache, v_cache, block_pairs)
+    return kc, np.array(v_cache, copy=True)
+
+
 MUTATIONS = [
     ("causal_visible", causal_strict),
     ("default_scale", scale_one_over_d),
@@ -125,6 +129,7 @@ MUTATIONS = [
     ("attention_state", state_lse_base2),
     ("merge_attn_states", merge_swapped),
     ("reshape_and_cache", cache_write_next_offset),
+    ("copy_blocks", copy_keys_only),
 ]
 
 

@@ -207,6 +207,58 @@ def _sdpa_fp64(q, k, v, mask, scale):
     return out[0].permute(1, 0, 2).numpy()
 
 
+def test_copy_blocks_bits_and_skips():
+    """Copied blocks hold the source bits in both pools; untouched blocks keep theirs; pairs
+    outside the pool and src == dst change nothing."""
+    rng = np.random.default_rng(21)
+    nb, hkv, bs, d = 12, 2, 16, 8
+    kp = rand_bf16(rng, nb, hkv, bs, d)
+    vp = rand_bf16(rng, nb, hkv, d, bs)
+    pairs = np.array([[3, 9], [4, 4], [0, 11], [-1, 2], [5, 12]], dtype=np.int32)
+    kc, vc = O.copy_blocks(kp, vp, pairs)
+    for b in range(nb):
+        src = {9: 3, 11: 0}.get(b, b)
+        assert np.array_equal(kc[b], kp[src]) and np.array_equal(vc[b], vp[src]), b
+    assert np.array_equal(kp, rand_bf16(np.random.default_rng(21), nb, hkv, bs, d))  # inputs untouched
+
+
+def test_copy_on_write_keeps_the_sharer_unchanged(page):
+    """["11. vLLM principles", 11.2 block-table example] A = [3, 7, 11] and B = [3, 7, 5] share
+    physical blocks 3 and 7.  B takes a private copy of block 7 (to block 12) before writing a
+    token into it; afterwards A's attention is the same as before, and B's equals attention over
+    its own keys laid out in a fresh pool."""
+    ex = page["block_table_sharing"]
+    a_bt, b_bt = np.array(ex["table_a"]), np.array(ex["table_b"])
+    rng = np.random.default_rng(22)
+    nb, hkv, bs, d, hq = 16, 1, 16, 8, 2
+    kp = rand_bf16(rng, nb, hkv, bs, d)
+    vp = rand_bf16(rng, nb, hkv, d, bs)
+    q = rand_bf16(rng, 2, hq, d)
+    ctx_len = 40  # both requests see 41 keys: blocks 0..2
+    qsl = np.array([0, 1, 2])
+    ctx = np.array([ctx_len, ctx_len])
+    seq = ctx + 1
+    bts = np.stack([a_bt, b_bt]).astype(np.int32)
+    before_o, before_l = O.paged_attention(q, kp, vp, bts, qsl, ctx, seq, bs)
+    # B copies shared block 7 and overwrites one of its tokens (slot 12*16 + 5) in its copy.
+    kc, vc = O.copy_blocks(kp, vp, np.array([[b_bt[1], 12]]))
+    b_new = b_bt.copy()
+    b_new[1] = 12
+    kn = rand_bf16(rng, 1, hkv, d)
+    vn = rand_bf16(rng, 1, hkv, d)
+    kc, vc = O.reshape_and_cache(kn, vn, kc, vc, np.array([12 * bs + 5]), bs)
+    bts2 = np.stack([a_bt, b_new]).astype(np.int32)
+    after_o, after_l = O.paged_attention(q, kc, vc, bts2, qsl, ctx, seq, bs)
+    assert np.array_equal(after_o[0], before_o[0]) and np.array_equal(after_l[0], before_l[0])
+    # B against its keys copied block by block into a fresh pool (blocks 0, 1, 2).
+    fk = np.stack([kc[b] for b in b_new])
+    fv = np.stack([vc[b] for b in b_new])
+    ref_o, ref_l = O.paged_attention(q[1:], fk, fv, np.array([[0, 1, 2]], np.int32), [0, 1], [ctx_len],
+                                     [ctx_len + 1], bs)
+    assert np.array_equal(after_o[1], ref_o[0]) and np.array_equal(after_l[1], ref_l[0])
+    assert not np.allclose(after_o[1], before_o[1])  # the write did reach B
+
+
 def test_tiny_prefill_matches_torch_sdpa():
     wl = W.tiny_prefill(seed=1)
     st = wl.steps[0]

@@ -371,6 +371,17 @@ def long_chunked_prefill(
     return build("long_chunked_prefill", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=seed, rng=rng)
 
 
+def spec_verify(seed: int = 0, num_seqs: int = 64, draft: int = 4, ctx_range=(1024, 4096)) -> Workload:
+    """Speculative-decoding verification rows: each request scores its next token plus ``draft``
+    drafted tokens (query length 1 + draft) against its cached context in one pass, as the
+    Tencent Cloud article's speculative decoding / MTP section describes with four drafts;
+    Llama-3-8B-shaped."""
+    rng = _rng(seed, 5)
+    ctx = rng.integers(ctx_range[0], ctx_range[1] + 1, size=num_seqs)
+    reqs = [RequestSpec(int(c), [1 + draft]) for c in ctx]
+    return build("spec_verify", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=seed, rng=rng)
+
+
 def cascade_shared_prefix(
     seed: int = 0,
     num_queries: int = 512,
@@ -405,6 +416,7 @@ _BUILDERS = {
     "decode_only": decode_only,
     "long_chunked_prefill": long_chunked_prefill,
     "cascade_shared_prefix": cascade_shared_prefix,
+    "spec_verify": spec_verify,
 }
 
 
