@@ -265,6 +265,33 @@ def spec_verify_hbm(torch, P, reps=10):
     return out
 
 
+def tiny_prefill_latency(torch, P, reps=20):
+    """The 31 + 29 + 30 batched prefill (4 q / 2 kv heads, D64): a latency-bound single launch."""
+    import workloads as W
+
+    wl = W.tiny_prefill(seed=0)
+    r = Runner(wl, torch, P)
+    st, s = wl.steps[0], r.steps[0]
+    P.append_kv(s["k"], s["v"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"], r.shape)
+    plan = P.plan_varlen(r.ws, st.query_start_loc, st.context_lens, st.seq_lens, r.shape)
+
+    def call():
+        P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"], s["seq"], r.shape, plan,
+                                 r.ws, out=s["out"])
+
+    call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    return {"workload": "tiny_prefill: prompts of 31, 29 and 30 tokens, 4 q / 2 kv heads, D64", "us_per_call": us,
+            "tokens/s": st.num_tokens / (us * 1e-6)}
+
+
 def mfma_paths(torch, P, reps=5):
     """MFMA-bound paths: the cascade shared-prefix pass (512 queries x 64 q heads over a
     16384-token prefix) and the long chunked prefill (one 32768-token prompt in 16 chunks of
@@ -308,6 +335,13 @@ def mfma_paths(torch, P, reps=5):
     prefix_ms = timed(lambda: P.cascade_prefix_attention(s["q"], r.k_cache, r.v_cache, pbt, cv.prefix_len,
                                                          r.shape, cws, out=o, lse=l), reps)
     cascade_ms = timed(cascade, reps)
+    suffix_ms = timed(lambda: P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, sbt, s["qsl"], sctx, sseq, sshape,
+                                                       splan, r.ws, out=os_, lse=ls_), reps)
+    merge_ms = timed(lambda: P.merge_attn_states(o, l, os_, ls_, out=merged), reps)
+    # suffix keys once per kv head + bf16 Q + fp32 O and LSE + block-table entries
+    suffix_bytes = (kv_bytes(cv.suffix_seq_lens, wl.num_kv_heads, wl.head_dim)
+                    + st.num_tokens * wl.num_q_heads * (wl.head_dim * 2 + wl.head_dim * 4 + 4)
+                    + int(np.sum(-(-cv.suffix_seq_lens // wl.block_size))) * 4)
     fplan = P.plan_varlen(r.ws, st.query_start_loc, st.context_lens, st.seq_lens, r.shape)
     single_ms = timed(lambda: P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"],
                                                        s["seq"], r.shape, fplan, r.ws, out=s["out"]), reps)
@@ -317,6 +351,9 @@ def mfma_paths(torch, P, reps=5):
         "ms": prefix_ms,
         "TFLOP/s": flops / (prefix_ms * 1e-3) / 1e12,
         "frac_of_bf16_peak": flops / (prefix_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        "suffix_pass_ms": suffix_ms,
+        "suffix_pass_GB/s": suffix_bytes / (suffix_ms * 1e-3) / 1e9,
+        "merge_ms": merge_ms,
         "cascade_total_ms": cascade_ms,
         "single_pass_ms": single_ms,
         "cascade_speedup": single_ms / cascade_ms,
@@ -334,14 +371,32 @@ def mfma_paths(torch, P, reps=5):
         tot_ms += timed(lambda: P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"],
                                                          s["seq"], r.shape, plan, r.ws, out=s["out"]), 2)
         tot_fl += step_flops(st, wl)
+    # The same prompt beside 128 decode rows at context 2048 (+1 per chunk): whole steps.
+    wl2 = W.long_chunked_prefill(seed=0)
+    del r
+    torch.cuda.empty_cache()
+    r2 = Runner(wl2, torch, P)
+    mixed_ms = 0.0
+    for s2 in r2.steps:
+        st2 = s2["st"]
+        P.append_kv(s2["k"], s2["v"], r2.k_cache, r2.v_cache, s2["bt"], s2["qsl"], s2["ctx"], r2.shape)
+        plan2 = P.plan_varlen(r2.ws, st2.query_start_loc, st2.context_lens, st2.seq_lens, r2.shape)
+        mixed_ms += timed(lambda: P.paged_attention_varlen(s2["q"], r2.k_cache, r2.v_cache, s2["bt"], s2["qsl"],
+                                                           s2["ctx"], s2["seq"], r2.shape, plan2, r2.ws,
+                                                           out=s2["out"]), 2)
+    out["long_chunked_prefill_with_decode"] = {
+        "workload": "the same 16 chunks, each step beside 128 decode rows at context 2048 + chunk index",
+        "ms_all_steps": mixed_ms,
+        "tokens/s/layer": sum(s2["st"].num_tokens for s2 in r2.steps) / (mixed_ms * 1e-3),
+    }
+    del r2
+    torch.cuda.empty_cache()
     out["long_chunked_prefill"] = {
         "workload": "one 32768-token prompt in 16 chunks of 2048 against its growing paged context, 32 q / 8 kv heads",
         "ms_all_chunks": tot_ms,
         "TFLOP/s": tot_fl / (tot_ms * 1e-3) / 1e12,
         "frac_of_bf16_peak": tot_fl / (tot_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
     }
-    del r
-    torch.cuda.empty_cache()
     return out
 
 
@@ -436,8 +491,9 @@ def main():
         log("bench: decode-only batch")
         line["decode_hbm"] = decode_hbm(torch, P)
     if not args.no_decode:
-        log("bench: speculative-verify batch")
+        log("bench: speculative-verify batch, tiny prefill")
         line["spec_verify_hbm"] = spec_verify_hbm(torch, P)
+        line["tiny_prefill"] = tiny_prefill_latency(torch, P)
     if args.mfma:
         log("bench: MFMA paths (cascade prefix, long chunked prefill)")
         line["mfma_paths"] = mfma_paths(torch, P)
