@@ -3,9 +3,12 @@
 Each case below plants one mistake in a step of the CPU oracle: an off-by-one causal mask, a
 wrong scale, the wrong kv head, shifted positions, a transposed value operand, a missing
 softmax normalisation, an LSE in the wrong base, a merge with its weights swapped, and a cache
-write at the wrong offset, a block copy that forgets the values.  For each, the pins of test_oracle_pins.py run against the mutated
-oracle, and at least one must fail.  The mutations live here, on the CPU, and are undone
-after each case.
+write at the wrong offset, a block copy that forgets the values; and in the FP8 half, a wrong
+exponent bias, ties rounded away from zero, no saturation, a multiplied instead of divided
+scale, one kv head's scale for all, the wrong block's scale, an ignored key scale.  For each,
+the pins of test_oracle_pins.py and test_oracle_fp8_pins.py run against the mutated oracle,
+and at least one must fail.  The mutations live here, on the CPU, and are undone after each
+case.
 """
 
 import inspect
@@ -17,9 +20,11 @@ import numpy as np
 import pytest
 
 import oracle  # noqa: F401  (the package; its functions are what the pins call)
+import test_oracle_fp8_pins as fp8_pins
 import test_oracle_pins as pins
 
-OM = sys.modules["oracle.paged_attention"]  # the module whose globals the oracle's calls resolve
+OM = sys.modules["oracle.paged_attention"]  # the modules whose globals the oracle's calls resolve
+F8 = sys.modules["oracle.kv_fp8"]
 
 
 def _pin_calls():
@@ -27,7 +32,8 @@ def _pin_calls():
     with open(pins.GOLDEN) as f:
         page = json.load(f)
     calls = []
-    for name, fn in sorted(vars(pins).items()):
+    items = [(n, f) for mod in (pins, fp8_pins) for n, f in sorted(vars(mod).items(), key=lambda x: x[0])]
+    for name, fn in items:
         if not name.startswith("test_") or not callable(fn):
             continue
         params = list(inspect.signature(fn).parameters)
@@ -46,12 +52,13 @@ def _pin_calls():
 
 
 def _patch(attr, fn):
-    """Replace `attr` in the oracle module and in the package namespace."""
-    saved = [(OM, attr, getattr(OM, attr))]
+    """Replace `attr` in the oracle module that defines it and in the package namespace."""
+    mod = F8 if hasattr(F8, attr) and getattr(F8, attr).__module__ == F8.__name__ else OM
+    saved = [(mod, attr, getattr(mod, attr))]
     if hasattr(oracle, attr) and callable(getattr(oracle, attr)):
         saved.append((oracle, attr, getattr(oracle, attr)))
         setattr(oracle, attr, fn)
-    setattr(OM, attr, fn)
+    setattr(mod, attr, fn)
     return saved
 
 
@@ -63,6 +70,9 @@ def _restore(saved):
 ORIG = {name: getattr(OM, name) for name in (
     "causal_visible", "default_scale", "gather_keys", "gather_values", "token_positions",
     "attention_state", "merge_attn_states", "reshape_and_cache", "copy_blocks")}
+ORIG8 = {name: getattr(F8, name) for name in (
+    "e4m3_decode", "e4m3_encode", "quantize", "reshape_and_cache_fp8", "dequantize_keys",
+    "dequantize_values")}
 
 
 def causal_strict(context_len, query_len, num_keys):
@@ -119,6 +129,40 @@ def copy_keys_only(k_cache, v_cache, block_pairs):
     return kc, np.array(v_cache, copy=True)
 
 
+def decode_bias_8(codes):
+    return ORIG8["e4m3_decode"](codes) * 0.5
+
+
+def encode_ties_away(x):
+    xs = np.asarray(x, dtype=np.float32)
+    up = np.nextafter(np.abs(xs), np.float32(np.inf)) * np.sign(xs)  # nudges a tie outwards
+    return ORIG8["e4m3_encode"](np.where(np.isfinite(xs), up, xs).astype(np.float32))
+
+
+def encode_no_saturation(x):
+    xs = np.asarray(x, dtype=np.float32)
+    c = ORIG8["e4m3_encode"](xs)
+    return np.where(np.abs(xs) > 448, np.uint8(0x7F), c).astype(np.uint8)
+
+
+def quantize_times_scale(x_bf16, scale):
+    return ORIG8["quantize"](x_bf16, 1.0 / float(scale))
+
+
+def cache_fp8_head0_scale(k, v, k_cache, v_cache, slots, k_scale, v_scale, block_size):
+    ks = np.repeat(np.asarray(k_scale)[:, :1], np.asarray(k_scale).shape[1], axis=1)
+    return ORIG8["reshape_and_cache_fp8"](k, v, k_cache, v_cache, slots, ks, v_scale, block_size)
+
+
+def values_scale_of_block0(v_cache, v_scale, row, num_keys, kv_head, block_size):
+    vs = np.broadcast_to(np.asarray(v_scale)[:1], np.asarray(v_scale).shape)
+    return ORIG8["dequantize_values"](v_cache, vs, row, num_keys, kv_head, block_size)
+
+
+def keys_unscaled(k_cache, k_scale, row, num_keys, kv_head, block_size):
+    return ORIG8["dequantize_keys"](k_cache, np.ones_like(np.asarray(k_scale)), row, num_keys, kv_head, block_size)
+
+
 MUTATIONS = [
     ("causal_visible", causal_strict),
     ("default_scale", scale_one_over_d),
@@ -130,6 +174,13 @@ MUTATIONS = [
     ("merge_attn_states", merge_swapped),
     ("reshape_and_cache", cache_write_next_offset),
     ("copy_blocks", copy_keys_only),
+    ("e4m3_decode", decode_bias_8),
+    ("e4m3_encode", encode_ties_away),
+    ("e4m3_encode", encode_no_saturation),
+    ("quantize", quantize_times_scale),
+    ("reshape_and_cache_fp8", cache_fp8_head0_scale),
+    ("dequantize_values", values_scale_of_block0),
+    ("dequantize_keys", keys_unscaled),
 ]
 
 

@@ -53,7 +53,8 @@ WORKLOAD_NAMES = (
     "cascade_shared_prefix",
 )
 
-_TAGS = {"pool_k": 1, "pool_v": 2, "new_k": 3, "new_v": 4, "q": 5}
+_TAGS = {"pool_k": 1, "pool_v": 2, "new_k": 3, "new_v": 4, "q": 5, "fp8_k": 6, "fp8_v": 7, "fp8_scale": 8}
+FP8_NAN = np.uint8(0x7F)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -308,6 +309,57 @@ def build(
         steps=steps,
         cascade=cascade,
     )
+
+
+@dataclass
+class Fp8Cache:
+    """An FP8 (e4m3 byte code) KV cache in the layouts of the bf16 pools, with one fp32 scale per
+    (physical block, kv head) tile of each pool."""
+
+    k_cache: np.ndarray  # uint8 [NB, Hkv, bs, D]
+    v_cache: np.ndarray  # uint8 [NB, Hkv, D, bs]
+    k_scale: np.ndarray  # float32 [NB, Hkv]
+    v_scale: np.ndarray  # float32 [NB, Hkv]
+
+
+def random_codes(n: int, seed: int, tag: int, max_magnitude: int = 0x57) -> np.ndarray:
+    """n random e4m3 byte codes: magnitude byte uniform on [0, max_magnitude] (0x57 is 15.0,
+    below the NaN code 0x7f), sign bit uniform; drawn chunk by chunk like normal_bf16."""
+    out = np.empty(n, dtype=np.uint8)
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+
+    def fill(ci: int) -> None:
+        lo = ci * _CHUNK
+        hi = min(n, lo + _CHUNK)
+        ss = np.random.SeedSequence(entropy=seed, spawn_key=(tag, 0, ci))
+        g = np.random.Generator(np.random.PCG64(ss))
+        mag = g.integers(0, max_magnitude, size=hi - lo, endpoint=True, dtype=np.uint8)
+        sign = g.integers(0, 1, size=hi - lo, endpoint=True, dtype=np.uint8) << np.uint8(7)
+        out[lo:hi] = mag | sign
+
+    if nchunks <= 1:
+        if n:
+            fill(0)
+    else:
+        with ThreadPoolExecutor(max_workers=_threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out
+
+
+def fp8_cache(wl: "Workload", seed: int = 0, scale_range=(0.04, 0.12)) -> Fp8Cache:
+    """FP8 pools for a workload: every element the bf16 pools hold as a cached value gets a
+    random code (random_codes), every poisoned element the NaN code 0x7f; the scales are
+    uniform fp32 draws on scale_range, one per (block, kv head) of each pool."""
+    kc = random_codes(wl.k_cache.size, seed, _TAGS["fp8_k"]).reshape(wl.k_cache.shape)
+    vc = random_codes(wl.v_cache.size, seed, _TAGS["fp8_v"]).reshape(wl.v_cache.shape)
+    kc[wl.k_cache == BF16_NAN] = FP8_NAN
+    vc[wl.v_cache == BF16_NAN] = FP8_NAN
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(entropy=seed, spawn_key=(_TAGS["fp8_scale"],))))
+    lo, hi = scale_range
+    shape = (wl.num_blocks, wl.num_kv_heads)
+    ks = g.uniform(lo, hi, size=shape).astype(np.float32)
+    vs = g.uniform(lo, hi, size=shape).astype(np.float32)
+    return Fp8Cache(k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs)
 
 
 def _rng(seed: int, which: int) -> np.random.Generator:
