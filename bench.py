@@ -227,6 +227,57 @@ def decode_hbm(torch, P, steps=10, warmup=3):
     return res
 
 
+def fp8_decode_hbm(torch, P, steps=10, warmup=3, bf16_ms=None):
+    """The decode-only batch over FP8 (e4m3) pools with per-(block, kv head) scales: varlen
+    kernel GB/s (K/V at one byte per element, plus the scales read) against 8 TB/s."""
+    import workloads as W
+
+    wl = W.decode_only(seed=0)
+    c = W.fp8_cache(wl, seed=0)
+    st = wl.steps[0]
+    shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    kc, vc, ks, vs = dev(c.k_cache), dev(c.v_cache), dev(c.k_scale), dev(c.v_scale)
+    del c
+    i16 = lambda a: dev(a.view(np.int16))  # noqa: E731
+    q, k, v = i16(st.q), i16(st.k), i16(st.v)
+    bt, qsl, ctx, seq = (dev(x.astype(np.int32)) for x in (st.block_tables, st.query_start_loc, st.context_lens,
+                                                           st.seq_lens))
+    ws = P.alloc_workspace(P.varlen_workspace_size(st.num_seqs, st.num_tokens, int(st.seq_lens.max()), shape))
+    out = torch.empty((st.num_tokens, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    P.append_kv_fp8(k, v, kc, vc, ks, vs, bt, qsl, ctx, shape)
+    plan = P.plan_varlen(ws, st.query_start_loc, st.context_lens, st.seq_lens, shape)
+
+    def call():
+        P.paged_attention_varlen_fp8(q, kc, vc, ks, vs, bt, qsl, ctx, seq, shape, plan, ws, out=out)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    P.timing_begin()
+    for _ in range(steps):
+        call()
+    total, n = P.timing_end()
+    ms = total / n
+    kvb = kv_bytes(st.seq_lens, wl.num_kv_heads, wl.head_dim) // 2
+    blocks = int(np.sum(-(-st.seq_lens // wl.block_size)))
+    nbytes = kvb + 2 * blocks * wl.num_kv_heads * 4 + 2 * st.num_tokens * wl.num_q_heads * wl.head_dim * 2 + blocks * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "workload": "decode_only over fp8 e4m3 pools: 256 seqs, ctx U[1024,8192], 32q/8kv, D128, bs16",
+        "kernel_ms": ms,
+        "algorithmic_bytes": nbytes,
+        "GB/s": gbs,
+        "frac_of_peak": gbs / HBM_PEAK_GBS,
+        "tokens/s/layer": st.num_tokens / (ms * 1e-3),
+    }
+    if bf16_ms:
+        res["speedup_vs_bf16_pools"] = bf16_ms / ms
+    del kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
 def spec_verify_hbm(torch, P, reps=10):
     """Speculative-verify batch (64 rows of 1 + 4 tokens, context 1024..4096): varlen launch
     GB/s against 8 TB/s (the five query tokens of a row share every K/V byte)."""
@@ -490,6 +541,8 @@ def main():
     if not args.no_decode:
         log("bench: decode-only batch")
         line["decode_hbm"] = decode_hbm(torch, P)
+        log("bench: decode-only batch over fp8 pools")
+        line["fp8_decode_hbm"] = fp8_decode_hbm(torch, P, bf16_ms=line["decode_hbm"]["kernel_ms"])
     if not args.no_decode:
         log("bench: speculative-verify batch, tiny prefill")
         line["spec_verify_hbm"] = spec_verify_hbm(torch, P)

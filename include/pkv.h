@@ -124,6 +124,42 @@ int pkv_append_kv(int64_t* slot_mapping, const void* k, const void* v, void* k_c
 int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
                     const pkv_shape* shape, void* stream);
 
+/* ---- FP8 (e4m3) KV cache ------------------------------------------------------------------
+ * Storing the KV cache in a low-precision float format such as FP8 cuts its size and speeds up
+ * attention, above all for long contexts [2048ai.net vLLM V1 article, quantisation section].
+ * Format: OCP FP8 E4M3 ("e4m3fn": bias 7, subnormals, no infinities, 0x7f / 0xff NaN, largest
+ * finite value 448), one byte per element, pools in the same layouts as the bf16 pools
+ * (k_cache uint8 [num_blocks, Hkv, bs, D], v_cache uint8 [num_blocks, Hkv, D, bs]).
+ * Scales: k_scale and v_scale are device fp32 [num_blocks, num_kv_heads], owned by the caller:
+ * a code stored in block b, kv head g means code_value * scale[b][g] (a per-head or per-tensor
+ * scale is the case of equal entries).  The scales of a block must be set before any token is
+ * written into it and stay fixed while the block holds tokens.
+ * Quantisation of a bf16 value x: y = x * (1 / scale) in fp32, clamped to [-448, 448], rounded
+ * to the nearest code with ties to even; NaN stores 0x7f.  Attention over fp8 pools equals
+ * attention over the dequantised keys and values. */
+
+/* a2 for fp8 pools: quantises k[t], v[t] (bf16 [num_tokens, Hkv, D]) under the scales of the
+ * block that slot_mapping[t] falls in and stores the codes there.  Slots are skipped as in
+ * pkv_reshape_and_cache.  Bit-exact against the definition above. */
+int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const float* k_scale, const float* v_scale,
+                              const int64_t* slot_mapping, int32_t num_tokens,
+                              const pkv_shape* shape, void* stream);
+
+/* a1 + a2 for fp8 pools, in one launch (as pkv_append_kv, quantising as
+ * pkv_reshape_and_cache_fp8). */
+int pkv_append_kv_fp8(int64_t* slot_mapping, const void* k, const void* v, void* k_cache,
+                      void* v_cache, const float* k_scale, const float* v_scale,
+                      const int32_t* block_tables, const int32_t* query_start_loc,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
+                      const pkv_shape* shape, void* stream);
+
+/* pkv_copy_blocks for fp8 pools: also copies the blocks' scales (k_scale[src][*] ->
+ * k_scale[dst][*], v_scale alike). */
+int pkv_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                        const int32_t* block_pairs, int32_t num_pairs, const pkv_shape* shape,
+                        void* stream);
+
 /* Builds the work list of one varlen attention call from host copies of the metadata:
  * validates seq_lens[r] == context_lens[r] + (qsl[r+1] - qsl[r]) and every length, cuts
  * query-length-1 rows into split-KV decode items and longer rows into prefill tiles of
@@ -162,6 +198,18 @@ int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const v
                                const pkv_varlen_plan* plan, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* a3/a4/a5 over fp8 pools: as pkv_paged_attention_varlen (same plan and workspace), reading
+ * e4m3 codes with their per-(block, kv head) scales.  Decode rows convert codes to bf16
+ * exactly and apply the key scale to the block's scores and the value scale to its
+ * probabilities; prefill tiles stage code * scale rounded to bf16. */
+int pkv_paged_attention_varlen_fp8(void* out, int32_t out_dtype, float* lse, const void* q,
+                                   const void* k_cache, const void* v_cache, const float* k_scale,
+                                   const float* v_scale, const int32_t* block_tables,
+                                   const int32_t* query_start_loc, const int32_t* context_lens,
+                                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_tokens,
+                                   const pkv_shape* shape, const pkv_varlen_plan* plan,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes for pkv_cascade_prefix_attention with these sizes. */
 size_t pkv_cascade_workspace_size(int32_t num_tokens, int32_t prefix_len, const pkv_shape* shape);
 
@@ -177,6 +225,15 @@ int pkv_cascade_prefix_attention(float* out_prefix, float* lse_prefix, const voi
                                  const int32_t* prefix_block_table, int32_t prefix_len,
                                  int32_t num_tokens, const pkv_shape* shape, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/* a6 over fp8 pools: as pkv_cascade_prefix_attention (same workspace size), the prefix keys
+ * and values read as e4m3 codes times their per-(block, kv head) scales. */
+int pkv_cascade_prefix_attention_fp8(float* out_prefix, float* lse_prefix, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* prefix_block_table, int32_t prefix_len,
+                                     int32_t num_tokens, const pkv_shape* shape, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* a8 — merge of two attention states over disjoint key sets [2048ai.net vLLM V1 article,
  * "Cascade Inference", the associative and commutative merge operator]:

@@ -27,6 +27,7 @@ from .paged_attention import (  # noqa: F401
     token_positions,
 )
 from .kv_fp8 import (  # noqa: F401
+    cascade_prefix_attention_fp8,
     dequantize_keys,
     dequantize_values,
     e4m3_decode,

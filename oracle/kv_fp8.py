@@ -152,3 +152,27 @@ def paged_attention_fp8(
                 o[tt, h, :] = oo
                 lse[tt, h] = ll
     return o, lse
+
+
+def cascade_prefix_attention_fp8(
+    q, k_cache, v_cache, k_scale, v_scale, prefix_block_table, prefix_len: int, block_size: int,
+    scale: Optional[float] = None,
+) -> Tuple[np.ndarray, np.ndarray]:
+    """State of every query token over the dequantised shared prefix keys 0..prefix_len-1
+    (no mask: every query comes after the prefix) [2048ai.net vLLM V1 article, "Cascade
+    Inference"].  Returns (o [T, Hq, D], lse [T, Hq]) in fp64."""
+    q = np.asarray(q)
+    T, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    sc = default_scale(D) if scale is None or scale <= 0 else float(scale)
+    o = np.zeros((T, Hq, D), dtype=np.float64)
+    lse = np.full((T, Hq), -np.inf, dtype=np.float64)
+    for g in range(Hkv):
+        K = dequantize_keys(k_cache, k_scale, prefix_block_table, prefix_len, g, block_size)
+        V = dequantize_values(v_cache, v_scale, prefix_block_table, prefix_len, g, block_size)
+        for hh in range(G):
+            h = g * G + hh
+            s = sc * (bf16_to_f64(q[:, h, :]) @ K.T)
+            o[:, h, :], lse[:, h] = attention_state(s, V)
+    return o, lse

@@ -9,16 +9,21 @@ from ._lib import PKV_DTYPE_BF16, PKV_DTYPE_F32, PkvError, PkvShape, PkvVarlenPl
 from .ops import (  # noqa: F401
     alloc_workspace,
     append_kv,
+    append_kv_fp8,
     cascade_prefix_attention,
+    cascade_prefix_attention_fp8,
     cascade_workspace_size,
     compute_slot_mapping,
     copy_blocks,
+    copy_blocks_fp8,
     make_shape,
     merge_attn_states,
     paged_attention_varlen,
+    paged_attention_varlen_fp8,
     plan_varlen,
     plan_varlen_host,
     reshape_and_cache,
+    reshape_and_cache_fp8,
     timing_begin,
     timing_end,
     varlen_workspace_size,

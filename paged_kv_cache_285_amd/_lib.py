@@ -22,12 +22,17 @@ EXPORTS = (
     "pkv_compute_slot_mapping",
     "pkv_reshape_and_cache",
     "pkv_append_kv",
+    "pkv_reshape_and_cache_fp8",
+    "pkv_append_kv_fp8",
     "pkv_copy_blocks",
+    "pkv_copy_blocks_fp8",
     "pkv_plan_varlen",
     "pkv_plan_varlen_host",
     "pkv_paged_attention_varlen",
+    "pkv_paged_attention_varlen_fp8",
     "pkv_cascade_workspace_size",
     "pkv_cascade_prefix_attention",
+    "pkv_cascade_prefix_attention_fp8",
     "pkv_merge_attn_states",
     "pkv_timing_begin",
     "pkv_timing_end",
@@ -86,17 +91,28 @@ _SIGS = {
     "pkv_compute_slot_mapping": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _SHAPE, _P]),
     "pkv_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _SHAPE, _P]),
     "pkv_append_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _P]),
+    "pkv_reshape_and_cache_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _SHAPE, _P]),
+    "pkv_append_kv_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _P]),
     "pkv_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _SHAPE, _P]),
+    "pkv_copy_blocks_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _SHAPE, _P]),
     "pkv_plan_varlen": (ctypes.c_int, [_PLAN, _P, _SZ, _P, _P, _P, _I32, _I32, _SHAPE, _P]),
     "pkv_plan_varlen_host": (ctypes.c_int, [_PLAN, _P, _I32, _P, _P, _P, _I32, _I32, _SHAPE]),
     "pkv_paged_attention_varlen": (
         ctypes.c_int,
         [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _PLAN, _P, _SZ, _P],
     ),
+    "pkv_paged_attention_varlen_fp8": (
+        ctypes.c_int,
+        [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _PLAN, _P, _SZ, _P],
+    ),
     "pkv_cascade_workspace_size": (_SZ, [_I32, _I32, _SHAPE]),
     "pkv_cascade_prefix_attention": (
         ctypes.c_int,
         [_P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _P, _SZ, _P],
+    ),
+    "pkv_cascade_prefix_attention_fp8": (
+        ctypes.c_int,
+        [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _P, _SZ, _P],
     ),
     "pkv_merge_attn_states": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
     "pkv_timing_begin": (ctypes.c_int, []),

@@ -431,15 +431,70 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
   return ok();
 }
 
+int pkv_append_kv_fp8(int64_t* slot_mapping, const void* k, const void* v, void* k_cache,
+                      void* v_cache, const float* k_scale, const float* v_scale,
+                      const int32_t* block_tables, const int32_t* query_start_loc,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
+                      const pkv_shape* shape, void* stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (num_tokens < 0 || num_seqs < 0) return fail(PKV_EINVAL, "negative sizes");
+  if (num_tokens == 0) return ok();
+  if (num_seqs == 0) return fail(PKV_EINVAL, "tokens without sequences");
+  if (!k || !v || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables ||
+      !query_start_loc || !context_lens)
+    return fail(PKV_EINVAL, "null pointer argument");
+  const int64_t num_slots = (int64_t)shape->num_blocks * shape->block_size;
+  hipError_t e = pkv::launch_append_kv_fp8(
+      slot_mapping, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale, v_scale, block_tables,
+      query_start_loc, context_lens, num_seqs, num_tokens, shape->num_kv_heads, shape->head_dim,
+      shape->bt_stride, num_slots, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append_kv_fp8 launch");
+  return ok();
+}
+
+int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const float* k_scale, const float* v_scale,
+                              const int64_t* slot_mapping, int32_t num_tokens,
+                              const pkv_shape* shape, void* stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (num_tokens < 0) return fail(PKV_EINVAL, "negative num_tokens");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !k_cache || !v_cache || !k_scale || !v_scale || !slot_mapping)
+    return fail(PKV_EINVAL, "null pointer argument");
+  const int64_t num_slots = (int64_t)shape->num_blocks * shape->block_size;
+  hipError_t e = pkv::launch_reshape_and_cache_fp8(
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint8_t*>(k_cache),
+      static_cast<uint8_t*>(v_cache), k_scale, v_scale, slot_mapping, num_tokens, shape->num_kv_heads,
+      shape->head_dim, num_slots, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "reshape_and_cache_fp8 launch");
+  return ok();
+}
+
 int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
                     const pkv_shape* shape, void* stream) {
   if (int rc = check_shape(shape)) return rc;
   if (num_pairs < 0) return fail(PKV_EINVAL, "negative num_pairs");
   if (num_pairs == 0) return ok();
   if (!k_cache || !v_cache || !block_pairs) return fail(PKV_EINVAL, "null pointer argument");
-  hipError_t e = pkv::launch_copy_blocks(static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
-                                         block_pairs, num_pairs, shape->num_blocks, shape->num_kv_heads,
-                                         shape->head_dim, (hipStream_t)stream);
+  hipError_t e = pkv::launch_copy_blocks(k_cache, v_cache, nullptr, nullptr, block_pairs, num_pairs,
+                                         shape->num_blocks, shape->num_kv_heads, shape->head_dim, 2,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
+  return ok();
+}
+
+int pkv_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                        const int32_t* block_pairs, int32_t num_pairs, const pkv_shape* shape,
+                        void* stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (num_pairs < 0) return fail(PKV_EINVAL, "negative num_pairs");
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !k_scale || !v_scale || !block_pairs)
+    return fail(PKV_EINVAL, "null pointer argument");
+  hipError_t e = pkv::launch_copy_blocks(k_cache, v_cache, k_scale, v_scale, block_pairs, num_pairs,
+                                         shape->num_blocks, shape->num_kv_heads, shape->head_dim, 1,
+                                         (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
   return ok();
 }
@@ -494,13 +549,13 @@ int pkv_plan_varlen(pkv_varlen_plan* plan, void* workspace, size_t workspace_byt
   return ok();
 }
 
-int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const void* q,
-                               const void* k_cache, const void* v_cache,
-                               const int32_t* block_tables, const int32_t* query_start_loc,
-                               const int32_t* context_lens, const int32_t* seq_lens,
-                               int32_t num_seqs, int32_t num_tokens, const pkv_shape* shape,
-                               const pkv_varlen_plan* plan, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+static int varlen_impl(void* out, int32_t out_dtype, float* lse, const void* q,
+                       const void* k_cache, const void* v_cache, const float* k_scale,
+                       const float* v_scale, bool fp8, const int32_t* block_tables,
+                       const int32_t* query_start_loc, const int32_t* context_lens,
+                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_tokens,
+                       const pkv_shape* shape, const pkv_varlen_plan* plan, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (int rc = check_shape(shape)) return rc;
   if (!plan) return fail(PKV_EINVAL, "plan is null");
   if (out_dtype != PKV_DTYPE_BF16 && out_dtype != PKV_DTYPE_F32)
@@ -511,7 +566,7 @@ int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const v
     return fail(PKV_EINVAL, "plan was made for different metadata or shape");
   if (num_tokens == 0 || plan->num_items == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens ||
-      !seq_lens || !workspace)
+      !seq_lens || !workspace || (fp8 && (!k_scale || !v_scale)))
     return fail(PKV_EINVAL, "null pointer argument");
   if ((size_t)plan->workspace_used > workspace_bytes)
     return fail(PKV_EWORKSPACE, "plan needs %lld workspace bytes, got %zu",
@@ -521,8 +576,10 @@ int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const v
   char* ws = static_cast<char*>(workspace);
   pkv::VarlenArgs a;
   a.q = static_cast<const uint16_t*>(q);
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
-  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.block_tables = block_tables;
   a.query_start_loc = query_start_loc;
   a.context_lens = context_lens;
@@ -540,8 +597,9 @@ int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const v
   a.scale_log2 = scale_log2(shape);
   const int G = shape->num_q_heads / shape->num_kv_heads;
   if (int rc = timing_mark((hipStream_t)stream, true)) return rc;
-  hipError_t e = pkv::launch_varlen(a, shape->head_dim, G, plan->num_prefill_items,
-                                    plan->num_decode_items, plan->tile_rows, (hipStream_t)stream);
+  hipError_t e = (fp8 ? pkv::launch_varlen_fp8 : pkv::launch_varlen)(
+      a, shape->head_dim, G, plan->num_prefill_items, plan->num_decode_items, plan->tile_rows,
+      (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "varlen attention launch");
   if (int rc = timing_mark((hipStream_t)stream, false)) return rc;
   if (plan->num_partials > 0) {
@@ -561,16 +619,40 @@ int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const v
   return ok();
 }
 
+int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* query_start_loc,
+                               const int32_t* context_lens, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_tokens, const pkv_shape* shape,
+                               const pkv_varlen_plan* plan, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return varlen_impl(out, out_dtype, lse, q, k_cache, v_cache, nullptr, nullptr, false,
+                     block_tables, query_start_loc, context_lens, seq_lens, num_seqs, num_tokens,
+                     shape, plan, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attention_varlen_fp8(void* out, int32_t out_dtype, float* lse, const void* q,
+                                   const void* k_cache, const void* v_cache, const float* k_scale,
+                                   const float* v_scale, const int32_t* block_tables,
+                                   const int32_t* query_start_loc, const int32_t* context_lens,
+                                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_tokens,
+                                   const pkv_shape* shape, const pkv_varlen_plan* plan,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return varlen_impl(out, out_dtype, lse, q, k_cache, v_cache, k_scale, v_scale, true,
+                     block_tables, query_start_loc, context_lens, seq_lens, num_seqs, num_tokens,
+                     shape, plan, workspace, workspace_bytes, stream);
+}
+
 size_t pkv_cascade_workspace_size(int32_t num_tokens, int32_t prefix_len, const pkv_shape* shape) {
   if (check_shape(shape) != PKV_OK || num_tokens < 0 || prefix_len <= 0) return 0;
   return cascade_bytes(cascade_split(num_tokens, prefix_len, shape), num_tokens, shape);
 }
 
-int pkv_cascade_prefix_attention(float* out_prefix, float* lse_prefix, const void* q,
-                                 const void* k_cache, const void* v_cache,
-                                 const int32_t* prefix_block_table, int32_t prefix_len,
-                                 int32_t num_tokens, const pkv_shape* shape, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+static int cascade_impl(float* out_prefix, float* lse_prefix, const void* q, const void* k_cache,
+                        const void* v_cache, const float* k_scale, const float* v_scale, bool fp8,
+                        const int32_t* prefix_block_table, int32_t prefix_len, int32_t num_tokens,
+                        const pkv_shape* shape, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   if (int rc = check_shape(shape)) return rc;
   if (prefix_len <= 0 || prefix_len % shape->block_size)
     return fail(PKV_EPREFIX, "prefix_len %d must be a positive multiple of block_size %d",
@@ -579,7 +661,8 @@ int pkv_cascade_prefix_attention(float* out_prefix, float* lse_prefix, const voi
     return fail(PKV_EINVAL, "prefix needs more blocks than the pool has");
   if (num_tokens < 0) return fail(PKV_EINVAL, "negative num_tokens");
   if (num_tokens == 0) return ok();
-  if (!out_prefix || !lse_prefix || !q || !k_cache || !v_cache || !prefix_block_table)
+  if (!out_prefix || !lse_prefix || !q || !k_cache || !v_cache || !prefix_block_table ||
+      (fp8 && (!k_scale || !v_scale)))
     return fail(PKV_EINVAL, "null pointer argument");
   const CascadeSplit cs = cascade_split(num_tokens, prefix_len, shape);
   const size_t need = cascade_bytes(cs, num_tokens, shape);
@@ -587,8 +670,10 @@ int pkv_cascade_prefix_attention(float* out_prefix, float* lse_prefix, const voi
     return fail(PKV_EWORKSPACE, "cascade needs %zu workspace bytes, got %zu", need, workspace_bytes);
   pkv::CascadeArgs a;
   a.q = static_cast<const uint16_t*>(q);
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
-  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.prefix_bt = prefix_block_table;
   a.prefix_len = prefix_len;
   a.num_tokens = num_tokens;
@@ -606,7 +691,8 @@ int pkv_cascade_prefix_attention(float* out_prefix, float* lse_prefix, const voi
   a.num_kv_heads = shape->num_kv_heads;
   a.scale_log2 = scale_log2(shape);
   const int G = shape->num_q_heads / shape->num_kv_heads;
-  hipError_t e = pkv::launch_cascade(a, shape->head_dim, G, (hipStream_t)stream);
+  hipError_t e = (fp8 ? pkv::launch_cascade_fp8 : pkv::launch_cascade)(a, shape->head_dim, G,
+                                                                       (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "cascade prefix launch");
   if (cs.segs > 1) {
     pkv::ReduceArgs ra;
@@ -623,6 +709,27 @@ int pkv_cascade_prefix_attention(float* out_prefix, float* lse_prefix, const voi
     if (e != hipSuccess) return hip_fail(e, "cascade segment reduce launch");
   }
   return ok();
+}
+
+int pkv_cascade_prefix_attention(float* out_prefix, float* lse_prefix, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* prefix_block_table, int32_t prefix_len,
+                                 int32_t num_tokens, const pkv_shape* shape, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return cascade_impl(out_prefix, lse_prefix, q, k_cache, v_cache, nullptr, nullptr, false,
+                      prefix_block_table, prefix_len, num_tokens, shape, workspace,
+                      workspace_bytes, stream);
+}
+
+int pkv_cascade_prefix_attention_fp8(float* out_prefix, float* lse_prefix, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* prefix_block_table, int32_t prefix_len,
+                                     int32_t num_tokens, const pkv_shape* shape, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return cascade_impl(out_prefix, lse_prefix, q, k_cache, v_cache, k_scale, v_scale, true,
+                      prefix_block_table, prefix_len, num_tokens, shape, workspace,
+                      workspace_bytes, stream);
 }
 
 int pkv_merge_attn_states(void* out, int32_t out_dtype, float* lse_out, const float* out_a,

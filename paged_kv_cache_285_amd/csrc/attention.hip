@@ -31,7 +31,20 @@
 //    prefix block table, cut into key segments when there are too few query tiles to fill
 //    the chip; the segment states are merged afterwards.
 //  * reduce_kernel: merges split-KV / segment partial states into the final output.
+//
+// FP8 KV cache [2048ai.net vLLM V1 article, quantisation section]: this file is compiled twice.
+// With PKV_KV_FP8=1 every kernel reads e4m3 pools (one byte per element, the same layouts) with
+// one fp32 scale per (physical block, kv head).  Cache chunks of 8 elements are then 8-byte
+// loads, so every path moves half the bytes.  Codes become bf16 exactly (every e4m3 value is a
+// bf16 value), and the scales are applied per cache block where they cost nothing in precision:
+// the key scale to the block's scores (in fp32) and the value scale to the block's p before
+// p is rounded for P.V.  The MFMA tiles stage the exact codes into LDS (same layout as bf16
+// pools) and pass each tile's 4 block scales of both pools through a small LDS slot array.
 #include "internal.h"
+
+#ifndef PKV_KV_FP8
+#define PKV_KV_FP8 0
+#endif
 
 #include <type_traits>
 
@@ -43,6 +56,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -76,6 +90,41 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
   return *p;
 #endif
 }
+
+__device__ __forceinline__ uint2 ld_stream(const uint2* p) {
+#if PKV_DECODE_NT
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v[0], v[1]);
+#else
+  return *p;
+#endif
+}
+
+// Cache chunk of 8 elements: 16 bytes of bf16, or 8 bytes of e4m3 codes.
+template <bool FP8>
+using Chunk = std::conditional_t<FP8, uint2, uint4>;
+template <bool FP8>
+using ChunkV = std::conditional_t<FP8, u32x2, u32x4>;
+
+// Two e4m3 codes (bytes 0-1, or 2-3 when HI) as a packed bf16 pair, exactly (every e4m3 value is
+// a bf16 value): one v_cvt_scalef32_pk_bf16_fp8 with scale 1.  That instruction only applies
+// the power of two of its scale operand, so the per-block scales are applied separately.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// 8 e4m3 codes -> 8 bf16 (16 bytes), exact.
+__device__ __forceinline__ uint4 widen8(uint2 c) {
+  return make_uint4(fp8x2_to_bf16x2<false>(c.x), fp8x2_to_bf16x2<true>(c.x), fp8x2_to_bf16x2<false>(c.y),
+                    fp8x2_to_bf16x2<true>(c.y));
+}
+__device__ __forceinline__ uint4 widen8(uint4 c) { return c; }
+__device__ __forceinline__ u32x4 widen8(u32x2 c) {
+  return u32x4{fp8x2_to_bf16x2<false>(c[0]), fp8x2_to_bf16x2<true>(c[0]), fp8x2_to_bf16x2<false>(c[1]),
+               fp8x2_to_bf16x2<true>(c[1])};
+}
+__device__ __forceinline__ u32x4 widen8(u32x4 c) { return c; }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -165,7 +214,7 @@ struct DecodeSmem {
   static constexpr int BYTES = (O_FLOATS + ML_FLOATS) * 4 + NW * SCR_BYTES;
 };
 
-template <int D, int G, int NW>
+template <int D, int G, int NW, bool FP8>
 __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char* smem_raw) {
   constexpr int CH = D / 8;    // 16-byte chunks per key row
   constexpr int CPT = D / 64;  // chunks of one key a lane holds
@@ -216,10 +265,11 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
   const int b_begin = it.kv_begin / kBlockSize;
   const int b_end = (kv_end + kBlockSize - 1) / kBlockSize;
-  const int64_t tile_stride = (int64_t)kBlockSize * CH;  // uint4 per (block, head) tile
+  using C8 = Chunk<FP8>;
+  const int64_t tile_stride = (int64_t)kBlockSize * CH;  // chunks per (block, head) tile
   const int64_t blk_stride = (int64_t)Hkv * tile_stride;
-  const uint4* kb = reinterpret_cast<const uint4*>(a.k_cache) + (int64_t)g * tile_stride;
-  const uint4* vb = reinterpret_cast<const uint4*>(a.v_cache) + (int64_t)g * tile_stride;
+  const C8* kb = reinterpret_cast<const C8*>(a.k_cache) + (int64_t)g * tile_stride;
+  const C8* vb = reinterpret_cast<const C8*>(a.v_cache) + (int64_t)g * tile_stride;
   const int th = lane & 1;  // token half of the V^T rows this lane holds
 
   // Blocks b_begin + wave + NW*k, k < nk (nk <= 64: a split has at most 256 blocks); their
@@ -227,12 +277,21 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   const int nb = b_end - b_begin;
   const int nk = nb > wave ? (nb - wave + NW - 1) / NW : 0;
   const int my_id = lane < nk ? bt[b_begin + wave + NW * lane] : 0;
+  // fp8 pools: the key and value scales of those blocks, likewise one per lane (issued before
+  // the first K/V loads, so waiting for those data covers them).
+  float my_ks = 1.f, my_vs = 1.f;
+  if constexpr (FP8) {
+    if (lane < nk) {
+      my_ks = a.k_scale[(int64_t)my_id * Hkv + g];
+      my_vs = a.v_scale[(int64_t)my_id * Hkv + g];
+    }
+  }
 
   constexpr int NKR = 2 * CPT;  // key chunks per lane per block
-  auto load = [&](int k, uint4 (&kr)[NKR], uint4 (&vr)[RPL]) {
+  auto load = [&](int k, C8 (&kr)[NKR], C8 (&vr)[RPL]) {
     const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
-    const uint4* kp = kb + phys * blk_stride;
-    const uint4* vp = vb + phys * blk_stride;
+    const C8* kp = kb + phys * blk_stride;
+    const C8* vp = vb + phys * blk_stride;
 #pragma unroll
     for (int ts = 0; ts < 2; ++ts)
 #pragma unroll
@@ -241,9 +300,19 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
     for (int i = 0; i < RPL; ++i) vr[i] = ld_stream(vp + lane + 64 * i);
   };
 
-  auto process = [&](int k, uint4 (&kr)[NKR], uint4 (&vr)[RPL]) {
+  auto process = [&](int k, const C8 (&kc)[NKR], const C8 (&vc)[RPL]) {
     const int t0 = (b_begin + wave + NW * k) * kBlockSize;
     const int nvalid = kv_end - t0;  // < 16 only in the last block
+    uint4 kr[NKR], vr[RPL];
+#pragma unroll
+    for (int i = 0; i < NKR; ++i) kr[i] = widen8(kc[i]);
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) vr[i] = widen8(vc[i]);
+    float slb = sl, vsb = 1.f;  // this block's score scale and value scale
+    if constexpr (FP8) {
+      slb = sl * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_ks), k));
+      vsb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_vs), k));
+    }
     // Q.K partial dot products: v[2*hh + ts].
     float v[NV];
 #pragma unroll
@@ -288,7 +357,7 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       tok[kk] = grp + 8 * ((n0 + kk) & 1);
-      sc[kk] = (tok[kk] < nvalid) ? sc[kk] * sl : -INFINITY;
+      sc[kk] = (tok[kk] < nvalid) ? sc[kk] * slb : -INFINITY;
       over |= sc[kk] > m_own + kLazy;
     }
     if (__ballot(over) != 0) {
@@ -321,7 +390,7 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
     for (int kk = 0; kk < NK; ++kk) {
       const float p = fast_exp2(sc[kk] - mref);
       if (owner) l_own += p;
-      pbuf[my_hh * 16 + tok[kk]] = __builtin_bit_cast(uint16_t, (__bf16)p);
+      pbuf[my_hh * 16 + tok[kk]] = __builtin_bit_cast(uint16_t, (__bf16)(FP8 ? p * vsb : p));
     }
     if (nvalid < kBlockSize) {
       // Zero the V^T entries of tokens past the end (the cache may hold NaN there).
@@ -360,7 +429,7 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   // The steady-state loads are unconditional so the compiler's wait counts only ever wait
   // for the block about to be used (a conditional load would make it wait for both).
   if (nk > 0) {
-    uint4 ka[NKR], va[RPL], kn[NKR], vn[RPL];
+    C8 ka[NKR], va[RPL], kn[NKR], vn[RPL];
     load(0, ka, va);
     int k = 0;
     for (; k + 2 < nk; k += 2) {
@@ -453,12 +522,34 @@ struct TileSmem {
   static constexpr int K_ELEMS = kKvTile * KP;
   static constexpr int V_ELEMS = D * VP;
   static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int BYTES = 2 * BUF_ELEMS * 2;
+  static constexpr int SC_OFF = 2 * BUF_ELEMS * 2;  // byte offset of the fp8 scale slots
+  static constexpr int SC_SLOTS = 3;                // per tile: 4 key scales, then 4 value scales
+  static constexpr int BYTES = SC_OFF + SC_SLOTS * 8 * 4;
 };
 
-template <int D, int G, bool CAUSAL, int NW>
-__device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t* __restrict__ k_cache,
-                          const uint16_t* __restrict__ v_cache, int Hkv, int g,
+// The key and value scales of a tile's 4 cache blocks, read (uniformly) from scale slot `sc`.
+struct TileScales {
+  float k[4], v[4];
+};
+__device__ __forceinline__ TileScales read_scales(const float* sc) {
+  const float4 a = *reinterpret_cast<const float4*>(sc);
+  const float4 b = *reinterpret_cast<const float4*>(sc + 4);
+  TileScales r;
+  r.k[0] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.x)));
+  r.k[1] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.y)));
+  r.k[2] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.z)));
+  r.k[3] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.w)));
+  r.v[0] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(b.x)));
+  r.v[1] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(b.y)));
+  r.v[2] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(b.z)));
+  r.v[3] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(b.w)));
+  return r;
+}
+
+template <int D, int G, bool CAUSAL, int NW, bool FP8>
+__device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __restrict__ k_cache,
+                          const void* __restrict__ v_cache, const float* __restrict__ k_scale,
+                          const float* __restrict__ v_scale, int Hkv, int g,
                           const int32_t* __restrict__ bt, int tok0, int ntok, int pos0, int kv_begin,
                           int kv_end, float sl, void* out, int out_f32, float* lse_out,
                           char* smem_raw) {
@@ -518,22 +609,32 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
   const bool does_v = !SPLIT || wave >= 4;
   const int sc = lane % LPT;
   const int sr = lane / LPT;
-  const int64_t tile_stride = (int64_t)kBlockSize * CH;
+  using C8 = Chunk<FP8>;
+  const int64_t tile_stride = (int64_t)kBlockSize * CH;  // chunks per (block, head) tile
   const int64_t blk_stride = (int64_t)Hkv * tile_stride;
-  const uint4* kbase = reinterpret_cast<const uint4*>(k_cache) + (int64_t)g * tile_stride;
-  const uint4* vbase = reinterpret_cast<const uint4*>(v_cache) + (int64_t)g * tile_stride;
+  const C8* kbase = reinterpret_cast<const C8*>(k_cache) + (int64_t)g * tile_stride;
+  const C8* vbase = reinterpret_cast<const C8*>(v_cache) + (int64_t)g * tile_stride;
   typedef __attribute__((address_space(4))) const int32_t cint32;
+  typedef __attribute__((address_space(4))) const float cfloat;
   const cint32* cbt = (const cint32*)bt;
   const int last_blk = (kv_end - 1) / kBlockSize;
-  uint4 st[PD][RS];
+  C8 st[PD][RS];
+  float ksc[PD], vsc[PD];  // fp8 pools: scales of the staged block
+  float* scl = reinterpret_cast<float*>(smem_raw + S::SC_OFF);  // scale slot of buffer b: scl + 8b
 
   // Loads only: the masking of keys past the end happens at store time, so nothing here
   // waits for the data.  Returns how many of the block's keys are valid (<= 0: none).
-  auto stage_load = [&](int tile, uint4 (&r)[RS]) -> int {
+  auto stage_load = [&](int tile, C8 (&r)[RS], float& ks, float& vs) -> int {
     const int lb = kv_begin / kBlockSize + 4 * tile + sblk;
     const int64_t phys = cbt[min(lb, last_blk)];
-    const uint4* kp = kbase + phys * blk_stride;
-    const uint4* vp = vbase + phys * blk_stride;
+    const C8* kp = kbase + phys * blk_stride;
+    const C8* vp = vbase + phys * blk_stride;
+    if constexpr (FP8) {
+      ks = ((const cfloat*)k_scale)[phys * Hkv + g];
+      vs = ((const cfloat*)v_scale)[phys * Hkv + g];
+    } else {
+      ks = vs = 1.f;
+    }
     if constexpr (SPLIT) {
       // One unconditional load stream per wave: K rows for waves 0-3, V^T chunks for 4-7.
 #pragma unroll
@@ -548,14 +649,20 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
     return kv_end - lb * kBlockSize;
   };
 
-  auto stage_store = [&](int buf, const uint4 (&r)[RS], int nvalid) {
+  auto stage_store = [&](int buf, const C8 (&r)[RS], int nvalid, float kscale, float vscale) {
     uint16_t* ks = smem + buf * S::BUF_ELEMS;
     uint16_t* vs = ks + S::K_ELEMS;
+    if constexpr (FP8) {
+      if (lane == 0) {
+        if (does_k) scl[8 * buf + sblk] = kscale;
+        if (does_v) scl[8 * buf + 4 + sblk] = vscale;
+      }
+    }
     if (does_k) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int kk = KPI * i + sr;
-        const uint4 x = (kk < nvalid) ? r[i] : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 x = (kk < nvalid) ? widen8(r[i]) : make_uint4(0u, 0u, 0u, 0u);
         *reinterpret_cast<uint4*>(ks + (sblk * kBlockSize + kk) * S::KP + sc * 8) = x;
       }
     }
@@ -574,8 +681,9 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
       for (int i = 0; i < NIV; ++i) {
         const int row = (lane >> 1) + 32 * i;
         uint16_t* dst = vs + row * S::VP + sblk * kBlockSize + 4 * (lane & 1);
-        *reinterpret_cast<uint2*>(dst) = make_uint2(r[vo + i].x & msk[0], r[vo + i].y & msk[1]);
-        *reinterpret_cast<uint2*>(dst + 8) = make_uint2(r[vo + i].z & msk[2], r[vo + i].w & msk[3]);
+        const uint4 x = widen8(r[vo + i]);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(x.x & msk[0], x.y & msk[1]);
+        *reinterpret_cast<uint2*>(dst + 8) = make_uint2(x.z & msk[2], x.w & msk[3]);
       }
     }
   };
@@ -584,17 +692,18 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
   const int min_pos = pos0;  // first token of the tile has the smallest position
 
   int nv[PD];
-  nv[0] = stage_load(0, st[0]);
-  if constexpr (PD == 2) nv[1] = stage_load(1, st[1]);
-  stage_store(0, st[0], nv[0]);
+  nv[0] = stage_load(0, st[0], ksc[0], vsc[0]);
+  if constexpr (PD == 2) nv[1] = stage_load(1, st[1], ksc[1], vsc[1]);
+  stage_store(0, st[0], nv[0], ksc[0], vsc[0]);
   __syncthreads();
 
   // One KV tile: prefetch tile t+PD into `ld`, compute tile t from LDS, then store tile t+1
   // (held in `sto`) into the other LDS buffer.
-  auto body = [&](int t, uint4 (&ld)[RS], int& nld, uint4 (&sto)[RS], int& nsto) {
+  auto body = [&](int t, C8 (&ld)[RS], int& nld, float& kld, float& vld, C8 (&sto)[RS], int& nsto,
+                  float& ksto, float& vsto) {
     const int k0 = kv_begin + t * kKvTile;
     const int buf = t & 1;
-    nld = stage_load(t + PD, ld);
+    nld = stage_load(t + PD, ld, kld, vld);
 
     const uint16_t* ks = smem + buf * S::BUF_ELEMS;
     const uint16_t* vs = ks + S::K_ELEMS;
@@ -629,13 +738,34 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
 
     // Online softmax for this lane's query column.  The running max m (log2 units of scaled
     // scores) is only raised when a score exceeds it by more than kLazy, for every lane at
-    // once, so the 64-register rescale of the output is rare; p stays <= 2^kLazy.
+    // once, so the 64-register rescale of the output is rare; p stays <= 2^kLazy.  With fp8
+    // pools, key block b of the tile (scores sacc[b >> 1][8 (b & 1) ..]) has score scale
+    // sl * k_scale[b], and its p are multiplied by v_scale[b] before the P.V.
+    float slk[4], svb[4];
     float mx = -INFINITY;
+    if constexpr (FP8) {
+      const TileScales tsc = read_scales(scl + 8 * buf);
+      float mb[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl;
+        for (int e = 0; e < 16; ++e) mb[2 * mt + (e >> 3)] = fmaxf(mb[2 * mt + (e >> 3)], sacc[mt][e]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        slk[b] = sl * tsc.k[b];
+        svb[b] = tsc.v[b];
+        mx = fmaxf(mx, mb[b] * slk[b]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) slk[b] = sl, svb[b] = 1.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl;
+    }
     if (__ballot(mx > m + kLazy) != 0) {
       const float mn = fmaxf(m, mx);
       const float alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
@@ -657,9 +787,9 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
       bf16x8 v;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(fmaf(sacc[mt][b0 + e], sl, -mref));
+        const float p = fast_exp2(fmaf(sacc[mt][b0 + e], slk[ks], -mref));
         lsum += p;
-        v[e] = (__bf16)p;
+        v[e] = (__bf16)(FP8 ? p * svb[ks] : p);
       }
       pb[ks] = v;
     }
@@ -674,16 +804,16 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
       }
     }
 
-    if (t + 1 < ntiles) stage_store(buf ^ 1, sto, nsto);
+    if (t + 1 < ntiles) stage_store(buf ^ 1, sto, nsto, ksto, vsto);
     __syncthreads();
   };
 
   int t = 0;
   for (; t + 1 < ntiles; t += 2) {
-    body(t, st[0], nv[0], st[PD - 1], nv[PD - 1]);
-    body(t + 1, st[PD - 1], nv[PD - 1], st[0], nv[0]);
+    body(t, st[0], nv[0], ksc[0], vsc[0], st[PD - 1], nv[PD - 1], ksc[PD - 1], vsc[PD - 1]);
+    body(t + 1, st[PD - 1], nv[PD - 1], ksc[PD - 1], vsc[PD - 1], st[0], nv[0], ksc[0], vsc[0]);
   }
-  if (t < ntiles) body(t, st[0], nv[0], st[PD - 1], nv[PD - 1]);
+  if (t < ntiles) body(t, st[0], nv[0], ksc[0], vsc[0], st[PD - 1], nv[PD - 1], ksc[PD - 1], vsc[PD - 1]);
 
   lsum += __shfl_xor(lsum, 32);
   if (!row_valid) return;
@@ -775,10 +905,10 @@ __device__ __forceinline__ void pipe_pv_step(PipeRegs<D>& R, const uint16_t* __r
 // new P^T step (a lane of half h holds keys 4h..4h+3 and 8+4h..8+4h+3 of the step as dwords
 // d0..d3; swapping d0<->d2 and d1<->d3 leaves it keys 8h..8h+7).  Returns in `need` whether
 // the running max moved, with the new max and the tile's row sum.
-template <int D, int CUR>
+template <int D, int CUR, bool FP8>
 __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __restrict__ kb,
                                           const uint16_t* __restrict__ vb, int n, int h, float sl,
-                                          bool& need, float& mnew, float& ts) {
+                                          const TileScales& tsc, bool& need, float& mnew, float& ts) {
   constexpr int NXT = 1 - CUR;
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
@@ -799,10 +929,18 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
     return *reinterpret_cast<const bf16x8*>(kb + (32 * mt + n) * S::KP + 16 * s + 8 * h);
   };
 
+  // Score scale and p multiplier of key block b of the tile (block b = 16-key step b).
+  float slk[4], svb[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    slk[b] = FP8 ? sl * tsc.k[b] : sl;
+    svb[b] = FP8 ? tsc.v[b] : 1.f;
+  }
   bf16x8 op[PF];
 #pragma unroll
   for (int i = 0; i < PF; ++i) op[i] = operand(i);
   float mx = -INFINITY, mref = 0.f;
+  float mb[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // fp8: per-block raw maxima
   uint32_t pk[4][4];
   ts = 0.f;
   need = false;
@@ -824,13 +962,22 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
       constexpr int PER = 32 / NMAX;
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        const int x = i * PER + e;
-        mx = fmaxf(mx, R.sacc[CUR][x >> 4][x & 15]);
+        const int x = i * PER + e;  // element x of the tile's scores lies in key block x >> 3
+        if constexpr (FP8)
+          mb[x >> 3] = fmaxf(mb[x >> 3], R.sacc[CUR][x >> 4][x & 15]);
+        else
+          mx = fmaxf(mx, R.sacc[CUR][x >> 4][x & 15]);
       }
       if (i == NMAX - 1) {
         // Lazy max: raised only past kLazy, for every lane of the wave at once, so that the
         // output rescale stays rare.
-        mx = fmaxf(mx, other_half(mx, h)) * sl;
+        if constexpr (FP8) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) mx = fmaxf(mx, mb[b] * slk[b]);
+          mx = fmaxf(mx, other_half(mx, h));
+        } else {
+          mx = fmaxf(mx, other_half(mx, h)) * sl;
+        }
         need = __ballot(mx > R.m + kLazy) != 0;
         mnew = need ? fmaxf(R.m, mx) : R.m;
         mref = (mnew == -INFINITY) ? 0.f : mnew;
@@ -840,11 +987,11 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
     for (int q = 0; q < 16; ++q) {
       if (NMAX + (q * SPAN) / 16 != i) continue;
       const int ks = q >> 2, u = q & 3, mt = ks >> 1, e0 = 8 * (ks & 1) + 2 * u;
-      const float p0 = fast_exp2(fmaf(R.sacc[CUR][mt][e0], sl, -mref));
-      const float p1 = fast_exp2(fmaf(R.sacc[CUR][mt][e0 + 1], sl, -mref));
+      const float p0 = fast_exp2(fmaf(R.sacc[CUR][mt][e0], slk[ks], -mref));
+      const float p1 = fast_exp2(fmaf(R.sacc[CUR][mt][e0 + 1], slk[ks], -mref));
       ts += p0;
       ts += p1;
-      pk[ks][u] = pack_bf16x2(p0, p1);
+      pk[ks][u] = FP8 ? pack_bf16x2(p0 * svb[ks], p1 * svb[ks]) : pack_bf16x2(p0, p1);
       if (u == 3) {
         // P^T(t-1) of this 16-key step had its last use in slot DT*ks + DT - 1 < i.
         const auto s02 = __builtin_amdgcn_permlane32_swap(pk[ks][0], pk[ks][2], false, false);
@@ -877,9 +1024,10 @@ __device__ __forceinline__ void pipe_commit(PipeRegs<D>& R, bool need, float mne
   R.lsum += ts;
 }
 
-template <int D, int G, bool CAUSAL>
-__device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t* __restrict__ k_cache,
-                          const uint16_t* __restrict__ v_cache, int Hkv, int g,
+template <int D, int G, bool CAUSAL, bool FP8>
+__device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __restrict__ k_cache,
+                          const void* __restrict__ v_cache, const float* __restrict__ k_scale,
+                          const float* __restrict__ v_scale, int Hkv, int g,
                           const int32_t* __restrict__ bt, int tok0, int ntok, int pos0, int kv_begin,
                           int kv_end, float sl, void* out, int out_f32, float* lse_out,
                           char* smem_raw) {
@@ -938,37 +1086,67 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
     const int blk0 = kv_begin / kBlockSize + sblk;
     // Physical ids of the wave's blocks of 64 consecutive tiles, one per lane (read back with
     // readlane, so the per-tile address needs no memory wait); refreshed every 64 tiles.
+    // fp8 pools: the waves that copy K also hold the key and value scales of those blocks,
+    // alike, and put each tile's scales into scale slot tile % 3 (read by every wave in the
+    // tile's softmax step; the slot is rewritten two steps later, past two barriers).
+    using C8 = ChunkV<FP8>;
+    float* scl = reinterpret_cast<float*>(smem_raw + S::SC_OFF);
     int bid_base = 0;
     int bid = bt[min(blk0 + 4 * lane, last_blk)];
-    auto block_id = [&](int tile) __attribute__((always_inline)) -> int {
+    float bks = 1.f, bvs = 1.f;
+    auto load_scales = [&]() __attribute__((always_inline)) {
+      if constexpr (FP8) {
+        if (wave < 4) {
+          bks = k_scale[(int64_t)bid * Hkv + g];
+          bvs = v_scale[(int64_t)bid * Hkv + g];
+        }
+      }
+    };
+    load_scales();
+    auto block_id = [&](int tile, float& ks, float& vs) __attribute__((always_inline)) -> int {
       if (tile - bid_base >= 64) {
         bid_base = tile;
         bid = bt[min(blk0 + 4 * (tile + lane), last_blk)];
+        load_scales();
       }
+      ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bks), tile - bid_base));
+      vs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bvs), tile - bid_base));
       return __builtin_amdgcn_readlane(bid, tile - bid_base);
     };
     bool jv[J];                // the job copies V
-    const u32x4* jbase[J];     // pool base of the job's kv head
+    const C8* jbase[J];        // pool base of the job's kv head
     int soff[J], sstep[J];     // LDS offset (bf16 units) of chunk i: soff + i * sstep
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       jv[j] = wave >= 4;
-      jbase[j] = reinterpret_cast<const u32x4*>(jv[j] ? v_cache : k_cache) + (int64_t)g * tile_stride;
+      jbase[j] = reinterpret_cast<const C8*>(jv[j] ? v_cache : k_cache) + (int64_t)g * tile_stride;
       // Chunk lane + 64i of the block tile: ((KPI*i + sr)*CH + sc) is that same index for K rows.
       soff[j] = jv[j] ? 2 * S::K_ELEMS + (lane >> 1) * S::VP + kBlockSize * sblk + 8 * (lane & 1)
                       : (kBlockSize * sblk + sr) * S::KP + sc * 8;
       sstep[j] = jv[j] ? 32 * S::VP : KPI * S::KP;
     }
     // K tiles alternate between the two K buffers, V tiles between the two V buffers.
-    auto load = [&](int j, int tile, u32x4 (&r)[NI]) __attribute__((always_inline)) -> int {
+    auto load = [&](int j, int tile, C8 (&r)[NI], float& ks, float& vs) __attribute__((always_inline)) -> int {
       const int lb = blk0 + 4 * tile;
-      const u32x4* p = jbase[j] + (int64_t)block_id(tile) * blk_stride;
+      const C8* p = jbase[j] + (int64_t)block_id(tile, ks, vs) * blk_stride;
 #pragma unroll
       for (int i = 0; i < NI; ++i) r[i] = p[lane + 64 * i];
       return jv[j] ? kv_end - lb * kBlockSize : kBlockSize;
     };
-    auto store = [&](int j, int buf, const u32x4 (&r)[NI], int nvalid) __attribute__((always_inline)) {
+    // Stores a loaded tile into LDS buffer `buf`; a K job also stores its block's scales into
+    // scale slot `slot`.
+    auto store = [&](int j, int buf, const C8 (&rc)[NI], int nvalid, float ks, float vs, int slot)
+        __attribute__((always_inline)) {
       uint16_t* dst = smem + buf * (jv[j] ? S::V_ELEMS : S::K_ELEMS);
+      if constexpr (FP8) {
+        if (!jv[j] && lane == 0) {
+          scl[8 * slot + sblk] = ks;
+          scl[8 * slot + 4 + sblk] = vs;
+        }
+      }
+      u32x4 r[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) r[i] = widen8(rc[i]);
       if (nvalid >= kBlockSize) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + soff[j] + i * sstep[j]) = r[i];
@@ -984,15 +1162,16 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
     };
 
     // Prologue: K(0) and K(1) in LDS, V(-1) = 0 (no tile before the first), S^T(0) computed.
-    u32x4 st[J][NI];
+    C8 st[J][NI];
     int nv[J];
+    float ksv[J], vsv[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       if (!jv[j]) {
-        nv[j] = load(j, 0, st[j]);
-        store(j, 0, st[j], nv[j]);
-        nv[j] = load(j, 1, st[j]);
-        store(j, 1, st[j], nv[j]);
+        nv[j] = load(j, 0, st[j], ksv[j], vsv[j]);
+        store(j, 0, st[j], nv[j], ksv[j], vsv[j], 0);
+        nv[j] = load(j, 1, st[j], ksv[j], vsv[j]);
+        store(j, 1, st[j], nv[j], ksv[j], vsv[j], 1);
       }
     }
     {
@@ -1020,17 +1199,19 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
       constexpr int CUR = decltype(cur)::value;
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < J; ++j) nv[j] = load(j, jv[j] ? t : t + 2, st[j]);
+      for (int j = 0; j < J; ++j) nv[j] = load(j, jv[j] ? t : t + 2, st[j], ksv[j], vsv[j]);
+      TileScales tsc;
+      if constexpr (FP8) tsc = read_scales(scl + 8 * (t % 3));
       const int k0 = kv_begin + t * kKvTile;
       if ((k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > pos0))
         pipe_mask<D, CUR, CAUSAL>(R, h, k0, kv_end);
       bool need;
       float mnew, ts;
-      pipe_step<D, CUR>(R, kbuf0 + ((t + 1) & 1) * S::K_ELEMS, vbuf0 + ((t + 1) & 1) * S::V_ELEMS, n, h, sl,
-                        need, mnew, ts);
+      pipe_step<D, CUR, FP8>(R, kbuf0 + ((t + 1) & 1) * S::K_ELEMS, vbuf0 + ((t + 1) & 1) * S::V_ELEMS, n, h,
+                             sl, tsc, need, mnew, ts);
       pipe_commit<D>(R, need, mnew, ts);
 #pragma unroll
-      for (int j = 0; j < J; ++j) store(j, t & 1, st[j], nv[j]);
+      for (int j = 0; j < J; ++j) store(j, t & 1, st[j], nv[j], ksv[j], vsv[j], (t + 2) % 3);
     };
     int t = 0;
     for (; t + 1 < ntiles; t += 2) {
@@ -1072,7 +1253,7 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const uint16_t
 // DECODE_ONLY instantiations carry no MFMA path, so they need far fewer registers and run
 // more waves per SIMD; a plan with any prefill tile uses the full kernel, with 4 or 8 waves
 // per workgroup (8 when the batch carries enough prefill rows to fill 256-row tiles).
-template <int D, int G, bool DECODE_ONLY, int NW>
+template <int D, int G, bool DECODE_ONLY, int NW, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu(DECODE_ONLY ? (G >= 8 ? PKV_DECODE_WAVES_G8 : PKV_DECODE_WAVES) : 2)))
 void varlen_kernel(VarlenArgs a) {
@@ -1081,20 +1262,20 @@ void varlen_kernel(VarlenArgs a) {
   const int g = x % a.num_kv_heads;
   const WorkItem it = a.items[x / a.num_kv_heads];
   if (DECODE_ONLY || it.kind == kDecode) {
-    decode_item<D, G, NW>(a, it, g, smem);
+    decode_item<D, G, NW, FP8>(a, it, g, smem);
   } else {
     const int r = it.seq;
     const int ctx = a.context_lens[r];
     const int tok0 = a.query_start_loc[r] + it.q_begin;
     const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
-    mfma_tile<D, G, true, NW>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g, bt, tok0,
-                              it.q_count, ctx + it.q_begin, it.kv_begin, it.kv_end, a.scale_log2,
-                              a.out, a.out_f32, a.lse, smem);
+    mfma_tile<D, G, true, NW, FP8>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale,
+                                   a.num_kv_heads, g, bt, tok0, it.q_count, ctx + it.q_begin,
+                                   it.kv_begin, it.kv_end, a.scale_log2, a.out, a.out_f32, a.lse, smem);
   }
 }
 
 // Wide-tile kernels: 256-row pipelined tiles on 8 waves (two per SIMD).
-template <int D, int G>
+template <int D, int G, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void prefill_wide_kernel(VarlenArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -1105,11 +1286,12 @@ void prefill_wide_kernel(VarlenArgs a) {
   const int ctx = a.context_lens[r];
   const int tok0 = a.query_start_loc[r] + it.q_begin;
   const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
-  pipe_tile<D, G, true>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g, bt, tok0, it.q_count,
-                        ctx + it.q_begin, it.kv_begin, it.kv_end, a.scale_log2, a.out, a.out_f32, a.lse, smem);
+  pipe_tile<D, G, true, FP8>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
+                             g, bt, tok0, it.q_count, ctx + it.q_begin, it.kv_begin, it.kv_end, a.scale_log2,
+                             a.out, a.out_f32, a.lse, smem);
 }
 
-template <int D, int G>
+template <int D, int G, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void cascade_kernel(CascadeArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -1129,8 +1311,8 @@ void cascade_kernel(CascadeArgs a) {
     out = a.part_o + (int64_t)seg * a.num_tokens * a.num_q_heads * D;
     lse = a.part_lse + (int64_t)seg * a.num_tokens * a.num_q_heads;
   }
-  pipe_tile<D, G, false>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.num_kv_heads, g, a.prefix_bt, tok0,
-                         ntok, 0, kv_begin, kv_end, a.scale_log2, out, 1, lse, smem);
+  pipe_tile<D, G, false, FP8>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
+                              g, a.prefix_bt, tok0, ntok, 0, kv_begin, kv_end, a.scale_log2, out, 1, lse, smem);
 }
 
 // One wave per (token, head) row; lane holds D/64 consecutive dims.
@@ -1199,31 +1381,33 @@ size_t varlen_smem(bool has_prefill) {
   return dec > pre ? dec : pre;
 }
 
+constexpr bool kFp8 = PKV_KV_FP8 != 0;
+
 template <int D, int G>
 hipError_t launch_varlen_t(const VarlenArgs& a, int n_prefill, int n_decode, int tile_rows,
                            hipStream_t stream) {
   const int Hkv = a.num_kv_heads;
   if (n_prefill + n_decode == 0) return hipSuccess;
   if (n_prefill == 0) {
-    auto kern = varlen_kernel<D, G, true, 4>;
+    auto kern = varlen_kernel<D, G, true, 4, kFp8>;
     const size_t smem = varlen_smem<D, G, 4>(false);
     hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_decode * Hkv)), dim3(256), smem, stream, a);
   } else if (tile_rows == kWideTileRows) {
     // Wide prefill tiles, then the decode items in a kernel of their own (the wide tile's
     // register budget allows two waves per SIMD, too few for the decode path).
-    auto kern = prefill_wide_kernel<D, G>;
+    auto kern = prefill_wide_kernel<D, G, kFp8>;
     hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_prefill * Hkv)), dim3(512),
                        (size_t)TileSmem<D>::BYTES, stream, a);
     if (n_decode > 0) {
       VarlenArgs b = a;
       b.items = a.items + n_prefill;
       b.num_items = n_decode;
-      auto dk = varlen_kernel<D, G, true, 4>;
+      auto dk = varlen_kernel<D, G, true, 4, kFp8>;
       const size_t smem = varlen_smem<D, G, 4>(false);
       hipLaunchKernelGGL(dk, dim3((unsigned)((int64_t)n_decode * Hkv)), dim3(256), smem, stream, b);
     }
   } else {
-    auto kern = varlen_kernel<D, G, false, 4>;
+    auto kern = varlen_kernel<D, G, false, 4, kFp8>;
     const size_t smem = varlen_smem<D, G, 4>(true);
     hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)(n_prefill + n_decode) * Hkv)), dim3(256), smem,
                        stream, a);
@@ -1235,7 +1419,7 @@ template <int D, int G>
 hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.num_tiles * a.num_segments * a.num_kv_heads;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((cascade_kernel<D, G>), dim3((unsigned)grid), dim3(512), (size_t)TileSmem<D>::BYTES,
+  hipLaunchKernelGGL((cascade_kernel<D, G, kFp8>), dim3((unsigned)grid), dim3(512), (size_t)TileSmem<D>::BYTES,
                      stream, a);
   return hipGetLastError();
 }
@@ -1263,19 +1447,27 @@ hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
   }                                                   \
   return hipErrorInvalidValue;
 
-hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, int n_prefill, int n_decode,
-                         int tile_rows, hipStream_t stream) {
+#if PKV_KV_FP8
+#define PKV_KV_NAME(name) name##_fp8
+#else
+#define PKV_KV_NAME(name) name
+#endif
+
+hipError_t PKV_KV_NAME(launch_varlen)(const VarlenArgs& a, int head_dim, int group, int n_prefill,
+                                      int n_decode, int tile_rows, hipStream_t stream) {
 #define CALL_V(D, G) launch_varlen_t<D, G>(a, n_prefill, n_decode, tile_rows, stream)
   PKV_DISPATCH_DG(head_dim, group, CALL_V)
 #undef CALL_V
 }
 
-hipError_t launch_cascade(const CascadeArgs& a, int head_dim, int group, hipStream_t stream) {
+hipError_t PKV_KV_NAME(launch_cascade)(const CascadeArgs& a, int head_dim, int group,
+                                       hipStream_t stream) {
 #define CALL_C(D, G) launch_cascade_t<D, G>(a, stream)
   PKV_DISPATCH_DG(head_dim, group, CALL_C)
 #undef CALL_C
 }
 
+#if !PKV_KV_FP8
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_tokens * a.num_q_heads;
   if (rows == 0) return hipSuccess;
@@ -1288,5 +1480,6 @@ hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t stream) 
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
+#endif
 
 }  // namespace pkv

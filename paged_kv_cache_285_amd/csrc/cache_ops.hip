@@ -110,14 +110,128 @@ __global__ void append_kv_kernel(int64_t* __restrict__ slot_out, const uint4* __
 }
 
 
+// ------------------------------------------------------------------------------------------
+// FP8 (OCP E4M3FN) cache write.  Storing the cache in a low-precision float format shrinks it and
+// speeds up attention [2048ai.net vLLM V1 article, quantisation section].  Every (physical block,
+// kv head) tile of each pool has its own fp32 scale (k_scale / v_scale, [num_blocks, Hkv]): a
+// stored code means code_value * scale.  A token's bf16 value x becomes
+// y = x * (1 / scale) in fp32, clamped to +-448 (the largest finite code; the conversion
+// instruction itself turns larger values into NaN instead of saturating), then rounded to the
+// nearest code, ties to even, by v_cvt_pk_fp8_f32.  A NaN input stores the NaN code 0x7f.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float fp8_clamp(float y) {
+  return fabsf(y) > 448.f ? copysignf(448.f, y) : y;
+}
+
+// The 8 bf16 values of chunk x as 8 e4m3 codes (byte e = value e).  NaN inputs get the code
+// 0x7f written explicitly, whatever code the conversion instruction gives a NaN.
+__device__ __forceinline__ uint2 quantize8(const uint4 x, float inv) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float f[4];
+    uint32_t nan_bytes = 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      f[2 * e] = __uint_as_float(w[2 * h + e] << 16) * inv;
+      f[2 * e + 1] = __uint_as_float(w[2 * h + e] & 0xffff0000u) * inv;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (f[e] != f[e]) nan_bytes |= 0xffu << (8 * e);
+      f[e] = fp8_clamp(f[e]);
+    }
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);  // bytes 0, 1
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], r, true);       // bytes 2, 3
+    out[h] = ((uint32_t)r & ~nan_bytes) | (0x7f7f7f7fu & nan_bytes);
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+// Store chunk c (8 values) of token slot `slot`, kv head h, into the fp8 pools: 8 key bytes in the
+// token's row, 8 value bytes down 8 rows of the dim-major value tile.
+__device__ __forceinline__ void store_fp8_chunk(const uint4 kx, const uint4 vx, uint2* __restrict__ k_cache,
+                                                uint8_t* __restrict__ v_cache,
+                                                const float* __restrict__ k_scale,
+                                                const float* __restrict__ v_scale, int64_t slot,
+                                                int64_t h, int64_t c, int32_t num_kv_heads,
+                                                int32_t chunks_per_head) {
+  const int64_t blk = slot / kBlockSize;
+  const int64_t off = slot - blk * kBlockSize;
+  const int64_t tile = blk * num_kv_heads + h;
+  const float kinv = 1.0f / k_scale[tile];
+  const float vinv = 1.0f / v_scale[tile];
+  k_cache[(tile * kBlockSize + off) * chunks_per_head + c] = quantize8(kx, kinv);
+  const uint2 vq = quantize8(vx, vinv);
+  uint8_t* vt = v_cache + (tile * chunks_per_head * 8 + c * 8) * kBlockSize + off;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vt[e * kBlockSize] = (uint8_t)(vq.x >> (8 * e));
+    vt[(4 + e) * kBlockSize] = (uint8_t)(vq.y >> (8 * e));
+  }
+}
+
+// As reshape_and_cache_kernel, quantising into fp8 pools.
+__global__ void reshape_and_cache_fp8_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
+                                             uint2* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                             const float* __restrict__ k_scale,
+                                             const float* __restrict__ v_scale,
+                                             const int64_t* __restrict__ slots, int32_t num_tokens,
+                                             int32_t num_kv_heads, int32_t chunks_per_head,
+                                             int64_t num_slots) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)num_kv_heads * chunks_per_head;
+  const int64_t t = gid / per_token;
+  if (t >= num_tokens) return;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t within = gid - t * per_token;
+  const int64_t h = within / chunks_per_head;
+  store_fp8_chunk(k[gid], v[gid], k_cache, v_cache, k_scale, v_scale, slot, h, within - h * chunks_per_head,
+                  num_kv_heads, chunks_per_head);
+}
+
+// As append_kv_kernel, quantising into fp8 pools.
+__global__ void append_kv_fp8_kernel(int64_t* __restrict__ slot_out, const uint4* __restrict__ k,
+                                     const uint4* __restrict__ v, uint2* __restrict__ k_cache,
+                                     uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
+                                     const float* __restrict__ v_scale, const int32_t* __restrict__ bt,
+                                     const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
+                                     int32_t num_seqs, int32_t num_tokens, int32_t num_kv_heads,
+                                     int32_t chunks_per_head, int32_t bt_stride, int64_t num_slots) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)num_kv_heads * chunks_per_head;
+  const int64_t t = gid / per_token;
+  if (t >= num_tokens) return;
+  int32_t lo = 0, hi = num_seqs - 1;  // largest r with qsl[r] <= t
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int32_t pos = ctx[lo] + (int32_t)(t - qsl[lo]);
+  const int32_t logical = pos / kBlockSize;
+  int64_t slot = -1;
+  if (pos >= 0 && logical < bt_stride)
+    slot = (int64_t)bt[(int64_t)lo * bt_stride + logical] * kBlockSize + (pos % kBlockSize);
+  const int64_t within = gid - t * per_token;
+  if (slot_out && within == 0) slot_out[t] = slot;
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t h = within / chunks_per_head;
+  store_fp8_chunk(k[gid], v[gid], k_cache, v_cache, k_scale, v_scale, slot, h, within - h * chunks_per_head,
+                  num_kv_heads, chunks_per_head);
+}
+
 // Copy-on-write support ["11. vLLM principles", section 11.2: requests that share a prefix
 // point their block tables at the same physical blocks]: before one of them writes into a
 // shared block, the block is copied to a fresh one.  Workgroup (pair, pool) copies the whole
 // physical block src -> dst of one pool (K for pool 0, V for pool 1; every kv head), 16 bytes
-// per thread and step.  Pairs naming a block outside [0, num_blocks) are skipped.
+// per thread and step, and, for fp8 pools, the block's per-kv-head scales of that pool.  Pairs
+// naming a block outside [0, num_blocks) are skipped.
 __global__ void copy_blocks_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                   float* __restrict__ k_scale, float* __restrict__ v_scale,
                                    const int32_t* __restrict__ pairs, int32_t num_blocks,
-                                   int64_t chunks_per_block) {
+                                   int32_t num_kv_heads, int64_t chunks_per_block) {
   const int32_t p = blockIdx.x;
   const int32_t src = pairs[2 * p];
   const int32_t dst = pairs[2 * p + 1];
@@ -126,6 +240,9 @@ __global__ void copy_blocks_kernel(uint4* __restrict__ k_cache, uint4* __restric
   const uint4* from = pool + (int64_t)src * chunks_per_block;
   uint4* to = pool + (int64_t)dst * chunks_per_block;
   for (int64_t c = threadIdx.x; c < chunks_per_block; c += blockDim.x) to[c] = from[c];
+  float* scale = blockIdx.y == 0 ? k_scale : v_scale;
+  if (scale && (int)threadIdx.x < num_kv_heads)
+    scale[(int64_t)dst * num_kv_heads + threadIdx.x] = scale[(int64_t)src * num_kv_heads + threadIdx.x];
 }
 
 }  // namespace
@@ -145,6 +262,40 @@ hipError_t launch_append_kv(int64_t* slot_mapping, const uint16_t* k, const uint
                      reinterpret_cast<const uint4*>(v), reinterpret_cast<uint4*>(k_cache), v_cache,
                      block_tables, qsl, ctx, num_seqs, num_tokens, num_kv_heads, chunks, bt_stride,
                      num_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_kv_fp8(int64_t* slot_mapping, const uint16_t* k, const uint16_t* v,
+                                uint8_t* k_cache, uint8_t* v_cache, const float* k_scale,
+                                const float* v_scale, const int32_t* block_tables, const int32_t* qsl,
+                                const int32_t* ctx, int32_t num_seqs, int32_t num_tokens,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t bt_stride,
+                                int64_t num_slots, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int32_t chunks = head_dim / 8;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(append_kv_fp8_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, slot_mapping,
+                     reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
+                     reinterpret_cast<uint2*>(k_cache), v_cache, k_scale, v_scale, block_tables, qsl, ctx,
+                     num_seqs, num_tokens, num_kv_heads, chunks, bt_stride, num_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_fp8(const uint16_t* k, const uint16_t* v, uint8_t* k_cache,
+                                        uint8_t* v_cache, const float* k_scale, const float* v_scale,
+                                        const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
+                                        int32_t head_dim, int64_t num_slots, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int32_t chunks = head_dim / 8;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(reshape_and_cache_fp8_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
+                     reinterpret_cast<uint2*>(k_cache), v_cache, k_scale, v_scale, slots, num_tokens,
+                     num_kv_heads, chunks, num_slots);
   return hipGetLastError();
 }
 
@@ -175,14 +326,15 @@ hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v, uint16
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(uint16_t* k_cache, uint16_t* v_cache, const int32_t* pairs,
-                              int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
-                              int32_t head_dim, hipStream_t stream) {
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes,
+                              hipStream_t stream) {
   if (num_pairs == 0) return hipSuccess;
-  const int64_t chunks = (int64_t)num_kv_heads * kBlockSize * head_dim / 8;
+  const int64_t chunks = (int64_t)num_kv_heads * kBlockSize * head_dim * elem_bytes / 16;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, 2), dim3(256), 0, stream,
-                     reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache), pairs,
-                     num_blocks, chunks);
+                     reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache), k_scale,
+                     v_scale, pairs, num_blocks, num_kv_heads, chunks);
   return hipGetLastError();
 }
 

@@ -31,8 +31,10 @@ static_assert(sizeof(WorkItem) == 32, "work item layout");
 
 struct VarlenArgs {
   const uint16_t* q;
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
+  const void* k_cache;     // bf16 pools, or fp8 (e4m3) pools for the *_fp8 launchers
+  const void* v_cache;
+  const float* k_scale;    // fp8 pools: scale per (physical block, kv head); else unused
+  const float* v_scale;
   const int32_t* block_tables;
   const int32_t* query_start_loc;
   const int32_t* context_lens;
@@ -52,8 +54,10 @@ struct VarlenArgs {
 
 struct CascadeArgs {
   const uint16_t* q;
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
   const int32_t* prefix_bt;
   int32_t prefix_len;
   int32_t num_tokens;
@@ -95,14 +99,32 @@ hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v, uint16
                                     uint16_t* v_cache, const int64_t* slots, int32_t num_tokens,
                                     int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
                                     hipStream_t stream);
-hipError_t launch_copy_blocks(uint16_t* k_cache, uint16_t* v_cache, const int32_t* pairs,
-                              int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
-                              int32_t head_dim, hipStream_t stream);
+hipError_t launch_append_kv_fp8(int64_t* slot_mapping, const uint16_t* k, const uint16_t* v,
+                                uint8_t* k_cache, uint8_t* v_cache, const float* k_scale,
+                                const float* v_scale, const int32_t* block_tables, const int32_t* qsl,
+                                const int32_t* ctx, int32_t num_seqs, int32_t num_tokens,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t bt_stride,
+                                int64_t num_slots, hipStream_t stream);
+hipError_t launch_reshape_and_cache_fp8(const uint16_t* k, const uint16_t* v, uint8_t* k_cache,
+                                        uint8_t* v_cache, const float* k_scale, const float* v_scale,
+                                        const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
+                                        int32_t head_dim, int64_t num_slots, hipStream_t stream);
+// Copies whole blocks of both pools (elem_bytes per element: 2 for bf16, 1 for fp8) and, when
+// k_scale / v_scale are given, their per-(block, kv head) scales.
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes,
+                              hipStream_t stream);
 // Launches the attention kernels of a varlen plan whose items list n_prefill prefill tiles of
 // tile_rows rows first, then n_decode decode items.
 hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, int n_prefill, int n_decode,
                          int tile_rows, hipStream_t stream);
 hipError_t launch_cascade(const CascadeArgs& a, int head_dim, int group, hipStream_t stream);
+// The same over fp8 (e4m3) pools with per-(block, kv head) scales (attention.hip built with
+// PKV_KV_FP8=1).
+hipError_t launch_varlen_fp8(const VarlenArgs& a, int head_dim, int group, int n_prefill,
+                             int n_decode, int tile_rows, hipStream_t stream);
+hipError_t launch_cascade_fp8(const CascadeArgs& a, int head_dim, int group, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_merge(void* out, int32_t out_f32, float* lse_out, const float* oa,
                         const float* la, const float* ob, const float* lb, int64_t rows,

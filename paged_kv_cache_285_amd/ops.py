@@ -16,6 +16,9 @@ import torch
 from ._lib import PKV_DTYPE_BF16, PKV_DTYPE_F32, PkvShape, PkvVarlenPlan, check, lib
 
 _16BIT = (torch.bfloat16, torch.int16, torch.uint16)
+# FP8 (e4m3) pools: raw byte codes, or torch's float8_e4m3fn view of the same bytes.
+_FP8 = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+_F32 = (torch.float32,)
 
 
 def make_shape(
@@ -159,6 +162,92 @@ def append_kv(
     return slot_mapping
 
 
+def reshape_and_cache_fp8(
+    k: torch.Tensor,
+    v: torch.Tensor,
+    k_cache: torch.Tensor,
+    v_cache: torch.Tensor,
+    k_scale: torch.Tensor,
+    v_scale: torch.Tensor,
+    slot_mapping: torch.Tensor,
+    shape: PkvShape,
+) -> None:
+    """Quantise the new tokens' bf16 K/V to e4m3 under their blocks' scales (fp32
+    [num_blocks, Hkv]) and write them into the fp8 pools at their slots (in place)."""
+    check(
+        lib().pkv_reshape_and_cache_fp8(
+            _dev(k, "k", _16BIT),
+            _dev(v, "v", _16BIT),
+            _dev(k_cache, "k_cache", _FP8),
+            _dev(v_cache, "v_cache", _FP8),
+            _dev(k_scale, "k_scale", _F32),
+            _dev(v_scale, "v_scale", _F32),
+            _dev(slot_mapping, "slot_mapping", (torch.int64,)),
+            int(k.shape[0]),
+            ctypes.byref(shape),
+            _stream(),
+        )
+    )
+
+
+def append_kv_fp8(
+    k: torch.Tensor,
+    v: torch.Tensor,
+    k_cache: torch.Tensor,
+    v_cache: torch.Tensor,
+    k_scale: torch.Tensor,
+    v_scale: torch.Tensor,
+    block_tables: torch.Tensor,
+    query_start_loc: torch.Tensor,
+    context_lens: torch.Tensor,
+    shape: PkvShape,
+    slot_mapping: Optional[torch.Tensor] = None,
+) -> Optional[torch.Tensor]:
+    """append_kv into fp8 pools: slot mapping and quantising cache write in one launch."""
+    check(
+        lib().pkv_append_kv_fp8(
+            _opt(slot_mapping, "slot_mapping", (torch.int64,)),
+            _dev(k, "k", _16BIT),
+            _dev(v, "v", _16BIT),
+            _dev(k_cache, "k_cache", _FP8),
+            _dev(v_cache, "v_cache", _FP8),
+            _dev(k_scale, "k_scale", _F32),
+            _dev(v_scale, "v_scale", _F32),
+            _dev(block_tables, "block_tables", (torch.int32,)),
+            _dev(query_start_loc, "query_start_loc", (torch.int32,)),
+            _dev(context_lens, "context_lens", (torch.int32,)),
+            int(context_lens.numel()),
+            int(k.shape[0]),
+            ctypes.byref(shape),
+            _stream(),
+        )
+    )
+    return slot_mapping
+
+
+def copy_blocks_fp8(
+    k_cache: torch.Tensor,
+    v_cache: torch.Tensor,
+    k_scale: torch.Tensor,
+    v_scale: torch.Tensor,
+    block_pairs: torch.Tensor,
+    shape: PkvShape,
+) -> None:
+    """copy_blocks for fp8 pools: the blocks' bytes and their per-kv-head scales."""
+    check(
+        lib().pkv_copy_blocks_fp8(
+            _dev(k_cache, "k_cache", _FP8),
+            _dev(v_cache, "v_cache", _FP8),
+            _dev(k_scale, "k_scale", _F32),
+            _dev(v_scale, "v_scale", _F32),
+            _dev(block_pairs, "block_pairs", (torch.int32,)),
+            int(block_pairs.shape[0]),
+            ctypes.byref(shape),
+            _stream(),
+        )
+    )
+
+
 def varlen_workspace_size(num_seqs: int, num_tokens: int, max_seq_len: int, shape: PkvShape) -> int:
     return int(lib().pkv_varlen_workspace_size(num_seqs, num_tokens, max_seq_len, ctypes.byref(shape)))
 
@@ -260,6 +349,54 @@ def paged_attention_varlen(
     return out
 
 
+def paged_attention_varlen_fp8(
+    q: torch.Tensor,
+    k_cache: torch.Tensor,
+    v_cache: torch.Tensor,
+    k_scale: torch.Tensor,
+    v_scale: torch.Tensor,
+    block_tables: torch.Tensor,
+    query_start_loc: torch.Tensor,
+    context_lens: torch.Tensor,
+    seq_lens: torch.Tensor,
+    shape: PkvShape,
+    plan: PkvVarlenPlan,
+    workspace: torch.Tensor,
+    out: Optional[torch.Tensor] = None,
+    out_dtype: torch.dtype = torch.bfloat16,
+    lse: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """paged_attention_varlen over fp8 (e4m3) pools with per-(block, kv head) scales."""
+    num_tokens = int(q.shape[0])
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    code = PKV_DTYPE_F32 if out.dtype == torch.float32 else PKV_DTYPE_BF16
+    check(
+        lib().pkv_paged_attention_varlen_fp8(
+            _dev(out, "out", _16BIT + (torch.float32,)),
+            code,
+            _opt(lse, "lse", (torch.float32,)),
+            _dev(q, "q", _16BIT),
+            _dev(k_cache, "k_cache", _FP8),
+            _dev(v_cache, "v_cache", _FP8),
+            _dev(k_scale, "k_scale", _F32),
+            _dev(v_scale, "v_scale", _F32),
+            _dev(block_tables, "block_tables", (torch.int32,)),
+            _dev(query_start_loc, "query_start_loc", (torch.int32,)),
+            _dev(context_lens, "context_lens", (torch.int32,)),
+            _dev(seq_lens, "seq_lens", (torch.int32,)),
+            int(context_lens.numel()),
+            num_tokens,
+            ctypes.byref(shape),
+            ctypes.byref(plan),
+            _dev(workspace, "workspace", (torch.uint8,)),
+            workspace.numel(),
+            _stream(),
+        )
+    )
+    return out
+
+
 def cascade_workspace_size(num_tokens: int, prefix_len: int, shape: PkvShape) -> int:
     return int(lib().pkv_cascade_workspace_size(num_tokens, prefix_len, ctypes.byref(shape)))
 
@@ -289,6 +426,47 @@ def cascade_prefix_attention(
             _dev(q, "q", _16BIT),
             _dev(k_cache, "k_cache", _16BIT),
             _dev(v_cache, "v_cache", _16BIT),
+            _dev(prefix_block_table, "prefix_block_table", (torch.int32,)),
+            int(prefix_len),
+            T,
+            ctypes.byref(shape),
+            _opt(ws, "workspace", (torch.uint8,)),
+            0 if ws is None else ws.numel(),
+            _stream(),
+        )
+    )
+    return out, lse
+
+
+def cascade_prefix_attention_fp8(
+    q: torch.Tensor,
+    k_cache: torch.Tensor,
+    v_cache: torch.Tensor,
+    k_scale: torch.Tensor,
+    v_scale: torch.Tensor,
+    prefix_block_table: torch.Tensor,
+    prefix_len: int,
+    shape: PkvShape,
+    workspace: Optional[torch.Tensor] = None,
+    out: Optional[torch.Tensor] = None,
+    lse: Optional[torch.Tensor] = None,
+) -> Tuple[torch.Tensor, torch.Tensor]:
+    """cascade_prefix_attention over fp8 (e4m3) pools with per-(block, kv head) scales."""
+    T, Hq = int(q.shape[0]), int(q.shape[1])
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    ws = workspace
+    check(
+        lib().pkv_cascade_prefix_attention_fp8(
+            _dev(out, "out_prefix", (torch.float32,)),
+            _dev(lse, "lse_prefix", (torch.float32,)),
+            _dev(q, "q", _16BIT),
+            _dev(k_cache, "k_cache", _FP8),
+            _dev(v_cache, "v_cache", _FP8),
+            _dev(k_scale, "k_scale", _F32),
+            _dev(v_scale, "v_scale", _F32),
             _dev(prefix_block_table, "prefix_block_table", (torch.int32,)),
             int(prefix_len),
             T,

@@ -67,6 +67,22 @@ def test_shape_validation_errors(P):
     assert lib.pkv_copy_blocks(None, None, None, 3, ctypes.byref(s), None) == -1
 
 
+def test_fp8_entry_points_validate_before_launching(P):
+    lib = P.lib()
+    s = shape(P)
+    z = ctypes.c_void_p(0)
+    assert lib.pkv_reshape_and_cache_fp8(z, z, z, z, z, z, z, 0, ctypes.byref(s), z) == 0
+    assert lib.pkv_reshape_and_cache_fp8(z, z, z, z, z, z, z, 5, ctypes.byref(s), z) == -1
+    assert lib.pkv_append_kv_fp8(z, z, z, z, z, z, z, z, z, z, 2, 3, ctypes.byref(s), z) == -1
+    assert lib.pkv_copy_blocks_fp8(z, z, z, z, z, 0, ctypes.byref(s), z) == 0
+    assert lib.pkv_copy_blocks_fp8(z, z, z, z, z, 2, ctypes.byref(s), z) == -1
+    assert lib.pkv_cascade_prefix_attention_fp8(z, z, z, z, z, z, z, z, 100, 4, ctypes.byref(s), z, 0, z) == -3
+    assert lib.pkv_paged_attention_varlen_fp8(z, 0, z, z, z, z, z, z, z, z, z, z, 1, 1, ctypes.byref(s), None, z, 0, z) == -1
+    bad = shape(P, head_dim=96)
+    assert lib.pkv_append_kv_fp8(z, z, z, z, z, z, z, z, z, z, 2, 3, ctypes.byref(bad), z) == -1
+    assert b"head_dim" in lib.pkv_last_error()
+
+
 def test_plan_rejects_inconsistent_metadata(P):
     s = shape(P)
     with pytest.raises(P.PkvError, match="seq_lens"):

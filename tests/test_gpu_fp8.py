@@ -1,0 +1,277 @@
+"""GPU parity of the FP8 (e4m3) KV cache path through the C ABI against the fp64 CPU oracle.
+
+Cache bytes (quantisation included), slots and copied scales must match bit for bit; attention
+over fp8 pools must hold the bf16-output bar of the bf16 path (max abs <= 1e-2 with bf16 output
+rounding excepted, relative L2 <= 5e-3, LSE within 1e-3) against the oracle's attention over the
+dequantised pools.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU, skipped
+    pytest.skip("no GPU", allow_module_level=True)
+
+import paged_kv_cache_285_amd as P  # noqa: E402
+from _gpu import bf16_out_to_f64, check_attention, check_lse, dev16, dev32  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def devf(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+class DeviceFp8:
+    """A workload's fp8 pools and scales on the device (scales uniform, or powers of two)."""
+
+    def __init__(self, wl, seed=0, pow2_scales=False):
+        self.wl = wl
+        c = W.fp8_cache(wl, seed=seed)
+        if pow2_scales:
+            rng = np.random.default_rng(seed + 100)
+            shape = (wl.num_blocks, wl.num_kv_heads)
+            c.k_scale = np.exp2(rng.integers(-6, -2, shape)).astype(np.float32)
+            c.v_scale = np.exp2(rng.integers(-6, -2, shape)).astype(np.float32)
+        self.c = c
+        self.k_cache, self.v_cache = dev8(c.k_cache), dev8(c.v_cache)
+        self.k_scale, self.v_scale = devf(c.k_scale), devf(c.v_scale)
+        self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride)
+        max_seq = max(int(s.seq_lens.max()) for s in wl.steps)
+        max_t = max(s.num_tokens for s in wl.steps)
+        max_b = max(s.num_seqs for s in wl.steps)
+        self.ws = P.alloc_workspace(P.varlen_workspace_size(max_b, max_t, max_seq, self.shape))
+
+    def tensors(self, st, k=None, v=None):
+        return dict(
+            q=dev16(st.q), k=dev16(st.k if k is None else k), v=dev16(st.v if v is None else v),
+            bt=dev32(st.block_tables), qsl=dev32(st.query_start_loc), ctx=dev32(st.context_lens),
+            seq=dev32(st.seq_lens),
+        )
+
+    def host_pools(self):
+        return self.k_cache.cpu().numpy(), self.v_cache.cpu().numpy()
+
+
+def _extreme_inputs(k, seed):
+    """Copies of bf16 K (or V) with some tokens scaled far past the largest code, some scaled
+    into the subnormal codes, and one NaN element: saturation, subnormals and NaN on the path."""
+    x = W.bf16_bits_to_f32(k).copy()
+    rng = np.random.default_rng(seed)
+    t = x.shape[0]
+    big = rng.choice(t, size=max(1, t // 8), replace=False)
+    tiny = rng.choice(t, size=max(1, t // 8), replace=False)
+    x[big] *= 1000.0
+    x[tiny] *= 1e-4
+    x[t // 2, 0, 3] = np.nan
+    return W.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("pow2_scales", [False, True])
+def test_fp8_append_kv_bitwise(pow2_scales):
+    """Fused slot mapping + quantising cache write: slots and every pool byte equal the oracle's,
+    with saturating, subnormal and NaN inputs; power-of-two scales make exact ties common."""
+    say(f"fp8 append_kv, pow2 scales={pow2_scales}")
+    wl = W.mixed_llama8b(seed=4, num_decode=9, ctx_range=(5, 300))
+    d = DeviceFp8(wl, seed=4, pow2_scales=pow2_scales)
+    kp, vp = d.c.k_cache, d.c.v_cache
+    for si, st in enumerate(wl.steps):
+        k = _extreme_inputs(st.k, 10 + si)
+        v = _extreme_inputs(st.v, 20 + si)
+        t = d.tensors(st, k, v)
+        slots = torch.empty(st.num_tokens, dtype=torch.int64, device="cuda")
+        P.append_kv_fp8(t["k"], t["v"], d.k_cache, d.v_cache, d.k_scale, d.v_scale, t["bt"], t["qsl"], t["ctx"],
+                        d.shape, slot_mapping=slots)
+        torch.cuda.synchronize()
+        ref = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, wl.block_size)
+        assert np.array_equal(slots.cpu().numpy(), ref)
+        kp, vp = O.reshape_and_cache_fp8(k, v, kp, vp, ref, d.c.k_scale, d.c.v_scale, wl.block_size)
+        gk, gv = d.host_pools()
+        for name, g, o in (("k_cache", gk, kp), ("v_cache", gv, vp)):
+            bad = np.argwhere(g != o)[:4]
+            assert not bad.size, f"{name} bytes differ at {bad.tolist()}: gpu {[hex(g[tuple(i)]) for i in bad]} " \
+                                 f"oracle {[hex(o[tuple(i)]) for i in bad]}"
+
+
+def test_fp8_reshape_and_cache_skips_bad_slots_bitwise():
+    say("fp8 reshape_and_cache with negative and out-of-pool slots")
+    wl = W.decode_only(seed=3, num_seqs=20, ctx_range=(10, 200))
+    st = wl.steps[0]
+    d = DeviceFp8(wl, seed=3)
+    slots = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, wl.block_size)
+    slots[::5] = -1
+    slots[3] = wl.num_blocks * wl.block_size + 7
+    t = d.tensors(st)
+    P.reshape_and_cache_fp8(t["k"], t["v"], d.k_cache, d.v_cache, d.k_scale, d.v_scale,
+                            torch.from_numpy(slots).cuda(), d.shape)
+    torch.cuda.synchronize()
+    kp, vp = O.reshape_and_cache_fp8(st.k, st.v, d.c.k_cache, d.c.v_cache, slots, d.c.k_scale, d.c.v_scale,
+                                     wl.block_size)
+    gk, gv = d.host_pools()
+    assert np.array_equal(gk, kp) and np.array_equal(gv, vp)
+
+
+def test_fp8_copy_blocks_copies_bytes_and_scales():
+    say("fp8 copy_blocks: 30 pairs plus skipped pairs")
+    wl = W.mixed_llama8b(seed=7, num_decode=8)
+    d = DeviceFp8(wl, seed=7)
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(wl.num_blocks)
+    pairs = np.stack([perm[:30], perm[30:60]], axis=1).astype(np.int32)
+    pairs = np.concatenate([pairs, [[-1, 3], [5, wl.num_blocks], [9, 9]]]).astype(np.int32)
+    P.copy_blocks_fp8(d.k_cache, d.v_cache, d.k_scale, d.v_scale, dev32(pairs), d.shape)
+    torch.cuda.synchronize()
+    kc, vc = O.copy_blocks(d.c.k_cache, d.c.v_cache, pairs)
+    ks, vs = O.copy_blocks(d.c.k_scale, d.c.v_scale, pairs)  # a scale row moves with its block
+    gk, gv = d.host_pools()
+    assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
+    assert np.array_equal(d.k_scale.cpu().numpy(), ks) and np.array_equal(d.v_scale.cpu().numpy(), vs)
+
+
+def run_and_check_fp8(wl, rows_per_step=None, want_lse=True, out_dtype=torch.bfloat16, seed=0, expect_tile_rows=None,
+                      check_pools=True):
+    bs = wl.block_size
+    d = DeviceFp8(wl, seed=seed)
+    kp, vp = d.c.k_cache, d.c.v_cache
+    rng = np.random.default_rng(seed)
+    stats = []
+    for si, st in enumerate(wl.steps):
+        say(f"  step {si}: B={st.num_seqs} T={st.num_tokens}")
+        t = d.tensors(st)
+        P.append_kv_fp8(t["k"], t["v"], d.k_cache, d.v_cache, d.k_scale, d.v_scale, t["bt"], t["qsl"], t["ctx"],
+                        d.shape)
+        plan = P.plan_varlen(d.ws, st.query_start_loc, st.context_lens, st.seq_lens, d.shape)
+        if expect_tile_rows is not None and plan.num_prefill_items:
+            assert plan.tile_rows == expect_tile_rows, plan.tile_rows
+        lse = torch.empty((st.num_tokens, wl.num_q_heads), dtype=torch.float32, device="cuda") if want_lse else None
+        out = P.paged_attention_varlen_fp8(
+            t["q"], d.k_cache, d.v_cache, d.k_scale, d.v_scale, t["bt"], t["qsl"], t["ctx"], t["seq"], d.shape, plan,
+            d.ws, out_dtype=out_dtype, lse=lse,
+        )
+        torch.cuda.synchronize()
+        slots = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, bs)
+        kp, vp = O.reshape_and_cache_fp8(st.k, st.v, kp, vp, slots, d.c.k_scale, d.c.v_scale, bs)
+        if check_pools:
+            gk, gv = d.host_pools()
+            assert np.array_equal(gk, kp) and np.array_equal(gv, vp), "fp8 pool bytes differ"
+        rows = None
+        if rows_per_step is not None and st.num_tokens > rows_per_step:
+            rows = np.sort(rng.choice(st.num_tokens, size=rows_per_step, replace=False))
+            extra = list(st.query_start_loc[:-1]) + list(st.query_start_loc[1:] - 1)
+            extra.append(int(st.query_start_loc[int(np.argmax(st.seq_lens))]))
+            rows = np.unique(np.concatenate([rows, np.array(extra)]))
+        o_ref, l_ref = O.paged_attention_fp8(
+            st.q, kp, vp, d.c.k_scale, d.c.v_scale, st.block_tables, st.query_start_loc, st.context_lens,
+            st.seq_lens, bs, rows=rows,
+        )
+        sel = slice(None) if rows is None else rows
+        r = check_attention(bf16_out_to_f64(out)[sel], o_ref[sel], f"fp8 {wl.name} step {si}",
+                            bf16_out=out_dtype != torch.float32)
+        if want_lse:
+            r["lse_max_abs"] = check_lse(lse.cpu().numpy()[sel], l_ref[sel], f"fp8 {wl.name} step {si} lse")
+        stats.append(r)
+        say(f"    plan items={plan.num_items} tile_rows={plan.tile_rows} partials={plan.num_partials} {r}")
+    return stats
+
+
+def test_fp8_tiny_prefill_parity():
+    say("fp8 tiny prefill (D=64, G=2)")
+    run_and_check_fp8(W.tiny_prefill(seed=0), seed=1)
+
+
+def test_fp8_decode_small_parity():
+    say("fp8 decode small (G=4), split-KV rows")
+    run_and_check_fp8(W.decode_only(seed=11, num_seqs=24, ctx_range=(30, 6000)), seed=11)
+
+
+def test_fp8_decode_group8_fp32_out_parity():
+    say("fp8 decode small (G=8), fp32 output")
+    run_and_check_fp8(W.decode_only(seed=12, num_seqs=16, ctx_range=(17, 3000), num_q_heads=64), seed=12,
+                      out_dtype=torch.float32)
+
+
+def test_fp8_mixed_batch_small_parity():
+    say("fp8 mixed batch small (128-row MFMA tiles + decode rows)")
+    run_and_check_fp8(W.mixed_llama8b(seed=1, num_decode=12, ctx_range=(20, 700)), seed=1, expect_tile_rows=128)
+
+
+def test_fp8_wide_tiles_parity():
+    say("fp8 long chunked prefill small (256-row pipelined tiles)")
+    wl = W.long_chunked_prefill(seed=2, prompt=4096, chunk=2048, num_decode=8, decode_ctx=300)
+    run_and_check_fp8(wl, rows_per_step=200, seed=2, expect_tile_rows=256)
+
+
+def test_fp8_spec_verify_small_parity():
+    say("fp8 speculative verification rows")
+    run_and_check_fp8(W.spec_verify(seed=5, num_seqs=12, draft=4, ctx_range=(40, 900)), seed=5)
+
+
+def test_fp8_cascade_small_parity():
+    """fp8 prefix pass, fp8 suffix pass and the merge against the oracle's prefix state and its
+    single-pass attention over the dequantised pools."""
+    say("fp8 cascade small")
+    wl = W.cascade_shared_prefix(seed=1, num_queries=40, prefix=1024, suffix_range=(1, 300))
+    _fp8_cascade_check(wl)
+
+
+def _fp8_cascade_check(wl, rows=None):
+    bs = wl.block_size
+    st = wl.steps[0]
+    cv = wl.cascade
+    d = DeviceFp8(wl, seed=9)
+    t = d.tensors(st)
+    P.append_kv_fp8(t["k"], t["v"], d.k_cache, d.v_cache, d.k_scale, d.v_scale, t["bt"], t["qsl"], t["ctx"], d.shape)
+    cws = P.alloc_workspace(P.cascade_workspace_size(st.num_tokens, cv.prefix_len, d.shape))
+    o_p, l_p = P.cascade_prefix_attention_fp8(t["q"], d.k_cache, d.v_cache, d.k_scale, d.v_scale,
+                                              dev32(cv.prefix_block_table), cv.prefix_len, d.shape, cws)
+    pb = cv.prefix_blocks(bs)
+    sbt = np.ascontiguousarray(st.block_tables[:, pb:])
+    sshape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, sbt.shape[1])
+    plan = P.plan_varlen(d.ws, st.query_start_loc, cv.suffix_context_lens, cv.suffix_seq_lens, sshape)
+    l_s = torch.empty((st.num_tokens, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    o_s = P.paged_attention_varlen_fp8(
+        t["q"], d.k_cache, d.v_cache, d.k_scale, d.v_scale, dev32(sbt), t["qsl"], dev32(cv.suffix_context_lens),
+        dev32(cv.suffix_seq_lens), sshape, plan, d.ws, out_dtype=torch.float32, lse=l_s,
+    )
+    lse_m = torch.empty_like(l_s)
+    out = P.merge_attn_states(o_p, l_p, o_s, l_s, lse_out=lse_m)
+    torch.cuda.synchronize()
+    slots = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, bs)
+    kp, vp = O.reshape_and_cache_fp8(st.k, st.v, d.c.k_cache, d.c.v_cache, slots, d.c.k_scale, d.c.v_scale, bs)
+    sel = slice(None) if rows is None else rows
+    qs = st.q if rows is None else st.q[rows]
+    po, pl = O.cascade_prefix_attention_fp8(qs, kp, vp, d.c.k_scale, d.c.v_scale, cv.prefix_block_table,
+                                            cv.prefix_len, bs)
+    check_attention(o_p.cpu().numpy().astype(np.float64)[sel], po, "fp8 cascade prefix", bf16_out=False)
+    check_lse(l_p.cpu().numpy()[sel], pl, "fp8 cascade prefix lse")
+    fo, fl = O.paged_attention_fp8(st.q, kp, vp, d.c.k_scale, d.c.v_scale, st.block_tables, st.query_start_loc,
+                                   st.context_lens, st.seq_lens, bs, rows=rows)
+    r = check_attention(bf16_out_to_f64(out)[sel], fo[sel], "fp8 cascade merged vs single pass")
+    check_lse(lse_m.cpu().numpy()[sel], fl[sel], "fp8 cascade merged lse")
+    say(f"    fp8 cascade merged {r}")
+
+
+def test_fp8_decode_full_size_sampled():
+    """The full decode-only batch (256 rows, context 1024..8192) over fp8 pools, sampled rows."""
+    say("fp8 decode_only full size, sampled rows")
+    run_and_check_fp8(W.decode_only(seed=0), rows_per_step=48, seed=0, check_pools=False)
+
+
+def test_fp8_mixed_full_size_sampled():
+    say("fp8 mixed batch full size (64 decode rows, ctx 128..4096), sampled rows")
+    run_and_check_fp8(W.mixed_llama8b(seed=0), rows_per_step=64, seed=0, check_pools=False)

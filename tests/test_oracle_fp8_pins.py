@@ -204,3 +204,19 @@ def test_attention_fp8_scales_follow_the_block():
     o3, l3 = O.paged_attention_fp8(st.q, k8, v8, c.k_scale, c.v_scale, *args, scale=2 / np.sqrt(wl.head_dim))
     np.testing.assert_allclose(o2, o3, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(l2, l3, rtol=1e-12, atol=1e-12)
+
+
+def test_cascade_prefix_fp8_equals_bf16_cascade_on_exact_values():
+    wl = W.cascade_shared_prefix(seed=2, num_queries=6, prefix=64, suffix_range=(1, 40), num_q_heads=8,
+                                 num_kv_heads=2, head_dim=64)
+    st, cv, bs = wl.steps[0], wl.cascade, wl.block_size
+    c = W.fp8_cache(wl, seed=2)
+    rng = np.random.default_rng(8)
+    ks = np.exp2(rng.integers(-5, -1, (wl.num_blocks, wl.num_kv_heads))).astype(np.float32)
+    vs = np.exp2(rng.integers(-5, -1, (wl.num_blocks, wl.num_kv_heads))).astype(np.float32)
+    kb = W.f32_to_bf16_bits((O.e4m3_decode(c.k_cache) * ks[:, :, None, None]).astype(np.float32))
+    vb = W.f32_to_bf16_bits((O.e4m3_decode(c.v_cache) * vs[:, :, None, None]).astype(np.float32))
+    o8, l8 = O.cascade_prefix_attention_fp8(st.q, c.k_cache, c.v_cache, ks, vs, cv.prefix_block_table, cv.prefix_len, bs)
+    ob, lb = O.cascade_prefix_attention(st.q, kb, vb, cv.prefix_block_table, cv.prefix_len, bs)
+    assert np.all(np.isfinite(l8))
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
