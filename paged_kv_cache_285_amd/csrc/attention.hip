@@ -78,6 +78,11 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Blocks of an fp8 decode item kept in flight per wave (1 or 2).
+#ifndef PKV_DECODE_DEPTH_FP8
+#define PKV_DECODE_DEPTH_FP8 2
+#endif
+
 // 16-byte load with the streaming (non-temporal) cache policy: for K/V bytes read once.
 #ifndef PKV_DECODE_NT
 #define PKV_DECODE_NT 1
@@ -427,8 +432,33 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
 
   // Software pipeline: the next block's loads are in flight while the current one computes.
   // The steady-state loads are unconditional so the compiler's wait counts only ever wait
-  // for the block about to be used (a conditional load would make it wait for both).
-  if (nk > 0) {
+  // for the block about to be used (a conditional load would make it wait for both).  An
+  // fp8 block is half the bytes, so fp8 pools keep two blocks in flight instead of one.
+  if constexpr (FP8 && PKV_DECODE_DEPTH_FP8 == 2) {
+    if (nk > 0) {
+      C8 k0[NKR], v0[RPL], k1[NKR], v1[RPL], k2[NKR], v2[RPL];
+      load(0, k0, v0);
+      if (nk > 1) load(1, k1, v1);
+      int k = 0;
+      for (; k + 4 < nk; k += 3) {  // sets 0, 1 hold blocks k, k + 1
+        load(k + 2, k2, v2);
+        process(k, k0, v0);
+        load(k + 3, k0, v0);
+        process(k + 1, k1, v1);
+        load(k + 4, k1, v1);
+        process(k + 2, k2, v2);
+      }
+      // 1 to 4 blocks left; k and (when present) k + 1 are loaded.
+      if (k + 2 < nk) load(k + 2, k2, v2);
+      process(k, k0, v0);
+      if (k + 1 < nk) {
+        if (k + 3 < nk) load(k + 3, k0, v0);
+        process(k + 1, k1, v1);
+        if (k + 2 < nk) process(k + 2, k2, v2);
+        if (k + 3 < nk) process(k + 3, k0, v0);
+      }
+    }
+  } else if (nk > 0) {
     C8 ka[NKR], va[RPL], kn[NKR], vn[RPL];
     load(0, ka, va);
     int k = 0;
