@@ -542,7 +542,7 @@ def main():
         log("bench: decode-only batch")
         line["decode_hbm"] = decode_hbm(torch, P)
         log("bench: decode-only batch over fp8 pools")
-        line["fp8_decode_hbm"] = fp8_decode_hbm(torch, P, bf16_ms=line["decode_hbm"]["kernel_ms"])
+        line["fp8_decode_hbm"] = fp8_decode_hbm(torch, P, steps=20, warmup=5, bf16_ms=line["decode_hbm"]["kernel_ms"])
     if not args.no_decode:
         log("bench: speculative-verify batch, tiny prefill")
         line["spec_verify_hbm"] = spec_verify_hbm(torch, P)
