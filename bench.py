@@ -8,8 +8,9 @@ reduce).  The 330 query tokens of the pass give the headline attention tokens/s 
 bf16) and resident in HBM before timing starts.
 
 Also reported: the dominant kernel's roofline (algorithmic bytes / HIP-event-timed launch
-duration against 8 TB/s), the decode-only batch's HBM GB/s, and the CPU fp64 oracle timed on a
-bounded sample of the same workload (``cpu_baseline``).
+duration against 8 TB/s; also with cold caches, a 1 GiB write before each launch evicting the
+L2s and the 256 MB MALL), the decode-only batch's HBM GB/s (warm and cold), and the CPU fp64
+oracle timed on a bounded sample of the same workload (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--mfma]
 """
@@ -86,7 +87,7 @@ class Runner:
             )
         )
 
-    def run_pass(self, events=None):
+    def run_pass(self, events=None, flush=None):
         P = self.P
         for i, s in enumerate(self.steps):
             st = s["st"]
@@ -94,6 +95,8 @@ class Runner:
             P.append_kv(s["k"], s["v"], self.k_cache, self.v_cache, s["bt"], s["qsl"], s["ctx"], self.shape,
                         slot_mapping=s["slots"])
             plan = P.plan_varlen(self.ws, st.query_start_loc, st.context_lens, st.seq_lens, self.shape)
+            if flush is not None:
+                flush()
             if events is not None:
                 events[i][0].record()
             P.paged_attention_varlen(
@@ -127,6 +130,34 @@ def time_passes(runner, torch, steps, warmup):
     kern_total, launches = P.timing_end()
     gc.enable()
     return start.elapsed_time(stop), kern_total / max(launches, 1), launches
+
+
+class Flusher:
+    """Writes a 1 GiB scratch buffer: evicts the L2s and the 256 MB MALL before a timed launch."""
+
+    def __init__(self, torch):
+        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n & 255)
+
+
+def time_flushed(runner, torch, passes):
+    """Kernel ms per varlen launch when every launch starts with cold caches (a 1 GiB write
+    before it, outside the kernel's HIP events)."""
+    P = runner.P
+    fl = Flusher(torch)
+    runner.run_pass(flush=fl)
+    torch.cuda.synchronize()
+    P.timing_begin()
+    for _ in range(passes):
+        runner.run_pass(flush=fl)
+    total, n = P.timing_end()
+    del fl
+    torch.cuda.empty_cache()
+    return total / max(n, 1)
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -210,6 +241,14 @@ def decode_hbm(torch, P, steps=10, warmup=3):
         call()
     total, n = P.timing_end()
     ms = total / n
+    fl = Flusher(torch)
+    P.timing_begin()
+    for _ in range(5):
+        fl()
+        call()
+    total_f, n_f = P.timing_end()
+    del fl
+    ms_f = total_f / n_f
     nbytes = step_bytes(st, wl)
     gbs = nbytes / (ms * 1e-3) / 1e9
     res = {
@@ -219,6 +258,8 @@ def decode_hbm(torch, P, steps=10, warmup=3):
         "GB/s": gbs,
         "frac_of_peak": gbs / HBM_PEAK_GBS,
         "tokens/s/layer": st.num_tokens / (ms * 1e-3),
+        "flushed_kernel_ms": ms_f,
+        "flushed_frac_of_peak": nbytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "blocks_per_split": plan.blocks_per_split,
         "items": plan.num_items,
     }
@@ -503,6 +544,8 @@ def main():
     flops_per_launch = [step_flops(st, wl) for st in wl.steps]
     mean_bytes = float(np.mean(bytes_per_launch))
     achieved = mean_bytes / (kern_ms * 1e-3) / 1e9
+    log("bench: the same launches with cold caches")
+    flushed_ms = time_flushed(runner, torch, passes=5)
     traffic = measured_traffic()
     line = {
         "metric": "paged-attn decode HBM GB/s (% peak) + mixed-batch attn tokens/s per layer",
@@ -536,6 +579,8 @@ def main():
             "avg_launch_ms": kern_ms,
             "launches_timed": launches,
             "flops_per_launch": float(np.mean(flops_per_launch)),
+            "flushed_avg_launch_ms": flushed_ms,
+            "flushed_frac": mean_bytes / (flushed_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
     }
     if not args.no_decode:

@@ -17,8 +17,9 @@ section].  Readings taken where the pages are silent:
 * attention over fp8 pools is the same softmax attention over the dequantised keys and
   values (code value * scale, exact in fp64).
 
-Pool layouts and slots are those of the bf16 cache (keys [num_blocks, Hkv, 16, D], values
-[num_blocks, Hkv, D, 16]), one byte per element.
+Pool layouts and slots are those of the bf16 cache (keys [NB, Hkv, 16, D], values
+[NB, Hkv, D, 16] for 16-token blocks; [NB, R, Hkv, 16, D] and [NB, R, Hkv, D, 16] for blocks of
+16 R tokens), one byte per element; the scales are per physical block of any size.
 """
 
 from __future__ import annotations
@@ -27,7 +28,15 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from .paged_attention import attention_state, bf16_to_f64, causal_visible, default_scale
+from .paged_attention import (
+    attention_state,
+    bf16_to_f64,
+    causal_visible,
+    default_scale,
+    key_tile_len,
+    tiles,
+    value_tile_len,
+)
 
 E4M3_MAX = 448.0
 
@@ -76,31 +85,40 @@ def reshape_and_cache_fp8(k, v, k_cache, v_cache, slots, k_scale, v_scale, block
     bf16 bits [T, Hkv, D]; k_scale, v_scale fp32 [num_blocks, Hkv]."""
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
+    kt, vt = tiles(kc), tiles(vc)
+    T = key_tile_len(kc)
+    assert kt.shape[1] * T == block_size and value_tile_len(vc) == T
     for t, s in enumerate(np.asarray(slots, dtype=np.int64)):
-        b = s // block_size
+        b, o = divmod(int(s), block_size)
         if s < 0 or b >= kc.shape[0]:
             continue
         for g in range(k.shape[1]):
-            kc[b, g, s % block_size, :] = quantize(k[t, g, :], k_scale[b][g])
-            vc[b, g, :, s % block_size] = quantize(v[t, g, :], v_scale[b][g])
+            kt[b, o // T, g, o % T, :] = quantize(k[t, g, :], k_scale[b][g])
+            vt[b, o // T, g, :, o % T] = quantize(v[t, g, :], v_scale[b][g])
     return kc, vc
 
 
 def dequantize_keys(k_cache, k_scale, block_table_row, num_keys: int, kv_head: int, block_size: int):
     """Keys 0..num_keys-1 of one request and kv head as fp64 [num_keys, D]."""
+    T = key_tile_len(k_cache)
+    assert tiles(k_cache).shape[1] * T == block_size
     j = np.arange(num_keys)
     phys = np.asarray(block_table_row, dtype=np.int64)[j // block_size]
+    o = j % block_size
     ks = np.asarray(k_scale, dtype=np.float32)[phys, kv_head].astype(np.float64)
-    return e4m3_decode(k_cache[phys, kv_head, j % block_size, :]) * ks[:, None]
+    return e4m3_decode(tiles(k_cache)[phys, o // T, kv_head, o % T, :]) * ks[:, None]
 
 
 def dequantize_values(v_cache, v_scale, block_table_row, num_keys: int, kv_head: int, block_size: int):
     """Values 0..num_keys-1 of one request and kv head as fp64 [num_keys, D] (the pool is
     dim-major)."""
+    T = value_tile_len(v_cache)
+    assert tiles(v_cache).shape[1] * T == block_size
     j = np.arange(num_keys)
     phys = np.asarray(block_table_row, dtype=np.int64)[j // block_size]
+    o = j % block_size
     vs = np.asarray(v_scale, dtype=np.float32)[phys, kv_head].astype(np.float64)
-    return e4m3_decode(v_cache[phys, kv_head, :, j % block_size]) * vs[:, None]
+    return e4m3_decode(tiles(v_cache)[phys, o // T, kv_head, :, o % T]) * vs[:, None]
 
 
 def paged_attention_fp8(
@@ -122,7 +140,7 @@ def paged_attention_fp8(
     e4m3_decode(code) * k_scale[block of j, g] (values alike)."""
     q = np.asarray(q)
     T, Hq, D = q.shape
-    Hkv = k_cache.shape[1]
+    Hkv = tiles(k_cache).shape[2]
     G = Hq // Hkv
     sc = default_scale(D) if scale is None or scale <= 0 else float(scale)
     qsl = np.asarray(query_start_loc, dtype=np.int64)
@@ -163,7 +181,7 @@ def cascade_prefix_attention_fp8(
     Inference"].  Returns (o [T, Hq, D], lse [T, Hq]) in fp64."""
     q = np.asarray(q)
     T, Hq, D = q.shape
-    Hkv = k_cache.shape[1]
+    Hkv = tiles(k_cache).shape[2]
     G = Hq // Hkv
     sc = default_scale(D) if scale is None or scale <= 0 else float(scale)
     o = np.zeros((T, Hq, D), dtype=np.float64)

@@ -53,6 +53,27 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+# ---------------------------------------------------------------------------
+# Pool layout.  Blocks hold a fixed number of tokens, such as 16 or 256 ("11. vLLM principles",
+# section 11.2).  A physical block of bs = R * T tokens is R consecutive tiles of T tokens:
+# keys [NB, R, Hkv, T, D] (a key is one row of its tile), values [NB, R, Hkv, D, T] (the T
+# tokens of one dimension are contiguous).  With R = 1 the tile axis is dropped: keys
+# [NB, Hkv, bs, D], values [NB, Hkv, D, bs].  The library uses T = 16: one tile for 16-token
+# blocks, 16 tiles for 256-token blocks.  (Layout reading: the pages fix no layout.)
+# ---------------------------------------------------------------------------
+def tiles(pool: np.ndarray) -> np.ndarray:
+    """The pool as [NB, R, Hkv, T, D] (keys) or [NB, R, Hkv, D, T] (values); a view."""
+    return pool[:, None] if pool.ndim == 4 else pool
+
+
+def key_tile_len(k_cache: np.ndarray) -> int:
+    return tiles(k_cache).shape[3]
+
+
+def value_tile_len(v_cache: np.ndarray) -> int:
+    return tiles(v_cache).shape[4]
+
+
 def default_scale(head_dim: int) -> float:
     """Scaled dot-product attention scale (reading: 1/sqrt(D); the pages give none)."""
     return 1.0 / math.sqrt(head_dim)
@@ -87,17 +108,21 @@ def slot_mapping(block_tables, query_start_loc, context_lens, block_size: int) -
 def reshape_and_cache(k, v, k_cache, v_cache, slots, block_size: int) -> Tuple[np.ndarray, np.ndarray]:
     """Return copies of the pools with token t's K/V stored at its slot (bitwise; slot < 0 skipped).
 
-    A slot names (block, offset).  The key pool is [num_blocks, Hkv, block_size, D]
-    (token t's key is one row); the value pool is [num_blocks, Hkv, D, block_size]
-    (token t's value is one column).
+    A slot names (block, offset); offset o lies in tile o // 16 of the block, at position o % 16.
+    Token t's key is one row of that key tile, its value one column of that value tile (pool
+    layout above).
     """
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
+    kt, vt = tiles(kc), tiles(vc)
+    T = key_tile_len(kc)
+    assert kt.shape[1] * T == block_size and value_tile_len(vc) == T
     for t, s in enumerate(np.asarray(slots, dtype=np.int64)):
         if s < 0:
             continue
-        kc[s // block_size, :, s % block_size, :] = k[t]
-        vc[s // block_size, :, :, s % block_size] = v[t]
+        b, o = divmod(int(s), block_size)
+        kt[b, o // T, :, o % T, :] = k[t]
+        vt[b, o // T, :, :, o % T] = v[t]
     return kc, vc
 
 
@@ -121,16 +146,23 @@ def copy_blocks(k_cache, v_cache, block_pairs) -> Tuple[np.ndarray, np.ndarray]:
 # ---------------------------------------------------------------------------
 def gather_keys(k_cache, block_table_row, num_keys: int, kv_head: int, block_size: int) -> np.ndarray:
     """Keys 0..num_keys-1 of one kv head, in logical order, as fp64 [num_keys, D]."""
+    T = key_tile_len(k_cache)
+    assert tiles(k_cache).shape[1] * T == block_size
     j = np.arange(num_keys)
     phys = np.asarray(block_table_row, dtype=np.int64)[j // block_size]
-    return bf16_to_f64(k_cache[phys, kv_head, j % block_size, :]).reshape(num_keys, k_cache.shape[-1])
+    o = j % block_size
+    return bf16_to_f64(tiles(k_cache)[phys, o // T, kv_head, o % T, :]).reshape(num_keys, k_cache.shape[-1])
 
 
 def gather_values(v_cache, block_table_row, num_keys: int, kv_head: int, block_size: int) -> np.ndarray:
     """Values 0..num_keys-1 of one kv head, in logical order, as fp64 [num_keys, D]."""
+    T = value_tile_len(v_cache)
+    vt = tiles(v_cache)
+    assert vt.shape[1] * T == block_size
     j = np.arange(num_keys)
     phys = np.asarray(block_table_row, dtype=np.int64)[j // block_size]
-    return bf16_to_f64(v_cache[phys, kv_head, :, j % block_size]).reshape(num_keys, v_cache.shape[2])
+    o = j % block_size
+    return bf16_to_f64(vt[phys, o // T, kv_head, :, o % T]).reshape(num_keys, vt.shape[3])
 
 
 # ---------------------------------------------------------------------------
@@ -193,7 +225,7 @@ def paged_attention(
     """
     q = np.asarray(q)
     T, Hq, D = q.shape
-    Hkv = k_cache.shape[1]
+    Hkv = tiles(k_cache).shape[2]
     if Hq % Hkv:
         raise ValueError("q heads must be a multiple of kv heads")
     G = Hq // Hkv
@@ -247,7 +279,7 @@ def cascade_prefix_attention(
     """
     q = np.asarray(q)
     T, Hq, D = q.shape
-    Hkv = k_cache.shape[1]
+    Hkv = tiles(k_cache).shape[2]
     G = Hq // Hkv
     sc = default_scale(D) if scale is None or scale <= 0 else float(scale)
     o = np.zeros((T, Hq, D), dtype=np.float64)

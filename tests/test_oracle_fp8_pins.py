@@ -220,3 +220,23 @@ def test_cascade_prefix_fp8_equals_bf16_cascade_on_exact_values():
     ob, lb = O.cascade_prefix_attention(st.q, kb, vb, cv.prefix_block_table, cv.prefix_len, bs)
     assert np.all(np.isfinite(l8))
     assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+
+
+def test_fp8_block_size_256_is_sixteen_16_token_blocks():
+    """fp8 pools of 256-token blocks: cache bytes and attention equal those of the bs=16 view of
+    the same memory, with each 256-token block's scales repeated over its 16 tiles."""
+    wl = W.decode_only(seed=9, num_seqs=4, ctx_range=(300, 700), block_size=256)
+    st, R = wl.steps[0], 16
+    c = W.fp8_cache(wl, seed=9)
+    bt16 = (st.block_tables[:, :, None] * R + np.arange(R)[None, None, :]).reshape(st.num_seqs, -1).astype(np.int32)
+    ks16, vs16 = np.repeat(c.k_scale, R, axis=0), np.repeat(c.v_scale, R, axis=0)
+    k16 = c.k_cache.reshape(wl.num_blocks * R, wl.num_kv_heads, 16, wl.head_dim)
+    v16 = c.v_cache.reshape(wl.num_blocks * R, wl.num_kv_heads, wl.head_dim, 16)
+    s256 = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, 256)
+    k8, v8 = O.reshape_and_cache_fp8(st.k, st.v, c.k_cache, c.v_cache, s256, c.k_scale, c.v_scale, 256)
+    k8b, v8b = O.reshape_and_cache_fp8(st.k, st.v, k16, v16, s256, ks16, vs16, 16)
+    assert np.array_equal(k8.reshape(k8b.shape), k8b) and np.array_equal(v8.reshape(v8b.shape), v8b)
+    args = (st.query_start_loc, st.context_lens, st.seq_lens)
+    o1, l1 = O.paged_attention_fp8(st.q, k8, v8, c.k_scale, c.v_scale, st.block_tables, *args, 256)
+    o2, l2 = O.paged_attention_fp8(st.q, k8b, v8b, ks16, vs16, bt16, *args, 16)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

@@ -3,7 +3,8 @@
 Each case below plants one mistake in a step of the CPU oracle: an off-by-one causal mask, a
 wrong scale, the wrong kv head, shifted positions, a transposed value operand, a missing
 softmax normalisation, an LSE in the wrong base, a merge with its weights swapped, and a cache
-write at the wrong offset, a block copy that forgets the values; and in the FP8 half, a wrong
+write at the wrong offset, a block copy that forgets the values, a 256-token block read with
+its kv heads outside its tiles; and in the FP8 half, a wrong
 exponent bias, ties rounded away from zero, no saturation, a multiplied instead of divided
 scale, one kv head's scale for all, the wrong block's scale, an ignored key scale.  For each,
 the pins of test_oracle_pins.py and test_oracle_fp8_pins.py run against the mutated oracle,
@@ -69,7 +70,7 @@ def _restore(saved):
 
 ORIG = {name: getattr(OM, name) for name in (
     "causal_visible", "default_scale", "gather_keys", "gather_values", "token_positions",
-    "attention_state", "merge_attn_states", "reshape_and_cache", "copy_blocks")}
+    "attention_state", "merge_attn_states", "reshape_and_cache", "copy_blocks", "tiles")}
 ORIG8 = {name: getattr(F8, name) for name in (
     "e4m3_decode", "e4m3_encode", "quantize", "reshape_and_cache_fp8", "dequantize_keys",
     "dequantize_values")}
@@ -129,6 +130,14 @@ def copy_keys_only(k_cache, v_cache, block_pairs):
     return kc, np.array(v_cache, copy=True)
 
 
+def tiles_heads_outer(pool):
+    """Reads a block of several tiles as [Hkv, tiles] instead of [tiles, Hkv]."""
+    if pool.ndim == 4:
+        return ORIG["tiles"](pool)
+    nb, r, h = pool.shape[:3]
+    return pool.reshape(nb, h, r, *pool.shape[3:]).transpose(0, 2, 1, 3, 4)
+
+
 def decode_bias_8(codes):
     return ORIG8["e4m3_decode"](codes) * 0.5
 
@@ -174,6 +183,7 @@ MUTATIONS = [
     ("merge_attn_states", merge_swapped),
     ("reshape_and_cache", cache_write_next_offset),
     ("copy_blocks", copy_keys_only),
+    ("tiles", tiles_heads_outer),
     ("e4m3_decode", decode_bias_8),
     ("e4m3_encode", encode_ties_away),
     ("e4m3_encode", encode_no_saturation),

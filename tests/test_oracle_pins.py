@@ -40,13 +40,20 @@ def empty_vpool(nb, hkv, bs, d):
 
 
 def token_view(pool):
-    """Key pool [NB, H, bs, D] -> [NB*bs, H, D]: flat token slots (an independent way to address a slot)."""
+    """Key pool [NB, H, bs, D] (or [NB, R, H, 16, D]) -> [NB*bs, H, D]: flat token slots (an
+    independent way to address a slot)."""
+    if pool.ndim == 5:
+        nb, r, h, t, d = pool.shape
+        return pool.transpose(0, 1, 3, 2, 4).reshape(nb * r * t, h, d)
     nb, h, bs, d = pool.shape
     return pool.transpose(0, 2, 1, 3).reshape(nb * bs, h, d)
 
 
 def vtoken_view(pool):
-    """Value pool [NB, H, D, bs] -> [NB*bs, H, D]."""
+    """Value pool [NB, H, D, bs] (or [NB, R, H, D, 16]) -> [NB*bs, H, D]."""
+    if pool.ndim == 5:
+        nb, r, h, d, t = pool.shape
+        return pool.transpose(0, 1, 4, 2, 3).reshape(nb * r * t, h, d)
     nb, h, d, bs = pool.shape
     return pool.transpose(0, 3, 1, 2).reshape(nb * bs, h, d)
 
@@ -289,9 +296,10 @@ def _dense_attention(q, keys, vals, positions, scale):
     return np.einsum("lhs,shd->lhd", w, vals)
 
 
-def test_mixed_batch_matches_dense_contiguous_attention():
+@pytest.mark.parametrize("block_size", [16, 256])
+def test_mixed_batch_matches_dense_contiguous_attention(block_size):
     """Paging invariance: the paged oracle equals dense attention on keys laid out in logical order."""
-    wl = W.mixed_llama8b(seed=2, num_decode=6, ctx_range=(20, 90))
+    wl = W.mixed_llama8b(seed=2, num_decode=6, ctx_range=(20, 90 if block_size == 16 else 600), block_size=block_size)
     bs, G = wl.block_size, wl.group
     kp, vp = wl.k_cache, wl.v_cache
     # logical key history per request, tracked here without the oracle's gather
@@ -562,3 +570,29 @@ def test_workload_poison_covers_unwritten_slots():
             assert np.isfinite(W.bf16_bits_to_f32(tv[cached])).all()
             fut = [int(st.block_tables[r][j // bs]) * bs + j % bs for j in range(c, int(st.seq_lens[r]))]
             assert np.isnan(W.bf16_bits_to_f32(tv[fut])).all()
+
+
+# ---------------------------------------------------------------------------
+# 256-token blocks: a block of 16 tiles behaves as 16 blocks of 16 tokens
+# ---------------------------------------------------------------------------
+def test_block_size_256_is_sixteen_16_token_blocks():
+    """A 256-token block is 16 consecutive 16-token tiles: the bs=256 pool read as a bs=16 pool of
+    16x the blocks, with table entry 16 b + i for tile i of block b, must give the same slots'
+    bytes and the same attention, bit for bit."""
+    wl = W.mixed_llama8b(seed=5, num_decode=7, ctx_range=(200, 900), block_size=256)
+    R = 16
+    kp, vp = wl.k_cache, wl.v_cache
+    k16 = kp.reshape(wl.num_blocks * R, wl.num_kv_heads, 16, wl.head_dim)
+    v16 = vp.reshape(wl.num_blocks * R, wl.num_kv_heads, wl.head_dim, 16)
+    for st in wl.steps:
+        bt16 = (st.block_tables[:, :, None] * R + np.arange(R)[None, None, :]).reshape(st.num_seqs, -1).astype(np.int32)
+        s256 = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, 256)
+        s16 = O.slot_mapping(bt16, st.query_start_loc, st.context_lens, 16)
+        assert np.array_equal(s256, s16)
+        kp, vp = O.reshape_and_cache(st.k, st.v, kp, vp, s256, 256)
+        k16, v16 = O.reshape_and_cache(st.k, st.v, k16, v16, s16, 16)
+        assert np.array_equal(kp.reshape(k16.shape), k16) and np.array_equal(vp.reshape(v16.shape), v16)
+        args = (st.query_start_loc, st.context_lens, st.seq_lens)
+        o256, l256 = O.paged_attention(st.q, kp, vp, st.block_tables, *args, 256)
+        o16, l16 = O.paged_attention(st.q, k16, v16, bt16, *args, 16)
+        assert np.array_equal(o256, o16) and np.array_equal(l256, l16)

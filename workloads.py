@@ -17,7 +17,9 @@ Value recipe (used by every workload):
     PCG64 stream keyed by (seed, array tag, chunk index), so the values do not
     depend on how many threads draw them;
   * pools: keys [num_blocks, Hkv, 16, D] (token-major), values
-    [num_blocks, Hkv, D, 16] (dim-major);
+    [num_blocks, Hkv, D, 16] (dim-major); a pool of 16 R-token blocks (R > 1, e.g. 256-token
+    blocks) holds R such 16-token tiles per block: keys [num_blocks, R, Hkv, 16, D], values
+    [num_blocks, R, Hkv, D, 16];
   * every pool slot that holds no cached token (unreferenced blocks, block
     table padding and the not-yet-written tail of each request) is set to
     bf16 NaN so that a kernel reading outside the visible keys shows up.
@@ -243,8 +245,19 @@ def build(
 
     H, D = num_kv_heads, head_dim
     nelem = num_blocks * H * bs * D
-    k_cache = normal_bf16(nelem, seed, _TAGS["pool_k"]).reshape(num_blocks, H, bs, D)
-    v_cache = normal_bf16(nelem, seed, _TAGS["pool_v"]).reshape(num_blocks, H, D, bs)
+    if bs > 16:
+        if bs % 16:
+            raise ValueError("blocks above 16 tokens must be whole 16-token tiles")
+        R = bs // 16
+        k_cache = normal_bf16(nelem, seed, _TAGS["pool_k"]).reshape(num_blocks, R, H, 16, D)
+        v_cache = normal_bf16(nelem, seed, _TAGS["pool_v"]).reshape(num_blocks, R, H, D, 16)
+    else:
+        R = 1
+        k_cache = normal_bf16(nelem, seed, _TAGS["pool_k"]).reshape(num_blocks, H, bs, D)
+        v_cache = normal_bf16(nelem, seed, _TAGS["pool_v"]).reshape(num_blocks, H, D, bs)
+    k5 = k_cache if R > 1 else k_cache[:, None]  # [NB, R, H, T, D] view
+    v5 = v_cache if R > 1 else v_cache[:, None]
+    T = bs // R
     if poison:
         referenced = np.zeros(num_blocks, dtype=bool)
         for r in range(nreq):
@@ -257,8 +270,10 @@ def build(
             for pos_blk in range(start // bs, nblk[r]):
                 lo = max(start - pos_blk * bs, 0)
                 phys = tables[r, pos_blk]
-                k_cache[phys, :, lo:, :] = BF16_NAN
-                v_cache[phys, :, :, lo:] = BF16_NAN
+                for t in range(R):
+                    lt = min(max(lo - t * T, 0), T)
+                    k5[phys, t, :, lt:, :] = BF16_NAN
+                    v5[phys, t, :, :, lt:] = BF16_NAN
 
     steps: List[Step] = []
     done = [r.context for r in requests]
@@ -388,7 +403,7 @@ def tiny_prefill(seed: int = 0) -> Workload:
     )
 
 
-def mixed_llama8b(seed: int = 0, num_decode: int = 64, ctx_range=(128, 4096)) -> Workload:
+def mixed_llama8b(seed: int = 0, num_decode: int = 64, ctx_range=(128, 4096), block_size: int = 16) -> Workload:
     """Mixed continuous batch on a Llama-3-8B-shaped layer (32 q / 8 kv heads, D=128).
 
     Three steps over one pool:
@@ -401,26 +416,31 @@ def mixed_llama8b(seed: int = 0, num_decode: int = 64, ctx_range=(128, 4096)) ->
     dctx = rng.integers(ctx_range[0], ctx_range[1] + 1, size=num_decode)
     reqs = [RequestSpec(0, [16, 16, 16]), RequestSpec(0, [16, 15]), RequestSpec(48, [59])]
     reqs += [RequestSpec(int(c), [1, 1, 1]) for c in dctx]
-    return build("mixed_llama8b", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=seed, rng=rng)
+    return build("mixed_llama8b", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=seed, rng=rng,
+                 block_size=block_size)
 
 
-def decode_only(seed: int = 0, num_seqs: int = 256, ctx_range=(1024, 8192), num_q_heads: int = 32) -> Workload:
+def decode_only(seed: int = 0, num_seqs: int = 256, ctx_range=(1024, 8192), num_q_heads: int = 32,
+                block_size: int = 16) -> Workload:
     """Memory-bound decode: one query token per sequence, context uniform in ``ctx_range``."""
     rng = _rng(seed, 2)
     ctx = rng.integers(ctx_range[0], ctx_range[1] + 1, size=num_seqs)
     reqs = [RequestSpec(int(c), [1]) for c in ctx]
-    return build("decode_only", reqs, num_q_heads=num_q_heads, num_kv_heads=8, head_dim=128, seed=seed, rng=rng)
+    return build("decode_only", reqs, num_q_heads=num_q_heads, num_kv_heads=8, head_dim=128, seed=seed, rng=rng,
+                 block_size=block_size)
 
 
 def long_chunked_prefill(
-    seed: int = 0, prompt: int = 32768, chunk: int = 2048, num_decode: int = 128, decode_ctx: int = 2048
+    seed: int = 0, prompt: int = 32768, chunk: int = 2048, num_decode: int = 128, decode_ctx: int = 2048,
+    block_size: int = 16,
 ) -> Workload:
     """One long prompt prefilled in fixed chunks against its growing paged context, beside decode rows."""
     rng = _rng(seed, 3)
     n = prompt // chunk
     reqs = [RequestSpec(0, [chunk] * n)]
     reqs += [RequestSpec(decode_ctx, [1] * n) for _ in range(num_decode)]
-    return build("long_chunked_prefill", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=seed, rng=rng)
+    return build("long_chunked_prefill", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=seed, rng=rng,
+                 block_size=block_size)
 
 
 def spec_verify(seed: int = 0, num_seqs: int = 64, draft: int = 4, ctx_range=(1024, 4096)) -> Workload:
@@ -442,6 +462,7 @@ def cascade_shared_prefix(
     num_q_heads: int = 64,
     num_kv_heads: int = 8,
     head_dim: int = 128,
+    block_size: int = 16,
 ) -> Workload:
     """Decode queries that all share one physical prefix, plus unique suffixes (which include the new token).
 
@@ -459,6 +480,7 @@ def cascade_shared_prefix(
         seed=seed,
         rng=rng,
         shared_prefix=prefix,
+        block_size=block_size,
     )
 
 
