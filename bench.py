@@ -63,7 +63,7 @@ class Runner:
         d32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()  # noqa: E731
         self.k_cache = d16(wl.k_cache)
         self.v_cache = d16(wl.v_cache)
-        self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride)
+        self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride, block_size=wl.block_size)
         self.steps = []
         for st in wl.steps:
             self.steps.append(
@@ -276,7 +276,7 @@ def fp8_decode_hbm(torch, P, steps=10, warmup=3, bf16_ms=None):
     wl = W.decode_only(seed=0)
     c = W.fp8_cache(wl, seed=0)
     st = wl.steps[0]
-    shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride)
+    shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride, block_size=wl.block_size)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     kc, vc, ks, vs = dev(c.k_cache), dev(c.v_cache), dev(c.k_scale), dev(c.v_scale)
     del c
@@ -401,7 +401,7 @@ def mfma_paths(torch, P, reps=5):
     l = torch.empty(st.q.shape[:2], dtype=torch.float32, device="cuda")
     pb = cv.prefix_len // wl.block_size
     sbt = torch.from_numpy(np.ascontiguousarray(st.block_tables[:, pb:])).cuda()
-    sshape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, sbt.shape[1])
+    sshape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, sbt.shape[1], block_size=wl.block_size)
     sctx, sseq = torch.from_numpy(cv.suffix_context_lens).cuda(), torch.from_numpy(cv.suffix_seq_lens).cuda()
     splan = P.plan_varlen(r.ws, st.query_start_loc, cv.suffix_context_lens, cv.suffix_seq_lens, sshape)
     os_, ls_ = torch.empty_like(o), torch.empty_like(l)

@@ -5,10 +5,15 @@
  *   q             bf16 [num_tokens, num_q_heads, head_dim]; the new tokens of every request,
  *                 concatenated request after request (batched prefill: Tencent Cloud
  *                 article on vLLM inference acceleration, batched-prefill paragraph).
- *   k_cache       bf16 [num_blocks, num_kv_heads, block_size, head_dim]: physical key blocks,
- *                 token-major (a key is one contiguous row).
- *   v_cache       bf16 [num_blocks, num_kv_heads, head_dim, block_size]: physical value blocks,
+ *   k_cache       bf16 [num_blocks, num_kv_heads, 16, head_dim] for 16-token blocks: physical
+ *                 key blocks, token-major (a key is one contiguous row).
+ *   v_cache       bf16 [num_blocks, num_kv_heads, head_dim, 16]: physical value blocks,
  *                 dim-major (16 tokens of one dimension are contiguous).
+ *                 A block of 256 tokens ("11. vLLM principles", section 11.2: blocks of 16 or
+ *                 256 tokens) is 16 consecutive such 16-token tiles: k_cache
+ *                 [num_blocks, 16, num_kv_heads, 16, head_dim], v_cache
+ *                 [num_blocks, 16, num_kv_heads, head_dim, 16].  Either way slot s (below) is
+ *                 row s % 16 of 16-token tile s / 16 of the pool.
  *                 Token p of a request lives in physical block block_tables[r][p / bs] at
  *                 offset p % bs ("11. vLLM principles", section 11.2 PagedAttention).
  *   block_tables  int32 [num_seqs, bt_stride]; logical block -> physical block per request.
@@ -56,7 +61,7 @@ extern "C" {
 #define PKV_DTYPE_F32 1
 
 /* Static shape of one attention layer's cache.  Supported: head_dim 64 or 128,
- * block_size 16, num_q_heads / num_kv_heads in {1, 2, 4, 8}. */
+ * block_size 16 or 256, num_q_heads / num_kv_heads in {1, 2, 4, 8}. */
 typedef struct pkv_shape {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -131,8 +136,8 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, in
  * finite value 448), one byte per element, pools in the same layouts as the bf16 pools
  * (k_cache uint8 [num_blocks, Hkv, bs, D], v_cache uint8 [num_blocks, Hkv, D, bs]).
  * Scales: k_scale and v_scale are device fp32 [num_blocks, num_kv_heads], owned by the caller:
- * a code stored in block b, kv head g means code_value * scale[b][g] (a per-head or per-tensor
- * scale is the case of equal entries).  The scales of a block must be set before any token is
+ * a code stored in block b (of block_size tokens), kv head g means code_value * scale[b][g] (a
+ * per-head or per-tensor scale is the case of equal entries).  The scales of a block must be set before any token is
  * written into it and stay fixed while the block holds tokens.
  * Quantisation of a bf16 value x: y = x * (1 / scale) in fp32, clamped to [-448, 448], rounded
  * to the nearest code with ties to even; NaN stores 0x7f.  Attention over fp8 pools equals

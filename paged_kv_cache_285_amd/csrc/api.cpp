@@ -46,8 +46,8 @@ int check_shape(const pkv_shape* s) {
   if (!s) return fail(PKV_EINVAL, "shape is null");
   if (s->head_dim != 64 && s->head_dim != 128)
     return fail(PKV_EINVAL, "head_dim %d unsupported (64 or 128)", s->head_dim);
-  if (s->block_size != pkv::kBlockSize)
-    return fail(PKV_EINVAL, "block_size %d unsupported (16)", s->block_size);
+  if (s->block_size != 16 && s->block_size != 256)
+    return fail(PKV_EINVAL, "block_size %d unsupported (16 or 256)", s->block_size);
   if (s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->num_q_heads % s->num_kv_heads)
     return fail(PKV_EINVAL, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
                 s->num_q_heads, s->num_kv_heads);
@@ -55,9 +55,15 @@ int check_shape(const pkv_shape* s) {
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(PKV_EINVAL, "q heads per kv head %d unsupported (1, 2, 4, 8)", G);
   if (s->num_blocks <= 0) return fail(PKV_EINVAL, "num_blocks must be positive");
+  if ((int64_t)s->num_blocks * (s->block_size / pkv::kBlockSize) > INT32_MAX)
+    return fail(PKV_EINVAL, "num_blocks %d too large: 16-token tile ids must fit int32", s->num_blocks);
   if (s->bt_stride <= 0) return fail(PKV_EINVAL, "bt_stride must be positive");
   return PKV_OK;
 }
+
+// log2(block_size) and log2(block_size / 16) of a checked shape.
+int32_t bs_log2(const pkv_shape* s) { return s->block_size == 256 ? 8 : 4; }
+int32_t bt_shift(const pkv_shape* s) { return bs_log2(s) - 4; }
 
 float scale_log2(const pkv_shape* s) {
   const double sc = s->scale > 0 ? (double)s->scale : 1.0 / std::sqrt((double)s->head_dim);
@@ -116,10 +122,10 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
     if ((int64_t)seq[r] != (int64_t)ctx[r] + ql)
       return fail(PKV_EINVAL, "seq_lens[%d]=%d != context_lens %d + query len %d", r, seq[r],
                   ctx[r], ql);
-    if (ceil_div(seq[r], pkv::kBlockSize) > s->bt_stride)
+    if (ceil_div(seq[r], s->block_size) > s->bt_stride)
       return fail(PKV_EINVAL, "seq_lens[%d]=%d needs more than bt_stride=%d blocks", r, seq[r],
                   s->bt_stride);
-    if (ceil_div(seq[r], pkv::kBlockSize) > s->num_blocks && ql > 0)
+    if (ceil_div(seq[r], s->block_size) > s->num_blocks && ql > 0)
       return fail(PKV_EINVAL, "seq_lens[%d]=%d needs more blocks than the pool has", r, seq[r]);
   }
   // Split size for decode rows: the smallest power of two (>= kMinBlocksPerSplit, <= 256
@@ -389,7 +395,7 @@ int pkv_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
     return fail(PKV_EINVAL, "null pointer argument");
   hipError_t e = pkv::launch_slot_mapping(slot_mapping, block_tables, query_start_loc,
                                           context_lens, num_seqs, num_tokens, shape->bt_stride,
-                                          (hipStream_t)stream);
+                                          bs_log2(shape), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "slot_mapping launch");
   return ok();
 }
@@ -409,7 +415,7 @@ int pkv_append_kv(int64_t* slot_mapping, const void* k, const void* v, void* k_c
       slot_mapping, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_tables,
       query_start_loc, context_lens, num_seqs, num_tokens, shape->num_kv_heads, shape->head_dim,
-      shape->bt_stride, num_slots, (hipStream_t)stream);
+      shape->bt_stride, num_slots, bs_log2(shape), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "append_kv launch");
   return ok();
 }
@@ -448,7 +454,7 @@ int pkv_append_kv_fp8(int64_t* slot_mapping, const void* k, const void* v, void*
       slot_mapping, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale, v_scale, block_tables,
       query_start_loc, context_lens, num_seqs, num_tokens, shape->num_kv_heads, shape->head_dim,
-      shape->bt_stride, num_slots, (hipStream_t)stream);
+      shape->bt_stride, num_slots, bs_log2(shape), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "append_kv_fp8 launch");
   return ok();
 }
@@ -466,7 +472,7 @@ int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void*
   hipError_t e = pkv::launch_reshape_and_cache_fp8(
       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint8_t*>(k_cache),
       static_cast<uint8_t*>(v_cache), k_scale, v_scale, slot_mapping, num_tokens, shape->num_kv_heads,
-      shape->head_dim, num_slots, (hipStream_t)stream);
+      shape->head_dim, num_slots, bs_log2(shape), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "reshape_and_cache_fp8 launch");
   return ok();
 }
@@ -478,8 +484,8 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, in
   if (num_pairs == 0) return ok();
   if (!k_cache || !v_cache || !block_pairs) return fail(PKV_EINVAL, "null pointer argument");
   hipError_t e = pkv::launch_copy_blocks(k_cache, v_cache, nullptr, nullptr, block_pairs, num_pairs,
-                                         shape->num_blocks, shape->num_kv_heads, shape->head_dim, 2,
-                                         (hipStream_t)stream);
+                                         shape->num_blocks, shape->block_size, shape->num_kv_heads,
+                                         shape->head_dim, 2, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
   return ok();
 }
@@ -493,8 +499,8 @@ int pkv_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_s
   if (!k_cache || !v_cache || !k_scale || !v_scale || !block_pairs)
     return fail(PKV_EINVAL, "null pointer argument");
   hipError_t e = pkv::launch_copy_blocks(k_cache, v_cache, k_scale, v_scale, block_pairs, num_pairs,
-                                         shape->num_blocks, shape->num_kv_heads, shape->head_dim, 1,
-                                         (hipStream_t)stream);
+                                         shape->num_blocks, shape->block_size, shape->num_kv_heads,
+                                         shape->head_dim, 1, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
   return ok();
 }
@@ -594,6 +600,7 @@ static int varlen_impl(void* out, int32_t out_dtype, float* lse, const void* q,
   a.num_q_heads = shape->num_q_heads;
   a.num_kv_heads = shape->num_kv_heads;
   a.bt_stride = shape->bt_stride;
+  a.bt_shift = bt_shift(shape);
   a.scale_log2 = scale_log2(shape);
   const int G = shape->num_q_heads / shape->num_kv_heads;
   if (int rc = timing_mark((hipStream_t)stream, true)) return rc;
@@ -689,6 +696,7 @@ static int cascade_impl(float* out_prefix, float* lse_prefix, const void* q, con
                  : nullptr;
   a.num_q_heads = shape->num_q_heads;
   a.num_kv_heads = shape->num_kv_heads;
+  a.bt_shift = bt_shift(shape);
   a.scale_log2 = scale_log2(shape);
   const int G = shape->num_q_heads / shape->num_kv_heads;
   hipError_t e = (fp8 ? pkv::launch_cascade_fp8 : pkv::launch_cascade)(a, shape->head_dim, G,

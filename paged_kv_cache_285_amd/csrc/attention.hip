@@ -131,6 +131,14 @@ __device__ __forceinline__ u32x4 widen8(u32x2 c) {
 }
 __device__ __forceinline__ u32x4 widen8(u32x4 c) { return c; }
 
+// Physical 16-token tile of logical tile j of a request.  A block of 16 << L tokens is 1 << L
+// consecutive 16-token tiles (L = 0 for 16-token blocks, 4 for 256-token blocks), so the tile
+// is (block_tables[j >> L] << L) + the low L bits of j.
+template <typename IntPtr>
+__device__ __forceinline__ int tile_of(IntPtr bt, int j, int L) {
+  return (bt[j >> L] << L) + (j & ((1 << L) - 1));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __builtin_bit_cast(
@@ -281,14 +289,15 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   // physical ids are fetched once, one per lane, and read back with v_readlane.
   const int nb = b_end - b_begin;
   const int nk = nb > wave ? (nb - wave + NW - 1) / NW : 0;
-  const int my_id = lane < nk ? bt[b_begin + wave + NW * lane] : 0;
+  const int L = a.bt_shift;
+  const int my_id = lane < nk ? tile_of(bt, b_begin + wave + NW * lane, L) : 0;
   // fp8 pools: the key and value scales of those blocks, likewise one per lane (issued before
   // the first K/V loads, so waiting for those data covers them).
   float my_ks = 1.f, my_vs = 1.f;
   if constexpr (FP8) {
     if (lane < nk) {
-      my_ks = a.k_scale[(int64_t)my_id * Hkv + g];
-      my_vs = a.v_scale[(int64_t)my_id * Hkv + g];
+      my_ks = a.k_scale[(int64_t)(my_id >> L) * Hkv + g];
+      my_vs = a.v_scale[(int64_t)(my_id >> L) * Hkv + g];
     }
   }
 
@@ -580,8 +589,8 @@ template <int D, int G, bool CAUSAL, int NW, bool FP8>
 __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __restrict__ k_cache,
                           const void* __restrict__ v_cache, const float* __restrict__ k_scale,
                           const float* __restrict__ v_scale, int Hkv, int g,
-                          const int32_t* __restrict__ bt, int tok0, int ntok, int pos0, int kv_begin,
-                          int kv_end, float sl, void* out, int out_f32, float* lse_out,
+                          const int32_t* __restrict__ bt, int L, int tok0, int ntok, int pos0,
+                          int kv_begin, int kv_end, float sl, void* out, int out_f32, float* lse_out,
                           char* smem_raw) {
   using S = TileSmem<D>;
   constexpr int KSTEPS = D / 16;  // QK^T contraction steps
@@ -656,12 +665,12 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
   // waits for the data.  Returns how many of the block's keys are valid (<= 0: none).
   auto stage_load = [&](int tile, C8 (&r)[RS], float& ks, float& vs) -> int {
     const int lb = kv_begin / kBlockSize + 4 * tile + sblk;
-    const int64_t phys = cbt[min(lb, last_blk)];
+    const int64_t phys = tile_of(cbt, min(lb, last_blk), L);
     const C8* kp = kbase + phys * blk_stride;
     const C8* vp = vbase + phys * blk_stride;
     if constexpr (FP8) {
-      ks = ((const cfloat*)k_scale)[phys * Hkv + g];
-      vs = ((const cfloat*)v_scale)[phys * Hkv + g];
+      ks = ((const cfloat*)k_scale)[(phys >> L) * Hkv + g];
+      vs = ((const cfloat*)v_scale)[(phys >> L) * Hkv + g];
     } else {
       ks = vs = 1.f;
     }
@@ -1058,8 +1067,8 @@ template <int D, int G, bool CAUSAL, bool FP8>
 __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __restrict__ k_cache,
                           const void* __restrict__ v_cache, const float* __restrict__ k_scale,
                           const float* __restrict__ v_scale, int Hkv, int g,
-                          const int32_t* __restrict__ bt, int tok0, int ntok, int pos0, int kv_begin,
-                          int kv_end, float sl, void* out, int out_f32, float* lse_out,
+                          const int32_t* __restrict__ bt, int L, int tok0, int ntok, int pos0,
+                          int kv_begin, int kv_end, float sl, void* out, int out_f32, float* lse_out,
                           char* smem_raw) {
   using S = TileSmem<D>;
   constexpr int KSTEPS = D / 16;
@@ -1122,13 +1131,13 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
     using C8 = ChunkV<FP8>;
     float* scl = reinterpret_cast<float*>(smem_raw + S::SC_OFF);
     int bid_base = 0;
-    int bid = bt[min(blk0 + 4 * lane, last_blk)];
+    int bid = tile_of(bt, min(blk0 + 4 * lane, last_blk), L);
     float bks = 1.f, bvs = 1.f;
     auto load_scales = [&]() __attribute__((always_inline)) {
       if constexpr (FP8) {
         if (wave < 4) {
-          bks = k_scale[(int64_t)bid * Hkv + g];
-          bvs = v_scale[(int64_t)bid * Hkv + g];
+          bks = k_scale[(int64_t)(bid >> L) * Hkv + g];
+          bvs = v_scale[(int64_t)(bid >> L) * Hkv + g];
         }
       }
     };
@@ -1136,7 +1145,7 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
     auto block_id = [&](int tile, float& ks, float& vs) __attribute__((always_inline)) -> int {
       if (tile - bid_base >= 64) {
         bid_base = tile;
-        bid = bt[min(blk0 + 4 * (tile + lane), last_blk)];
+        bid = tile_of(bt, min(blk0 + 4 * (tile + lane), last_blk), L);
         load_scales();
       }
       ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bks), tile - bid_base));
@@ -1299,7 +1308,7 @@ void varlen_kernel(VarlenArgs a) {
     const int tok0 = a.query_start_loc[r] + it.q_begin;
     const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
     mfma_tile<D, G, true, NW, FP8>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale,
-                                   a.num_kv_heads, g, bt, tok0, it.q_count, ctx + it.q_begin,
+                                   a.num_kv_heads, g, bt, a.bt_shift, tok0, it.q_count, ctx + it.q_begin,
                                    it.kv_begin, it.kv_end, a.scale_log2, a.out, a.out_f32, a.lse, smem);
   }
 }
@@ -1317,7 +1326,7 @@ void prefill_wide_kernel(VarlenArgs a) {
   const int tok0 = a.query_start_loc[r] + it.q_begin;
   const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
   pipe_tile<D, G, true, FP8>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
-                             g, bt, tok0, it.q_count, ctx + it.q_begin, it.kv_begin, it.kv_end, a.scale_log2,
+                             g, bt, a.bt_shift, tok0, it.q_count, ctx + it.q_begin, it.kv_begin, it.kv_end, a.scale_log2,
                              a.out, a.out_f32, a.lse, smem);
 }
 
@@ -1342,7 +1351,8 @@ void cascade_kernel(CascadeArgs a) {
     lse = a.part_lse + (int64_t)seg * a.num_tokens * a.num_q_heads;
   }
   pipe_tile<D, G, false, FP8>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
-                              g, a.prefix_bt, tok0, ntok, 0, kv_begin, kv_end, a.scale_log2, out, 1, lse, smem);
+                              g, a.prefix_bt, a.bt_shift, tok0, ntok, 0, kv_begin, kv_end, a.scale_log2, out, 1,
+                              lse, smem);
 }
 
 // One wave per (token, head) row; lane holds D/64 consecutive dims.

@@ -16,7 +16,7 @@ namespace {
 __global__ void slot_mapping_kernel(int64_t* __restrict__ slots, const int32_t* __restrict__ bt,
                                     const int32_t* __restrict__ qsl,
                                     const int32_t* __restrict__ ctx, int32_t num_seqs,
-                                    int32_t num_tokens, int32_t bt_stride) {
+                                    int32_t num_tokens, int32_t bt_stride, int32_t bs_log2) {
   const int32_t t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= num_tokens) return;
   int32_t lo = 0, hi = num_seqs - 1;  // largest r with qsl[r] <= t
@@ -26,19 +26,21 @@ __global__ void slot_mapping_kernel(int64_t* __restrict__ slots, const int32_t* 
   }
   const int32_t r = lo;
   const int32_t pos = ctx[r] + (t - qsl[r]);
-  const int32_t logical = pos / kBlockSize;
+  const int32_t logical = pos >> bs_log2;
   if (pos < 0 || logical >= bt_stride) {
     slots[t] = -1;
     return;
   }
   const int64_t phys = bt[(int64_t)r * bt_stride + logical];
-  slots[t] = phys * kBlockSize + (pos % kBlockSize);
+  slots[t] = (phys << bs_log2) + (pos & ((1 << bs_log2) - 1));
 }
 
 // One thread per 16-byte chunk (8 bf16) of one token's K and V for one kv head.  A slot names
-// (block, offset).  The key pool is [num_blocks, Hkv, 16, D]: the token's key is one 16-byte
-// store.  The value pool is [num_blocks, Hkv, D, 16] (dim-major, so attention can read
-// 16-token rows of one dimension): the token's 8 values go to 8 rows, 2 bytes each.
+// (block, offset).  A block of 16 or 256 tokens is 1 or 16 consecutive 16-token tiles, so
+// slot / 16 is the token's 16-token tile in the pool and slot % 16 its row there, whatever the
+// block size.  The key pool is [tiles, Hkv, 16, D]: the token's key is one 16-byte store.  The
+// value pool is [tiles, Hkv, D, 16] (dim-major, so attention can read 16-token rows of one
+// dimension): the token's 8 values go to 8 rows, 2 bytes each.
 __global__ void reshape_and_cache_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                          uint4* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
                                          const int64_t* __restrict__ slots, int32_t num_tokens,
@@ -75,7 +77,8 @@ __global__ void append_kv_kernel(int64_t* __restrict__ slot_out, const uint4* __
                                  uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt,
                                  const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
                                  int32_t num_seqs, int32_t num_tokens, int32_t num_kv_heads,
-                                 int32_t chunks_per_head, int32_t bt_stride, int64_t num_slots) {
+                                 int32_t chunks_per_head, int32_t bt_stride, int64_t num_slots,
+                                 int32_t bs_log2) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_token = (int64_t)num_kv_heads * chunks_per_head;
   const int64_t t = gid / per_token;
@@ -86,10 +89,10 @@ __global__ void append_kv_kernel(int64_t* __restrict__ slot_out, const uint4* __
     if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
   }
   const int32_t pos = ctx[lo] + (int32_t)(t - qsl[lo]);
-  const int32_t logical = pos / kBlockSize;
+  const int32_t logical = pos >> bs_log2;
   int64_t slot = -1;
   if (pos >= 0 && logical < bt_stride)
-    slot = (int64_t)bt[(int64_t)lo * bt_stride + logical] * kBlockSize + (pos % kBlockSize);
+    slot = ((int64_t)bt[(int64_t)lo * bt_stride + logical] << bs_log2) + (pos & ((1 << bs_log2) - 1));
   const int64_t within = gid - t * per_token;
   if (slot_out && within == 0) slot_out[t] = slot;
   if (slot < 0 || slot >= num_slots) return;
@@ -156,12 +159,13 @@ __device__ __forceinline__ void store_fp8_chunk(const uint4 kx, const uint4 vx, 
                                                 const float* __restrict__ k_scale,
                                                 const float* __restrict__ v_scale, int64_t slot,
                                                 int64_t h, int64_t c, int32_t num_kv_heads,
-                                                int32_t chunks_per_head) {
-  const int64_t blk = slot / kBlockSize;
+                                                int32_t chunks_per_head, int32_t bs_log2) {
+  const int64_t blk = slot / kBlockSize;  // 16-token tile
   const int64_t off = slot - blk * kBlockSize;
   const int64_t tile = blk * num_kv_heads + h;
-  const float kinv = 1.0f / k_scale[tile];
-  const float vinv = 1.0f / v_scale[tile];
+  const int64_t sidx = (slot >> bs_log2) * num_kv_heads + h;  // scales: per (block, kv head)
+  const float kinv = 1.0f / k_scale[sidx];
+  const float vinv = 1.0f / v_scale[sidx];
   k_cache[(tile * kBlockSize + off) * chunks_per_head + c] = quantize8(kx, kinv);
   const uint2 vq = quantize8(vx, vinv);
   uint8_t* vt = v_cache + (tile * chunks_per_head * 8 + c * 8) * kBlockSize + off;
@@ -179,7 +183,7 @@ __global__ void reshape_and_cache_fp8_kernel(const uint4* __restrict__ k, const 
                                              const float* __restrict__ v_scale,
                                              const int64_t* __restrict__ slots, int32_t num_tokens,
                                              int32_t num_kv_heads, int32_t chunks_per_head,
-                                             int64_t num_slots) {
+                                             int64_t num_slots, int32_t bs_log2) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_token = (int64_t)num_kv_heads * chunks_per_head;
   const int64_t t = gid / per_token;
@@ -189,7 +193,7 @@ __global__ void reshape_and_cache_fp8_kernel(const uint4* __restrict__ k, const 
   const int64_t within = gid - t * per_token;
   const int64_t h = within / chunks_per_head;
   store_fp8_chunk(k[gid], v[gid], k_cache, v_cache, k_scale, v_scale, slot, h, within - h * chunks_per_head,
-                  num_kv_heads, chunks_per_head);
+                  num_kv_heads, chunks_per_head, bs_log2);
 }
 
 // As append_kv_kernel, quantising into fp8 pools.
@@ -199,7 +203,8 @@ __global__ void append_kv_fp8_kernel(int64_t* __restrict__ slot_out, const uint4
                                      const float* __restrict__ v_scale, const int32_t* __restrict__ bt,
                                      const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
                                      int32_t num_seqs, int32_t num_tokens, int32_t num_kv_heads,
-                                     int32_t chunks_per_head, int32_t bt_stride, int64_t num_slots) {
+                                     int32_t chunks_per_head, int32_t bt_stride, int64_t num_slots,
+                                     int32_t bs_log2) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_token = (int64_t)num_kv_heads * chunks_per_head;
   const int64_t t = gid / per_token;
@@ -210,16 +215,16 @@ __global__ void append_kv_fp8_kernel(int64_t* __restrict__ slot_out, const uint4
     if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
   }
   const int32_t pos = ctx[lo] + (int32_t)(t - qsl[lo]);
-  const int32_t logical = pos / kBlockSize;
+  const int32_t logical = pos >> bs_log2;
   int64_t slot = -1;
   if (pos >= 0 && logical < bt_stride)
-    slot = (int64_t)bt[(int64_t)lo * bt_stride + logical] * kBlockSize + (pos % kBlockSize);
+    slot = ((int64_t)bt[(int64_t)lo * bt_stride + logical] << bs_log2) + (pos & ((1 << bs_log2) - 1));
   const int64_t within = gid - t * per_token;
   if (slot_out && within == 0) slot_out[t] = slot;
   if (slot < 0 || slot >= num_slots) return;
   const int64_t h = within / chunks_per_head;
   store_fp8_chunk(k[gid], v[gid], k_cache, v_cache, k_scale, v_scale, slot, h, within - h * chunks_per_head,
-                  num_kv_heads, chunks_per_head);
+                  num_kv_heads, chunks_per_head, bs_log2);
 }
 
 // Copy-on-write support ["11. vLLM principles", section 11.2: requests that share a prefix
@@ -251,7 +256,8 @@ hipError_t launch_append_kv(int64_t* slot_mapping, const uint16_t* k, const uint
                             uint16_t* k_cache, uint16_t* v_cache, const int32_t* block_tables,
                             const int32_t* qsl, const int32_t* ctx, int32_t num_seqs,
                             int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                            int32_t bt_stride, int64_t num_slots, hipStream_t stream) {
+                            int32_t bt_stride, int64_t num_slots, int32_t bs_log2,
+                            hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const int32_t chunks = head_dim / 8;
   const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
@@ -261,7 +267,7 @@ hipError_t launch_append_kv(int64_t* slot_mapping, const uint16_t* k, const uint
                      slot_mapping, reinterpret_cast<const uint4*>(k),
                      reinterpret_cast<const uint4*>(v), reinterpret_cast<uint4*>(k_cache), v_cache,
                      block_tables, qsl, ctx, num_seqs, num_tokens, num_kv_heads, chunks, bt_stride,
-                     num_slots);
+                     num_slots, bs_log2);
   return hipGetLastError();
 }
 
@@ -270,7 +276,7 @@ hipError_t launch_append_kv_fp8(int64_t* slot_mapping, const uint16_t* k, const 
                                 const float* v_scale, const int32_t* block_tables, const int32_t* qsl,
                                 const int32_t* ctx, int32_t num_seqs, int32_t num_tokens,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t bt_stride,
-                                int64_t num_slots, hipStream_t stream) {
+                                int64_t num_slots, int32_t bs_log2, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const int32_t chunks = head_dim / 8;
   const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
@@ -279,14 +285,15 @@ hipError_t launch_append_kv_fp8(int64_t* slot_mapping, const uint16_t* k, const 
   hipLaunchKernelGGL(append_kv_fp8_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, slot_mapping,
                      reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
                      reinterpret_cast<uint2*>(k_cache), v_cache, k_scale, v_scale, block_tables, qsl, ctx,
-                     num_seqs, num_tokens, num_kv_heads, chunks, bt_stride, num_slots);
+                     num_seqs, num_tokens, num_kv_heads, chunks, bt_stride, num_slots, bs_log2);
   return hipGetLastError();
 }
 
 hipError_t launch_reshape_and_cache_fp8(const uint16_t* k, const uint16_t* v, uint8_t* k_cache,
                                         uint8_t* v_cache, const float* k_scale, const float* v_scale,
                                         const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                                        int32_t head_dim, int64_t num_slots, hipStream_t stream) {
+                                        int32_t head_dim, int64_t num_slots, int32_t bs_log2,
+                                        hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const int32_t chunks = head_dim / 8;
   const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
@@ -295,18 +302,19 @@ hipError_t launch_reshape_and_cache_fp8(const uint16_t* k, const uint16_t* v, ui
   hipLaunchKernelGGL(reshape_and_cache_fp8_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
                      reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
                      reinterpret_cast<uint2*>(k_cache), v_cache, k_scale, v_scale, slots, num_tokens,
-                     num_kv_heads, chunks, num_slots);
+                     num_kv_heads, chunks, num_slots, bs_log2);
   return hipGetLastError();
 }
 
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
                                const int32_t* qsl, const int32_t* ctx, int32_t num_seqs,
-                               int32_t num_tokens, int32_t bt_stride, hipStream_t stream) {
+                               int32_t num_tokens, int32_t bt_stride, int32_t bs_log2,
+                               hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const int threads = 256;
   const int blocks = (num_tokens + threads - 1) / threads;
   hipLaunchKernelGGL(slot_mapping_kernel, dim3(blocks), dim3(threads), 0, stream, slot_mapping,
-                     block_tables, qsl, ctx, num_seqs, num_tokens, bt_stride);
+                     block_tables, qsl, ctx, num_seqs, num_tokens, bt_stride, bs_log2);
   return hipGetLastError();
 }
 
@@ -328,10 +336,10 @@ hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v, uint16
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
-                              int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes,
-                              hipStream_t stream) {
+                              int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t elem_bytes, hipStream_t stream) {
   if (num_pairs == 0) return hipSuccess;
-  const int64_t chunks = (int64_t)num_kv_heads * kBlockSize * head_dim * elem_bytes / 16;
+  const int64_t chunks = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes / 16;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, 2), dim3(256), 0, stream,
                      reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache), k_scale,
                      v_scale, pairs, num_blocks, num_kv_heads, chunks);

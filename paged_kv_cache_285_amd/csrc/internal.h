@@ -49,6 +49,7 @@ struct VarlenArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t bt_stride;
+  int32_t bt_shift;  // log2(block_size / 16): a block is 1 << bt_shift 16-token tiles
   float scale_log2;  // softmax scale * log2(e)
 };
 
@@ -70,6 +71,7 @@ struct CascadeArgs {
   float* part_lse;     // [num_segments, T, Hq]
   int32_t num_q_heads;
   int32_t num_kv_heads;
+  int32_t bt_shift;  // log2(block_size / 16)
   float scale_log2;
 };
 
@@ -87,14 +89,18 @@ struct ReduceArgs {
 };
 
 // Launchers (defined in the .hip files); return the hipError_t of the launch.
+// bs_log2 = log2(block_size); slots are flat token indices, so a slot's 16-token tile is
+// slot / 16 whatever the block size.
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
                                const int32_t* qsl, const int32_t* ctx, int32_t num_seqs,
-                               int32_t num_tokens, int32_t bt_stride, hipStream_t stream);
+                               int32_t num_tokens, int32_t bt_stride, int32_t bs_log2,
+                               hipStream_t stream);
 hipError_t launch_append_kv(int64_t* slot_mapping, const uint16_t* k, const uint16_t* v,
                             uint16_t* k_cache, uint16_t* v_cache, const int32_t* block_tables,
                             const int32_t* qsl, const int32_t* ctx, int32_t num_seqs,
                             int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                            int32_t bt_stride, int64_t num_slots, hipStream_t stream);
+                            int32_t bt_stride, int64_t num_slots, int32_t bs_log2,
+                            hipStream_t stream);
 hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v, uint16_t* k_cache,
                                     uint16_t* v_cache, const int64_t* slots, int32_t num_tokens,
                                     int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
@@ -104,17 +110,18 @@ hipError_t launch_append_kv_fp8(int64_t* slot_mapping, const uint16_t* k, const 
                                 const float* v_scale, const int32_t* block_tables, const int32_t* qsl,
                                 const int32_t* ctx, int32_t num_seqs, int32_t num_tokens,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t bt_stride,
-                                int64_t num_slots, hipStream_t stream);
+                                int64_t num_slots, int32_t bs_log2, hipStream_t stream);
 hipError_t launch_reshape_and_cache_fp8(const uint16_t* k, const uint16_t* v, uint8_t* k_cache,
                                         uint8_t* v_cache, const float* k_scale, const float* v_scale,
                                         const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                                        int32_t head_dim, int64_t num_slots, hipStream_t stream);
+                                        int32_t head_dim, int64_t num_slots, int32_t bs_log2,
+                                        hipStream_t stream);
 // Copies whole blocks of both pools (elem_bytes per element: 2 for bf16, 1 for fp8) and, when
 // k_scale / v_scale are given, their per-(block, kv head) scales.
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
-                              int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes,
-                              hipStream_t stream);
+                              int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t elem_bytes, hipStream_t stream);
 // Launches the attention kernels of a varlen plan whose items list n_prefill prefill tiles of
 // tile_rows rows first, then n_decode decode items.
 hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, int n_prefill, int n_decode,

@@ -77,7 +77,7 @@ class DeviceWorkload:
         self.wl = wl
         self.k_cache = dev16(wl.k_cache)
         self.v_cache = dev16(wl.v_cache)
-        self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride)
+        self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride, block_size=wl.block_size)
         max_seq = max(int(s.seq_lens.max()) for s in wl.steps)
         max_t = max(s.num_tokens for s in wl.steps)
         max_b = max(s.num_seqs for s in wl.steps)

@@ -67,6 +67,20 @@ def test_shape_validation_errors(P):
     assert lib.pkv_copy_blocks(None, None, None, 3, ctypes.byref(s), None) == -1
 
 
+def test_block_size_256_accepted_and_checked(P):
+    lib = P.lib()
+    s = shape(P, block_size=256, num_blocks=100, bt_stride=4)
+    assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, ctypes.byref(s), None) == 0
+    # 4 entries of 256 tokens cover 1024 tokens; 1025 do not
+    ok_plan, _ = P.plan_varlen_host([0, 1], [1023], [1024], s)
+    assert ok_plan.num_items >= 1
+    with pytest.raises(P.PkvError):
+        P.plan_varlen_host([0, 1], [1024], [1025], s)
+    assert lib.pkv_cascade_prefix_attention(None, None, None, None, None, None, 512 + 16, 4, ctypes.byref(s), None, 0, None) == -3
+    huge = shape(P, block_size=256, num_blocks=1 << 28)
+    assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, ctypes.byref(huge), None) == -1
+
+
 def test_fp8_entry_points_validate_before_launching(P):
     lib = P.lib()
     s = shape(P)

@@ -51,7 +51,7 @@ class DeviceFp8:
         self.c = c
         self.k_cache, self.v_cache = dev8(c.k_cache), dev8(c.v_cache)
         self.k_scale, self.v_scale = devf(c.k_scale), devf(c.v_scale)
-        self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride)
+        self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride, block_size=wl.block_size)
         max_seq = max(int(s.seq_lens.max()) for s in wl.steps)
         max_t = max(s.num_tokens for s in wl.steps)
         max_b = max(s.num_seqs for s in wl.steps)
@@ -241,7 +241,7 @@ def _fp8_cascade_check(wl, rows=None):
                                               dev32(cv.prefix_block_table), cv.prefix_len, d.shape, cws)
     pb = cv.prefix_blocks(bs)
     sbt = np.ascontiguousarray(st.block_tables[:, pb:])
-    sshape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, sbt.shape[1])
+    sshape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, sbt.shape[1], block_size=wl.block_size)
     plan = P.plan_varlen(d.ws, st.query_start_loc, cv.suffix_context_lens, cv.suffix_seq_lens, sshape)
     l_s = torch.empty((st.num_tokens, wl.num_q_heads), dtype=torch.float32, device="cuda")
     o_s = P.paged_attention_varlen_fp8(
@@ -275,3 +275,13 @@ def test_fp8_decode_full_size_sampled():
 def test_fp8_mixed_full_size_sampled():
     say("fp8 mixed batch full size (64 decode rows, ctx 128..4096), sampled rows")
     run_and_check_fp8(W.mixed_llama8b(seed=0), rows_per_step=64, seed=0, check_pools=False)
+
+
+@pytest.mark.parametrize("case", ["mixed", "decode"])
+def test_fp8_block_size_256_parity(case):
+    """fp8 pools of 256-token blocks (one scale per 256-token block and kv head)."""
+    say(f"fp8, 256-token blocks: {case}")
+    if case == "mixed":
+        run_and_check_fp8(W.mixed_llama8b(seed=31, num_decode=10, ctx_range=(20, 900), block_size=256), seed=31)
+    else:
+        run_and_check_fp8(W.decode_only(seed=32, num_seqs=20, ctx_range=(30, 5000), block_size=256), seed=32)

@@ -311,7 +311,7 @@ def _cascade_check(wl, rows=None):
     # suffix pass: the same varlen kernel over the suffix view of the block tables
     pb = cv.prefix_blocks(bs)
     sbt_np = np.ascontiguousarray(st.block_tables[:, pb:])
-    sshape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, sbt_np.shape[1])
+    sshape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, sbt_np.shape[1], block_size=wl.block_size)
     sctx, sseq = dev32(cv.suffix_context_lens), dev32(cv.suffix_seq_lens)
     plan = P.plan_varlen(dw.ws, st.query_start_loc, cv.suffix_context_lens, cv.suffix_seq_lens, sshape)
     l_s = torch.empty((st.num_tokens, wl.num_q_heads), dtype=torch.float32, device="cuda")
@@ -399,3 +399,43 @@ def test_cascade_full_size_sampled():
 def test_long_chunked_prefill_full_size_sampled():
     say("long_chunked_prefill full size (32768-token prompt in 16 chunks + 128 decode rows), sampled")
     run_and_check(W.long_chunked_prefill(seed=0), rows_per_step=24, check_pools=False, want_lse=False)
+
+
+# ---------------------------------------------------------------------------
+# 256-token blocks: the same kernels, block tables naming blocks of 16 tiles
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", ["mixed", "decode", "wide"])
+def test_block_size_256_parity(case):
+    say(f"256-token blocks: {case}")
+    if case == "mixed":
+        run_and_check(W.mixed_llama8b(seed=21, num_decode=12, ctx_range=(20, 900), block_size=256),
+                      expect_tile_rows=128)
+    elif case == "decode":
+        run_and_check(W.decode_only(seed=22, num_seqs=24, ctx_range=(30, 6000), block_size=256))
+    else:
+        wl = W.long_chunked_prefill(seed=23, prompt=4096, chunk=2048, num_decode=8, decode_ctx=300, block_size=256)
+        run_and_check(wl, rows_per_step=200, expect_tile_rows=256)
+
+
+def test_block_size_256_cascade():
+    say("256-token blocks: cascade prefix + suffix + merge")
+    _cascade_check(W.cascade_shared_prefix(seed=24, num_queries=40, prefix=1024, suffix_range=(1, 300),
+                                           block_size=256))
+
+
+def test_block_size_256_copy_blocks_bitwise():
+    say("256-token blocks: copy_blocks")
+    wl = W.mixed_llama8b(seed=25, num_decode=8, ctx_range=(100, 3000), block_size=256)
+    dw = DeviceWorkload(wl)
+    perm = np.random.default_rng(25).permutation(wl.num_blocks)
+    n = wl.num_blocks // 2
+    pairs = np.stack([perm[:n], perm[n:2 * n]], axis=1).astype(np.int32)
+    P.copy_blocks(dw.k_cache, dw.v_cache, dev32(pairs), dw.shape)
+    torch.cuda.synchronize()
+    kc, vc = O.copy_blocks(wl.k_cache, wl.v_cache, pairs)
+    assert np.array_equal(host16(dw.k_cache), kc) and np.array_equal(host16(dw.v_cache), vc)
+
+
+def test_block_size_256_full_size_decode_sampled():
+    say("256-token blocks: decode_only full size, sampled rows")
+    run_and_check(W.decode_only(seed=0, block_size=256), rows_per_step=48, check_pools=False)
