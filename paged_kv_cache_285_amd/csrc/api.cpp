@@ -81,7 +81,7 @@ VarlenLayout varlen_layout(int64_t items, int64_t tokens, int64_t partials, int6
   VarlenLayout L;
   L.items_off = 0;
   L.split_off = align256(L.items_off + (size_t)items * sizeof(pkv::WorkItem));
-  L.plse_off = align256(L.split_off + (size_t)tokens * 2 * sizeof(int32_t));
+  L.plse_off = align256(L.split_off + (size_t)tokens * 3 * sizeof(int32_t));
   L.po_off = align256(L.plse_off + (size_t)partials * Hq * sizeof(float));
   L.total = align256(L.po_off + (size_t)partials * Hq * D * sizeof(float));
   return L;
@@ -96,7 +96,7 @@ int decode_target_wgs() {
 
 struct Plan {
   std::vector<pkv::WorkItem> items;
-  std::vector<int32_t> token_split;  // per token {partial_base, count}
+  std::vector<int32_t> token_split;  // per token {first partial row, count, row stride}
   int32_t num_partials = 0;
   int32_t bps = 0;
   int32_t tile_rows = pkv::kTileRows;
@@ -149,7 +149,12 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
   }
   P.bps = bps;
   P.items.clear();
-  P.token_split.assign((size_t)num_tokens * 2, 0);
+  P.token_split.assign((size_t)num_tokens * 3, 0);
+  for (int32_t t = 0; t < num_tokens; ++t) {
+    P.token_split[3 * t] = -1;
+    P.token_split[3 * t + 1] = 1;
+    P.token_split[3 * t + 2] = 1;
+  }
   std::vector<pkv::WorkItem> pre, dec;
   int32_t partials = 0;
   for (int r = 0; r < num_seqs; ++r) {
@@ -160,11 +165,8 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
       const int32_t splits = (int32_t)ceil_div(nblk, bps);
       const int32_t t = qsl[r];
       if (splits > 1) {
-        P.token_split[2 * t] = partials;
-        P.token_split[2 * t + 1] = splits;
-      } else {
-        P.token_split[2 * t] = -1;
-        P.token_split[2 * t + 1] = 1;
+        P.token_split[3 * t] = partials;
+        P.token_split[3 * t + 1] = splits;
       }
       for (int32_t sidx = 0; sidx < splits; ++sidx) {
         pkv::WorkItem it;
@@ -181,6 +183,34 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
       if (splits > 1) partials += splits;
     } else {
       const int32_t tiles = (int32_t)ceil_div(ql, tok_per_tile);
+      // A short row over a long context (one 128-row tile of at most kSplitRowsMax rows) is
+      // cut into key splits: token t of split s writes partial row base + s * ql + t, and the
+      // reduce merges the splits of each token (stride ql).
+      const bool cut = P.tile_rows == pkv::kTileRows && (int64_t)ql * G <= pkv::kSplitRowsMax &&
+                       seq[r] > pkv::kPrefillSplitKeys;
+      if (cut) {
+        const int32_t splits = (int32_t)ceil_div(seq[r], pkv::kPrefillSplitKeys);
+        for (int32_t i = 0; i < ql; ++i) {
+          const int32_t t = qsl[r] + i;
+          P.token_split[3 * t] = partials + i;
+          P.token_split[3 * t + 1] = splits;
+          P.token_split[3 * t + 2] = ql;
+        }
+        for (int32_t sidx = 0; sidx < splits; ++sidx) {
+          pkv::WorkItem it;
+          it.seq = r;
+          it.kind = pkv::kPrefill;
+          it.q_begin = 0;
+          it.q_count = ql;
+          it.kv_begin = sidx * pkv::kPrefillSplitKeys;
+          it.kv_end = std::min<int32_t>(seq[r], (sidx + 1) * pkv::kPrefillSplitKeys);
+          it.partial_base = partials + sidx * ql;
+          it.split = sidx;
+          pre.push_back(it);
+        }
+        partials += splits * ql;
+        continue;
+      }
       for (int32_t i = 0; i < tiles; ++i) {
         pkv::WorkItem it;
         it.seq = r;
@@ -377,9 +407,12 @@ size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t m
   if (check_shape(shape) != PKV_OK || num_seqs < 0 || num_tokens < 0 || max_seq_len < 0) return 0;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   const int64_t per_row = ceil_div(ceil_div(max_seq_len, pkv::kBlockSize), pkv::kMinBlocksPerSplit);
+  // Key splits of short multi-token rows: at most kSplitRowsMax / G tokens per such row.
+  const int64_t cut_splits = ceil_div(max_seq_len, pkv::kPrefillSplitKeys);
+  const int64_t cut_tokens = std::min<int64_t>(num_tokens, (int64_t)num_seqs * std::max(1, pkv::kSplitRowsMax / G));
   const int64_t items = ceil_div((int64_t)num_tokens * G, 128) + num_seqs +
-                        (int64_t)num_seqs * std::max<int64_t>(1, per_row);
-  const int64_t partials = (int64_t)num_seqs * std::max<int64_t>(1, per_row);
+                        (int64_t)num_seqs * std::max<int64_t>(1, per_row) + (int64_t)num_seqs * cut_splits;
+  const int64_t partials = (int64_t)num_seqs * std::max<int64_t>(1, per_row) + cut_tokens * cut_splits;
   return varlen_layout(items, num_tokens, partials, shape->num_q_heads, shape->head_dim).total;
 }
 

@@ -78,11 +78,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Blocks of an fp8 decode item kept in flight per wave (1 or 2).
-#ifndef PKV_DECODE_DEPTH_FP8
-#define PKV_DECODE_DEPTH_FP8 2
-#endif
-
 // 16-byte load with the streaming (non-temporal) cache policy: for K/V bytes read once.
 #ifndef PKV_DECODE_NT
 #define PKV_DECODE_NT 1
@@ -227,7 +222,50 @@ struct DecodeSmem {
   static constexpr int BYTES = (O_FLOATS + ML_FLOATS) * 4 + NW * SCR_BYTES;
 };
 
-template <int D, int G, int NW, bool FP8>
+// Merges the NW per-wave states of a decode item (unnormalised o [NW][G][D], running max m
+// (log2 units) and row sum l [NW][G] in LDS) and stores the output and LSE, or the item's
+// split-KV partial state.
+template <int D, int G, int NW>
+__device__ __forceinline__ void decode_merge(const VarlenArgs& a, const WorkItem& it, int g, int token,
+                                             char* smem_raw) {
+  constexpr int CH = D / 8;
+  using SM = DecodeSmem<D, G, NW>;
+  const float* s_o = reinterpret_cast<const float*>(smem_raw);
+  const float* s_m = s_o + SM::O_FLOATS;
+  const float* s_l = s_m + NW * G;
+  const int Hq = a.num_q_heads;
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < G * CH) {
+    const int hh = t / CH, cc = t % CH;
+    float mm = -INFINITY, ll = 0.f, oo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oo[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float* src = s_o + (w * G + hh) * D + cc * 8;
+      float o2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o2[e] = src[e];
+      merge_state<8>(mm, ll, oo, s_m[w * G + hh], s_l[w * G + hh], o2);
+    }
+    const float inv = (ll > 0.f) ? 1.f / ll : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oo[e] *= inv;
+    const float lse = (ll > 0.f) ? (mm + __log2f(ll)) * kLn2 : -INFINITY;
+    const int head = g * G + hh;
+    if (it.partial_base < 0) {
+      store8(a.out, a.out_f32, ((int64_t)token * Hq + head) * D + cc * 8, oo);
+      if (a.lse && cc == 0) a.lse[(int64_t)token * Hq + head] = lse;
+    } else {
+      const int64_t prow = (int64_t)(it.partial_base + it.split) * Hq + head;
+      store8(a.part_o, 1, prow * D + cc * 8, oo);
+      if (cc == 0) a.part_lse[prow] = lse;
+    }
+  }
+}
+
+template <int D, int G, int NW, bool FP8, int DEPTH>
 __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char* smem_raw) {
   constexpr int CH = D / 8;    // 16-byte chunks per key row
   constexpr int CPT = D / 64;  // chunks of one key a lane holds
@@ -253,12 +291,16 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   const int my_hh = n0 >> 1;  // the same head for both scores when NK == 2
   const bool owner = (c & ((1 << DUP) - 1)) == 0;
 
+  // fp8 pools with D = 128: a key row is 128 bytes, so lane c reads dims 16c .. 16c+15 of its
+  // tokens with one 16-byte load (8 lanes cover the row, a wave load covers whole cache lines);
+  // otherwise lane c holds dims 8c + 64k.  The query chunks follow the same dims.
+  constexpr bool WIDEK = FP8 && CPT == 2;
   uint4 qv[G][CPT];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
 #pragma unroll
     for (int k = 0; k < CPT; ++k)
-      qv[hh][k] = reinterpret_cast<const uint4*>(a.q + ((int64_t)token * Hq + g * G + hh) * D)[c + 8 * k];
+      qv[hh][k] = reinterpret_cast<const uint4*>(a.q + ((int64_t)token * Hq + g * G + hh) * D)[WIDEK ? 2 * c + k : c + 8 * k];
 
   float m[G];        // wave-uniform running max per head (log2 units of scaled scores)
   float o[G][RPL];   // P.V accumulators: head hh, V^T row (lane >> 1) + 32 i, token half
@@ -306,10 +348,20 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
     const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
     const C8* kp = kb + phys * blk_stride;
     const C8* vp = vb + phys * blk_stride;
+    if constexpr (WIDEK) {
+      const uint4* kp4 = reinterpret_cast<const uint4*>(kp);
 #pragma unroll
-    for (int ts = 0; ts < 2; ++ts)
+      for (int ts = 0; ts < 2; ++ts) {
+        const uint4 x = ld_stream(kp4 + (grp + 8 * ts) * (CH / 2) + c);
+        kr[2 * ts] = C8{x.x, x.y};
+        kr[2 * ts + 1] = C8{x.z, x.w};
+      }
+    } else {
 #pragma unroll
-      for (int cc = 0; cc < CPT; ++cc) kr[ts * CPT + cc] = ld_stream(kp + (grp + 8 * ts) * CH + c + 8 * cc);
+      for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) kr[ts * CPT + cc] = ld_stream(kp + (grp + 8 * ts) * CH + c + 8 * cc);
+    }
 #pragma unroll
     for (int i = 0; i < RPL; ++i) vr[i] = ld_stream(vp + lane + 64 * i);
   };
@@ -441,9 +493,9 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
 
   // Software pipeline: the next block's loads are in flight while the current one computes.
   // The steady-state loads are unconditional so the compiler's wait counts only ever wait
-  // for the block about to be used (a conditional load would make it wait for both).  An
-  // fp8 block is half the bytes, so fp8 pools keep two blocks in flight instead of one.
-  if constexpr (FP8 && PKV_DECODE_DEPTH_FP8 == 2) {
+  // for the block about to be used (a conditional load would make it wait for both).  DEPTH
+  // blocks stay in flight per wave: 2 for fp8 blocks (half the bytes), else 1.
+  if constexpr (DEPTH == 2) {
     if (nk > 0) {
       C8 k0[NKR], v0[RPL], k1[NKR], v1[RPL], k2[NKR], v2[RPL];
       load(0, k0, v0);
@@ -517,35 +569,7 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
       s_l[wave * G + hh] = lh;
     }
   }
-  __syncthreads();
-  const int t = threadIdx.x;
-  if (t < G * CH) {
-    const int hh = t / CH, cc = t % CH;
-    float mm = -INFINITY, ll = 0.f, oo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) oo[e] = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float* src = s_o + (w * G + hh) * D + cc * 8;
-      float o2[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o2[e] = src[e];
-      merge_state<8>(mm, ll, oo, s_m[w * G + hh], s_l[w * G + hh], o2);
-    }
-    const float inv = (ll > 0.f) ? 1.f / ll : 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) oo[e] *= inv;
-    const float lse = (ll > 0.f) ? (mm + __log2f(ll)) * kLn2 : -INFINITY;
-    const int head = g * G + hh;
-    if (it.partial_base < 0) {
-      store8(a.out, a.out_f32, ((int64_t)token * Hq + head) * D + cc * 8, oo);
-      if (a.lse && cc == 0) a.lse[(int64_t)token * Hq + head] = lse;
-    } else {
-      const int64_t prow = (int64_t)(it.partial_base + it.split) * Hq + head;
-      store8(a.part_o, 1, prow * D + cc * 8, oo);
-      if (cc == 0) a.part_lse[prow] = lse;
-    }
-  }
+  decode_merge<D, G, NW>(a, it, g, token, smem_raw);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -591,7 +615,7 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
                           const float* __restrict__ v_scale, int Hkv, int g,
                           const int32_t* __restrict__ bt, int L, int tok0, int ntok, int pos0,
                           int kv_begin, int kv_end, float sl, void* out, int out_f32, float* lse_out,
-                          char* smem_raw) {
+                          int orow0, char* smem_raw) {
   using S = TileSmem<D>;
   constexpr int KSTEPS = D / 16;  // QK^T contraction steps
   constexpr int DT = D / 32;      // output d tiles
@@ -608,6 +632,7 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
   const int hh = pr % G;
   const bool row_valid = tq < ntok;
   const int qpos = row_valid ? pos0 + tq : 0x7fffffff;
+  const bool wave_active = wave * 32 < ntok * G;  // wave-uniform
 
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
 
@@ -747,99 +772,103 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
     const uint16_t* ks = smem + buf * S::BUF_ELEMS;
     const uint16_t* vs = ks + S::K_ELEMS;
 
-    // S^T = K Q^T: two 32-key row tiles, their MFMA chains interleaved.
-    floatx16 sacc[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(ks + (32 * mt + n) * S::KP + 16 * s + 8 * h);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sacc[mt], 0, 0, 0);
-      }
-
-    // Mask (raw scores): only tiles reaching past the first row's position or the sequence end.
-    const bool need_mask = (k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > min_pos);
-    if (need_mask) {
+    // A wave whose 32 rows are all padding (a tile of a short row, such as a speculative-verify
+    // row of 1 + k tokens) only helps stage the tiles.
+    if (wave_active) {
+      // S^T = K Q^T: two 32-key row tiles, their MFMA chains interleaved.
+      floatx16 sacc[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
-          const bool vis = key < kv_end && (!CAUSAL || key <= qpos);
-          sacc[mt][e] = vis ? sacc[mt][e] : -INFINITY;
+        for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 ka =
+              *reinterpret_cast<const bf16x8*>(ks + (32 * mt + n) * S::KP + 16 * s + 8 * h);
+          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sacc[mt], 0, 0, 0);
         }
-    }
 
-    // Online softmax for this lane's query column.  The running max m (log2 units of scaled
-    // scores) is only raised when a score exceeds it by more than kLazy, for every lane at
-    // once, so the 64-register rescale of the output is rare; p stays <= 2^kLazy.  With fp8
-    // pools, key block b of the tile (scores sacc[b >> 1][8 (b & 1) ..]) has score scale
-    // sl * k_scale[b], and its p are multiplied by v_scale[b] before the P.V.
-    float slk[4], svb[4];
-    float mx = -INFINITY;
-    if constexpr (FP8) {
-      const TileScales tsc = read_scales(scl + 8 * buf);
-      float mb[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      // Mask (raw scores): only tiles reaching past the first row's position or the sequence end.
+      const bool need_mask = (k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > min_pos);
+      if (need_mask) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mb[2 * mt + (e >> 3)] = fmaxf(mb[2 * mt + (e >> 3)], sacc[mt][e]);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        slk[b] = sl * tsc.k[b];
-        svb[b] = tsc.v[b];
-        mx = fmaxf(mx, mb[b] * slk[b]);
+          for (int e = 0; e < 16; ++e) {
+            const int key = k0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+            const bool vis = key < kv_end && (!CAUSAL || key <= qpos);
+            sacc[mt][e] = vis ? sacc[mt][e] : -INFINITY;
+          }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-    } else {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) slk[b] = sl, svb[b] = 1.f;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl;
-    }
-    if (__ballot(mx > m + kLazy) != 0) {
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
-      lsum *= alpha;
-#pragma unroll
-      for (int d = 0; d < DT; ++d)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
-      m = mn;
-    }
-    const float mref = (m == -INFINITY) ? 0.f : m;
 
-    // P^T operands: K-step ks covers keys 32*(ks/2) + 8*jj0 + 0..15, jj0 = 2*(ks%2).  The row
-    // sum is accumulated in fp32 (a sum of the bf16-rounded p would cost ~1e-3 in the LSE).
-    bf16x8 pb[4];
+      // Online softmax for this lane's query column.  The running max m (log2 units of scaled
+      // scores) is only raised when a score exceeds it by more than kLazy, for every lane at
+      // once, so the 64-register rescale of the output is rare; p stays <= 2^kLazy.  With fp8
+      // pools, key block b of the tile (scores sacc[b >> 1][8 (b & 1) ..]) has score scale
+      // sl * k_scale[b], and its p are multiplied by v_scale[b] before the P.V.
+      float slk[4], svb[4];
+      float mx = -INFINITY;
+      if constexpr (FP8) {
+        const TileScales tsc = read_scales(scl + 8 * buf);
+        float mb[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int mt = ks >> 1, b0 = 8 * (ks & 1);
-      bf16x8 v;
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(fmaf(sacc[mt][b0 + e], slk[ks], -mref));
-        lsum += p;
-        v[e] = (__bf16)(FP8 ? p * svb[ks] : p);
+          for (int e = 0; e < 16; ++e) mb[2 * mt + (e >> 3)] = fmaxf(mb[2 * mt + (e >> 3)], sacc[mt][e]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          slk[b] = sl * tsc.k[b];
+          svb[b] = tsc.v[b];
+          mx = fmaxf(mx, mb[b] * slk[b]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) slk[b] = sl, svb[b] = 1.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl;
       }
-      pb[ks] = v;
-    }
-
-    // O^T += V^T P^T.
+      if (__ballot(mx > m + kLazy) != 0) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
+        lsum *= alpha;
 #pragma unroll
-    for (int d = 0; d < DT; ++d) {
+        for (int d = 0; d < DT; ++d)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+        m = mn;
+      }
+      const float mref = (m == -INFINITY) ? 0.f : m;
+
+      // P^T operands: K-step ks covers keys 32*(ks/2) + 8*jj0 + 0..15, jj0 = 2*(ks%2).  The row
+      // sum is accumulated in fp32 (a sum of the bf16-rounded p would cost ~1e-3 in the LSE).
+      bf16x8 pb[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(vs + (32 * d + n) * S::VP + 16 * ks + 8 * h);
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xv, pb[ks], oacc[d], 0, 0, 0);
+        const int mt = ks >> 1, b0 = 8 * (ks & 1);
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(fmaf(sacc[mt][b0 + e], slk[ks], -mref));
+          lsum += p;
+          v[e] = (__bf16)(FP8 ? p * svb[ks] : p);
+        }
+        pb[ks] = v;
+      }
+
+      // O^T += V^T P^T.
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 xv = *reinterpret_cast<const bf16x8*>(vs + (32 * d + n) * S::VP + 16 * ks + 8 * h);
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xv, pb[ks], oacc[d], 0, 0, 0);
+        }
       }
     }
 
@@ -857,7 +886,7 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
   lsum += __shfl_xor(lsum, 32);
   if (!row_valid) return;
   const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
-  const int64_t orow = (int64_t)(tok0 + tq) * Hq + g * G + hh;
+  const int64_t orow = (int64_t)(orow0 + tq) * Hq + g * G + hh;
 #pragma unroll
   for (int d = 0; d < DT; ++d) {
 #pragma unroll
@@ -1301,15 +1330,20 @@ void varlen_kernel(VarlenArgs a) {
   const int g = x % a.num_kv_heads;
   const WorkItem it = a.items[x / a.num_kv_heads];
   if (DECODE_ONLY || it.kind == kDecode) {
-    decode_item<D, G, NW, FP8>(a, it, g, smem);
+    decode_item<D, G, NW, FP8, FP8 ? 2 : 1>(a, it, g, smem);
   } else {
     const int r = it.seq;
     const int ctx = a.context_lens[r];
     const int tok0 = a.query_start_loc[r] + it.q_begin;
     const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
+    // A key split of a short row writes fp32 partial states (rows partial_base + token) that
+    // the reduce merges; otherwise the tile writes the output rows of its tokens.
+    const bool part = it.partial_base >= 0;
     mfma_tile<D, G, true, NW, FP8>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale,
                                    a.num_kv_heads, g, bt, a.bt_shift, tok0, it.q_count, ctx + it.q_begin,
-                                   it.kv_begin, it.kv_end, a.scale_log2, a.out, a.out_f32, a.lse, smem);
+                                   it.kv_begin, it.kv_end, a.scale_log2, part ? (void*)a.part_o : a.out,
+                                   part ? 1 : a.out_f32, part ? a.part_lse : a.lse,
+                                   part ? it.partial_base : tok0, smem);
   }
 }
 
@@ -1368,9 +1402,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   int64_t base, stride;
   int count;
   if (a.token_split) {
-    base = a.token_split[2 * token];
-    count = a.token_split[2 * token + 1];
-    stride = 1;
+    base = a.token_split[3 * token];
+    count = a.token_split[3 * token + 1];
+    stride = a.token_split[3 * token + 2];
     if (count <= 1) return;  // written directly by the attention kernel
   } else {
     base = token;

@@ -13,6 +13,11 @@ constexpr int kTileRows = 128;       // packed (token, q head) rows of a varlen 
 constexpr int kWideTileRows = 256;   // rows of a wide tile (prefill-heavy batches, cascade)
 constexpr int kPrefillRowsForWideTiles = 2048;  // packed prefill rows from which wide tiles pay
 constexpr int kMinBlocksPerSplit = 16;
+// Short multi-token rows (at most kSplitRowsMax packed (token, q head) rows, such as
+// speculative-verify rows) over a long context are cut into key splits of kPrefillSplitKeys
+// keys, so that no workgroup walks a whole long context alone.
+constexpr int kSplitRowsMax = 64;
+constexpr int kPrefillSplitKeys = 1024;
 
 enum ItemKind : int32_t { kDecode = 0, kPrefill = 1 };
 
@@ -24,8 +29,10 @@ struct WorkItem {
   int32_t q_count;       // prefill: query tokens in the tile; decode: splits of the row
   int32_t kv_begin;      // first key (token index) of this item
   int32_t kv_end;        // one past the last key
-  int32_t partial_base;  // decode: partial row base of the request (-1: write the output)
-  int32_t split;         // decode: split index within the request
+  int32_t partial_base;  // -1: write the output; decode: partial row base of the request, the
+                         // item writes row partial_base + split; prefill: the partial row of the
+                         // tile's first token for this split, token t writes partial_base + t
+  int32_t split;         // split index within the request (or tile)
 };
 static_assert(sizeof(WorkItem) == 32, "work item layout");
 
@@ -79,7 +86,7 @@ struct CascadeArgs {
 struct ReduceArgs {
   const float* part_o;
   const float* part_lse;
-  const int32_t* token_split;  // per token {partial_base, count}; nullptr: uniform layout
+  const int32_t* token_split;  // per token {first partial row, count, row stride}; nullptr: uniform layout
   int32_t uniform_count;       // uniform layout: partial row of split s = (s * T + token)
   int32_t num_tokens;
   int32_t num_q_heads;

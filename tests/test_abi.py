@@ -122,8 +122,14 @@ def test_plan_covers_every_row_exactly_once(P, lengths):
     tok_per_tile = plan.tile_rows // G
     cover_tok = np.zeros(int(qsl[-1]), int)
     dec_keys = {}
+    cut_keys = {}
     for seqi, kind, qb, qc, kb, ke, pbase, split in items:
-        if kind == 1:
+        if kind == 1 and pbase >= 0:
+            # a key split of a short row: the whole row, keys [kb, ke), partial rows pbase + t
+            assert ql[seqi] * G <= 64 and qb == 0 and qc == ql[seqi] and seq[seqi] > 1024
+            cover_tok[qsl[seqi] : qsl[seqi] + qc] += split == 0
+            cut_keys.setdefault(seqi, []).append((kb, ke, pbase, split))
+        elif kind == 1:
             assert ql[seqi] > 1 and 0 < qc <= tok_per_tile
             cover_tok[qsl[seqi] + qb : qsl[seqi] + qb + qc] += 1
             assert kb == 0 and ke == min(seq[seqi], ctx[seqi] + qb + qc)
@@ -132,6 +138,16 @@ def test_plan_covers_every_row_exactly_once(P, lengths):
             cover_tok[qsl[seqi]] += split == 0
             dec_keys.setdefault(seqi, []).append((kb, ke, pbase, split, qc))
     assert (cover_tok == 1).all()
+    partial_rows = []
+    for r, ranges in cut_keys.items():
+        ranges.sort()
+        assert ranges[0][0] == 0 and ranges[-1][1] == seq[r] and len(ranges) == -(-seq[r] // 1024)
+        for i, (a, b) in enumerate(zip(ranges, ranges[1:])):
+            assert a[1] == b[0] == 1024 * (i + 1)
+        base = ranges[0][2]
+        for i, x in enumerate(ranges):
+            assert x[3] == i and x[2] == base + i * ql[r]
+        partial_rows += list(range(base, base + len(ranges) * ql[r]))
     for r, ranges in dec_keys.items():
         ranges.sort()
         assert ranges[0][0] == 0 and ranges[-1][1] == seq[r]
@@ -140,6 +156,10 @@ def test_plan_covers_every_row_exactly_once(P, lengths):
         assert all(x[3] == i and x[4] == len(ranges) for i, x in enumerate(ranges))
         if len(ranges) == 1:
             assert ranges[0][2] == -1
+        else:
+            partial_rows += list(range(ranges[0][2], ranges[0][2] + len(ranges)))
+    # every partial row belongs to exactly one (token, split)
+    assert sorted(partial_rows) == list(range(plan.num_partials))
     # heaviest first within each kind
     pre = items[items[:, 1] == 1]
     cost = pre[:, 3].astype(np.int64) * (pre[:, 5] - pre[:, 4])

@@ -221,6 +221,11 @@ def test_fp8_spec_verify_small_parity():
     run_and_check_fp8(W.spec_verify(seed=5, num_seqs=12, draft=4, ctx_range=(40, 900)), seed=5)
 
 
+def test_fp8_spec_verify_long_context_parity():
+    say("fp8 speculative verification rows over long contexts (key splits)")
+    run_and_check_fp8(W.spec_verify(seed=6, num_seqs=8, ctx_range=(1100, 2600)), seed=6)
+
+
 def test_fp8_cascade_small_parity():
     """fp8 prefix pass, fp8 suffix pass and the merge against the oracle's prefix state and its
     single-pass attention over the dequantised pools."""

@@ -126,6 +126,16 @@ def test_spec_verify_small_parity():
     run_and_check(W.spec_verify(seed=3, num_seqs=4, draft=7, ctx_range=(1100, 3000)))
 
 
+def test_short_rows_split_at_key_boundaries():
+    """Short rows cut into 1024-key splits, with contexts placed so that the last split starts
+    before, at, and after the first query's position (a token can see no key of a split)."""
+    say("short rows over long contexts: split boundaries")
+    ctxs = [1019, 1020, 1023, 1024, 1025, 2043, 2047, 2048, 3071, 1100]
+    reqs = [W.RequestSpec(c, [5]) for c in ctxs] + [W.RequestSpec(1500, [16]), W.RequestSpec(1030, [2])]
+    wl = W.build("short_rows", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=13)
+    run_and_check(wl)
+
+
 def test_spec_verify_full_size_sampled():
     say("spec_verify full: 64 rows of 5 tokens, ctx U[1024, 4096], sampled rows")
     run_and_check(W.spec_verify(seed=0), rows_per_step=48, check_pools=False)
