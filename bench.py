@@ -319,6 +319,57 @@ def fp8_decode_hbm(torch, P, steps=10, warmup=3, bf16_ms=None):
     return res
 
 
+def decode_graph_step(torch, P, reps=50):
+    """A small decode step (16 rows, context 512..2048: fused cache write + device-split decode +
+    reduce) issued eagerly vs replayed from a HIP graph captured once: per-step wall time."""
+    import workloads as W
+
+    wl = W.decode_only(seed=7, num_seqs=16, ctx_range=(512, 2048))
+    st = wl.steps[0]
+    r = Runner(wl, torch, P)
+    s = r.steps[0]
+    max_seq = wl.bt_stride * wl.block_size
+    ws = P.alloc_workspace(P.decode_workspace_size(st.num_seqs, max_seq, r.shape))
+    lse = torch.empty(st.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def step():
+        P.append_kv(s["k"], s["v"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"], r.shape)
+        P.paged_attention_decode(s["q"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["seq"], r.shape, max_seq,
+                                 workspace=ws, out=s["out"], lse=lse)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    eager_us = timed(step)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.synchronize()
+    graph_us = timed(g.replay)
+    out = {
+        "workload": "decode step, 16 rows, ctx U[512,2048], 32q/8kv, D128: append_kv + paged_attention_decode",
+        "eager_us_per_step": eager_us,
+        "graph_us_per_step": graph_us,
+        "speedup": eager_us / graph_us,
+    }
+    del r, g
+    torch.cuda.empty_cache()
+    return out
+
+
 def spec_verify_hbm(torch, P, reps=10):
     """Speculative-verify batch (64 rows of 1 + 4 tokens, context 1024..4096): varlen launch
     GB/s against 8 TB/s (the five query tokens of a row share every K/V byte)."""
@@ -592,6 +643,7 @@ def main():
         log("bench: speculative-verify batch, tiny prefill")
         line["spec_verify_hbm"] = spec_verify_hbm(torch, P)
         line["tiny_prefill"] = tiny_prefill_latency(torch, P)
+        line["decode_graph_step"] = decode_graph_step(torch, P)
     if args.mfma:
         log("bench: MFMA paths (cascade prefix, long chunked prefill)")
         line["mfma_paths"] = mfma_paths(torch, P)

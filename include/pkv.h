@@ -215,6 +215,38 @@ int pkv_paged_attention_varlen_fp8(void* out, int32_t out_dtype, float* lse, con
                                    const pkv_shape* shape, const pkv_varlen_plan* plan,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Graph-capturable decode step (f4) -----------------------------------------------------
+ * Recording a step once and replaying it saves the per-launch CPU cost; the recording needs
+ * fixed shapes, so batches are padded up to a few bucketed sizes (1, 2, 4, ..., 512) ["11. vLLM
+ * principles", section 11.5].  pkv_paged_attention_decode is the decode part of
+ * pkv_paged_attention_varlen for batches of one query token per row, with no host plan: its
+ * launches depend only on (num_seqs, max_seq_len, shape), and block_tables, query_start_loc,
+ * seq_lens and q are read on the device.  So a step captured once in a HIP graph (this call,
+ * after pkv_append_kv) replays correctly for any new metadata written into the same buffers,
+ * as long as every seq_lens[r] <= max_seq_len.  Rows are cut into splits of a fixed key count
+ * chosen from (num_seqs, max_seq_len); splits past a row's end contribute nothing.  A padded row
+ * with seq_lens[r] == 0 gets output 0 and lse -inf. */
+
+/* Workspace bytes for pkv_paged_attention_decode(_fp8) with these sizes (0 if none needed). */
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t max_seq_len, const pkv_shape* shape);
+
+/* Decode attention (a3) for num_seqs rows of one query token each: token query_start_loc[r] of
+ * q attends to keys 0..seq_lens[r]-1 of row r.  out bf16 or fp32 [num_tokens, Hq, D], lse
+ * nullable fp32 [num_tokens, Hq].  Errors as pkv_paged_attention_varlen. */
+int pkv_paged_attention_decode(void* out, int32_t out_dtype, float* lse, const void* q,
+                               const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                               const int32_t* query_start_loc, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t max_seq_len, const pkv_shape* shape,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same over fp8 (e4m3) pools with per-(block, kv head) scales. */
+int pkv_paged_attention_decode_fp8(void* out, int32_t out_dtype, float* lse, const void* q,
+                                   const void* k_cache, const void* v_cache, const float* k_scale,
+                                   const float* v_scale, const int32_t* block_tables,
+                                   const int32_t* query_start_loc, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t max_seq_len, const pkv_shape* shape,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes for pkv_cascade_prefix_attention with these sizes. */
 size_t pkv_cascade_workspace_size(int32_t num_tokens, int32_t prefix_len, const pkv_shape* shape);
 

@@ -16,8 +16,10 @@ from .ops import (  # noqa: F401
     compute_slot_mapping,
     copy_blocks,
     copy_blocks_fp8,
+    decode_workspace_size,
     make_shape,
     merge_attn_states,
+    paged_attention_decode,
     paged_attention_varlen,
     paged_attention_varlen_fp8,
     plan_varlen,

@@ -30,6 +30,9 @@ EXPORTS = (
     "pkv_plan_varlen_host",
     "pkv_paged_attention_varlen",
     "pkv_paged_attention_varlen_fp8",
+    "pkv_decode_workspace_size",
+    "pkv_paged_attention_decode",
+    "pkv_paged_attention_decode_fp8",
     "pkv_cascade_workspace_size",
     "pkv_cascade_prefix_attention",
     "pkv_cascade_prefix_attention_fp8",
@@ -104,6 +107,15 @@ _SIGS = {
     "pkv_paged_attention_varlen_fp8": (
         ctypes.c_int,
         [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _PLAN, _P, _SZ, _P],
+    ),
+    "pkv_decode_workspace_size": (_SZ, [_I32, _I32, _SHAPE]),
+    "pkv_paged_attention_decode": (
+        ctypes.c_int,
+        [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _P, _SZ, _P],
+    ),
+    "pkv_paged_attention_decode_fp8": (
+        ctypes.c_int,
+        [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _P, _SZ, _P],
     ),
     "pkv_cascade_workspace_size": (_SZ, [_I32, _I32, _SHAPE]),
     "pkv_cascade_prefix_attention": (

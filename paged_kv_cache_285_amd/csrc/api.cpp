@@ -683,6 +683,122 @@ int pkv_paged_attention_varlen_fp8(void* out, int32_t out_dtype, float* lse, con
                      shape, plan, workspace, workspace_bytes, stream);
 }
 
+// Work split of a graph-capturable decode batch: the split size the varlen planner would pick
+// if every row had max_seq_len keys (a power of two of 16 to 256 blocks of 16 keys), and the
+// number of splits of the longest row.
+struct DecodeSplit {
+  int32_t splits, split_keys;
+};
+static DecodeSplit decode_split(int32_t num_seqs, int32_t max_seq_len, const pkv_shape* s) {
+  const int64_t blocks = ceil_div(std::max(max_seq_len, 1), pkv::kBlockSize);
+  int64_t bps = pkv::kMinBlocksPerSplit;
+  while (bps < 256 && (int64_t)num_seqs * ceil_div(blocks, bps) * s->num_kv_heads > decode_target_wgs()) bps *= 2;
+  DecodeSplit d;
+  d.split_keys = (int32_t)(bps * pkv::kBlockSize);
+  d.splits = (int32_t)ceil_div(std::max(max_seq_len, 1), d.split_keys);
+  return d;
+}
+
+static size_t decode_bytes(int32_t num_seqs, const DecodeSplit& d, const pkv_shape* s) {
+  if (d.splits <= 1) return 0;
+  const size_t rows = (size_t)d.splits * num_seqs * s->num_q_heads;
+  return align256(rows * sizeof(float)) + align256(rows * s->head_dim * sizeof(float));
+}
+
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t max_seq_len, const pkv_shape* shape) {
+  if (check_shape(shape) != PKV_OK || num_seqs < 0 || max_seq_len < 0) return 0;
+  return decode_bytes(num_seqs, decode_split(num_seqs, max_seq_len, shape), shape);
+}
+
+static int decode_impl(void* out, int32_t out_dtype, float* lse, const void* q, const void* k_cache,
+                       const void* v_cache, const float* k_scale, const float* v_scale, bool fp8,
+                       const int32_t* block_tables, const int32_t* query_start_loc,
+                       const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                       const pkv_shape* shape, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (out_dtype != PKV_DTYPE_BF16 && out_dtype != PKV_DTYPE_F32)
+    return fail(PKV_EINVAL, "out_dtype %d unsupported", out_dtype);
+  if (num_seqs < 0 || max_seq_len < 0) return fail(PKV_EINVAL, "negative sizes");
+  if (ceil_div(max_seq_len, shape->block_size) > shape->bt_stride)
+    return fail(PKV_EINVAL, "max_seq_len %d needs more than bt_stride=%d blocks", max_seq_len,
+                shape->bt_stride);
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !seq_lens ||
+      (fp8 && (!k_scale || !v_scale)))
+    return fail(PKV_EINVAL, "null pointer argument");
+  const DecodeSplit d = decode_split(num_seqs, max_seq_len, shape);
+  const size_t need = decode_bytes(num_seqs, d, shape);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_EWORKSPACE, "decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  pkv::VarlenArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.query_start_loc = query_start_loc;
+  a.context_lens = nullptr;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.out_f32 = out_dtype == PKV_DTYPE_F32;
+  a.items = nullptr;
+  a.num_items = 0;
+  const size_t rows = (size_t)d.splits * num_seqs * shape->num_q_heads;
+  a.part_lse = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_o = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)))
+                  : nullptr;
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.bt_stride = shape->bt_stride;
+  a.bt_shift = bt_shift(shape);
+  a.scale_log2 = scale_log2(shape);
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (int rc = timing_mark((hipStream_t)stream, true)) return rc;
+  hipError_t e = (fp8 ? pkv::launch_decode_graph_fp8 : pkv::launch_decode_graph)(
+      a, shape->head_dim, G, num_seqs, d.splits, d.split_keys, num_seqs, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (int rc = timing_mark((hipStream_t)stream, false)) return rc;
+  if (d.splits > 1) {
+    pkv::ReduceArgs ra;
+    ra.part_o = a.part_o;
+    ra.part_lse = a.part_lse;
+    ra.token_split = nullptr;
+    ra.uniform_count = d.splits;
+    ra.num_tokens = num_seqs;
+    ra.num_q_heads = shape->num_q_heads;
+    ra.out = out;
+    ra.out_f32 = a.out_f32;
+    ra.lse = lse;
+    e = pkv::launch_reduce(ra, shape->head_dim, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode split reduce launch");
+  }
+  return ok();
+}
+
+int pkv_paged_attention_decode(void* out, int32_t out_dtype, float* lse, const void* q,
+                               const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                               const int32_t* query_start_loc, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t max_seq_len, const pkv_shape* shape,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, out_dtype, lse, q, k_cache, v_cache, nullptr, nullptr, false, block_tables,
+                     query_start_loc, seq_lens, num_seqs, max_seq_len, shape, workspace,
+                     workspace_bytes, stream);
+}
+
+int pkv_paged_attention_decode_fp8(void* out, int32_t out_dtype, float* lse, const void* q,
+                                   const void* k_cache, const void* v_cache, const float* k_scale,
+                                   const float* v_scale, const int32_t* block_tables,
+                                   const int32_t* query_start_loc, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t max_seq_len, const pkv_shape* shape,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, out_dtype, lse, q, k_cache, v_cache, k_scale, v_scale, true, block_tables,
+                     query_start_loc, seq_lens, num_seqs, max_seq_len, shape, workspace,
+                     workspace_bytes, stream);
+}
+
 size_t pkv_cascade_workspace_size(int32_t num_tokens, int32_t prefix_len, const pkv_shape* shape) {
   if (check_shape(shape) != PKV_OK || num_tokens < 0 || prefix_len <= 0) return 0;
   return cascade_bytes(cascade_split(num_tokens, prefix_len, shape), num_tokens, shape);

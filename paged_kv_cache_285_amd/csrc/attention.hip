@@ -1347,6 +1347,32 @@ void varlen_kernel(VarlenArgs a) {
   }
 }
 
+// Decode batch with a device-side work split, for graph capture: the grid depends only on
+// (num_seqs, splits), each workgroup takes row x / (splits * Hkv), split (x / Hkv) % splits and
+// kv head x % Hkv, and reads the row's length from seq_lens on the device.  A split past the
+// row's end is an empty state (lse -inf) that the reduce weights by zero; a row of length 0
+// gets output 0 and lse -inf.  Partial rows are laid out split-major (split * T + token).
+template <int D, int G, bool FP8>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(G >= 8 ? PKV_DECODE_WAVES_G8 : PKV_DECODE_WAVES)))
+void decode_graph_kernel(VarlenArgs a, int32_t splits, int32_t split_keys, int32_t num_tokens) {
+  extern __shared__ __align__(16) char smem[];
+  const int x = blockIdx.x;
+  const int g = x % a.num_kv_heads;
+  const int s = (x / a.num_kv_heads) % splits;
+  const int r = x / (a.num_kv_heads * splits);
+  WorkItem it;
+  it.seq = r;
+  it.kind = kDecode;
+  it.q_begin = 0;
+  it.q_count = splits;
+  it.kv_begin = s * split_keys;
+  it.kv_end = min(a.seq_lens[r], (s + 1) * split_keys);  // may be <= kv_begin: an empty state
+  it.split = s;
+  it.partial_base = splits > 1 ? s * num_tokens + a.query_start_loc[r] - s : -1;
+  decode_item<D, G, 4, FP8, FP8 ? 2 : 1>(a, it, g, smem);
+}
+
 // Wide-tile kernels: 256-row pipelined tiles on 8 waves (two per SIMD).
 template <int D, int G, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
@@ -1490,6 +1516,17 @@ hipError_t launch_varlen_t(const VarlenArgs& a, int n_prefill, int n_decode, int
 }
 
 template <int D, int G>
+hipError_t launch_decode_graph_t(const VarlenArgs& a, int num_seqs, int splits, int split_keys, int num_tokens,
+                                 hipStream_t stream) {
+  const int64_t grid = (int64_t)num_seqs * splits * a.num_kv_heads;
+  if (grid == 0) return hipSuccess;
+  const size_t smem = varlen_smem<D, G, 4>(false);
+  hipLaunchKernelGGL((decode_graph_kernel<D, G, kFp8>), dim3((unsigned)grid), dim3(256), smem, stream, a, splits,
+                     split_keys, num_tokens);
+  return hipGetLastError();
+}
+
+template <int D, int G>
 hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.num_tiles * a.num_segments * a.num_kv_heads;
   if (grid == 0) return hipSuccess;
@@ -1539,6 +1576,14 @@ hipError_t PKV_KV_NAME(launch_cascade)(const CascadeArgs& a, int head_dim, int g
 #define CALL_C(D, G) launch_cascade_t<D, G>(a, stream)
   PKV_DISPATCH_DG(head_dim, group, CALL_C)
 #undef CALL_C
+}
+
+hipError_t PKV_KV_NAME(launch_decode_graph)(const VarlenArgs& a, int head_dim, int group, int num_seqs,
+                                           int splits, int split_keys, int num_tokens,
+                                           hipStream_t stream) {
+#define CALL_G(D, G) launch_decode_graph_t<D, G>(a, num_seqs, splits, split_keys, num_tokens, stream)
+  PKV_DISPATCH_DG(head_dim, group, CALL_G)
+#undef CALL_G
 }
 
 #if !PKV_KV_FP8

@@ -139,6 +139,13 @@ hipError_t launch_cascade(const CascadeArgs& a, int head_dim, int group, hipStre
 hipError_t launch_varlen_fp8(const VarlenArgs& a, int head_dim, int group, int n_prefill,
                              int n_decode, int tile_rows, hipStream_t stream);
 hipError_t launch_cascade_fp8(const CascadeArgs& a, int head_dim, int group, hipStream_t stream);
+// Decode batch (one query token per row) split into `splits` key ranges of split_keys keys per
+// row, with the split computed on the device (graph-capturable); num_tokens = rows of the
+// partial layout (split * num_tokens + token).
+hipError_t launch_decode_graph(const VarlenArgs& a, int head_dim, int group, int num_seqs, int splits,
+                               int split_keys, int num_tokens, hipStream_t stream);
+hipError_t launch_decode_graph_fp8(const VarlenArgs& a, int head_dim, int group, int num_seqs,
+                                   int splits, int split_keys, int num_tokens, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_merge(void* out, int32_t out_f32, float* lse_out, const float* oa,
                         const float* la, const float* ob, const float* lb, int64_t rows,

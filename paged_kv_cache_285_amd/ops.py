@@ -397,6 +397,56 @@ def paged_attention_varlen_fp8(
     return out
 
 
+def decode_workspace_size(num_seqs: int, max_seq_len: int, shape: PkvShape) -> int:
+    return int(lib().pkv_decode_workspace_size(num_seqs, max_seq_len, ctypes.byref(shape)))
+
+
+def paged_attention_decode(
+    q: torch.Tensor,
+    k_cache: torch.Tensor,
+    v_cache: torch.Tensor,
+    block_tables: torch.Tensor,
+    query_start_loc: torch.Tensor,
+    seq_lens: torch.Tensor,
+    shape: PkvShape,
+    max_seq_len: int,
+    workspace: Optional[torch.Tensor] = None,
+    out: Optional[torch.Tensor] = None,
+    out_dtype: torch.dtype = torch.bfloat16,
+    lse: Optional[torch.Tensor] = None,
+    k_scale: Optional[torch.Tensor] = None,
+    v_scale: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """Decode attention (one query token per row) with the work split on the device: the
+    launches depend only on (rows, max_seq_len), so the call can be captured in a graph and
+    replayed with new metadata in the same buffers.  With k_scale / v_scale the pools are fp8."""
+    num_seqs = int(seq_lens.numel())
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    code = PKV_DTYPE_F32 if out.dtype == torch.float32 else PKV_DTYPE_BF16
+    ws = workspace
+    common = (
+        _dev(block_tables, "block_tables", (torch.int32,)),
+        _dev(query_start_loc, "query_start_loc", (torch.int32,)),
+        _dev(seq_lens, "seq_lens", (torch.int32,)),
+        num_seqs,
+        int(max_seq_len),
+        ctypes.byref(shape),
+        _opt(ws, "workspace", (torch.uint8,)),
+        0 if ws is None else ws.numel(),
+        _stream(),
+    )
+    head = (_dev(out, "out", _16BIT + (torch.float32,)), code, _opt(lse, "lse", (torch.float32,)), _dev(q, "q", _16BIT))
+    if k_scale is None:
+        check(lib().pkv_paged_attention_decode(
+            *head, _dev(k_cache, "k_cache", _16BIT), _dev(v_cache, "v_cache", _16BIT), *common))
+    else:
+        check(lib().pkv_paged_attention_decode_fp8(
+            *head, _dev(k_cache, "k_cache", _FP8), _dev(v_cache, "v_cache", _FP8),
+            _dev(k_scale, "k_scale", _F32), _dev(v_scale, "v_scale", _F32), *common))
+    return out
+
+
 def cascade_workspace_size(num_tokens: int, prefix_len: int, shape: PkvShape) -> int:
     return int(lib().pkv_cascade_workspace_size(num_tokens, prefix_len, ctypes.byref(shape)))
 

@@ -81,6 +81,21 @@ def test_block_size_256_accepted_and_checked(P):
     assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, ctypes.byref(huge), None) == -1
 
 
+def test_decode_entry_points_validate_before_launching(P):
+    lib = P.lib()
+    s = shape(P)  # bt_stride 64 x 16 keys = 1024 keys per row at most
+    z = ctypes.c_void_p(0)
+    assert lib.pkv_paged_attention_decode(z, 0, z, z, z, z, z, z, z, 0, 100, ctypes.byref(s), z, 0, z) == 0
+    assert lib.pkv_paged_attention_decode(z, 0, z, z, z, z, z, z, z, 4, 100, ctypes.byref(s), z, 0, z) == -1
+    assert lib.pkv_paged_attention_decode(z, 0, z, z, z, z, z, z, z, 4, 5000, ctypes.byref(s), z, 0, z) == -1
+    assert b"bt_stride" in lib.pkv_last_error()
+    assert lib.pkv_paged_attention_decode(z, 3, z, z, z, z, z, z, z, 4, 100, ctypes.byref(s), z, 0, z) == -1
+    assert lib.pkv_paged_attention_decode_fp8(z, 0, z, z, z, z, z, z, z, z, z, 4, 100, ctypes.byref(s), z, 0, z) == -1
+    # one split needs no workspace; long rows need partial states
+    assert P.decode_workspace_size(8, 256, s) == 0
+    assert P.decode_workspace_size(256, 8192, shape(P, bt_stride=600)) > 0
+
+
 def test_fp8_entry_points_validate_before_launching(P):
     lib = P.lib()
     s = shape(P)

@@ -226,6 +226,28 @@ def test_fp8_spec_verify_long_context_parity():
     run_and_check_fp8(W.spec_verify(seed=6, num_seqs=8, ctx_range=(1100, 2600)), seed=6)
 
 
+def test_fp8_decode_device_split_parity():
+    say("fp8 decode with device-side split")
+    wl = W.decode_only(seed=43, num_seqs=16, ctx_range=(1, 5000))
+    st = wl.steps[0]
+    d = DeviceFp8(wl, seed=43)
+    t = d.tensors(st)
+    P.append_kv_fp8(t["k"], t["v"], d.k_cache, d.v_cache, d.k_scale, d.v_scale, t["bt"], t["qsl"], t["ctx"], d.shape)
+    max_seq = wl.bt_stride * wl.block_size
+    ws = P.alloc_workspace(P.decode_workspace_size(st.num_seqs, max_seq, d.shape))
+    lse = torch.empty(st.q.shape[:2], dtype=torch.float32, device="cuda")
+    out = P.paged_attention_decode(t["q"], d.k_cache, d.v_cache, t["bt"], t["qsl"], t["seq"], d.shape, max_seq,
+                                   workspace=ws, lse=lse, k_scale=d.k_scale, v_scale=d.v_scale)
+    torch.cuda.synchronize()
+    slots = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, wl.block_size)
+    kp, vp = O.reshape_and_cache_fp8(st.k, st.v, d.c.k_cache, d.c.v_cache, slots, d.c.k_scale, d.c.v_scale,
+                                     wl.block_size)
+    ref, lref = O.paged_attention_fp8(st.q, kp, vp, d.c.k_scale, d.c.v_scale, st.block_tables, st.query_start_loc,
+                                      st.context_lens, st.seq_lens, wl.block_size)
+    check_attention(bf16_out_to_f64(out), ref, "fp8 device-split decode")
+    check_lse(lse.cpu().numpy(), lref, "fp8 device-split decode lse")
+
+
 def test_fp8_cascade_small_parity():
     """fp8 prefix pass, fp8 suffix pass and the merge against the oracle's prefix state and its
     single-pass attention over the dequantised pools."""

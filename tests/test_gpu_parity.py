@@ -184,6 +184,118 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(lse, ref_l), f"replay {rep}: lse differs"
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_decode_device_split_matches_oracle(out_dtype):
+    """Decode with the work split on the device (no host plan): against the oracle, and a row of
+    length 0 gives output 0 and lse -inf."""
+    say(f"decode with device-side split, out {out_dtype}")
+    wl = W.decode_only(seed=41, num_seqs=20, ctx_range=(1, 5000))
+    st = wl.steps[0]
+    dw = DeviceWorkload(wl)
+    t = dw.step_tensors(st)
+    P.append_kv(t["k"], t["v"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], t["ctx"], dw.shape)
+    max_seq = wl.bt_stride * wl.block_size  # the longest row the block tables can hold
+    ws = P.alloc_workspace(P.decode_workspace_size(st.num_seqs, max_seq, dw.shape))
+    lse = torch.empty(st.q.shape[:2], dtype=torch.float32, device="cuda")
+    out = P.paged_attention_decode(t["q"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], t["seq"], dw.shape, max_seq,
+                                   workspace=ws, out_dtype=out_dtype, lse=lse)
+    torch.cuda.synchronize()
+    slots = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, wl.block_size)
+    kp, vp = O.reshape_and_cache(st.k, st.v, wl.k_cache, wl.v_cache, slots, wl.block_size)
+    ref, lref = O.paged_attention(st.q, kp, vp, st.block_tables, st.query_start_loc, st.context_lens, st.seq_lens,
+                                  wl.block_size)
+    r = check_attention(bf16_out_to_f64(out), ref, "device-split decode", bf16_out=out_dtype != torch.float32)
+    check_lse(lse.cpu().numpy(), lref, "device-split decode lse")
+    say(f"    {r}")
+    seq0 = t["seq"].clone()
+    seq0[3] = 0
+    out0 = P.paged_attention_decode(t["q"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], seq0, dw.shape, max_seq,
+                                    workspace=ws, out_dtype=out_dtype, lse=lse)
+    torch.cuda.synchronize()
+    assert not bf16_out_to_f64(out0)[3].any() and bool(torch.isneginf(lse[3]).all())
+
+
+def test_decode_step_graph_replays_with_new_metadata():
+    """A decode step (fused cache write + device-split decode) for a padded bucket of 8 rows is
+    captured once in a HIP graph, then replayed for three different batches written into the
+    same buffers (5 real rows, 3 padding rows of length 0 whose cache writes go to a spare
+    block), with eager work between replays: every replay matches the eager call bit for bit
+    and the oracle to tolerance."""
+    say("graph capture of a bucketed decode step, replayed with new metadata")
+    B, real, NB, WST, max_seq = 8, 5, 1200, 200, 3200
+    wls = []
+    for i in range(3):
+        rng = np.random.default_rng(100 + i)
+        ctxs = rng.integers(10, 3000, size=real)
+        reqs = [W.RequestSpec(int(c), [1]) for c in ctxs]
+        wls.append(W.build("bucket", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=100 + i,
+                           num_blocks=NB, bt_stride=WST))
+    shape = P.make_shape(32, 8, 128, NB, WST)
+
+    def padded(wl):
+        st = wl.steps[0]
+        used = {int(b) for r in range(real) for b in st.block_tables[r, : (int(st.seq_lens[r]) + 15) // 16]}
+        spare = max(set(range(NB)) - used)  # padding rows write here; no real row reads it
+        bt = np.full((B, WST), spare, np.int32)
+        bt[:real] = st.block_tables
+        qsl = np.arange(B + 1, dtype=np.int32)
+        ctx = np.zeros(B, np.int32)
+        ctx[:real] = st.context_lens
+        seq = np.zeros(B, np.int32)
+        seq[:real] = st.seq_lens
+        pad = lambda x: np.concatenate([x, np.zeros((B - real,) + x.shape[1:], x.dtype)])  # noqa: E731
+        return dict(q=pad(st.q), k=pad(st.k), v=pad(st.v), bt=bt, qsl=qsl, ctx=ctx, seq=seq)
+
+    m0 = padded(wls[0])
+    buf = {k: (dev16(v) if v.dtype == np.uint16 else dev32(v)) for k, v in m0.items()}
+    kc, vc = dev16(wls[0].k_cache), dev16(wls[0].v_cache)
+    ws = P.alloc_workspace(P.decode_workspace_size(B, max_seq, shape))
+    out = torch.empty((B, 32, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 32), dtype=torch.float32, device="cuda")
+
+    def step():
+        P.append_kv(buf["k"], buf["v"], kc, vc, buf["bt"], buf["qsl"], buf["ctx"], shape)
+        P.paged_attention_decode(buf["q"], kc, vc, buf["bt"], buf["qsl"], buf["seq"], shape, max_seq, workspace=ws,
+                                 out=out, lse=lse)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.synchronize()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for i, wl in enumerate(wls):
+        m = padded(wl)
+        for k, v in m.items():
+            buf[k].copy_(torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v))
+        kc.copy_(torch.from_numpy(wl.k_cache.view(np.int16)))
+        vc.copy_(torch.from_numpy(wl.v_cache.view(np.int16)))
+        out.zero_()
+        lse.zero_()
+        scratch.add_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_g, l_g = out.clone(), lse.clone()
+        # eager on the same inputs (the cache write is idempotent)
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g.view(torch.int16), out.view(torch.int16)), f"replay {i}: differs from eager"
+        assert torch.equal(l_g, lse), f"replay {i}: lse differs from eager"
+        st = wl.steps[0]
+        slots = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, wl.block_size)
+        kp, vp = O.reshape_and_cache(st.k, st.v, wl.k_cache, wl.v_cache, slots, wl.block_size)
+        ref, lref = O.paged_attention(st.q, kp, vp, st.block_tables, st.query_start_loc, st.context_lens,
+                                      st.seq_lens, wl.block_size)
+        check_attention(bf16_out_to_f64(o_g)[:real], ref, f"graph replay {i}")
+        check_lse(l_g.cpu().numpy()[:real], lref, f"graph replay {i} lse")
+        assert not bf16_out_to_f64(o_g)[real:].any() and bool(torch.isneginf(l_g[real:]).all())
+
+
 WIDE_SHAPES = [(64, 1), (64, 2), (64, 4), (64, 8), (128, 1), (128, 2), (128, 4), (128, 8)]
 
 
