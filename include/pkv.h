@@ -86,6 +86,7 @@ typedef struct pkv_varlen_plan {
   int64_t workspace_used;  /* bytes of the workspace the plan occupies */
   int32_t head_dim, num_q_heads, num_kv_heads, block_size; /* shape the plan was made for */
   int32_t tile_rows;       /* packed (token, q head) rows per prefill tile: 128 or 256 */
+  int32_t num_short_items; /* items of rows of 2 .. 32 / G query tokens (short items) */
 } pkv_varlen_plan;
 
 /* Size in bytes of a workspace that fits any plan with at most these sizes. */
@@ -178,9 +179,9 @@ int pkv_plan_varlen(pkv_varlen_plan* plan, void* workspace, size_t workspace_byt
                     const pkv_shape* shape, void* stream);
 
 /* The same planning into host memory only (no device work): writes up to `max_items`
- * work items of 8 int32 each {seq, kind (0 decode, 1 prefill), q_begin, q_count (prefill:
- * tokens of the tile; decode: splits of the row), kv_begin, kv_end, partial_base, split}
- * into `items`.  For inspection and tests. */
+ * work items of 8 int32 each {seq, kind (0 decode, 1 prefill, 2 short), q_begin, q_count
+ * (prefill and short: tokens; decode: splits of the row), kv_begin, kv_end, partial_base,
+ * split} into `items`.  For inspection and tests. */
 int pkv_plan_varlen_host(pkv_varlen_plan* plan, int32_t* items, int32_t max_items,
                          const int32_t* h_query_start_loc, const int32_t* h_context_lens,
                          const int32_t* h_seq_lens, int32_t num_seqs, int32_t num_tokens,

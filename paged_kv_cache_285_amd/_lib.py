@@ -72,6 +72,7 @@ class PkvVarlenPlan(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
         ("tile_rows", ctypes.c_int32),
+        ("num_short_items", ctypes.c_int32),
     ]
 
 

@@ -100,7 +100,7 @@ struct Plan {
   int32_t num_partials = 0;
   int32_t bps = 0;
   int32_t tile_rows = pkv::kTileRows;
-  int32_t n_prefill = 0, n_decode = 0;
+  int32_t n_prefill = 0, n_decode = 0, n_short = 0;
 };
 
 int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* seq,
@@ -140,11 +140,15 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
   }
   P.tile_rows = wide_rows >= pkv::kPrefillRowsForWideTiles ? pkv::kWideTileRows : pkv::kTileRows;
   const int tok_per_tile = P.tile_rows / G;
+  // Rows of 2 .. kShortRowsMax / G tokens run as short items, split like decode rows.
+  auto is_short = [&](int32_t ql) { return ql > 1 && (int64_t)ql * G <= pkv::kShortRowsMax; };
   int bps = pkv::kMinBlocksPerSplit;
   for (; bps < 256; bps *= 2) {
     int64_t n = 0;
-    for (int r = 0; r < num_seqs; ++r)
-      if (qsl[r + 1] - qsl[r] == 1) n += ceil_div(ceil_div(seq[r], pkv::kBlockSize), bps);
+    for (int r = 0; r < num_seqs; ++r) {
+      const int32_t ql = qsl[r + 1] - qsl[r];
+      if (ql == 1 || is_short(ql)) n += ceil_div(ceil_div(seq[r], pkv::kBlockSize), bps);
+    }
     if (n * s->num_kv_heads <= decode_target_wgs()) break;
   }
   P.bps = bps;
@@ -155,7 +159,7 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
     P.token_split[3 * t + 1] = 1;
     P.token_split[3 * t + 2] = 1;
   }
-  std::vector<pkv::WorkItem> pre, dec;
+  std::vector<pkv::WorkItem> pre, dec, shrt;
   int32_t partials = 0;
   for (int r = 0; r < num_seqs; ++r) {
     const int32_t ql = qsl[r + 1] - qsl[r];
@@ -181,6 +185,32 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
         dec.push_back(it);
       }
       if (splits > 1) partials += splits;
+    } else if (is_short(ql)) {
+      // Token t of split s writes partial row base + s * ql + t; the reduce merges the splits
+      // of each token (stride ql).
+      const int32_t nblk = (int32_t)ceil_div(seq[r], pkv::kBlockSize);
+      const int32_t splits = (int32_t)ceil_div(nblk, bps);
+      if (splits > 1) {
+        for (int32_t i = 0; i < ql; ++i) {
+          const int32_t t = qsl[r] + i;
+          P.token_split[3 * t] = partials + i;
+          P.token_split[3 * t + 1] = splits;
+          P.token_split[3 * t + 2] = ql;
+        }
+      }
+      for (int32_t sidx = 0; sidx < splits; ++sidx) {
+        pkv::WorkItem it;
+        it.seq = r;
+        it.kind = pkv::kShort;
+        it.q_begin = 0;
+        it.q_count = ql;
+        it.kv_begin = sidx * bps * pkv::kBlockSize;
+        it.kv_end = std::min<int32_t>(seq[r], (sidx + 1) * bps * pkv::kBlockSize);
+        it.partial_base = splits > 1 ? partials + sidx * ql : -1;
+        it.split = sidx;
+        shrt.push_back(it);
+      }
+      if (splits > 1) partials += splits * ql;
     } else {
       const int32_t tiles = (int32_t)ceil_div(ql, tok_per_tile);
       // A short row over a long context (one 128-row tile of at most kSplitRowsMax rows) is
@@ -229,11 +259,15 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
   std::stable_sort(pre.begin(), pre.end(), [](const pkv::WorkItem& x, const pkv::WorkItem& y) {
     return (int64_t)x.q_count * (x.kv_end - x.kv_begin) > (int64_t)y.q_count * (y.kv_end - y.kv_begin);
   });
-  std::stable_sort(dec.begin(), dec.end(), [](const pkv::WorkItem& x, const pkv::WorkItem& y) {
+  auto by_keys = [](const pkv::WorkItem& x, const pkv::WorkItem& y) {
     return (x.kv_end - x.kv_begin) > (y.kv_end - y.kv_begin);
-  });
+  };
+  std::stable_sort(dec.begin(), dec.end(), by_keys);
+  std::stable_sort(shrt.begin(), shrt.end(), by_keys);
   P.items = pre;
   P.items.insert(P.items.end(), dec.begin(), dec.end());
+  P.items.insert(P.items.end(), shrt.begin(), shrt.end());
+  P.n_short = (int32_t)shrt.size();
   P.num_partials = partials;
   P.n_prefill = (int32_t)pre.size();
   P.n_decode = (int32_t)dec.size();
@@ -247,6 +281,7 @@ void fill_plan_struct(pkv_varlen_plan* out, const Plan& P, int32_t num_seqs, int
   out->num_items = (int32_t)P.items.size();
   out->num_prefill_items = P.n_prefill;
   out->num_decode_items = P.n_decode;
+  out->num_short_items = P.n_short;
   out->num_partials = P.num_partials;
   out->blocks_per_split = P.bps;
   out->has_splits = P.num_partials > 0;
@@ -412,7 +447,9 @@ size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t m
   const int64_t cut_tokens = std::min<int64_t>(num_tokens, (int64_t)num_seqs * std::max(1, pkv::kSplitRowsMax / G));
   const int64_t items = ceil_div((int64_t)num_tokens * G, 128) + num_seqs +
                         (int64_t)num_seqs * std::max<int64_t>(1, per_row) + (int64_t)num_seqs * cut_splits;
-  const int64_t partials = (int64_t)num_seqs * std::max<int64_t>(1, per_row) + cut_tokens * cut_splits;
+  const int64_t short_tokens = std::min<int64_t>(num_tokens, (int64_t)num_seqs * std::max(1, pkv::kShortRowsMax / G));
+  const int64_t partials = (int64_t)num_seqs * std::max<int64_t>(1, per_row) + cut_tokens * cut_splits +
+                           short_tokens * std::max<int64_t>(1, per_row);
   return varlen_layout(items, num_tokens, partials, shape->num_q_heads, shape->head_dim).total;
 }
 
@@ -638,8 +675,8 @@ static int varlen_impl(void* out, int32_t out_dtype, float* lse, const void* q,
   const int G = shape->num_q_heads / shape->num_kv_heads;
   if (int rc = timing_mark((hipStream_t)stream, true)) return rc;
   hipError_t e = (fp8 ? pkv::launch_varlen_fp8 : pkv::launch_varlen)(
-      a, shape->head_dim, G, plan->num_prefill_items, plan->num_decode_items, plan->tile_rows,
-      (hipStream_t)stream);
+      a, shape->head_dim, G, plan->num_prefill_items, plan->num_decode_items, plan->num_short_items,
+      plan->tile_rows, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "varlen attention launch");
   if (int rc = timing_mark((hipStream_t)stream, false)) return rc;
   if (plan->num_partials > 0) {

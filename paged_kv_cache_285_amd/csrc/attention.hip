@@ -46,6 +46,7 @@
 #define PKV_KV_FP8 0
 #endif
 
+#include <algorithm>
 #include <type_traits>
 
 namespace pkv {
@@ -95,6 +96,14 @@ __device__ __forceinline__ uint2 ld_stream(const uint2* p) {
 #if PKV_DECODE_NT
   const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
   return make_uint2(v[0], v[1]);
+#else
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ uint32_t ld_stream(const uint32_t* p) {
+#if PKV_DECODE_NT
+  return __builtin_nontemporal_load(p);
 #else
   return *p;
 #endif
@@ -570,6 +579,271 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
     }
   }
   decode_merge<D, G, NW>(a, it, g, token, smem_raw);
+}
+
+// ------------------------------------------------------------------------------------------
+// Short item: a row of a few query tokens (at most 32 packed (token, q head) rows, such as a
+// speculative-verify row of 1 + k tokens) over a key range, on the matrix cores, with the
+// decode item's work split (4 waves, whole 16-key blocks per wave, block ids and scales
+// fetched once per lane) and two blocks in flight per wave.  The packed rows are the columns
+// of two 16-column groups:
+//  * S^T = K Q^T per group: v_mfma_f32_16x16x32_bf16 over D/32 K-steps.  A = the block's 16
+//    key rows: lane (i = lane % 16, q = lane / 16) holds dims 32s + 8q .. +7 of key i, one
+//    16-byte load (8 bytes of fp8).  B = Q^T: lane (n, q) holds the same dims of column n.
+//  * The 16x16 result gives lane (n, q) keys 4q .. 4q+3 of column n, so the causal mask and
+//    the softmax are lane-local apart from the rare raise of a column's running max (a 4-lane
+//    reduction), and those 4 p are exactly the B operand (keys 4q .. 4q+3, column n) of
+//  * O^T += V^T P^T per group: v_mfma_f32_16x16x16_bf16 per 16 dims.  A = V^T: lane (d, q)
+//    holds keys 4q .. 4q+3 of dim 16 dg + d, one 8-byte load (4 of fp8) shared by both groups.
+// The 4 waves' states are merged in LDS one wave after another (fixed order: the result does
+// not depend on timing).
+// ------------------------------------------------------------------------------------------
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// 4 e4m3 codes -> 4 bf16 (exact); 4 bf16 pass through.
+__device__ __forceinline__ uint2 widen4(uint32_t c) {
+  return make_uint2(fp8x2_to_bf16x2<false>(c), fp8x2_to_bf16x2<true>(c));
+}
+__device__ __forceinline__ uint2 widen4(uint2 c) { return c; }
+
+template <int D, int NW>
+struct ShortSmem {
+  static constexpr int COLS = 32;
+  static constexpr int DP = D + 4;  // row pitch (floats): 16 columns' float4 stores hit distinct banks
+  static constexpr int BYTES = (COLS * DP + 2 * NW * COLS) * 4;
+};
+
+template <int D, int G, int NW, bool FP8>
+__device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char* smem_raw) {
+  constexpr int CH = D / 8;   // 8-element chunks per key row
+  constexpr int KS = D / 32;  // K-steps of S^T
+  constexpr int DG = D / 16;  // 16-dim groups of O^T
+  constexpr int NC = 2;       // column groups
+  using SM = ShortSmem<D, NW>;
+  using KC = Chunk<FP8>;                                  // 8 key elements
+  using VC = std::conditional_t<FP8, uint32_t, uint2>;  // 4 value elements
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15;
+  const int q = lane >> 4;
+  const int r = it.seq;
+  const int ntok = it.q_count;
+  const int tok0 = a.query_start_loc[r] + it.q_begin;
+  const int pos0 = a.context_lens[r] + it.q_begin;  // position of the row's first token
+  const int kv_end = it.kv_end;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int ncols = ntok * G;  // <= 32
+  const float sl = a.scale_log2;
+
+  bf16x8 qb[NC][KS];
+  int qpos[NC];
+#pragma unroll
+  for (int cg = 0; cg < NC; ++cg) {
+    const int n = 16 * cg + n16;
+    const bool valid = n < ncols;
+    const int t = valid ? n / G : 0;
+    qpos[cg] = pos0 + t;
+    const uint4* qrow = reinterpret_cast<const uint4*>(a.q + ((int64_t)(tok0 + t) * Hq + g * G + n % G) * D);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qb[cg][s] = __builtin_bit_cast(bf16x8, valid ? qrow[4 * s + q] : make_uint4(0u, 0u, 0u, 0u));
+  }
+  floatx4 o[NC][DG];
+  float m[NC], lsum[NC];
+#pragma unroll
+  for (int cg = 0; cg < NC; ++cg) {
+    m[cg] = -INFINITY;
+    lsum[cg] = 0.f;
+#pragma unroll
+    for (int d = 0; d < DG; ++d) o[cg][d] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
+  const int b_begin = it.kv_begin / kBlockSize;
+  const int b_end = (kv_end + kBlockSize - 1) / kBlockSize;
+  const int nb = b_end - b_begin;
+  const int nk = nb > wave ? (nb - wave + NW - 1) / NW : 0;
+  const int L = a.bt_shift;
+  const int my_id = lane < nk ? tile_of(bt, b_begin + wave + NW * lane, L) : 0;
+  float my_ks = 1.f, my_vs = 1.f;
+  if constexpr (FP8) {
+    if (lane < nk) {
+      my_ks = a.k_scale[(int64_t)(my_id >> L) * Hkv + g];
+      my_vs = a.v_scale[(int64_t)(my_id >> L) * Hkv + g];
+    }
+  }
+  const int64_t ktile = (int64_t)kBlockSize * CH;  // KC per (block, head) tile
+  const int64_t vtile = (int64_t)4 * D;           // VC per (block, head) tile
+  const KC* kb = reinterpret_cast<const KC*>(a.k_cache) + (int64_t)g * ktile;
+  const VC* vb = reinterpret_cast<const VC*>(a.v_cache) + (int64_t)g * vtile;
+
+  auto load = [&](int k, KC (&kr)[KS], VC (&vr)[DG]) __attribute__((always_inline)) {
+    const int64_t phys = __builtin_amdgcn_readlane(my_id, k);
+    const KC* kp = kb + phys * Hkv * ktile;
+    const VC* vp = vb + phys * Hkv * vtile;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kr[s] = ld_stream(kp + n16 * CH + 4 * s + q);
+#pragma unroll
+    for (int d = 0; d < DG; ++d) vr[d] = ld_stream(vp + (16 * d + n16) * 4 + q);
+  };
+
+  auto process = [&](int k, const KC (&kr)[KS], const VC (&vr)[DG]) __attribute__((always_inline)) {
+    const int t0 = (b_begin + wave + NW * k) * kBlockSize;  // first key of the block
+    const int nvalid = kv_end - t0;                         // < 16 only in the last block
+    float slb = sl, vsb = 1.f;
+    if constexpr (FP8) {
+      slb = sl * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_ks), k));
+      vsb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_vs), k));
+    }
+    uint2 vmask = make_uint2(0xffffffffu, 0xffffffffu);  // values of keys past the end -> 0
+    if (nvalid < kBlockSize) {
+      const int t = 4 * q;
+      vmask.x = (t < nvalid ? 0x0000ffffu : 0u) | (t + 1 < nvalid ? 0xffff0000u : 0u);
+      vmask.y = (t + 2 < nvalid ? 0x0000ffffu : 0u) | (t + 3 < nvalid ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int cg = 0; cg < NC; ++cg) {
+      floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, widen8(kr[s])), qb[cg][s], sacc,
+                                                       0, 0, 0);
+      float sc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = t0 + 4 * q + j;
+        sc[j] = (4 * q + j < nvalid && key <= qpos[cg]) ? sacc[j] * slb : -INFINITY;
+      }
+      const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      if (__ballot(lm > m[cg] + kLazy) != 0) {
+        float cm = fmaxf(lm, __shfl_xor(lm, 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        const float mn = fmaxf(m[cg], cm);
+        const float alpha = fast_exp2(m[cg] - ((mn == -INFINITY) ? 0.f : mn));
+        lsum[cg] *= alpha;
+#pragma unroll
+        for (int d = 0; d < DG; ++d) o[cg][d] *= alpha;
+        m[cg] = mn;
+      }
+      const float mref = (m[cg] == -INFINITY) ? 0.f : m[cg];
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = fast_exp2(sc[j] - mref);
+        lsum[cg] += p[j];
+      }
+      const uint2 pw = FP8 ? make_uint2(pack_bf16x2(p[0] * vsb, p[1] * vsb), pack_bf16x2(p[2] * vsb, p[3] * vsb))
+                           : make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+      const shortx4 pb = __builtin_bit_cast(shortx4, pw);
+#pragma unroll
+      for (int d = 0; d < DG; ++d) {
+        uint2 v = widen4(vr[d]);  // converted per group: cheaper than holding both groups' operands
+        v.x &= vmask.x;
+        v.y &= vmask.y;
+        o[cg][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, v), pb, o[cg][d], 0, 0, 0);
+      }
+    }
+  };
+
+  // Two blocks in flight per wave (three register sets), unconditional steady-state loads.
+  if (nk > 0) {
+    KC k0[KS], k1[KS], k2[KS];
+    VC v0[DG], v1[DG], v2[DG];
+    load(0, k0, v0);
+    if (nk > 1) load(1, k1, v1);
+    int k = 0;
+    for (; k + 4 < nk; k += 3) {  // sets 0, 1 hold blocks k, k + 1
+      load(k + 2, k2, v2);
+      process(k, k0, v0);
+      load(k + 3, k0, v0);
+      process(k + 1, k1, v1);
+      load(k + 4, k1, v1);
+      process(k + 2, k2, v2);
+    }
+    if (k + 2 < nk) load(k + 2, k2, v2);
+    process(k, k0, v0);
+    if (k + 1 < nk) {
+      if (k + 3 < nk) load(k + 3, k0, v0);
+      process(k + 1, k1, v1);
+      if (k + 2 < nk) process(k + 2, k2, v2);
+      if (k + 3 < nk) process(k + 3, k0, v0);
+    }
+  }
+
+  // Merge the waves: every wave publishes (m, l) per column; each lane rescales its o to the
+  // columns' common max; the waves then add their o into one LDS buffer in wave order.
+  float* s_o = reinterpret_cast<float*>(smem_raw);  // [COLS][DP]
+  float* s_m = s_o + SM::COLS * SM::DP;              // [NW][COLS]
+  float* s_l = s_m + NW * SM::COLS;                  // [NW][COLS]
+#pragma unroll
+  for (int cg = 0; cg < NC; ++cg) {
+    lsum[cg] += __shfl_xor(lsum[cg], 16);
+    lsum[cg] += __shfl_xor(lsum[cg], 32);
+    if (q == 0) {
+      s_m[wave * SM::COLS + 16 * cg + n16] = m[cg];
+      s_l[wave * SM::COLS + 16 * cg + n16] = lsum[cg];
+    }
+  }
+  __syncthreads();
+  float fac[NC];
+#pragma unroll
+  for (int cg = 0; cg < NC; ++cg) {
+    const int n = 16 * cg + n16;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_m[w * SM::COLS + n]);
+    fac[cg] = (mx == -INFINITY) ? 0.f : fast_exp2(m[cg] - mx);
+  }
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int cg = 0; cg < NC; ++cg)
+#pragma unroll
+        for (int d = 0; d < DG; ++d) {
+          float4* dst = reinterpret_cast<float4*>(s_o + (16 * cg + n16) * SM::DP + 16 * d + 4 * q);
+          float4 x = make_float4(o[cg][d][0] * fac[cg], o[cg][d][1] * fac[cg], o[cg][d][2] * fac[cg],
+                                 o[cg][d][3] * fac[cg]);
+          if (w > 0) {
+            const float4 y = *dst;
+            x.x += y.x;
+            x.y += y.y;
+            x.z += y.z;
+            x.w += y.w;
+          }
+          *dst = x;
+        }
+    }
+    __syncthreads();
+  }
+  // Store: thread per 8 output values of a valid column.
+  for (int idx = threadIdx.x; idx < ncols * CH; idx += 64 * NW) {
+    const int n = idx / CH, cc = idx % CH;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_m[w * SM::COLS + n]);
+    float ll = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) ll += s_l[w * SM::COLS + n] * fast_exp2(s_m[w * SM::COLS + n] - mx);
+    }
+    const float inv = (ll > 0.f) ? 1.f / ll : 0.f;
+    float oo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oo[e] = s_o[n * SM::DP + 8 * cc + e] * inv;
+    const float lse = (ll > 0.f) ? (mx + __log2f(ll)) * kLn2 : -INFINITY;
+    const int t = n / G, head = g * G + n % G;
+    if (it.partial_base < 0) {
+      store8(a.out, a.out_f32, ((int64_t)(tok0 + t) * Hq + head) * D + cc * 8, oo);
+      if (a.lse && cc == 0) a.lse[(int64_t)(tok0 + t) * Hq + head] = lse;
+    } else {
+      const int64_t prow = (int64_t)(it.partial_base + t) * Hq + head;
+      store8(a.part_o, 1, prow * D + cc * 8, oo);
+      if (cc == 0) a.part_lse[prow] = lse;
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1347,6 +1621,18 @@ void varlen_kernel(VarlenArgs a) {
   }
 }
 
+// Short items (rows of a few query tokens over long contexts) in a kernel of their own: their
+// two-column-group MFMA path needs a register budget of two waves per SIMD, which the decode
+// kernels must not inherit.
+template <int D, int G, bool FP8>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void short_kernel(VarlenArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int x = blockIdx.x;
+  const int g = x % a.num_kv_heads;
+  short_item<D, G, 4, FP8>(a, a.items[x / a.num_kv_heads], g, smem);
+}
+
 // Decode batch with a device-side work split, for graph capture: the grid depends only on
 // (num_seqs, splits), each workgroup takes row x / (splits * Hkv), split (x / Hkv) % splits and
 // kv head x % Hkv, and reads the row's length from seq_lens on the device.  A split past the
@@ -1484,33 +1770,42 @@ size_t varlen_smem(bool has_prefill) {
 constexpr bool kFp8 = PKV_KV_FP8 != 0;
 
 template <int D, int G>
-hipError_t launch_varlen_t(const VarlenArgs& a, int n_prefill, int n_decode, int tile_rows,
+hipError_t launch_varlen_t(const VarlenArgs& a, int n_prefill, int n_decode, int n_short, int tile_rows,
                            hipStream_t stream) {
   const int Hkv = a.num_kv_heads;
-  if (n_prefill + n_decode == 0) return hipSuccess;
-  if (n_prefill == 0) {
-    auto kern = varlen_kernel<D, G, true, 4, kFp8>;
-    const size_t smem = varlen_smem<D, G, 4>(false);
-    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_decode * Hkv)), dim3(256), smem, stream, a);
-  } else if (tile_rows == kWideTileRows) {
-    // Wide prefill tiles, then the decode items in a kernel of their own (the wide tile's
-    // register budget allows two waves per SIMD, too few for the decode path).
-    auto kern = prefill_wide_kernel<D, G, kFp8>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_prefill * Hkv)), dim3(512),
-                       (size_t)TileSmem<D>::BYTES, stream, a);
-    if (n_decode > 0) {
-      VarlenArgs b = a;
-      b.items = a.items + n_prefill;
-      b.num_items = n_decode;
-      auto dk = varlen_kernel<D, G, true, 4, kFp8>;
+  if (n_prefill + n_decode > 0) {
+    if (n_prefill == 0) {
+      auto kern = varlen_kernel<D, G, true, 4, kFp8>;
       const size_t smem = varlen_smem<D, G, 4>(false);
-      hipLaunchKernelGGL(dk, dim3((unsigned)((int64_t)n_decode * Hkv)), dim3(256), smem, stream, b);
+      hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_decode * Hkv)), dim3(256), smem, stream, a);
+    } else if (tile_rows == kWideTileRows) {
+      // Wide prefill tiles, then the decode items in a kernel of their own (the wide tile's
+      // register budget allows two waves per SIMD, too few for the decode path).
+      auto kern = prefill_wide_kernel<D, G, kFp8>;
+      hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_prefill * Hkv)), dim3(512),
+                         (size_t)TileSmem<D>::BYTES, stream, a);
+      if (n_decode > 0) {
+        VarlenArgs b = a;
+        b.items = a.items + n_prefill;
+        b.num_items = n_decode;
+        auto dk = varlen_kernel<D, G, true, 4, kFp8>;
+        const size_t smem = varlen_smem<D, G, 4>(false);
+        hipLaunchKernelGGL(dk, dim3((unsigned)((int64_t)n_decode * Hkv)), dim3(256), smem, stream, b);
+      }
+    } else {
+      auto kern = varlen_kernel<D, G, false, 4, kFp8>;
+      const size_t smem = varlen_smem<D, G, 4>(true);
+      hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)(n_prefill + n_decode) * Hkv)), dim3(256), smem,
+                         stream, a);
     }
-  } else {
-    auto kern = varlen_kernel<D, G, false, 4, kFp8>;
-    const size_t smem = varlen_smem<D, G, 4>(true);
-    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)(n_prefill + n_decode) * Hkv)), dim3(256), smem,
-                       stream, a);
+  }
+  if (n_short > 0) {
+    VarlenArgs b = a;
+    b.items = a.items + n_prefill + n_decode;
+    b.num_items = n_short;
+    const size_t smem = (size_t)ShortSmem<D, 4>::BYTES;
+    hipLaunchKernelGGL((short_kernel<D, G, kFp8>), dim3((unsigned)((int64_t)n_short * Hkv)), dim3(256), smem,
+                       stream, b);
   }
   return hipGetLastError();
 }
@@ -1565,8 +1860,8 @@ hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
 #endif
 
 hipError_t PKV_KV_NAME(launch_varlen)(const VarlenArgs& a, int head_dim, int group, int n_prefill,
-                                      int n_decode, int tile_rows, hipStream_t stream) {
-#define CALL_V(D, G) launch_varlen_t<D, G>(a, n_prefill, n_decode, tile_rows, stream)
+                                      int n_decode, int n_short, int tile_rows, hipStream_t stream) {
+#define CALL_V(D, G) launch_varlen_t<D, G>(a, n_prefill, n_decode, n_short, tile_rows, stream)
   PKV_DISPATCH_DG(head_dim, group, CALL_V)
 #undef CALL_V
 }

@@ -122,7 +122,7 @@ def test_plan_rejects_inconsistent_metadata(P):
         P.plan_varlen_host([0, 1], [64 * 16], [64 * 16 + 1], s)
 
 
-@pytest.mark.parametrize("lengths", [(1, 1, 1, 2, 5, 17, 100, 300), (1, 1, 2, 5, 8, 17)])
+@pytest.mark.parametrize("lengths", [(1, 1, 1, 2, 5, 17, 100, 300), (1, 1, 2, 5, 8, 12, 16, 17)])
 def test_plan_covers_every_row_exactly_once(P, lengths):
     s = shape(P, bt_stride=600)
     rng = np.random.default_rng(0)
@@ -132,16 +132,23 @@ def test_plan_covers_every_row_exactly_once(P, lengths):
     qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
     seq = (ctx + ql).astype(np.int32)
     plan, items = P.plan_varlen_host(qsl, ctx, seq, s)
-    assert plan.num_items == len(items) == plan.num_prefill_items + plan.num_decode_items
+    assert plan.num_items == len(items) == plan.num_prefill_items + plan.num_decode_items + plan.num_short_items
     G = 4
     tok_per_tile = plan.tile_rows // G
     cover_tok = np.zeros(int(qsl[-1]), int)
     dec_keys = {}
     cut_keys = {}
+    short_keys = {}
+    partial_rows = []
     for seqi, kind, qb, qc, kb, ke, pbase, split in items:
-        if kind == 1 and pbase >= 0:
+        if kind == 2:
+            # a short row (2 .. 32 / G tokens) split by keys like a decode row
+            assert 1 < ql[seqi] and ql[seqi] * G <= 32 and qb == 0 and qc == ql[seqi]
+            cover_tok[qsl[seqi] : qsl[seqi] + qc] += split == 0
+            short_keys.setdefault(seqi, []).append((kb, ke, pbase, split))
+        elif kind == 1 and pbase >= 0:
             # a key split of a short row: the whole row, keys [kb, ke), partial rows pbase + t
-            assert ql[seqi] * G <= 64 and qb == 0 and qc == ql[seqi] and seq[seqi] > 1024
+            assert 32 < ql[seqi] * G <= 64 and qb == 0 and qc == ql[seqi] and seq[seqi] > 1024
             cover_tok[qsl[seqi] : qsl[seqi] + qc] += split == 0
             cut_keys.setdefault(seqi, []).append((kb, ke, pbase, split))
         elif kind == 1:
@@ -153,7 +160,6 @@ def test_plan_covers_every_row_exactly_once(P, lengths):
             cover_tok[qsl[seqi]] += split == 0
             dec_keys.setdefault(seqi, []).append((kb, ke, pbase, split, qc))
     assert (cover_tok == 1).all()
-    partial_rows = []
     for r, ranges in cut_keys.items():
         ranges.sort()
         assert ranges[0][0] == 0 and ranges[-1][1] == seq[r] and len(ranges) == -(-seq[r] // 1024)
@@ -163,6 +169,18 @@ def test_plan_covers_every_row_exactly_once(P, lengths):
         for i, x in enumerate(ranges):
             assert x[3] == i and x[2] == base + i * ql[r]
         partial_rows += list(range(base, base + len(ranges) * ql[r]))
+    for r, ranges in short_keys.items():
+        ranges.sort()
+        assert ranges[0][0] == 0 and ranges[-1][1] == seq[r]
+        for a, b in zip(ranges, ranges[1:]):
+            assert a[1] == b[0] and a[1] % 16 == 0
+        if len(ranges) == 1:
+            assert ranges[0][2] == -1
+        else:
+            base = ranges[0][2]
+            for i, x in enumerate(ranges):
+                assert x[3] == i and x[2] == base + i * ql[r]
+            partial_rows += list(range(base, base + len(ranges) * ql[r]))
     for r, ranges in dec_keys.items():
         ranges.sort()
         assert ranges[0][0] == 0 and ranges[-1][1] == seq[r]

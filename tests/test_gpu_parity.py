@@ -136,6 +136,19 @@ def test_short_rows_split_at_key_boundaries():
     run_and_check(wl)
 
 
+@pytest.mark.parametrize("head_dim,group", [(64, 1), (128, 2), (128, 8), (64, 4)])
+def test_short_rows_every_shape(head_dim, group):
+    """Rows of 2 .. 32 / G query tokens (short items: MFMA columns = packed (token, q head) rows)
+    with contexts from empty to a few thousand keys, split or not, for several shapes."""
+    say(f"short rows, D={head_dim} G={group}")
+    rng = np.random.default_rng(head_dim + group)
+    qmax = 32 // group
+    reqs = [W.RequestSpec(int(c), [int(q)]) for c, q in zip(rng.integers(0, 3000, 10), rng.integers(2, qmax + 1, 10))]
+    reqs += [W.RequestSpec(0, [qmax]), W.RequestSpec(17, [2]), W.RequestSpec(1, [1])]
+    wl = W.build("short_rows", reqs, num_q_heads=8 * group, num_kv_heads=8, head_dim=head_dim, seed=head_dim * group)
+    run_and_check(wl)
+
+
 def test_spec_verify_full_size_sampled():
     say("spec_verify full: 64 rows of 5 tokens, ctx U[1024, 4096], sampled rows")
     run_and_check(W.spec_verify(seed=0), rows_per_step=48, check_pools=False)
