@@ -12,7 +12,7 @@ duration against 8 TB/s; also with cold caches, a 1 GiB write before each launch
 L2s and the 256 MB MALL), the decode-only batch's HBM GB/s (warm and cold), and the CPU fp64
 oracle timed on a bounded sample of the same workload (``cpu_baseline``).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--mfma]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-graph] [--mfma]
 """
 
 from __future__ import annotations
@@ -560,6 +560,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed decode step")
     ap.add_argument("--mfma", action="store_true", help="also time the MFMA-bound cascade prefix and long prefill")
     ap.add_argument(
         "--copy-calibration",
@@ -653,7 +654,8 @@ def main():
         log("bench: speculative-verify batch, tiny prefill")
         line["spec_verify_hbm"] = spec_verify_hbm(torch, P)
         line["tiny_prefill"] = tiny_prefill_latency(torch, P)
-        line["decode_graph_step"] = decode_graph_step(torch, P)
+        if not args.no_graph:
+            line["decode_graph_step"] = decode_graph_step(torch, P)
     if args.mfma:
         log("bench: MFMA paths (cascade prefix, long chunked prefill)")
         line["mfma_paths"] = mfma_paths(torch, P)
