@@ -91,6 +91,11 @@ def test_decode_entry_points_validate_before_launching(P):
     assert b"bt_stride" in lib.pkv_last_error()
     assert lib.pkv_paged_attention_decode(z, 3, z, z, z, z, z, z, z, 4, 100, ctypes.byref(s), z, 0, z) == -1
     assert lib.pkv_paged_attention_decode_fp8(z, 0, z, z, z, z, z, z, z, z, z, 4, 100, ctypes.byref(s), z, 0, z) == -1
+    # long rows need partial states: too small a workspace is refused before any launch
+    fake = ctypes.c_void_p(256)  # never dereferenced: the size check comes first
+    s600 = shape(P, bt_stride=600)
+    assert lib.pkv_paged_attention_decode(fake, 0, z, fake, fake, fake, fake, fake, fake, 256, 8192,
+                                          ctypes.byref(s600), fake, 16, z) == -2
     # one split needs no workspace; long rows need partial states
     assert P.decode_workspace_size(8, 256, s) == 0
     assert P.decode_workspace_size(256, 8192, shape(P, bt_stride=600)) > 0
@@ -204,10 +209,12 @@ def test_plan_covers_every_row_exactly_once(P, lengths):
 
 def test_workspace_bound_holds_for_every_plan(P):
     rng = np.random.default_rng(1)
-    for trial in range(20):
-        s = shape(P, bt_stride=700, num_q_heads=int(rng.choice([8, 16, 32, 64])))
+    for trial in range(40):
+        bs = int(rng.choice([16, 256]))
+        s = shape(P, bt_stride=700 if bs == 16 else 44, block_size=bs, num_q_heads=int(rng.choice([8, 16, 32, 64])))
         B = int(rng.integers(1, 300))
-        ql = rng.choice([0, 1, 1, 1, 3, 64, 500], size=B)
+        # decode rows, short rows (ql * G <= 32), cut rows (<= 64), tiles, and empty rows
+        ql = rng.choice([0, 1, 1, 1, 2, 3, 4, 8, 12, 16, 32, 64, 500], size=B)
         ctx = rng.integers(0, 10000, size=B)
         qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
         seq = (ctx + ql).astype(np.int32)
