@@ -108,9 +108,11 @@ class Runner:
 
 
 def time_passes(runner, torch, steps, warmup):
-    """Time `steps` passes bracketed by device syncs; the library's launch timing brackets each
-    varlen attention kernel with HIP events on its stream.  Returns (total ms, kernel ms per
-    launch, launches)."""
+    """Time `steps` passes bracketed by device syncs, then `steps` more with the library's
+    launch timing on, which brackets each varlen attention kernel with a pair of HIP events on
+    its stream.  The events add GPU time between launches (about 7 us per launch here), so the
+    step time comes from the first loop and the kernel time from the second.  Returns (total ms
+    of the first loop, kernel ms per launch, launches timed)."""
     import gc
 
     P = runner.P
@@ -118,14 +120,17 @@ def time_passes(runner, torch, steps, warmup):
         runner.run_pass()
     torch.cuda.synchronize()
     gc.collect()
-    gc.disable()  # no collector pauses inside the timed region
+    gc.disable()  # no collector pauses inside the timed regions
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    P.timing_begin()
     start.record()
     for _ in range(steps):
         runner.run_pass()
     stop.record()
+    torch.cuda.synchronize()
+    P.timing_begin()
+    for _ in range(steps):
+        runner.run_pass()
     torch.cuda.synchronize()
     kern_total, launches = P.timing_end()
     gc.enable()

@@ -11,28 +11,89 @@
 namespace pkv {
 namespace {
 
-// One thread per new token.  The owning request is found by binary search over
-// query_start_loc (num_seqs + 1 ascending entries).
-__global__ void slot_mapping_kernel(int64_t* __restrict__ slots, const int32_t* __restrict__ bt,
-                                    const int32_t* __restrict__ qsl,
-                                    const int32_t* __restrict__ ctx, int32_t num_seqs,
-                                    int32_t num_tokens, int32_t bt_stride, int32_t bs_log2) {
-  const int32_t t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= num_tokens) return;
-  int32_t lo = 0, hi = num_seqs - 1;  // largest r with qsl[r] <= t
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+constexpr int kCacheThreads = 256;
+constexpr int kRunMax = kCacheThreads + 1;  // tokens a workgroup's run of threads can touch
+
+// Owner and position of every token of a workgroup's run [t0, t0 + n) of new tokens, into LDS.
+// query_start_loc holds num_seqs + 1 ascending entries; the owner of token t is the request r
+// with qsl[r] <= t < qsl[r + 1] (requests with no new token own nothing) and the token's
+// position is context_lens[r] + t - qsl[r].  A binary search per thread would chain about
+// log2(num_seqs) dependent loads before the block table could be read; here the workgroup
+// finds the owners together in one round of loads (two when num_seqs exceeds the workgroup):
+//   * beyond blockDim requests, a coarse round samples qsl every S = ceil(num_seqs / blockDim)
+//     requests and narrows the candidates to [last sample <= t0, first sample past the run);
+//   * then thread j takes candidates lo + j, lo + j + blockDim, ..., loads qsl[r], qsl[r + 1]
+//     and context_lens[r] together and writes r and the position for each token of the run
+//     that r owns.
+// Tokens nobody claims (a malformed qsl) keep owner -1.  Every thread of the workgroup must
+// call this.
+__device__ void find_owners(const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
+                            int32_t num_seqs, int64_t t0, int32_t n, int32_t* s_owner,
+                            int32_t* s_pos, int32_t* s_range) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int64_t t_end = t0 + n;  // one past the run's last token
+  for (int i = tid; i < n; i += nt) s_owner[i] = -1;
+  int32_t lo = 0, hi = num_seqs;
+  if (num_seqs > nt) {
+    if (tid == 0) {
+      s_range[0] = 0;
+      s_range[1] = num_seqs;
+    }
+    __syncthreads();
+    const int32_t S = (num_seqs + nt - 1) / nt;
+    const int64_t r = (int64_t)tid * S;
+    if (r < num_seqs) {
+      const int32_t a = qsl[r];
+      if (a <= t0) atomicMax(&s_range[0], (int32_t)r);
+      if (a >= t_end) atomicMin(&s_range[1], (int32_t)r);
+    }
+    __syncthreads();
+    lo = s_range[0];
+    hi = s_range[1];
   }
-  const int32_t r = lo;
-  const int32_t pos = ctx[r] + (t - qsl[r]);
+  for (int64_t r = (int64_t)lo + tid; r < hi; r += nt) {
+    const int32_t a = qsl[r], b = qsl[r + 1], c = ctx[r];
+    const int64_t from = a > t0 ? a : t0, to = b < t_end ? b : t_end;
+    for (int64_t t = from; t < to; ++t) {
+      s_owner[t - t0] = (int32_t)r;
+      s_pos[t - t0] = c + (int32_t)(t - a);
+    }
+  }
+  __syncthreads();
+}
+
+// The run of tokens touched by this workgroup when thread gid handles token gid / per_token.
+__device__ __forceinline__ void token_run(int64_t per_token, int32_t num_tokens, int64_t& t0, int32_t& n) {
+  const int64_t g0 = (int64_t)blockIdx.x * blockDim.x;
+  t0 = g0 / per_token;
+  int64_t t1 = (g0 + blockDim.x - 1) / per_token;  // last token (inclusive)
+  if (t1 > num_tokens - 1) t1 = num_tokens - 1;
+  n = (int32_t)(t1 - t0 + 1);
+}
+
+// Slot of a token from its owner and position, or -1 (no owner, negative position, or a
+// position past the block table's width).
+__device__ __forceinline__ int64_t slot_of(const int32_t* __restrict__ bt, int32_t owner, int32_t pos,
+                                           int32_t bt_stride, int32_t bs_log2) {
+  if (owner < 0 || pos < 0) return -1;
   const int32_t logical = pos >> bs_log2;
-  if (pos < 0 || logical >= bt_stride) {
-    slots[t] = -1;
-    return;
-  }
-  const int64_t phys = bt[(int64_t)r * bt_stride + logical];
-  slots[t] = (phys << bs_log2) + (pos & ((1 << bs_log2) - 1));
+  if (logical >= bt_stride) return -1;
+  return ((int64_t)bt[(int64_t)owner * bt_stride + logical] << bs_log2) + (pos & ((1 << bs_log2) - 1));
+}
+
+// One thread per new token.
+__global__ void __launch_bounds__(kCacheThreads)
+slot_mapping_kernel(int64_t* __restrict__ slots, const int32_t* __restrict__ bt,
+                    const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx, int32_t num_seqs,
+                    int32_t num_tokens, int32_t bt_stride, int32_t bs_log2) {
+  __shared__ int32_t s_owner[kRunMax], s_pos[kRunMax], s_range[2];
+  int64_t t0;
+  int32_t n;
+  token_run(1, num_tokens, t0, n);
+  find_owners(qsl, ctx, num_seqs, t0, n, s_owner, s_pos, s_range);
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= num_tokens) return;
+  slots[t] = slot_of(bt, s_owner[t - t0], s_pos[t - t0], bt_stride, bs_log2);
 }
 
 // One thread per 16-byte chunk (8 bf16) of one token's K and V for one kv head.  A slot names
@@ -70,29 +131,32 @@ __global__ void reshape_and_cache_kernel(const uint4* __restrict__ k, const uint
 }
 
 // Slot mapping and cache write in one launch: one thread per 16-byte chunk of one token's K
-// and V for one kv head computes the token's slot from the block table (as above) and stores
-// the chunk; the (head 0, chunk 0) thread also records the slot when slot_mapping is given.
-__global__ void append_kv_kernel(int64_t* __restrict__ slot_out, const uint4* __restrict__ k,
-                                 const uint4* __restrict__ v, uint4* __restrict__ k_cache,
-                                 uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt,
-                                 const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
-                                 int32_t num_seqs, int32_t num_tokens, int32_t num_kv_heads,
-                                 int32_t chunks_per_head, int32_t bt_stride, int64_t num_slots,
-                                 int32_t bs_log2) {
+// and V for one kv head.  The chunk loads are issued first; the workgroup finds its tokens'
+// owners meanwhile (find_owners), then each thread reads its token's block table entry and
+// stores the chunk; the (head 0, chunk 0) thread also records the slot when slot_mapping is
+// given.
+__global__ void __launch_bounds__(kCacheThreads)
+append_kv_kernel(int64_t* __restrict__ slot_out, const uint4* __restrict__ k, const uint4* __restrict__ v,
+                 uint4* __restrict__ k_cache, uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt,
+                 const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx, int32_t num_seqs,
+                 int32_t num_tokens, int32_t num_kv_heads, int32_t chunks_per_head, int32_t bt_stride,
+                 int64_t num_slots, int32_t bs_log2) {
+  __shared__ int32_t s_owner[kRunMax], s_pos[kRunMax], s_range[2];
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_token = (int64_t)num_kv_heads * chunks_per_head;
   const int64_t t = gid / per_token;
-  if (t >= num_tokens) return;
-  int32_t lo = 0, hi = num_seqs - 1;  // largest r with qsl[r] <= t
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+  const bool live = t < num_tokens;
+  uint4 kx = {}, vx = {};
+  if (live) {
+    kx = k[gid];
+    vx = v[gid];
   }
-  const int32_t pos = ctx[lo] + (int32_t)(t - qsl[lo]);
-  const int32_t logical = pos >> bs_log2;
-  int64_t slot = -1;
-  if (pos >= 0 && logical < bt_stride)
-    slot = ((int64_t)bt[(int64_t)lo * bt_stride + logical] << bs_log2) + (pos & ((1 << bs_log2) - 1));
+  int64_t t0;
+  int32_t n;
+  token_run(per_token, num_tokens, t0, n);
+  find_owners(qsl, ctx, num_seqs, t0, n, s_owner, s_pos, s_range);
+  if (!live) return;
+  const int64_t slot = slot_of(bt, s_owner[t - t0], s_pos[t - t0], bt_stride, bs_log2);
   const int64_t within = gid - t * per_token;
   if (slot_out && within == 0) slot_out[t] = slot;
   if (slot < 0 || slot >= num_slots) return;
@@ -101,9 +165,8 @@ __global__ void append_kv_kernel(int64_t* __restrict__ slot_out, const uint4* __
   const int64_t blk = slot / kBlockSize;
   const int64_t off = slot - blk * kBlockSize;
   const int64_t tile = blk * num_kv_heads + h;
-  k_cache[(tile * kBlockSize + off) * chunks_per_head + c] = k[gid];
-  const uint4 x = v[gid];
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  k_cache[(tile * kBlockSize + off) * chunks_per_head + c] = kx;
+  const uint32_t w[4] = {vx.x, vx.y, vx.z, vx.w};
   uint16_t* vt = v_cache + (tile * chunks_per_head * 8 + c * 8) * kBlockSize + off;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -197,33 +260,34 @@ __global__ void reshape_and_cache_fp8_kernel(const uint4* __restrict__ k, const 
 }
 
 // As append_kv_kernel, quantising into fp8 pools.
-__global__ void append_kv_fp8_kernel(int64_t* __restrict__ slot_out, const uint4* __restrict__ k,
-                                     const uint4* __restrict__ v, uint2* __restrict__ k_cache,
-                                     uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
-                                     const float* __restrict__ v_scale, const int32_t* __restrict__ bt,
-                                     const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
-                                     int32_t num_seqs, int32_t num_tokens, int32_t num_kv_heads,
-                                     int32_t chunks_per_head, int32_t bt_stride, int64_t num_slots,
-                                     int32_t bs_log2) {
+__global__ void __launch_bounds__(kCacheThreads)
+append_kv_fp8_kernel(int64_t* __restrict__ slot_out, const uint4* __restrict__ k, const uint4* __restrict__ v,
+                     uint2* __restrict__ k_cache, uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
+                     const float* __restrict__ v_scale, const int32_t* __restrict__ bt,
+                     const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx, int32_t num_seqs,
+                     int32_t num_tokens, int32_t num_kv_heads, int32_t chunks_per_head, int32_t bt_stride,
+                     int64_t num_slots, int32_t bs_log2) {
+  __shared__ int32_t s_owner[kRunMax], s_pos[kRunMax], s_range[2];
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_token = (int64_t)num_kv_heads * chunks_per_head;
   const int64_t t = gid / per_token;
-  if (t >= num_tokens) return;
-  int32_t lo = 0, hi = num_seqs - 1;  // largest r with qsl[r] <= t
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+  const bool live = t < num_tokens;
+  uint4 kx = {}, vx = {};
+  if (live) {
+    kx = k[gid];
+    vx = v[gid];
   }
-  const int32_t pos = ctx[lo] + (int32_t)(t - qsl[lo]);
-  const int32_t logical = pos >> bs_log2;
-  int64_t slot = -1;
-  if (pos >= 0 && logical < bt_stride)
-    slot = ((int64_t)bt[(int64_t)lo * bt_stride + logical] << bs_log2) + (pos & ((1 << bs_log2) - 1));
+  int64_t t0;
+  int32_t n;
+  token_run(per_token, num_tokens, t0, n);
+  find_owners(qsl, ctx, num_seqs, t0, n, s_owner, s_pos, s_range);
+  if (!live) return;
+  const int64_t slot = slot_of(bt, s_owner[t - t0], s_pos[t - t0], bt_stride, bs_log2);
   const int64_t within = gid - t * per_token;
   if (slot_out && within == 0) slot_out[t] = slot;
   if (slot < 0 || slot >= num_slots) return;
   const int64_t h = within / chunks_per_head;
-  store_fp8_chunk(k[gid], v[gid], k_cache, v_cache, k_scale, v_scale, slot, h, within - h * chunks_per_head,
+  store_fp8_chunk(kx, vx, k_cache, v_cache, k_scale, v_scale, slot, h, within - h * chunks_per_head,
                   num_kv_heads, chunks_per_head, bs_log2);
 }
 
@@ -261,7 +325,7 @@ hipError_t launch_append_kv(int64_t* slot_mapping, const uint16_t* k, const uint
   if (num_tokens == 0) return hipSuccess;
   const int32_t chunks = head_dim / 8;
   const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
-  const int threads = 256;
+  const int threads = kCacheThreads;
   const int64_t blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
                      slot_mapping, reinterpret_cast<const uint4*>(k),
@@ -280,7 +344,7 @@ hipError_t launch_append_kv_fp8(int64_t* slot_mapping, const uint16_t* k, const 
   if (num_tokens == 0) return hipSuccess;
   const int32_t chunks = head_dim / 8;
   const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
-  const int threads = 256;
+  const int threads = kCacheThreads;
   const int64_t blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(append_kv_fp8_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, slot_mapping,
                      reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
@@ -311,7 +375,7 @@ hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
                                int32_t num_tokens, int32_t bt_stride, int32_t bs_log2,
                                hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  const int threads = 256;
+  const int threads = kCacheThreads;
   const int blocks = (num_tokens + threads - 1) / threads;
   hipLaunchKernelGGL(slot_mapping_kernel, dim3(blocks), dim3(threads), 0, stream, slot_mapping,
                      block_tables, qsl, ctx, num_seqs, num_tokens, bt_stride, bs_log2);

@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 import paged_kv_cache_285_amd as P
+import workloads as W
 
 ATOL = 1e-2  # max abs error allowed for bf16 outputs against the fp64 oracle
 RTOL_L2 = 5e-3  # relative L2 error allowed
@@ -105,3 +106,28 @@ class DeviceWorkload:
             out_dtype=out_dtype, lse=lse,
         )
         return slots, out, lse, plan
+
+
+def many_requests(seed, num_req, num_kv_heads, head_dim):
+    """A one-step batch of `num_req` requests with 1..5 new tokens each, with runs of requests
+    that have no new token (query length 0) inserted between them: (workload, step arrays)."""
+    rng = np.random.default_rng(seed)
+    reqs = [W.RequestSpec(context=int(rng.integers(0, 40)), chunks=[int(rng.integers(1, 6))]) for _ in range(num_req)]
+    wl = W.build("many_requests", reqs, num_q_heads=2 * num_kv_heads, num_kv_heads=num_kv_heads,
+                 head_dim=head_dim, seed=seed)
+    st = wl.steps[0]
+    qlen = np.diff(st.query_start_loc)
+    ql2, ctx2, bt2 = [], [], []
+    for r in range(st.num_seqs):
+        # before a fifth of the requests, a run of 1..300 requests with no new token
+        for _ in range(int(rng.integers(1, 301)) if rng.random() < 0.2 else 0):
+            ql2.append(0)
+            ctx2.append(int(rng.integers(0, 40)))
+            bt2.append(st.block_tables[int(rng.integers(0, st.num_seqs))])
+        ql2.append(int(qlen[r]))
+        ctx2.append(int(st.context_lens[r]))
+        bt2.append(st.block_tables[r])
+    qsl2 = np.zeros(len(ql2) + 1, dtype=np.int32)
+    np.cumsum(ql2, out=qsl2[1:])
+    return wl, st, qsl2, np.array(ctx2, dtype=np.int32), np.ascontiguousarray(np.stack(bt2).astype(np.int32))
+

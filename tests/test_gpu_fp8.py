@@ -21,7 +21,7 @@ if not torch.cuda.is_available():  # pragma: no cover - collected on CPU, skippe
     pytest.skip("no GPU", allow_module_level=True)
 
 import paged_kv_cache_285_amd as P  # noqa: E402
-from _gpu import bf16_out_to_f64, check_attention, check_lse, dev16, dev32  # noqa: E402
+from _gpu import bf16_out_to_f64, check_attention, check_lse, dev16, dev32, many_requests  # noqa: E402
 
 
 def say(*a):
@@ -312,3 +312,21 @@ def test_fp8_block_size_256_parity(case):
         run_and_check_fp8(W.mixed_llama8b(seed=31, num_decode=10, ctx_range=(20, 900), block_size=256), seed=31)
     else:
         run_and_check_fp8(W.decode_only(seed=32, num_seqs=20, ctx_range=(30, 5000), block_size=256), seed=32)
+
+
+def test_fp8_append_kv_over_many_requests_bitwise():
+    """The quantising fused append over 1500 requests with runs of requests that have no new
+    token (the workgroup owner search's coarse round): slots and pool bytes equal the oracle's."""
+    wl, st, qsl, ctx, bt = many_requests(23, 1500, 2, 128)
+    say(f"fp8 append_kv over {len(ctx)} requests, T={st.num_tokens}")
+    d = DeviceFp8(wl, seed=23)
+    slots = torch.empty(st.num_tokens, dtype=torch.int64, device="cuda")
+    P.append_kv_fp8(dev16(st.k), dev16(st.v), d.k_cache, d.v_cache, d.k_scale, d.v_scale, dev32(bt), dev32(qsl),
+                    dev32(ctx), d.shape, slot_mapping=slots)
+    torch.cuda.synchronize()
+    ref = O.slot_mapping(bt, qsl, ctx, wl.block_size)
+    assert np.array_equal(slots.cpu().numpy(), ref)
+    kp, vp = O.reshape_and_cache_fp8(st.k, st.v, d.c.k_cache, d.c.v_cache, ref, d.c.k_scale, d.c.v_scale,
+                                     wl.block_size)
+    gk, gv = d.host_pools()
+    assert np.array_equal(gk, kp) and np.array_equal(gv, vp), "fp8 pool bytes differ"

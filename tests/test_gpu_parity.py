@@ -21,6 +21,7 @@ if not torch.cuda.is_available():  # pragma: no cover - collected on CPU, skippe
 import paged_kv_cache_285_amd as P  # noqa: E402
 from _gpu import (  # noqa: E402
     DeviceWorkload,
+    many_requests,
     bf16_out_to_f64,
     check_attention,
     check_lse,
@@ -574,3 +575,27 @@ def test_block_size_256_copy_blocks_bitwise():
 def test_block_size_256_full_size_decode_sampled():
     say("256-token blocks: decode_only full size, sampled rows")
     run_and_check(W.decode_only(seed=0, block_size=256), rows_per_step=48, check_pools=False)
+
+
+@pytest.mark.parametrize("num_req,num_kv_heads,head_dim", [(900, 2, 64), (200, 1, 64), (3000, 8, 128)])
+def test_slot_search_over_many_requests(num_req, num_kv_heads, head_dim):
+    """Slot mapping and the fused append over batches with more requests than a workgroup has
+    threads and long runs of requests with no new token: slots and pool bits equal the
+    oracle's (the same slots as without the empty requests)."""
+    wl, st, qsl, ctx, bt = many_requests(11 + num_req, num_req, num_kv_heads, head_dim)
+    say(f"slot search: {len(ctx)} requests ({num_req} with tokens), T={st.num_tokens}, Hkv={num_kv_heads}, D={head_dim}")
+    ref = O.slot_mapping(bt, qsl, ctx, wl.block_size)
+    assert np.array_equal(ref, O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, wl.block_size))
+    shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride,
+                         block_size=wl.block_size)
+    btd, qsld, ctxd = dev32(bt), dev32(qsl), dev32(ctx)
+    slots = P.compute_slot_mapping(btd, qsld, ctxd, shape, st.num_tokens)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots.cpu().numpy(), ref), "slot mapping differs"
+    kc, vc = dev16(wl.k_cache), dev16(wl.v_cache)
+    slots2 = torch.empty(st.num_tokens, dtype=torch.int64, device="cuda")
+    P.append_kv(dev16(st.k), dev16(st.v), kc, vc, btd, qsld, ctxd, shape, slot_mapping=slots2)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots2.cpu().numpy(), ref), "append_kv slots differ"
+    kp, vp = O.reshape_and_cache(st.k, st.v, wl.k_cache, wl.v_cache, ref, wl.block_size)
+    assert np.array_equal(host16(kc), kp) and np.array_equal(host16(vc), vp), "pool bits differ"
