@@ -96,8 +96,11 @@ size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t m
 /* a1 — slot mapping [Tencent Cloud article, chunked prefill / prefix caching sections, and
  * "11. vLLM principles" section 11.2]: for token i of request r at position
  * p = context_lens[r] + i, slot = block_tables[r][p / bs] * bs + p % bs.
- * Writes slot_mapping[num_tokens] (int64).  A token whose logical block index is
- * >= bt_stride gets slot -1.  num_tokens == 0 is a no-op. */
+ * Writes slot_mapping[num_tokens] (int64).  query_start_loc holds num_seqs + 1 ascending
+ * entries (requests with no new token are allowed); token t belongs to the request r with
+ * query_start_loc[r] <= t < query_start_loc[r + 1].  A token whose logical block index is
+ * >= bt_stride, or whose position is negative, gets slot -1 (so does a token that no request
+ * owns, which only a malformed query_start_loc produces).  num_tokens == 0 is a no-op. */
 int pkv_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
                              const int32_t* query_start_loc, const int32_t* context_lens,
                              int32_t num_seqs, int32_t num_tokens, const pkv_shape* shape,

@@ -599,3 +599,37 @@ def test_slot_search_over_many_requests(num_req, num_kv_heads, head_dim):
     assert np.array_equal(slots2.cpu().numpy(), ref), "append_kv slots differ"
     kp, vp = O.reshape_and_cache(st.k, st.v, wl.k_cache, wl.v_cache, ref, wl.block_size)
     assert np.array_equal(host16(kc), kp) and np.array_equal(host16(vc), vp), "pool bits differ"
+
+
+def test_slots_past_the_table_or_before_zero_are_skipped():
+    """Requests whose positions run past the block table, or are negative, get slot -1 for
+    those tokens and write nothing; the other requests' slots and pool bits equal the oracle's."""
+    wl = W.decode_only(seed=31, num_seqs=40, ctx_range=(5, 600))
+    st = wl.steps[0]
+    B = st.num_seqs
+    ql = np.diff(st.query_start_loc).astype(np.int64)
+    bad_past, bad_neg = [3, 17, 29], [8, 30]
+    ql2 = ql.copy()
+    ql2[bad_past + bad_neg] = 3
+    ctx2 = st.context_lens.astype(np.int64).copy()
+    ctx2[bad_past] = wl.bt_stride * wl.block_size + np.array([0, 5, 40])  # every position past the table
+    ctx2[bad_neg] = -4  # positions -4, -3, -2
+    qsl2 = np.concatenate([[0], np.cumsum(ql2)]).astype(np.int32)
+    T = int(qsl2[-1])
+    rng = np.random.default_rng(31)
+    k = W.f32_to_bf16_bits(rng.standard_normal((T, wl.num_kv_heads, wl.head_dim)).astype(np.float32))
+    v = W.f32_to_bf16_bits(rng.standard_normal((T, wl.num_kv_heads, wl.head_dim)).astype(np.float32))
+    good = np.array([r for r in range(B) if r not in bad_past + bad_neg])
+    good_tok = np.concatenate([np.arange(qsl2[r], qsl2[r + 1]) for r in good])
+    qsl_good = np.concatenate([[0], np.cumsum(ql2[good])]).astype(np.int32)
+    ref = np.full(T, -1, dtype=np.int64)
+    ref[good_tok] = O.slot_mapping(st.block_tables[good], qsl_good, ctx2[good], wl.block_size)
+    dw = DeviceWorkload(wl)
+    btd, qsld, ctxd = dev32(st.block_tables), dev32(qsl2), dev32(ctx2)
+    slots = P.compute_slot_mapping(btd, qsld, ctxd, dw.shape, T)
+    slots2 = torch.empty(T, dtype=torch.int64, device="cuda")
+    P.append_kv(dev16(k), dev16(v), dw.k_cache, dw.v_cache, btd, qsld, ctxd, dw.shape, slot_mapping=slots2)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots.cpu().numpy(), ref) and np.array_equal(slots2.cpu().numpy(), ref)
+    kp, vp = O.reshape_and_cache(k, v, wl.k_cache, wl.v_cache, ref, wl.block_size)
+    assert np.array_equal(host16(dw.k_cache), kp) and np.array_equal(host16(dw.v_cache), vp)
