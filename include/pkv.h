@@ -9,10 +9,11 @@
  *                 key blocks, token-major (a key is one contiguous row).
  *   v_cache       bf16 [num_blocks, num_kv_heads, head_dim, 16]: physical value blocks,
  *                 dim-major (16 tokens of one dimension are contiguous).
- *                 A block of 256 tokens ("11. vLLM principles", section 11.2: blocks of 16 or
- *                 256 tokens) is 16 consecutive such 16-token tiles: k_cache
- *                 [num_blocks, 16, num_kv_heads, 16, head_dim], v_cache
- *                 [num_blocks, 16, num_kv_heads, head_dim, 16].  Either way slot s (below) is
+ *                 A block of bs = 16 R tokens (R = 2, 4, 8 or 16: blocks of 32 to 256 tokens;
+ *                 "11. vLLM principles", section 11.2 names blocks of 16 or 256 tokens) is R
+ *                 consecutive such 16-token tiles: k_cache
+ *                 [num_blocks, R, num_kv_heads, 16, head_dim], v_cache
+ *                 [num_blocks, R, num_kv_heads, head_dim, 16].  Either way slot s (below) is
  *                 row s % 16 of 16-token tile s / 16 of the pool.
  *                 Token p of a request lives in physical block block_tables[r][p / bs] at
  *                 offset p % bs ("11. vLLM principles", section 11.2 PagedAttention).
@@ -61,7 +62,7 @@ extern "C" {
 #define PKV_DTYPE_F32 1
 
 /* Static shape of one attention layer's cache.  Supported: head_dim 64 or 128,
- * block_size 16 or 256, num_q_heads / num_kv_heads in {1, 2, 4, 8}. */
+ * block_size 16, 32, 64, 128 or 256, num_q_heads / num_kv_heads in {1, 2, 4, 8}. */
 typedef struct pkv_shape {
   int32_t num_q_heads;
   int32_t num_kv_heads;

@@ -59,7 +59,7 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 # keys [NB, R, Hkv, T, D] (a key is one row of its tile), values [NB, R, Hkv, D, T] (the T
 # tokens of one dimension are contiguous).  With R = 1 the tile axis is dropped: keys
 # [NB, Hkv, bs, D], values [NB, Hkv, D, bs].  The library uses T = 16: one tile for 16-token
-# blocks, 16 tiles for 256-token blocks.  (Layout reading: the pages fix no layout.)
+# blocks, bs / 16 tiles for larger blocks.  (Layout reading: the pages fix no layout.)
 # ---------------------------------------------------------------------------
 def tiles(pool: np.ndarray) -> np.ndarray:
     """The pool as [NB, R, Hkv, T, D] (keys) or [NB, R, Hkv, D, T] (values); a view."""

@@ -46,8 +46,9 @@ int check_shape(const pkv_shape* s) {
   if (!s) return fail(PKV_EINVAL, "shape is null");
   if (s->head_dim != 64 && s->head_dim != 128)
     return fail(PKV_EINVAL, "head_dim %d unsupported (64 or 128)", s->head_dim);
-  if (s->block_size != 16 && s->block_size != 256)
-    return fail(PKV_EINVAL, "block_size %d unsupported (16 or 256)", s->block_size);
+  if (s->block_size != 16 && s->block_size != 32 && s->block_size != 64 && s->block_size != 128 &&
+      s->block_size != 256)
+    return fail(PKV_EINVAL, "block_size %d unsupported (16, 32, 64, 128 or 256)", s->block_size);
   if (s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->num_q_heads % s->num_kv_heads)
     return fail(PKV_EINVAL, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
                 s->num_q_heads, s->num_kv_heads);
@@ -61,8 +62,8 @@ int check_shape(const pkv_shape* s) {
   return PKV_OK;
 }
 
-// log2(block_size) and log2(block_size / 16) of a checked shape.
-int32_t bs_log2(const pkv_shape* s) { return s->block_size == 256 ? 8 : 4; }
+// log2(block_size) and log2(block_size / 16) of a checked shape (block_size a power of two).
+int32_t bs_log2(const pkv_shape* s) { return __builtin_ctz((unsigned)s->block_size); }
 int32_t bt_shift(const pkv_shape* s) { return bs_log2(s) - 4; }
 
 float scale_log2(const pkv_shape* s) {

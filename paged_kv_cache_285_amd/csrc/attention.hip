@@ -136,7 +136,7 @@ __device__ __forceinline__ u32x4 widen8(u32x2 c) {
 __device__ __forceinline__ u32x4 widen8(u32x4 c) { return c; }
 
 // Physical 16-token tile of logical tile j of a request.  A block of 16 << L tokens is 1 << L
-// consecutive 16-token tiles (L = 0 for 16-token blocks, 4 for 256-token blocks), so the tile
+// consecutive 16-token tiles (L = 0 for 16-token blocks, ..., 4 for 256-token blocks), so the tile
 // is (block_tables[j >> L] << L) + the low L bits of j.
 template <typename IntPtr>
 __device__ __forceinline__ int tile_of(IntPtr bt, int j, int L) {

@@ -97,7 +97,7 @@ slot_mapping_kernel(int64_t* __restrict__ slots, const int32_t* __restrict__ bt,
 }
 
 // One thread per 16-byte chunk (8 bf16) of one token's K and V for one kv head.  A slot names
-// (block, offset).  A block of 16 or 256 tokens is 1 or 16 consecutive 16-token tiles, so
+// (block, offset).  A block of 16 R tokens (R = 1, 2, ..., 16) is R consecutive 16-token tiles, so
 // slot / 16 is the token's 16-token tile in the pool and slot % 16 its row there, whatever the
 // block size.  The key pool is [tiles, Hkv, 16, D]: the token's key is one 16-byte store.  The
 // value pool is [tiles, Hkv, D, 16] (dim-major, so attention can read 16-token rows of one

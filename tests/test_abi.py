@@ -51,7 +51,7 @@ def shape(P, **kw):
 
 def test_shape_validation_errors(P):
     lib = P.lib()
-    for bad in (dict(head_dim=96), dict(num_q_heads=12), dict(num_q_heads=48, num_kv_heads=4), dict(block_size=32)):
+    for bad in (dict(head_dim=96), dict(num_q_heads=12), dict(num_q_heads=48, num_kv_heads=4), dict(block_size=48)):
         s = shape(P, **bad)
         rc = lib.pkv_reshape_and_cache(None, None, None, None, None, 0, ctypes.byref(s), None)
         assert rc == -1, bad
@@ -67,18 +67,28 @@ def test_shape_validation_errors(P):
     assert lib.pkv_copy_blocks(None, None, None, 3, ctypes.byref(s), None) == -1
 
 
-def test_block_size_256_accepted_and_checked(P):
+@pytest.mark.parametrize("bs", [32, 64, 128, 256])
+def test_block_sizes_accepted_and_checked(P, bs):
     lib = P.lib()
-    s = shape(P, block_size=256, num_blocks=100, bt_stride=4)
+    s = shape(P, block_size=bs, num_blocks=100, bt_stride=4)
     assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, ctypes.byref(s), None) == 0
-    # 4 entries of 256 tokens cover 1024 tokens; 1025 do not
-    ok_plan, _ = P.plan_varlen_host([0, 1], [1023], [1024], s)
+    # 4 entries of bs tokens cover 4 * bs tokens; one more does not
+    ok_plan, _ = P.plan_varlen_host([0, 1], [4 * bs - 1], [4 * bs], s)
     assert ok_plan.num_items >= 1
     with pytest.raises(P.PkvError):
-        P.plan_varlen_host([0, 1], [1024], [1025], s)
-    assert lib.pkv_cascade_prefix_attention(None, None, None, None, None, None, 512 + 16, 4, ctypes.byref(s), None, 0, None) == -3
-    huge = shape(P, block_size=256, num_blocks=1 << 28)
+        P.plan_varlen_host([0, 1], [4 * bs], [4 * bs + 1], s)
+    assert lib.pkv_cascade_prefix_attention(None, None, None, None, None, None, 2 * bs + 16, 4, ctypes.byref(s), None, 0, None) == -3
+    huge = shape(P, block_size=bs, num_blocks=(1 << 31) // (bs // 16))
     assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, ctypes.byref(huge), None) == -1
+    fits = shape(P, block_size=bs, num_blocks=((1 << 31) - 1) // (bs // 16))
+    assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, ctypes.byref(fits), None) == 0
+
+
+@pytest.mark.parametrize("bs", [0, 8, 24, 48, 96, 512, -16])
+def test_other_block_sizes_rejected(P, bs):
+    s = shape(P, block_size=bs)
+    assert P.lib().pkv_reshape_and_cache(None, None, None, None, None, 0, ctypes.byref(s), None) == -1
+    assert b"block_size" in P.lib().pkv_last_error()
 
 
 def test_decode_entry_points_validate_before_launching(P):
@@ -210,8 +220,8 @@ def test_plan_covers_every_row_exactly_once(P, lengths):
 def test_workspace_bound_holds_for_every_plan(P):
     rng = np.random.default_rng(1)
     for trial in range(40):
-        bs = int(rng.choice([16, 256]))
-        s = shape(P, bt_stride=700 if bs == 16 else 44, block_size=bs, num_q_heads=int(rng.choice([8, 16, 32, 64])))
+        bs = int(rng.choice([16, 32, 64, 128, 256]))
+        s = shape(P, bt_stride=-(-10500 // bs), block_size=bs, num_q_heads=int(rng.choice([8, 16, 32, 64])))
         B = int(rng.integers(1, 300))
         # decode rows, short rows (ql * G <= 32), cut rows (<= 64), tiles, and empty rows
         ql = rng.choice([0, 1, 1, 1, 2, 3, 4, 8, 12, 16, 32, 64, 500], size=B)

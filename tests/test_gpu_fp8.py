@@ -314,6 +314,13 @@ def test_fp8_block_size_256_parity(case):
         run_and_check_fp8(W.decode_only(seed=32, num_seqs=20, ctx_range=(30, 5000), block_size=256), seed=32)
 
 
+@pytest.mark.parametrize("bs", [32, 128])
+def test_fp8_block_sizes_32_and_128_parity(bs):
+    """fp8 pools of 32- and 128-token blocks (one scale per block and kv head): the mixed batch."""
+    say(f"fp8, {bs}-token blocks: mixed")
+    run_and_check_fp8(W.mixed_llama8b(seed=70 + bs, num_decode=10, ctx_range=(20, 1500), block_size=bs), seed=70 + bs)
+
+
 def test_fp8_append_kv_over_many_requests_bitwise():
     """The quantising fused append over 1500 requests with runs of requests that have no new
     token (the workgroup owner search's coarse round): slots and pool bytes equal the oracle's."""

@@ -577,6 +577,68 @@ def test_block_size_256_full_size_decode_sampled():
     run_and_check(W.decode_only(seed=0, block_size=256), rows_per_step=48, check_pools=False)
 
 
+# ---------------------------------------------------------------------------
+# Blocks of 32, 64 and 128 tokens (2, 4 and 8 tiles of 16 tokens)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("bs", [32, 64, 128])
+@pytest.mark.parametrize("case", ["mixed", "decode"])
+def test_block_sizes_32_to_128_parity(case, bs):
+    say(f"{bs}-token blocks: {case}")
+    if case == "mixed":
+        run_and_check(W.mixed_llama8b(seed=60 + bs, num_decode=12, ctx_range=(20, 1500), block_size=bs))
+    else:
+        run_and_check(W.decode_only(seed=61 + bs, num_seqs=24, ctx_range=(1, 6000), block_size=bs))
+
+
+@pytest.mark.parametrize("bs", [32, 128])
+def test_block_sizes_wide_tiles_and_cascade(bs):
+    say(f"{bs}-token blocks: 256-row tiles, then cascade prefix + suffix + merge")
+    wl = W.long_chunked_prefill(seed=62 + bs, prompt=4096, chunk=2048, num_decode=8, decode_ctx=300, block_size=bs)
+    run_and_check(wl, rows_per_step=200, expect_tile_rows=256)
+    _cascade_check(W.cascade_shared_prefix(seed=63 + bs, num_queries=40, prefix=1024, suffix_range=(1, 300),
+                                           block_size=bs))
+
+
+def test_block_size_64_copy_on_write_then_device_split_decode():
+    """64-token blocks, copy-on-write: a third of the requests' blocks are copied into spare
+    blocks (bit for bit, as the oracle's copy) and those block-table entries are pointed at the
+    copies; the fused append and the device-split decode over the remapped tables then match
+    the oracle over the same tables."""
+    say("64-token blocks: copy_blocks into spare blocks, remapped tables, device-split decode")
+    wl = W.decode_only(seed=64, num_seqs=20, ctx_range=(1, 5000), block_size=64)
+    st = wl.steps[0]
+    dw = DeviceWorkload(wl)
+    used = np.concatenate([st.block_tables[r, : -(-int(st.seq_lens[r]) // wl.block_size)] for r in range(st.num_seqs)])
+    spare = np.setdiff1d(np.arange(wl.num_blocks), st.block_tables)
+    rng = np.random.default_rng(64)
+    n = min(len(spare), len(used) // 3)
+    src = rng.choice(used, size=n, replace=False)
+    dst = rng.choice(spare, size=n, replace=False)
+    pairs = np.stack([src, dst], axis=1).astype(np.int32)
+    P.copy_blocks(dw.k_cache, dw.v_cache, dev32(pairs), dw.shape)
+    torch.cuda.synchronize()
+    kc, vc = O.copy_blocks(wl.k_cache, wl.v_cache, pairs)
+    assert np.array_equal(host16(dw.k_cache), kc) and np.array_equal(host16(dw.v_cache), vc)
+    remap = np.arange(wl.num_blocks, dtype=np.int32)
+    remap[src] = dst
+    bt = remap[st.block_tables]
+    t = dw.step_tensors(st)
+    t["bt"] = dev32(bt)
+    P.append_kv(t["k"], t["v"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], t["ctx"], dw.shape)
+    max_seq = wl.bt_stride * wl.block_size
+    ws = P.alloc_workspace(P.decode_workspace_size(st.num_seqs, max_seq, dw.shape))
+    lse = torch.empty(st.q.shape[:2], dtype=torch.float32, device="cuda")
+    out = P.paged_attention_decode(t["q"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], t["seq"], dw.shape, max_seq,
+                                   workspace=ws, lse=lse)
+    torch.cuda.synchronize()
+    slots = O.slot_mapping(bt, st.query_start_loc, st.context_lens, wl.block_size)
+    kp, vp = O.reshape_and_cache(st.k, st.v, kc, vc, slots, wl.block_size)
+    assert np.array_equal(host16(dw.k_cache), kp) and np.array_equal(host16(dw.v_cache), vp)
+    ref, lref = O.paged_attention(st.q, kp, vp, bt, st.query_start_loc, st.context_lens, st.seq_lens, wl.block_size)
+    say(f"    {n} blocks copied; {check_attention(bf16_out_to_f64(out), ref, 'device-split decode, 64-token blocks')}")
+    check_lse(lse.cpu().numpy(), lref, "device-split decode lse, 64-token blocks")
+
+
 @pytest.mark.parametrize("num_req,num_kv_heads,head_dim", [(900, 2, 64), (200, 1, 64), (3000, 8, 128)])
 def test_slot_search_over_many_requests(num_req, num_kv_heads, head_dim):
     """Slot mapping and the fused append over batches with more requests than a workgroup has

@@ -296,7 +296,7 @@ def _dense_attention(q, keys, vals, positions, scale):
     return np.einsum("lhs,shd->lhd", w, vals)
 
 
-@pytest.mark.parametrize("block_size", [16, 256])
+@pytest.mark.parametrize("block_size", [16, 32, 256])
 def test_mixed_batch_matches_dense_contiguous_attention(block_size):
     """Paging invariance: the paged oracle equals dense attention on keys laid out in logical order."""
     wl = W.mixed_llama8b(seed=2, num_decode=6, ctx_range=(20, 90 if block_size == 16 else 600), block_size=block_size)
@@ -573,26 +573,27 @@ def test_workload_poison_covers_unwritten_slots():
 
 
 # ---------------------------------------------------------------------------
-# 256-token blocks: a block of 16 tiles behaves as 16 blocks of 16 tokens
+# Blocks of 16 R tokens: a block of R tiles behaves as R blocks of 16 tokens
 # ---------------------------------------------------------------------------
-def test_block_size_256_is_sixteen_16_token_blocks():
-    """A 256-token block is 16 consecutive 16-token tiles: the bs=256 pool read as a bs=16 pool of
-    16x the blocks, with table entry 16 b + i for tile i of block b, must give the same slots'
+@pytest.mark.parametrize("bs", [32, 64, 256])
+def test_large_block_is_r_16_token_blocks(bs):
+    """A block of bs = 16 R tokens is R consecutive 16-token tiles: the pool read as a bs=16 pool
+    of R x the blocks, with table entry R b + i for tile i of block b, must give the same slots'
     bytes and the same attention, bit for bit."""
-    wl = W.mixed_llama8b(seed=5, num_decode=7, ctx_range=(200, 900), block_size=256)
-    R = 16
+    wl = W.mixed_llama8b(seed=5, num_decode=7, ctx_range=(200, 900), block_size=bs)
+    R = bs // 16
     kp, vp = wl.k_cache, wl.v_cache
     k16 = kp.reshape(wl.num_blocks * R, wl.num_kv_heads, 16, wl.head_dim)
     v16 = vp.reshape(wl.num_blocks * R, wl.num_kv_heads, wl.head_dim, 16)
     for st in wl.steps:
         bt16 = (st.block_tables[:, :, None] * R + np.arange(R)[None, None, :]).reshape(st.num_seqs, -1).astype(np.int32)
-        s256 = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, 256)
+        sbig = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, bs)
         s16 = O.slot_mapping(bt16, st.query_start_loc, st.context_lens, 16)
-        assert np.array_equal(s256, s16)
-        kp, vp = O.reshape_and_cache(st.k, st.v, kp, vp, s256, 256)
+        assert np.array_equal(sbig, s16)
+        kp, vp = O.reshape_and_cache(st.k, st.v, kp, vp, sbig, bs)
         k16, v16 = O.reshape_and_cache(st.k, st.v, k16, v16, s16, 16)
         assert np.array_equal(kp.reshape(k16.shape), k16) and np.array_equal(vp.reshape(v16.shape), v16)
         args = (st.query_start_loc, st.context_lens, st.seq_lens)
-        o256, l256 = O.paged_attention(st.q, kp, vp, st.block_tables, *args, 256)
+        obig, lbig = O.paged_attention(st.q, kp, vp, st.block_tables, *args, bs)
         o16, l16 = O.paged_attention(st.q, k16, v16, bt16, *args, 16)
-        assert np.array_equal(o256, o16) and np.array_equal(l256, l16)
+        assert np.array_equal(obig, o16) and np.array_equal(lbig, l16)
