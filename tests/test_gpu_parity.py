@@ -128,12 +128,19 @@ def test_spec_verify_small_parity():
 
 
 def test_short_rows_split_at_key_boundaries():
-    """Short rows cut into 1024-key splits, with contexts placed so that the last split starts
-    before, at, and after the first query's position (a token can see no key of a split)."""
+    """Short rows cut into key splits (512 keys for this batch), with contexts placed so that
+    a split starts before, at, and after the first query's position (a token can see no key of
+    a split)."""
     say("short rows over long contexts: split boundaries")
     ctxs = [1019, 1020, 1023, 1024, 1025, 2043, 2047, 2048, 3071, 1100]
     reqs = [W.RequestSpec(c, [5]) for c in ctxs] + [W.RequestSpec(1500, [16]), W.RequestSpec(1030, [2])]
     wl = W.build("short_rows", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=13)
+    st = wl.steps[0]
+    shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride)
+    _, items = P.plan_varlen_host(st.query_start_loc, st.context_lens, st.seq_lens, shape)
+    short = items[items[:, 1] == 2]
+    # the rows at context 1020 .. 1025 have a split starting at key 1024, as the cases need
+    assert all(1024 in short[short[:, 0] == r, 4] for r in range(1, 5))
     run_and_check(wl)
 
 
