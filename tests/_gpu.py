@@ -2,6 +2,8 @@
 
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 import torch
 
@@ -39,13 +41,48 @@ def bf16_spacing(x: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
+# Set by peaked_tolerance(): the per-element bound for inputs whose softmax rows one key dominates.
+_PEAKED_ATOL = None
+
+
+@contextlib.contextmanager
+def peaked_tolerance(wl, fp8: bool = False):
+    """Element bound for rows whose softmax one key dominates (large-magnitude scores).
+
+    The kernels round each p to bf16 (unit roundoff 2^-8) before it weights the values, while
+    the fp32 sum of the unrounded p normalises; for a row whose weight sits on one key the
+    output then moves by up to 2^-8 of that key's value, which for N(0, 1) values reaches
+    ~0.018, past the 1e-2 that spread rows keep.  So inside this context
+    |gpu - ref| <= 2^-8 * max|v| + 2^-8 * |ref| (its own bf16 output rounding) + 1e-4, with
+    max|v| over every value of the workload (fp8 pools: 2^-4 more for the e4m3 code rounding).
+    Relative L2 keeps its bound."""
+    global _PEAKED_ATOL
+    arrs = [wl.v_cache] + [st.v for st in wl.steps]
+    vmax = max(float(np.nanmax(np.abs((a.astype(np.uint32) << 16).view(np.float32)))) for a in arrs)
+    _PEAKED_ATOL = 2.0**-8 * vmax * (1.0 + 2.0**-4 if fp8 else 1.0) + 1e-4
+    try:
+        yield _PEAKED_ATOL
+    finally:
+        _PEAKED_ATOL = None
+
+
 def check_attention(gpu: np.ndarray, ref: np.ndarray, what: str, bf16_out: bool = True) -> dict:
     """Assert max |gpu - ref| <= ATOL (allowing elements whose only error is bf16 output
-    rounding, i.e. gpu is a bf16 neighbour of ref) and relative L2 <= RTOL_L2."""
+    rounding, i.e. gpu is a bf16 neighbour of ref) and relative L2 <= RTOL_L2; inside
+    peaked_tolerance() the element bound is that context's instead."""
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     assert np.isfinite(ref).all(), f"{what}: oracle produced non-finite values"
     assert np.isfinite(gpu).all(), f"{what}: GPU produced non-finite values at {np.argwhere(~np.isfinite(gpu))[:5]}"
     err = np.abs(gpu - ref)
+    if _PEAKED_ATOL is not None:
+        bound = _PEAKED_ATOL + 2.0**-8 * np.abs(ref)
+        assert (err <= bound).all(), (
+            f"{what}: {int((err > bound).sum())} elements exceed the peaked-row bound; worst excess "
+            f"{(err - bound).max():.4g} at {np.unravel_index((err - bound).argmax(), err.shape)}"
+        )
+        rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
+        assert rel <= RTOL_L2, f"{what}: relative L2 {rel:.3g} > {RTOL_L2}"
+        return {"max_abs": float(err.max()) if err.size else 0.0, "rel_l2": rel, "peaked_atol": _PEAKED_ATOL}
     bad = err > ATOL
     rounding_only = 0
     if bad.any():

@@ -21,7 +21,7 @@ if not torch.cuda.is_available():  # pragma: no cover - collected on CPU, skippe
     pytest.skip("no GPU", allow_module_level=True)
 
 import paged_kv_cache_285_amd as P  # noqa: E402
-from _gpu import bf16_out_to_f64, check_attention, check_lse, dev16, dev32, many_requests  # noqa: E402
+from _gpu import bf16_out_to_f64, check_attention, check_lse, dev16, dev32, many_requests, peaked_tolerance  # noqa: E402
 
 
 def say(*a):
@@ -246,6 +246,35 @@ def test_fp8_decode_device_split_parity():
                                       st.context_lens, st.seq_lens, wl.block_size)
     check_attention(bf16_out_to_f64(out), ref, "fp8 device-split decode")
     check_lse(lse.cpu().numpy(), lref, "fp8 device-split decode lse")
+
+
+def _large_scores(wl, factor=16.0):
+    """Every query times `factor` (exact on bf16 bits): the running maximum of a row moves far
+    past its 2^8 window after the first tile or block, so the rescale branches run."""
+    for st in wl.steps:
+        x = (st.q.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+        assert np.isfinite(x).all()
+        st.q[...] = (x.view(np.uint32) >> 16).astype(np.uint16)
+    return wl
+
+
+def test_fp8_large_scores_take_the_rescale_paths():
+    """fp8 pools with queries 16x N(0, 1): split and unsplit decode rows, a speculative-verify
+    row, a chunk on 128-row tiles, then a long chunk on 256-row pipelined tiles and the cascade."""
+    say("fp8 large scores")
+    reqs = [W.RequestSpec(c, [1]) for c in (3000, 1500, 700, 40)]
+    reqs += [W.RequestSpec(2000, [5]), W.RequestSpec(300, [200])]
+    wl = W.build("fp8_large_mixed", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=31)
+    with peaked_tolerance(wl, fp8=True):
+        run_and_check_fp8(_large_scores(wl), seed=31)
+    reqs = [W.RequestSpec(300, [2048 // 4 + 37]), W.RequestSpec(2500, [1])]
+    wl = W.build("fp8_large_wide", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=32)
+    with peaked_tolerance(wl, fp8=True):
+        run_and_check_fp8(_large_scores(wl), seed=32, expect_tile_rows=256)
+    wl = W.cascade_shared_prefix(seed=33, num_queries=70, prefix=1040, suffix_range=(1, 200),
+                                 num_q_heads=16, num_kv_heads=2, head_dim=128)
+    with peaked_tolerance(wl, fp8=True):
+        _fp8_cascade_check(_large_scores(wl))
 
 
 def test_fp8_cascade_small_parity():

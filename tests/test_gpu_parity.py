@@ -28,6 +28,7 @@ from _gpu import (  # noqa: E402
     dev16,
     dev32,
     host16,
+    peaked_tolerance,
 )
 
 
@@ -431,6 +432,50 @@ def test_permutation_invariance_and_rerun_bit_identical():
     a = o1.view(torch.int16).cpu().numpy()
     assert np.array_equal(a, o1b.view(torch.int16).cpu().numpy())
     assert np.array_equal(a, o2.view(torch.int16).cpu().numpy())
+
+
+def _scale_bf16(bits: np.ndarray, factor: float) -> np.ndarray:
+    """bf16 bit patterns times a power of two (exact while nothing overflows)."""
+    x = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+    assert np.isfinite(x).all()
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _large_scores(wl, factor=16.0):
+    """Every query times `factor`: scaled scores then spread over ~+-70 in log2 units, so the
+    running maximum of a row moves by far more than its 2^8 window after the first tile or block
+    and the kernels take their rescale branches (output and row sum times exp2(m_old - m_new)),
+    which N(0, 1) queries never reach.  Most rows' softmax then sits on one or two keys."""
+    for st in wl.steps:
+        st.q[...] = _scale_bf16(st.q, factor)
+    return wl
+
+
+@pytest.mark.parametrize("case", ["mixed", "wide"])
+def test_large_scores_take_the_rescale_paths(case):
+    """Decode rows (split and unsplit), a speculative-verify row (short item), a chunk over a
+    cached context (128-row tiles) and, for "wide", a long chunk on 256-row pipelined tiles, all
+    with queries 16x N(0, 1); the element bound is the peaked-row one (p rounding)."""
+    say(f"large scores: {case}")
+    if case == "mixed":
+        reqs = [W.RequestSpec(c, [1]) for c in (3000, 1500, 700, 40)]
+        reqs += [W.RequestSpec(2000, [5]), W.RequestSpec(300, [200])]
+        wl = W.build("large_mixed", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=21)
+        with peaked_tolerance(wl):
+            run_and_check(_large_scores(wl))
+    else:
+        reqs = [W.RequestSpec(300, [2048 // 4 + 37]), W.RequestSpec(2500, [1])]
+        wl = W.build("large_wide", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=22)
+        with peaked_tolerance(wl):
+            run_and_check(_large_scores(wl), expect_tile_rows=256)
+
+
+def test_large_scores_cascade():
+    say("large scores: cascade")
+    wl = W.cascade_shared_prefix(seed=23, num_queries=70, prefix=1040, suffix_range=(1, 200),
+                                 num_q_heads=16, num_kv_heads=2, head_dim=128)
+    with peaked_tolerance(wl):
+        _cascade_check(_large_scores(wl))
 
 
 def test_cascade_small_parity():
