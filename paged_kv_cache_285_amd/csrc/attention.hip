@@ -1549,8 +1549,12 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
         pipe_mask<D, CUR, CAUSAL>(R, h, k0, kv_end);
       bool need;
       float mnew, ts;
+      // A wave in its matrix/softmax block issues ahead of the other wave on its SIMD while that
+      // one runs its commit, LDS stores and barrier wait (1-3 % faster than equal priority).
+      __builtin_amdgcn_s_setprio(1);
       pipe_step<D, CUR, FP8>(R, kbuf0 + ((t + 1) & 1) * S::K_ELEMS, vbuf0 + ((t + 1) & 1) * S::V_ELEMS, n, h,
                              sl, tsc, need, mnew, ts);
+      __builtin_amdgcn_s_setprio(0);
       pipe_commit<D>(R, need, mnew, ts);
 #pragma unroll
       for (int j = 0; j < J; ++j) store(j, t & 1, st[j], nv[j], ksv[j], vsv[j], (t + 2) % 3);
