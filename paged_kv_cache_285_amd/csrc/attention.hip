@@ -864,6 +864,19 @@ struct TileSmem {
   static constexpr int BYTES = SC_OFF + SC_SLOTS * 8 * 4;
 };
 
+// LDS of the pipelined 256-row tile: a ring of four K and four V tile buffers (same pitches
+// as TileSmem), so that a tile is staged three steps (K) or one step (V) before its use and one
+// barrier serves two steps, then eight fp8 scale slots.  143.6 KB at D = 128.
+template <int D>
+struct PipeSmem {
+  using T = TileSmem<D>;
+  static constexpr int NB = 4;                       // ring depth (power of two)
+  static constexpr int V_OFF = NB * T::K_ELEMS;      // bf16 elements to the first V buffer
+  static constexpr int SC_OFF = NB * T::BUF_ELEMS * 2;  // byte offset of the scale slots
+  static constexpr int SC_SLOTS = 8;                 // per tile: 4 key scales, then 4 value scales
+  static constexpr int BYTES = SC_OFF + SC_SLOTS * 8 * 4;
+};
+
 // The key and value scales of a tile's 4 cache blocks, read (uniformly) from scale slot `sc`.
 struct TileScales {
   float k[4], v[4];
@@ -1187,10 +1200,11 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
 // tile loop is software-pipelined so that one wave's instruction stream mixes matrix and vector
 // work: step t issues the MFMAs of S^T(t+1) = K(t+1) Q^T and O^T += V(t-1)^T P^T(t-1) while the
 // VALU computes the softmax of tile t (whose S^T the previous step produced).  Step t also
-// loads K(t+2) and V(t) at its start and stores them into LDS at its end (waves 0-3 copy K,
-// waves 4-7 copy V; two buffers each), with one barrier per step.  P^T is built from the S^T accumulator with
-// two lane-half swaps per K-step so that a lane holds 8 consecutive keys; the V^T operand is
-// then one 16-byte read of the value tile in its natural dim-major order.
+// loads K(t+3) and V(t+1) at its start and stores them into LDS at its end (waves 0-3 copy K,
+// waves 4-7 copy V; a ring of four buffers each), with one barrier per two steps.  P^T is built
+// from the S^T accumulator with two lane-half swaps per K-step so that a lane holds 8
+// consecutive keys; the V^T operand is then one 16-byte read of the value tile in its natural
+// dim-major order.
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct PipeRegs {
@@ -1374,6 +1388,8 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
                           int kv_begin, int kv_end, float sl, void* out, int out_f32, float* lse_out,
                           char* smem_raw) {
   using S = TileSmem<D>;
+  using PS = PipeSmem<D>;
+  constexpr int NB = PS::NB;
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
   constexpr int CH = D / 8;             // 16-byte chunks per key row
@@ -1387,7 +1403,7 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
   const int h = lane >> 5;
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
   uint16_t* kbuf0 = smem;
-  uint16_t* vbuf0 = smem + 2 * S::K_ELEMS;
+  uint16_t* vbuf0 = smem + PS::V_OFF;
 
   PipeRegs<D> R;
   const int pr = 32 * wave + n;
@@ -1429,10 +1445,10 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
     // Physical ids of the wave's blocks of 64 consecutive tiles, one per lane (read back with
     // readlane, so the per-tile address needs no memory wait); refreshed every 64 tiles.
     // fp8 pools: the waves that copy K also hold the key and value scales of those blocks,
-    // alike, and put each tile's scales into scale slot tile % 3 (read by every wave in the
-    // tile's softmax step; the slot is rewritten two steps later, past two barriers).
+    // alike, and put each tile's scales into scale slot tile % 8 (read by every wave in the
+    // tile's softmax step; the slot is rewritten five steps later, past two barriers).
     using C8 = ChunkV<FP8>;
-    float* scl = reinterpret_cast<float*>(smem_raw + S::SC_OFF);
+    float* scl = reinterpret_cast<float*>(smem_raw + PS::SC_OFF);
     int bid_base = 0;
     int bid = tile_of(bt, min(blk0 + 4 * lane, last_blk), L);
     float bks = 1.f, bvs = 1.f;
@@ -1463,11 +1479,11 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       jv[j] = wave >= 4;
       jbase[j] = reinterpret_cast<const C8*>(jv[j] ? v_cache : k_cache) + (int64_t)g * tile_stride;
       // Chunk lane + 64i of the block tile: ((KPI*i + sr)*CH + sc) is that same index for K rows.
-      soff[j] = jv[j] ? 2 * S::K_ELEMS + (lane >> 1) * S::VP + kBlockSize * sblk + 8 * (lane & 1)
+      soff[j] = jv[j] ? PS::V_OFF + (lane >> 1) * S::VP + kBlockSize * sblk + 8 * (lane & 1)
                       : (kBlockSize * sblk + sr) * S::KP + sc * 8;
       sstep[j] = jv[j] ? 32 * S::VP : KPI * S::KP;
     }
-    // K tiles alternate between the two K buffers, V tiles between the two V buffers.
+    // Tile x goes to K buffer x % NB or V buffer x % NB.
     auto load = [&](int j, int tile, C8 (&r)[NI], float& ks, float& vs) __attribute__((always_inline)) -> int {
       const int lb = blk0 + 4 * tile;
       const C8* p = jbase[j] + (int64_t)block_id(tile, ks, vs) * blk_stride;
@@ -1503,21 +1519,26 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       }
     };
 
-    // Prologue: K(0) and K(1) in LDS, V(-1) = 0 (no tile before the first), S^T(0) computed.
+    // Prologue: K(0), K(1), K(2) and V(0) in LDS, V(-1) = 0 (no tile before the first),
+    // S^T(0) computed.
     C8 st[J][NI];
     int nv[J];
     float ksv[J], vsv[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       if (!jv[j]) {
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+          nv[j] = load(j, x, st[j], ksv[j], vsv[j]);
+          store(j, x, st[j], nv[j], ksv[j], vsv[j], x);
+        }
+      } else {
         nv[j] = load(j, 0, st[j], ksv[j], vsv[j]);
         store(j, 0, st[j], nv[j], ksv[j], vsv[j], 0);
-        nv[j] = load(j, 1, st[j], ksv[j], vsv[j]);
-        store(j, 1, st[j], nv[j], ksv[j], vsv[j], 1);
       }
     }
     {
-      u32x4* z = reinterpret_cast<u32x4*>(vbuf0 + S::V_ELEMS);
+      u32x4* z = reinterpret_cast<u32x4*>(vbuf0 + (NB - 1) * S::V_ELEMS);
       for (int i = threadIdx.x; i < S::V_ELEMS / 8; i += 512) z[i] = u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
@@ -1535,15 +1556,17 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) R.pb[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 
-    // Step t: load K(t+2) / V(t), compute S^T(t+1), P.V(t-1) and softmax(t), then store the
-    // loaded tiles (their buffers were last read in step t-1), so the whole step covers the load.
+    // Step t: load K(t+3) / V(t+1), compute S^T(t+1), P.V(t-1) and softmax(t), then store the
+    // loaded tiles, so the whole step covers the load.  A tile staged in step t is first read in
+    // step t+2, and its buffer was last read in step t-2, so one barrier before every even step
+    // orders both (the steps alternate the S^T sets, so even steps are the CUR == 0 ones).
     auto step = [&](auto cur, int t) __attribute__((always_inline)) {
       constexpr int CUR = decltype(cur)::value;
-      __syncthreads();
+      if constexpr (CUR == 0) __syncthreads();
 #pragma unroll
-      for (int j = 0; j < J; ++j) nv[j] = load(j, jv[j] ? t : t + 2, st[j], ksv[j], vsv[j]);
+      for (int j = 0; j < J; ++j) nv[j] = load(j, jv[j] ? t + 1 : t + 3, st[j], ksv[j], vsv[j]);
       TileScales tsc;
-      if constexpr (FP8) tsc = read_scales(scl + 8 * (t % 3));
+      if constexpr (FP8) tsc = read_scales(scl + 8 * (t % PS::SC_SLOTS));
       const int k0 = kv_begin + t * kKvTile;
       if ((k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > pos0))
         pipe_mask<D, CUR, CAUSAL>(R, h, k0, kv_end);
@@ -1552,12 +1575,13 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       // A wave in its matrix/softmax block issues ahead of the other wave on its SIMD while that
       // one runs its commit, LDS stores and barrier wait (1-3 % faster than equal priority).
       __builtin_amdgcn_s_setprio(1);
-      pipe_step<D, CUR, FP8>(R, kbuf0 + ((t + 1) & 1) * S::K_ELEMS, vbuf0 + ((t + 1) & 1) * S::V_ELEMS, n, h,
-                             sl, tsc, need, mnew, ts);
+      pipe_step<D, CUR, FP8>(R, kbuf0 + ((t + 1) & (NB - 1)) * S::K_ELEMS,
+                             vbuf0 + ((t - 1) & (NB - 1)) * S::V_ELEMS, n, h, sl, tsc, need, mnew, ts);
       __builtin_amdgcn_s_setprio(0);
       pipe_commit<D>(R, need, mnew, ts);
 #pragma unroll
-      for (int j = 0; j < J; ++j) store(j, t & 1, st[j], nv[j], ksv[j], vsv[j], (t + 2) % 3);
+      for (int j = 0; j < J; ++j)
+        store(j, (jv[j] ? t + 1 : t + 3) & (NB - 1), st[j], nv[j], ksv[j], vsv[j], (t + 3) % PS::SC_SLOTS);
     };
     int t = 0;
     for (; t + 1 < ntiles; t += 2) {
@@ -1567,7 +1591,7 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
     if (t < ntiles) step(std::integral_constant<int, 0>(), t);
     // The last P.V (tile ntiles - 1, stored by the last step).
     __syncthreads();
-    const uint16_t* vlast = vbuf0 + ((ntiles - 1) & 1) * S::V_ELEMS;
+    const uint16_t* vlast = vbuf0 + ((ntiles - 1) & (NB - 1)) * S::V_ELEMS;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) pipe_pv_step<D>(R, vlast, n, h, ks);
   }
@@ -1787,7 +1811,7 @@ hipError_t launch_varlen_t(const VarlenArgs& a, int n_prefill, int n_decode, int
       // register budget allows two waves per SIMD, too few for the decode path).
       auto kern = prefill_wide_kernel<D, G, kFp8>;
       hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_prefill * Hkv)), dim3(512),
-                         (size_t)TileSmem<D>::BYTES, stream, a);
+                         (size_t)PipeSmem<D>::BYTES, stream, a);
       if (n_decode > 0) {
         VarlenArgs b = a;
         b.items = a.items + n_prefill;
@@ -1829,7 +1853,7 @@ template <int D, int G>
 hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.num_tiles * a.num_segments * a.num_kv_heads;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((cascade_kernel<D, G, kFp8>), dim3((unsigned)grid), dim3(512), (size_t)TileSmem<D>::BYTES,
+  hipLaunchKernelGGL((cascade_kernel<D, G, kFp8>), dim3((unsigned)grid), dim3(512), (size_t)PipeSmem<D>::BYTES,
                      stream, a);
   return hipGetLastError();
 }
