@@ -158,6 +158,22 @@ def test_short_rows_every_shape(head_dim, group):
     run_and_check(wl)
 
 
+@pytest.mark.parametrize("case", ["mixed", "wide"])
+def test_fp32_output_from_every_item_kind(case):
+    """fp32 output (and LSE) from decode rows, short rows, 128-row tiles and, for "wide",
+    256-row pipelined tiles: every kernel's fp32 store path against the oracle."""
+    say(f"fp32 output: {case}")
+    if case == "mixed":
+        reqs = [W.RequestSpec(c, [1]) for c in (2500, 900, 30)]
+        reqs += [W.RequestSpec(1500, [4]), W.RequestSpec(200, [150]), W.RequestSpec(0, [40])]
+        wl = W.build("fp32_mixed", reqs, num_q_heads=16, num_kv_heads=4, head_dim=128, seed=41)
+        run_and_check(wl, out_dtype=torch.float32)
+    else:
+        reqs = [W.RequestSpec(100, [1024 + 19]), W.RequestSpec(700, [1])]
+        wl = W.build("fp32_wide", reqs, num_q_heads=4, num_kv_heads=2, head_dim=64, seed=42)
+        run_and_check(wl, out_dtype=torch.float32, expect_tile_rows=256)
+
+
 def test_spec_verify_full_size_sampled():
     say("spec_verify full: 64 rows of 5 tokens, ctx U[1024, 4096], sampled rows")
     run_and_check(W.spec_verify(seed=0), rows_per_step=48, check_pools=False)
