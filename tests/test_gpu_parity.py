@@ -174,6 +174,18 @@ def test_fp32_output_from_every_item_kind(case):
         run_and_check(wl, out_dtype=torch.float32, expect_tile_rows=256)
 
 
+def test_lengths_at_block_tile_and_split_edges():
+    """Contexts and chunk ends on either side of a 16-key block, a 64-key MFMA tile and a
+    1024-key split: decode rows, short rows and tile rows in one batch."""
+    say("lengths at block, tile and split edges")
+    dec = [(0, 1), (15, 1), (16, 1), (63, 1), (64, 1), (1023, 1), (1024, 1), (1025, 1)]
+    short = [(15, 2), (16, 3), (63, 5), (64, 8), (1023, 2), (1024, 7)]
+    tiles = [(0, 16), (15, 17), (48, 16), (63, 65), (64, 64), (1023, 33), (1024, 64), (0, 129)]
+    reqs = [W.RequestSpec(c, [q]) for c, q in dec + short + tiles]
+    wl = W.build("edges", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=43)
+    run_and_check(wl)
+
+
 def test_spec_verify_full_size_sampled():
     say("spec_verify full: 64 rows of 5 tokens, ctx U[1024, 4096], sampled rows")
     run_and_check(W.spec_verify(seed=0), rows_per_step=48, check_pools=False)
