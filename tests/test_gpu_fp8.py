@@ -277,6 +277,13 @@ def test_fp8_large_scores_take_the_rescale_paths():
         _fp8_cascade_check(_large_scores(wl))
 
 
+def test_fp8_cascade_prefix_cut_into_segments():
+    say("fp8 cascade with key segments")
+    wl = W.cascade_shared_prefix(seed=26, num_queries=20, prefix=4112, suffix_range=(1, 100),
+                                 num_q_heads=16, num_kv_heads=2, head_dim=128)
+    _fp8_cascade_check(wl)
+
+
 def test_fp8_cascade_small_parity():
     """fp8 prefix pass, fp8 suffix pass and the merge against the oracle's prefix state and its
     single-pass attention over the dequantised pools."""

@@ -506,6 +506,15 @@ def test_large_scores_cascade():
         _cascade_check(_large_scores(wl))
 
 
+def test_cascade_prefix_cut_into_segments():
+    """Too few query tiles to fill the chip: the prefix pass cuts a 4112-key prefix (not a
+    multiple of the 64-key tile) into key segments, the last one ragged, and merges them."""
+    say("cascade with key segments")
+    wl = W.cascade_shared_prefix(seed=25, num_queries=20, prefix=4112, suffix_range=(1, 100),
+                                 num_q_heads=16, num_kv_heads=2, head_dim=128)
+    _cascade_check(wl)
+
+
 def test_cascade_small_parity():
     say("cascade small")
     wl = W.cascade_shared_prefix(seed=1, num_queries=40, prefix=1024, suffix_range=(1, 300))
