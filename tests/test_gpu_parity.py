@@ -784,3 +784,23 @@ def test_slots_past_the_table_or_before_zero_are_skipped():
     assert np.array_equal(slots.cpu().numpy(), ref) and np.array_equal(slots2.cpu().numpy(), ref)
     kp, vp = O.reshape_and_cache(k, v, wl.k_cache, wl.v_cache, ref, wl.block_size)
     assert np.array_equal(host16(dw.k_cache), kp) and np.array_equal(host16(dw.v_cache), vp)
+
+
+@pytest.mark.parametrize("bs", [16, 256])
+def test_slot_mapping_past_2_pow_31(bs):
+    """Block ids near the top of the int32 range: slots (block id x block size + offset) pass
+    2^31 and must come out as exact int64 values (no pool is touched)."""
+    say(f"slot mapping above 2^31, block size {bs}")
+    rng = np.random.default_rng(bs)
+    B, W_ = 30, 6
+    num_blocks = (1 << 31) // (bs // 16) - 1
+    bt = rng.integers(num_blocks // 2, num_blocks, size=(B, W_)).astype(np.int32)
+    ql = rng.integers(0, 5, size=B)
+    ctx = rng.integers(0, W_ * bs - 4, size=B)
+    qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    ref = O.slot_mapping(bt, qsl, ctx.astype(np.int32), bs)
+    assert ref.max() >= 1 << 31
+    shape = P.make_shape(8, 2, 128, num_blocks, W_, block_size=bs)
+    slots = P.compute_slot_mapping(dev32(bt), dev32(qsl), dev32(ctx), shape, int(qsl[-1]))
+    torch.cuda.synchronize()
+    assert np.array_equal(slots.cpu().numpy(), ref)
