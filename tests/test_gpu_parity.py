@@ -804,3 +804,19 @@ def test_slot_mapping_past_2_pow_31(bs):
     slots = P.compute_slot_mapping(dev32(bt), dev32(qsl), dev32(ctx), shape, int(qsl[-1]))
     torch.cuda.synchronize()
     assert np.array_equal(slots.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("group,head_dim", [(8, 128), (4, 64)])
+def test_one_kv_head(group, head_dim):
+    """A single kv head (multi-query attention): decode rows with and without splits, a short
+    row, 128-row tiles, and then 256-row tiles and the cascade, all on one kv head."""
+    say(f"one kv head, G={group}, D={head_dim}")
+    reqs = [W.RequestSpec(c, [1]) for c in (2000, 300, 7)]
+    reqs += [W.RequestSpec(600, [2]), W.RequestSpec(100, [90])]
+    wl = W.build("mqa_mixed", reqs, num_q_heads=group, num_kv_heads=1, head_dim=head_dim, seed=44 + group)
+    run_and_check(wl)
+    reqs = [W.RequestSpec(50, [2048 // group + 11]), W.RequestSpec(900, [1])]
+    wl = W.build("mqa_wide", reqs, num_q_heads=group, num_kv_heads=1, head_dim=head_dim, seed=45 + group)
+    run_and_check(wl, expect_tile_rows=256)
+    _cascade_check(W.cascade_shared_prefix(seed=46 + group, num_queries=30, prefix=1024, suffix_range=(1, 200),
+                                           num_q_heads=group, num_kv_heads=1, head_dim=head_dim))
