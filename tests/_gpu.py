@@ -111,11 +111,12 @@ def check_lse(gpu: np.ndarray, ref: np.ndarray, what: str) -> float:
 class DeviceWorkload:
     """A workload's pools and per-step metadata on the device, plus the library shape."""
 
-    def __init__(self, wl):
+    def __init__(self, wl, scale: float = 0.0):
         self.wl = wl
         self.k_cache = dev16(wl.k_cache)
         self.v_cache = dev16(wl.v_cache)
-        self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride, block_size=wl.block_size)
+        self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride,
+                                  block_size=wl.block_size, scale=scale)
         max_seq = max(int(s.seq_lens.max()) for s in wl.steps)
         max_t = max(s.num_tokens for s in wl.steps)
         max_b = max(s.num_seqs for s in wl.steps)

@@ -38,10 +38,11 @@ def say(*a):
 
 
 def run_and_check(wl, rows_per_step=None, check_pools=True, want_lse=True, out_dtype=torch.bfloat16, seed=0,
-                  expect_tile_rows=None):
-    """Run every step of ``wl`` on the GPU and compare with the oracle (optionally on sampled rows)."""
+                  expect_tile_rows=None, scale=None):
+    """Run every step of ``wl`` on the GPU and compare with the oracle (optionally on sampled rows);
+    ``scale``: a softmax scale other than 1/sqrt(head_dim), for both."""
     bs = wl.block_size
-    dw = DeviceWorkload(wl)
+    dw = DeviceWorkload(wl, scale=scale or 0.0)
     kp, vp = wl.k_cache, wl.v_cache
     rng = np.random.default_rng(seed)
     stats = []
@@ -69,7 +70,8 @@ def run_and_check(wl, rows_per_step=None, check_pools=True, want_lse=True, out_d
             extra.append(int(st.query_start_loc[int(np.argmax(st.seq_lens))]))
             rows = np.unique(np.concatenate([rows, np.array(extra)]))
         o_ref, l_ref = O.paged_attention(
-            st.q, kp, vp, st.block_tables, st.query_start_loc, st.context_lens, st.seq_lens, bs, rows=rows
+            st.q, kp, vp, st.block_tables, st.query_start_loc, st.context_lens, st.seq_lens, bs, rows=rows,
+            scale=scale,
         )
         o_gpu = bf16_out_to_f64(out_g)
         sel = slice(None) if rows is None else rows
@@ -521,11 +523,11 @@ def test_cascade_small_parity():
     _cascade_check(wl)
 
 
-def _cascade_check(wl, rows=None):
+def _cascade_check(wl, rows=None, scale=None):
     bs = wl.block_size
     st = wl.steps[0]
     cv = wl.cascade
-    dw = DeviceWorkload(wl)
+    dw = DeviceWorkload(wl, scale=scale or 0.0)
     t = dw.step_tensors(st)
     slots = P.compute_slot_mapping(t["bt"], t["qsl"], t["ctx"], dw.shape, st.num_tokens)
     P.reshape_and_cache(t["k"], t["v"], dw.k_cache, dw.v_cache, slots, dw.shape)
@@ -536,7 +538,8 @@ def _cascade_check(wl, rows=None):
     # suffix pass: the same varlen kernel over the suffix view of the block tables
     pb = cv.prefix_blocks(bs)
     sbt_np = np.ascontiguousarray(st.block_tables[:, pb:])
-    sshape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, sbt_np.shape[1], block_size=wl.block_size)
+    sshape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, sbt_np.shape[1],
+                          block_size=wl.block_size, scale=scale or 0.0)
     sctx, sseq = dev32(cv.suffix_context_lens), dev32(cv.suffix_seq_lens)
     plan = P.plan_varlen(dw.ws, st.query_start_loc, cv.suffix_context_lens, cv.suffix_seq_lens, sshape)
     l_s = torch.empty((st.num_tokens, wl.num_q_heads), dtype=torch.float32, device="cuda")
@@ -551,10 +554,11 @@ def _cascade_check(wl, rows=None):
     kp, vp = O.reshape_and_cache(st.k, st.v, wl.k_cache, wl.v_cache, slots_o, bs)
     sel = slice(None) if rows is None else rows
     qs = st.q if rows is None else st.q[rows]
-    po, pl = O.cascade_prefix_attention(qs, kp, vp, cv.prefix_block_table, cv.prefix_len, bs)
+    po, pl = O.cascade_prefix_attention(qs, kp, vp, cv.prefix_block_table, cv.prefix_len, bs, scale=scale)
     check_attention(o_p.cpu().numpy().astype(np.float64)[sel], po, "cascade prefix", bf16_out=False)
     check_lse(l_p.cpu().numpy()[sel], pl, "cascade prefix lse")
-    fo, fl = O.paged_attention(st.q, kp, vp, st.block_tables, st.query_start_loc, st.context_lens, st.seq_lens, bs, rows=rows)
+    fo, fl = O.paged_attention(st.q, kp, vp, st.block_tables, st.query_start_loc, st.context_lens, st.seq_lens, bs, rows=rows,
+                               scale=scale)
     r = check_attention(bf16_out_to_f64(out)[sel], fo[sel], "cascade merged vs single pass")
     check_lse(lse_m.cpu().numpy()[sel], fl[sel], "cascade merged lse")
     say(f"    cascade merged {r}")
@@ -820,3 +824,19 @@ def test_one_kv_head(group, head_dim):
     run_and_check(wl, expect_tile_rows=256)
     _cascade_check(W.cascade_shared_prefix(seed=46 + group, num_queries=30, prefix=1024, suffix_range=(1, 200),
                                            num_q_heads=group, num_kv_heads=1, head_dim=head_dim))
+
+
+def test_explicit_softmax_scale():
+    """pkv_shape.scale > 0 replaces 1/sqrt(head_dim) in every path (decode, short, 128-row and
+    256-row tiles, cascade prefix and suffix), against the oracle at the same scale.  0.05
+    against the default 0.088 at D 128: scores 0.57x as large, a difference far beyond the
+    tolerance in rows of many keys, and no row that one key dominates."""
+    say("explicit softmax scale 0.05")
+    reqs = [W.RequestSpec(c, [1]) for c in (1800, 60)]
+    reqs += [W.RequestSpec(700, [3]), W.RequestSpec(40, [70])]
+    run_and_check(W.build("scaled_mixed", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=47), scale=0.05)
+    reqs = [W.RequestSpec(0, [2048 // 4 + 5])]
+    run_and_check(W.build("scaled_wide", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=48),
+                  expect_tile_rows=256, scale=0.05)
+    _cascade_check(W.cascade_shared_prefix(seed=49, num_queries=24, prefix=1024, suffix_range=(1, 100),
+                                           num_q_heads=8, num_kv_heads=2, head_dim=128), scale=0.05)
