@@ -40,7 +40,7 @@ def devf(a: np.ndarray) -> torch.Tensor:
 class DeviceFp8:
     """A workload's fp8 pools and scales on the device (scales uniform, or powers of two)."""
 
-    def __init__(self, wl, seed=0, pow2_scales=False):
+    def __init__(self, wl, seed=0, pow2_scales=False, scale=0.0):
         self.wl = wl
         c = W.fp8_cache(wl, seed=seed)
         if pow2_scales:
@@ -51,7 +51,8 @@ class DeviceFp8:
         self.c = c
         self.k_cache, self.v_cache = dev8(c.k_cache), dev8(c.v_cache)
         self.k_scale, self.v_scale = devf(c.k_scale), devf(c.v_scale)
-        self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride, block_size=wl.block_size)
+        self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride,
+                                  block_size=wl.block_size, scale=scale)
         max_seq = max(int(s.seq_lens.max()) for s in wl.steps)
         max_t = max(s.num_tokens for s in wl.steps)
         max_b = max(s.num_seqs for s in wl.steps)
@@ -144,9 +145,9 @@ def test_fp8_copy_blocks_copies_bytes_and_scales():
 
 
 def run_and_check_fp8(wl, rows_per_step=None, want_lse=True, out_dtype=torch.bfloat16, seed=0, expect_tile_rows=None,
-                      check_pools=True):
+                      check_pools=True, scale=None):
     bs = wl.block_size
-    d = DeviceFp8(wl, seed=seed)
+    d = DeviceFp8(wl, seed=seed, scale=scale or 0.0)
     kp, vp = d.c.k_cache, d.c.v_cache
     rng = np.random.default_rng(seed)
     stats = []
@@ -177,7 +178,7 @@ def run_and_check_fp8(wl, rows_per_step=None, want_lse=True, out_dtype=torch.bfl
             rows = np.unique(np.concatenate([rows, np.array(extra)]))
         o_ref, l_ref = O.paged_attention_fp8(
             st.q, kp, vp, d.c.k_scale, d.c.v_scale, st.block_tables, st.query_start_loc, st.context_lens,
-            st.seq_lens, bs, rows=rows,
+            st.seq_lens, bs, rows=rows, scale=scale,
         )
         sel = slice(None) if rows is None else rows
         r = check_attention(bf16_out_to_f64(out)[sel], o_ref[sel], f"fp8 {wl.name} step {si}",
@@ -373,3 +374,16 @@ def test_fp8_append_kv_over_many_requests_bitwise():
                                      wl.block_size)
     gk, gv = d.host_pools()
     assert np.array_equal(gk, kp) and np.array_equal(gv, vp), "fp8 pool bytes differ"
+
+
+def test_fp8_explicit_softmax_scale():
+    """pkv_shape.scale > 0 over fp8 pools (the score scale is multiplied with each block's key
+    scale): decode, short, 128-row and 256-row tiles against the oracle at the same scale."""
+    say("fp8 explicit softmax scale 0.05")
+    reqs = [W.RequestSpec(c, [1]) for c in (1800, 60)]
+    reqs += [W.RequestSpec(700, [3]), W.RequestSpec(40, [70])]
+    run_and_check_fp8(W.build("fp8_scaled_mixed", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=51),
+                      seed=51, scale=0.05)
+    reqs = [W.RequestSpec(0, [2048 // 4 + 5])]
+    run_and_check_fp8(W.build("fp8_scaled_wide", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=52),
+                      seed=52, expect_tile_rows=256, scale=0.05)
