@@ -33,13 +33,15 @@ __device__ void find_owners(const int32_t* __restrict__ qsl, const int32_t* __re
   const int tid = threadIdx.x, nt = blockDim.x;
   const int64_t t_end = t0 + n;  // one past the run's last token
   for (int i = tid; i < n; i += nt) s_owner[i] = -1;
+  if (tid == 0) {
+    s_range[0] = 0;
+    s_range[1] = num_seqs;
+  }
+  // Every reset above happens before any thread records an owner below: a request's tokens can
+  // lie in entries another wave resets.
+  __syncthreads();
   int32_t lo = 0, hi = num_seqs;
   if (num_seqs > nt) {
-    if (tid == 0) {
-      s_range[0] = 0;
-      s_range[1] = num_seqs;
-    }
-    __syncthreads();
     const int32_t S = (num_seqs + nt - 1) / nt;
     const int64_t r = (int64_t)tid * S;
     if (r < num_seqs) {
