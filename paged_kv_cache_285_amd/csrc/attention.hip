@@ -164,14 +164,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Merge state (m2, l2, o2) into (m, l, o); m in log2 units of scaled scores.
+// Merge state (m2, l2, r2, o2) into (m, l, r, o); m in log2 units of scaled scores, l the fp32
+// sum of p, r the sum of the bf16-rounded weights that o accumulated.
 template <int N>
-__device__ __forceinline__ void merge_state(float& m, float& l, float (&o)[N], float m2, float l2,
-                                            const float (&o2)[N]) {
+__device__ __forceinline__ void merge_state(float& m, float& l, float& r, float (&o)[N], float m2, float l2,
+                                            float r2, const float (&o2)[N]) {
   const float mn = fmaxf(m, m2);
   if (mn == -INFINITY) return;
   const float f1 = fast_exp2(m - mn), f2 = fast_exp2(m2 - mn);
   l = l * f1 + l2 * f2;
+  r = r * f1 + r2 * f2;
 #pragma unroll
   for (int e = 0; e < N; ++e) o[e] = o[e] * f1 + o2[e] * f2;
   m = mn;
@@ -226,14 +228,14 @@ __device__ __forceinline__ void transpose_stage(const float (&in)[N], float (&ou
 template <int D, int G, int NW>
 struct DecodeSmem {
   static constexpr int O_FLOATS = NW * G * D;                 // per-wave output states
-  static constexpr int ML_FLOATS = 2 * NW * G;                // per-wave m and l
+  static constexpr int ML_FLOATS = 3 * NW * G;                // per-wave m, l and r
   static constexpr int SCR_BYTES = G * 16 * 4 + G * 16 * 2;   // per-wave scores + bf16 p
   static constexpr int BYTES = (O_FLOATS + ML_FLOATS) * 4 + NW * SCR_BYTES;
 };
 
 // Merges the NW per-wave states of a decode item (unnormalised o [NW][G][D], running max m
-// (log2 units) and row sum l [NW][G] in LDS) and stores the output and LSE, or the item's
-// split-KV partial state.
+// (log2 units), row sum l and rounded-weight sum r [NW][G] in LDS) and stores the output
+// (o / r) and LSE (from l), or the item's split-KV partial state.
 template <int D, int G, int NW>
 __device__ __forceinline__ void decode_merge(const VarlenArgs& a, const WorkItem& it, int g, int token,
                                              char* smem_raw) {
@@ -242,12 +244,13 @@ __device__ __forceinline__ void decode_merge(const VarlenArgs& a, const WorkItem
   const float* s_o = reinterpret_cast<const float*>(smem_raw);
   const float* s_m = s_o + SM::O_FLOATS;
   const float* s_l = s_m + NW * G;
+  const float* s_r = s_l + NW * G;
   const int Hq = a.num_q_heads;
   __syncthreads();
   const int t = threadIdx.x;
   if (t < G * CH) {
     const int hh = t / CH, cc = t % CH;
-    float mm = -INFINITY, ll = 0.f, oo[8];
+    float mm = -INFINITY, ll = 0.f, rr = 0.f, oo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) oo[e] = 0.f;
 #pragma unroll
@@ -256,9 +259,9 @@ __device__ __forceinline__ void decode_merge(const VarlenArgs& a, const WorkItem
       float o2[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o2[e] = src[e];
-      merge_state<8>(mm, ll, oo, s_m[w * G + hh], s_l[w * G + hh], o2);
+      merge_state<8>(mm, ll, rr, oo, s_m[w * G + hh], s_l[w * G + hh], s_r[w * G + hh], o2);
     }
-    const float inv = (ll > 0.f) ? 1.f / ll : 0.f;
+    const float inv = (rr > 0.f) ? 1.f / rr : 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) oo[e] *= inv;
     const float lse = (ll > 0.f) ? (mm + __log2f(ll)) * kLn2 : -INFINITY;
@@ -313,7 +316,8 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
 
   float m[G];        // wave-uniform running max per head (log2 units of scaled scores)
   float o[G][RPL];   // P.V accumulators: head hh, V^T row (lane >> 1) + 32 i, token half
-  float l_own = 0.f; // sum of p over the scores this lane owns (head my_hh)
+  float l_own = 0.f; // sum of p over the scores this lane owns (head my_hh), for the LSE
+  float r_own = 0.f; // sum of the bf16-rounded weights P.V applies to them, for the output
   float m_own = -INFINITY;
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
@@ -351,6 +355,7 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
       my_vs = a.v_scale[(int64_t)(my_id >> L) * Hkv + g];
     }
   }
+  const float my_rvs = FP8 ? 1.f / my_vs : 1.f;  // the rounded weight p * v_scale counts p
 
   constexpr int NKR = 2 * CPT;  // key chunks per lane per block
   auto load = [&](int k, C8 (&kr)[NKR], C8 (&vr)[RPL]) {
@@ -383,10 +388,11 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
     for (int i = 0; i < NKR; ++i) kr[i] = widen8(kc[i]);
 #pragma unroll
     for (int i = 0; i < RPL; ++i) vr[i] = widen8(vc[i]);
-    float slb = sl, vsb = 1.f;  // this block's score scale and value scale
+    float slb = sl, vsb = 1.f, rvsb = 1.f;  // this block's score scale and value scale
     if constexpr (FP8) {
       slb = sl * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_ks), k));
       vsb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_vs), k));
+      rvsb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_rvs), k));
     }
     // Q.K partial dot products: v[2*hh + ts].
     float v[NV];
@@ -448,7 +454,9 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
         bm = fmaxf(fmaxf(bm, fmaxf(x.x, x.y)), fmaxf(x.z, x.w));
       }
       const float mn_own = fmaxf(m_own, bm);
-      l_own *= fast_exp2(m_own - ((mn_own == -INFINITY) ? 0.f : mn_own));
+      const float f_own = fast_exp2(m_own - ((mn_own == -INFINITY) ? 0.f : mn_own));
+      l_own *= f_own;
+      r_own *= f_own;
       m_own = mn_own;
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
@@ -464,8 +472,12 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const float p = fast_exp2(sc[kk] - mref);
-      if (owner) l_own += p;
-      pbuf[my_hh * 16 + tok[kk]] = __builtin_bit_cast(uint16_t, (__bf16)(FP8 ? p * vsb : p));
+      const __bf16 pw = (__bf16)(FP8 ? p * vsb : p);
+      if (owner) {
+        l_own += p;
+        r_own += FP8 ? (float)pw * rvsb : (float)pw;
+      }
+      pbuf[my_hh * 16 + tok[kk]] = __builtin_bit_cast(uint16_t, pw);
     }
     if (nvalid < kBlockSize) {
       // Zero the V^T entries of tokens past the end (the cache may hold NaN there).
@@ -553,16 +565,21 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
 #pragma unroll
     for (int i = 0; i < RPL; ++i) o[hh][i] += dpp_f32<0xB1>(o[hh][i]);
   float lsum = owner ? l_own : 0.f;
-  if constexpr (G <= 4) lsum += __shfl_xor(lsum, 1);
-  if constexpr (G <= 2) lsum += __shfl_xor(lsum, 2);
-  if constexpr (G <= 1) lsum += __shfl_xor(lsum, 4);
+  float rsum = owner ? r_own : 0.f;
+  if constexpr (G <= 4) lsum += __shfl_xor(lsum, 1), rsum += __shfl_xor(rsum, 1);
+  if constexpr (G <= 2) lsum += __shfl_xor(lsum, 2), rsum += __shfl_xor(rsum, 2);
+  if constexpr (G <= 1) lsum += __shfl_xor(lsum, 4), rsum += __shfl_xor(rsum, 4);
   lsum += __shfl_xor(lsum, 8);
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
+  rsum += __shfl_xor(rsum, 8);
+  rsum += __shfl_xor(rsum, 16);
+  rsum += __shfl_xor(rsum, 32);
 
   float* s_o = reinterpret_cast<float*>(smem_raw);  // [NW][G][D]
   float* s_m = s_o + SM::O_FLOATS;                   // [NW][G]
   float* s_l = s_m + NW * G;                         // [NW][G]
+  float* s_r = s_l + NW * G;                         // [NW][G]
   if (th == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
@@ -573,9 +590,11 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
   for (int hh = 0; hh < G; ++hh) {
     const int src = hh * (8 / G);
     const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsum), src));
+    const float rh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsum), src));
     if (lane == 0) {
       s_m[wave * G + hh] = m[hh];
       s_l[wave * G + hh] = lh;
+      s_r[wave * G + hh] = rh;
     }
   }
   decode_merge<D, G, NW>(a, it, g, token, smem_raw);
@@ -607,12 +626,19 @@ __device__ __forceinline__ uint2 widen4(uint32_t c) {
 }
 __device__ __forceinline__ uint2 widen4(uint2 c) { return c; }
 
+// LDS of a short item: the packed query rows (bf16, pitch QP) while the blocks stream, then, in
+// the same bytes, the waves' output sums (fp32, pitch DP); the per-wave m, l and r after them.
 template <int D, int NW>
 struct ShortSmem {
   static constexpr int COLS = 32;
   static constexpr int DP = D + 4;  // row pitch (floats): 16 columns' float4 stores hit distinct banks
-  static constexpr int BYTES = (COLS * DP + 2 * NW * COLS) * 4;
+  static constexpr int QP = D + 8;  // query row pitch (bf16): conflict-free 16-byte operand reads
+  static_assert(COLS * QP * 2 <= COLS * DP * 4, "query rows fit the output rows");
+  static constexpr int BYTES = (COLS * DP + 3 * NW * COLS) * 4;
 };
+
+// bf16 pair (1, 1): v_dot2 against it sums a packed pair of bf16 weights exactly in fp32.
+constexpr uint32_t kBf16OnePair = 0x3f803f80u;
 
 template <int D, int G, int NW, bool FP8>
 __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char* smem_raw) {
@@ -637,25 +663,27 @@ __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char*
   const int ncols = ntok * G;  // <= 32
   const float sl = a.scale_log2;
 
-  bf16x8 qb[NC][KS];
+  // The packed query rows go to LDS once (zeros for padding columns); the Q^T operands of every
+  // block are read back from there, which keeps 32 VGPRs free for the blocks in flight.
+  uint16_t* sq = reinterpret_cast<uint16_t*>(smem_raw);
+  for (int idx = threadIdx.x; idx < SM::COLS * CH; idx += 64 * NW) {
+    const int n = idx / CH, cc = idx % CH;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (n < ncols)
+      x = reinterpret_cast<const uint4*>(a.q + ((int64_t)(tok0 + n / G) * Hq + g * G + n % G) * D)[cc];
+    *reinterpret_cast<uint4*>(sq + n * SM::QP + 8 * cc) = x;
+  }
   int qpos[NC];
 #pragma unroll
-  for (int cg = 0; cg < NC; ++cg) {
-    const int n = 16 * cg + n16;
-    const bool valid = n < ncols;
-    const int t = valid ? n / G : 0;
-    qpos[cg] = pos0 + t;
-    const uint4* qrow = reinterpret_cast<const uint4*>(a.q + ((int64_t)(tok0 + t) * Hq + g * G + n % G) * D);
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qb[cg][s] = __builtin_bit_cast(bf16x8, valid ? qrow[4 * s + q] : make_uint4(0u, 0u, 0u, 0u));
-  }
+  for (int cg = 0; cg < NC; ++cg) qpos[cg] = pos0 + min(16 * cg + n16, ncols - 1) / G;
+  __syncthreads();
   floatx4 o[NC][DG];
-  float m[NC], lsum[NC];
+  float m[NC], lsum[NC], rsum[NC];  // running max; fp32 sum of p (LSE); sum of rounded weights (output)
 #pragma unroll
   for (int cg = 0; cg < NC; ++cg) {
     m[cg] = -INFINITY;
     lsum[cg] = 0.f;
+    rsum[cg] = 0.f;
 #pragma unroll
     for (int d = 0; d < DG; ++d) o[cg][d] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
@@ -674,6 +702,7 @@ __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char*
       my_vs = a.v_scale[(int64_t)(my_id >> L) * Hkv + g];
     }
   }
+  const float my_rvs = FP8 ? 1.f / my_vs : 1.f;  // the rounded weight p * v_scale counts p
   const int64_t ktile = (int64_t)kBlockSize * CH;  // KC per (block, head) tile
   const int64_t vtile = (int64_t)4 * D;           // VC per (block, head) tile
   const KC* kb = reinterpret_cast<const KC*>(a.k_cache) + (int64_t)g * ktile;
@@ -692,10 +721,11 @@ __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char*
   auto process = [&](int k, const KC (&kr)[KS], const VC (&vr)[DG]) __attribute__((always_inline)) {
     const int t0 = (b_begin + wave + NW * k) * kBlockSize;  // first key of the block
     const int nvalid = kv_end - t0;                         // < 16 only in the last block
-    float slb = sl, vsb = 1.f;
+    float slb = sl, vsb = 1.f, rvsb = 1.f;
     if constexpr (FP8) {
       slb = sl * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_ks), k));
       vsb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_vs), k));
+      rvsb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_rvs), k));
     }
     uint2 vmask = make_uint2(0xffffffffu, 0xffffffffu);  // values of keys past the end -> 0
     if (nvalid < kBlockSize) {
@@ -703,13 +733,18 @@ __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char*
       vmask.x = (t < nvalid ? 0x0000ffffu : 0u) | (t + 1 < nvalid ? 0xffff0000u : 0u);
       vmask.y = (t + 2 < nvalid ? 0x0000ffffu : 0u) | (t + 3 < nvalid ? 0xffff0000u : 0u);
     }
+    // Keep the Q^T operand reads inside the loop (the compiler would otherwise hoist these
+    // loop-invariant loads and hold them in registers again).
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int cg = 0; cg < NC; ++cg) {
       floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, widen8(kr[s])), qb[cg][s], sacc,
-                                                       0, 0, 0);
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 qop = *reinterpret_cast<const bf16x8*>(sq + (16 * cg + n16) * SM::QP + 32 * s + 8 * q);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, widen8(kr[s])), qop, sacc, 0,
+                                                       0, 0);
+      }
       float sc[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -723,6 +758,7 @@ __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char*
         const float mn = fmaxf(m[cg], cm);
         const float alpha = fast_exp2(m[cg] - ((mn == -INFINITY) ? 0.f : mn));
         lsum[cg] *= alpha;
+        rsum[cg] *= alpha;
 #pragma unroll
         for (int d = 0; d < DG; ++d) o[cg][d] *= alpha;
         m[cg] = mn;
@@ -736,6 +772,10 @@ __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char*
       }
       const uint2 pw = FP8 ? make_uint2(pack_bf16x2(p[0] * vsb, p[1] * vsb), pack_bf16x2(p[2] * vsb, p[3] * vsb))
                            : make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+      if constexpr (FP8)
+        rsum[cg] = fmaf(dot2(pw.y, kBf16OnePair, dot2(pw.x, kBf16OnePair, 0.f)), rvsb, rsum[cg]);
+      else
+        rsum[cg] = dot2(pw.y, kBf16OnePair, dot2(pw.x, kBf16OnePair, rsum[cg]));
       const shortx4 pb = __builtin_bit_cast(shortx4, pw);
 #pragma unroll
       for (int d = 0; d < DG; ++d) {
@@ -774,16 +814,20 @@ __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char*
 
   // Merge the waves: every wave publishes (m, l) per column; each lane rescales its o to the
   // columns' common max; the waves then add their o into one LDS buffer in wave order.
-  float* s_o = reinterpret_cast<float*>(smem_raw);  // [COLS][DP]
+  float* s_o = reinterpret_cast<float*>(smem_raw);  // [COLS][DP], over the query rows
   float* s_m = s_o + SM::COLS * SM::DP;              // [NW][COLS]
   float* s_l = s_m + NW * SM::COLS;                  // [NW][COLS]
+  float* s_r = s_l + NW * SM::COLS;                  // [NW][COLS]
 #pragma unroll
   for (int cg = 0; cg < NC; ++cg) {
     lsum[cg] += __shfl_xor(lsum[cg], 16);
     lsum[cg] += __shfl_xor(lsum[cg], 32);
+    rsum[cg] += __shfl_xor(rsum[cg], 16);
+    rsum[cg] += __shfl_xor(rsum[cg], 32);
     if (q == 0) {
       s_m[wave * SM::COLS + 16 * cg + n16] = m[cg];
       s_l[wave * SM::COLS + 16 * cg + n16] = lsum[cg];
+      s_r[wave * SM::COLS + 16 * cg + n16] = rsum[cg];
     }
   }
   __syncthreads();
@@ -824,12 +868,16 @@ __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char*
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_m[w * SM::COLS + n]);
-    float ll = 0.f;
+    float ll = 0.f, rr = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) ll += s_l[w * SM::COLS + n] * fast_exp2(s_m[w * SM::COLS + n] - mx);
+      for (int w = 0; w < NW; ++w) {
+        const float f = fast_exp2(s_m[w * SM::COLS + n] - mx);
+        ll += s_l[w * SM::COLS + n] * f;
+        rr += s_r[w * SM::COLS + n] * f;
+      }
     }
-    const float inv = (ll > 0.f) ? 1.f / ll : 0.f;
+    const float inv = (rr > 0.f) ? 1.f / rr : 0.f;
     float oo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) oo[e] = s_o[n * SM::DP + 8 * cc + e] * inv;
@@ -940,7 +988,9 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
   for (int d = 0; d < DT; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
-  float m = -INFINITY, lsum = 0.f;
+  // Running max; fp32 sum of p (for the LSE); sum of the bf16-rounded weights P.V applies (for
+  // the output, so that a row one key dominates comes out as that key's value).
+  float m = -INFINITY, lsum = 0.f, rsum = 0.f;
 
   // Staging of the 64-key tile (4 cache blocks).  K rows are token-major: key
   // kk = KPI*i + lane/LPT, chunk lane%LPT.  The value pool is dim-major, so the V^T tile is a
@@ -1095,7 +1145,7 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       // once, so the 64-register rescale of the output is rare; p stays <= 2^kLazy.  With fp8
       // pools, key block b of the tile (scores sacc[b >> 1][8 (b & 1) ..]) has score scale
       // sl * k_scale[b], and its p are multiplied by v_scale[b] before the P.V.
-      float slk[4], svb[4];
+      float slk[4], svb[4], rsv[4];
       float mx = -INFINITY;
       if constexpr (FP8) {
         const TileScales tsc = read_scales(scl + 8 * buf);
@@ -1108,12 +1158,13 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
         for (int b = 0; b < 4; ++b) {
           slk[b] = sl * tsc.k[b];
           svb[b] = tsc.v[b];
+          rsv[b] = __builtin_amdgcn_rcpf(tsc.v[b]);
           mx = fmaxf(mx, mb[b] * slk[b]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
       } else {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) slk[b] = sl, svb[b] = 1.f;
+        for (int b = 0; b < 4; ++b) slk[b] = sl, svb[b] = 1.f, rsv[b] = 1.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -1124,6 +1175,7 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
         const float mn = fmaxf(m, mx);
         const float alpha = fast_exp2(m - ((mn == -INFINITY) ? 0.f : mn));
         lsum *= alpha;
+        rsum *= alpha;
 #pragma unroll
         for (int d = 0; d < DT; ++d)
 #pragma unroll
@@ -1132,8 +1184,10 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       }
       const float mref = (m == -INFINITY) ? 0.f : m;
 
-      // P^T operands: K-step ks covers keys 32*(ks/2) + 8*jj0 + 0..15, jj0 = 2*(ks%2).  The row
-      // sum is accumulated in fp32 (a sum of the bf16-rounded p would cost ~1e-3 in the LSE).
+      // P^T operands: K-step ks covers keys 32*(ks/2) + 8*jj0 + 0..15, jj0 = 2*(ks%2).  Two row
+      // sums: the fp32 sum of p gives the LSE (a sum of rounded p would cost ~1e-3 there), the
+      // sum of the rounded weights (v_dot2 of each bf16 pair against (1, 1); fp8: divided by the
+      // block's value scale) normalises the output.
       bf16x8 pb[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -1146,6 +1200,11 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
           v[e] = (__bf16)(FP8 ? p * svb[ks] : p);
         }
         pb[ks] = v;
+        const u32x4 w = __builtin_bit_cast(u32x4, v);
+        float rb = FP8 ? 0.f : rsum;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rb = dot2(w[u], kBf16OnePair, rb);
+        rsum = FP8 ? fmaf(rb, rsv[ks], rsum) : rb;
       }
 
       // O^T += V^T P^T.
@@ -1171,8 +1230,9 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
   if (t < ntiles) body(t, st[0], nv[0], ksc[0], vsc[0], st[PD - 1], nv[PD - 1], ksc[PD - 1], vsc[PD - 1]);
 
   lsum += __shfl_xor(lsum, 32);
+  rsum += __shfl_xor(rsum, 32);
   if (!row_valid) return;
-  const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+  const float inv = (rsum > 0.f) ? 1.f / rsum : 0.f;
   const int64_t orow = (int64_t)(orow0 + tq) * Hq + g * G + hh;
 #pragma unroll
   for (int d = 0; d < DT; ++d) {
@@ -1214,7 +1274,8 @@ struct PipeRegs {
   floatx16 oacc[DT];    // O^T accumulators
   floatx16 sacc[2][2];  // two S^T sets (tile t and t+1), each two 32-key halves
   bf16x8 pb[4];         // P^T (four 16-key steps): tile t-1 until its P.V step, then tile t
-  float m, lsum;        // running max (log2 units of scaled scores) and row sum
+  float m, lsum;        // running max (log2 units of scaled scores) and fp32 row sum (LSE)
+  float lr;             // sum of the bf16-rounded weights P.V applied (normalises the output)
   int qpos;             // position of the lane's query row
 };
 
@@ -1260,11 +1321,13 @@ __device__ __forceinline__ void pipe_pv_step(PipeRegs<D>& R, const uint16_t* __r
 // the fourth piece of a 16-key step also swapping the pairs across the wave halves into the
 // new P^T step (a lane of half h holds keys 4h..4h+3 and 8+4h..8+4h+3 of the step as dwords
 // d0..d3; swapping d0<->d2 and d1<->d3 leaves it keys 8h..8h+7).  Returns in `need` whether
-// the running max moved, with the new max and the tile's row sum.
+// the running max moved, with the new max, the tile's fp32 row sum and the tile's sum of rounded
+// weights (v_dot2 of each bf16 pair against (1, 1); fp8: per key block, divided by its value scale).
 template <int D, int CUR, bool FP8>
 __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __restrict__ kb,
                                           const uint16_t* __restrict__ vb, int n, int h, float sl,
-                                          const TileScales& tsc, bool& need, float& mnew, float& ts) {
+                                          const TileScales& tsc, bool& need, float& mnew, float& ts,
+                                          float& tr) {
   constexpr int NXT = 1 - CUR;
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
@@ -1298,7 +1361,9 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
   float mx = -INFINITY, mref = 0.f;
   float mb[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // fp8: per-block raw maxima
   uint32_t pk[4][4];
+  float trb[4] = {0.f, 0.f, 0.f, 0.f};  // fp8: rounded-weight sums per key block
   ts = 0.f;
+  tr = 0.f;
   need = false;
   mnew = R.m;
 #pragma unroll
@@ -1348,6 +1413,10 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
       ts += p0;
       ts += p1;
       pk[ks][u] = FP8 ? pack_bf16x2(p0 * svb[ks], p1 * svb[ks]) : pack_bf16x2(p0, p1);
+      if constexpr (FP8)
+        trb[ks] = dot2(pk[ks][u], kBf16OnePair, trb[ks]);
+      else
+        tr = dot2(pk[ks][u], kBf16OnePair, tr);
       if (u == 3) {
         // P^T(t-1) of this 16-key step had its last use in slot DT*ks + DT - 1 < i.
         const auto s02 = __builtin_amdgcn_permlane32_swap(pk[ks][0], pk[ks][2], false, false);
@@ -1362,15 +1431,20 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (FP8) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tr = fmaf(trb[b], __builtin_amdgcn_rcpf(tsc.v[b]), tr);
+  }
 }
 
 // After a step: apply a moved running max to the output (which now holds tiles up to t-1) and
-// the row sum, then add the tile's row sum.
+// the row sums, then add the tile's row sums.
 template <int D>
-__device__ __forceinline__ void pipe_commit(PipeRegs<D>& R, bool need, float mnew, float ts) {
+__device__ __forceinline__ void pipe_commit(PipeRegs<D>& R, bool need, float mnew, float ts, float tr) {
   if (need) {
     const float alpha = fast_exp2(R.m - mnew);
     R.lsum *= alpha;
+    R.lr *= alpha;
 #pragma unroll
     for (int d = 0; d < D / 32; ++d)
 #pragma unroll
@@ -1378,6 +1452,7 @@ __device__ __forceinline__ void pipe_commit(PipeRegs<D>& R, bool need, float mne
   }
   R.m = mnew;
   R.lsum += ts;
+  R.lr += tr;
 }
 
 template <int D, int G, bool CAUSAL, bool FP8>
@@ -1426,6 +1501,7 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
     for (int e = 0; e < 16; ++e) R.oacc[d][e] = 0.f;
   R.m = -INFINITY;
   R.lsum = 0.f;
+  R.lr = 0.f;
 
   const int ntiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
   if (ntiles > 0) {
@@ -1571,14 +1647,14 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       if ((k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > pos0))
         pipe_mask<D, CUR, CAUSAL>(R, h, k0, kv_end);
       bool need;
-      float mnew, ts;
+      float mnew, ts, tr;
       // A wave in its matrix/softmax block issues ahead of the other wave on its SIMD while that
       // one runs its commit, LDS stores and barrier wait (1-3 % faster than equal priority).
       __builtin_amdgcn_s_setprio(1);
       pipe_step<D, CUR, FP8>(R, kbuf0 + ((t + 1) & (NB - 1)) * S::K_ELEMS,
-                             vbuf0 + ((t - 1) & (NB - 1)) * S::V_ELEMS, n, h, sl, tsc, need, mnew, ts);
+                             vbuf0 + ((t - 1) & (NB - 1)) * S::V_ELEMS, n, h, sl, tsc, need, mnew, ts, tr);
       __builtin_amdgcn_s_setprio(0);
-      pipe_commit<D>(R, need, mnew, ts);
+      pipe_commit<D>(R, need, mnew, ts, tr);
 #pragma unroll
       for (int j = 0; j < J; ++j)
         store(j, (jv[j] ? t + 1 : t + 3) & (NB - 1), st[j], nv[j], ksv[j], vsv[j], (t + 3) % PS::SC_SLOTS);
@@ -1597,8 +1673,9 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
   }
 
   const float lsum = R.lsum + other_half(R.lsum, h);
+  const float lr = R.lr + other_half(R.lr, h);
   if (!row_valid) return;
-  const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+  const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
   const int64_t orow = (int64_t)(tok0 + tq) * Hq + g * G + hh;
 #pragma unroll
   for (int d = 0; d < DT; ++d) {

@@ -41,63 +41,82 @@ def bf16_spacing(x: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
-# Set by peaked_tolerance(): the per-element bound for inputs whose softmax rows one key dominates.
-_PEAKED_ATOL = None
+# Largest |value| the rows under test attend over (None: unknown).  Set for every workload that
+# DeviceWorkload / the fp8 helpers upload, and by value_range() around other checks.
+_VMAX = None
+
+
+def workload_vmax(wl, fp8: bool = False) -> float:
+    """max |v| over a workload's pools and new values (fp8 pools: e4m3 rounding adds up to 2^-4)."""
+    arrs = [wl.v_cache] + [st.v for st in wl.steps]
+    vmax = max(float(np.nanmax(np.abs((a.astype(np.uint32) << 16).view(np.float32)))) for a in arrs)
+    return vmax * (1.0 + 2.0**-4 if fp8 else 1.0)
+
+
+def set_value_range(wl, fp8: bool = False, vmax=None) -> None:
+    global _VMAX
+    _VMAX = workload_vmax(wl, fp8) if vmax is None else float(vmax)
 
 
 @contextlib.contextmanager
-def peaked_tolerance(wl, fp8: bool = False):
-    """Element bound for rows whose softmax one key dominates (large-magnitude scores).
-
-    The kernels round each p to bf16 (unit roundoff 2^-8) before it weights the values, while
-    the fp32 sum of the unrounded p normalises; for a row whose weight sits on one key the
-    output then moves by up to 2^-8 of that key's value, which for N(0, 1) values reaches
-    ~0.018, past the 1e-2 that spread rows keep.  So inside this context
-    |gpu - ref| <= 2^-8 * max|v| + 2^-8 * |ref| (its own bf16 output rounding) + 1e-4, with
-    max|v| over every value of the workload (fp8 pools: 2^-4 more for the e4m3 code rounding).
-    Relative L2 keeps its bound."""
-    global _PEAKED_ATOL
-    arrs = [wl.v_cache] + [st.v for st in wl.steps]
-    vmax = max(float(np.nanmax(np.abs((a.astype(np.uint32) << 16).view(np.float32)))) for a in arrs)
-    _PEAKED_ATOL = 2.0**-8 * vmax * (1.0 + 2.0**-4 if fp8 else 1.0) + 1e-4
+def value_range(wl, fp8: bool = False):
+    """Checks inside this context use the value range of ``wl``."""
+    global _VMAX
+    old = _VMAX
+    _VMAX = workload_vmax(wl, fp8)
     try:
-        yield _PEAKED_ATOL
+        yield _VMAX
     finally:
-        _PEAKED_ATOL = None
+        _VMAX = old
+
+
+# Inputs whose softmax rows one key dominates (queries 16x N(0,1)) are checked under the same rule.
+peaked_tolerance = value_range
+
+
+def rounding_bound(ref: np.ndarray, gpu: np.ndarray, bf16_out: bool) -> np.ndarray:
+    """Per-element error the method's two prescribed roundings can produce.
+
+    * P to bf16 before P.V: each weight p_j carries a relative error up to 2^-9 (round to
+      nearest even, 8 significant bits); the output is normalised by the sum of those same
+      rounded weights, so it is a convex combination whose weights moved by
+      w_j (e_j - e_mean) / (1 + e_mean), and |o_gpu - o| <= 2^-8 (1 + 2^-8) max_j |v_j - o|
+      <= 2^-8 (1 + 2^-8) (max|v| + |o|).
+    * The output to bf16: half a bf16 spacing at its magnitude.
+    Plus 1e-5 of fp32 accumulation."""
+    b = np.full(ref.shape, 1e-5)
+    if _VMAX is not None:
+        b = b + 2.0**-8 * (1.0 + 2.0**-8) * (_VMAX + np.abs(ref))
+    if bf16_out:
+        b = b + 0.5 * bf16_spacing(np.maximum(np.abs(ref), np.abs(gpu)))
+    return b
 
 
 def check_attention(gpu: np.ndarray, ref: np.ndarray, what: str, bf16_out: bool = True) -> dict:
-    """Assert max |gpu - ref| <= ATOL (allowing elements whose only error is bf16 output
-    rounding, i.e. gpu is a bf16 neighbour of ref) and relative L2 <= RTOL_L2; inside
-    peaked_tolerance() the element bound is that context's instead."""
+    """Assert max |gpu - ref| <= ATOL and relative L2 <= RTOL_L2.  An element above ATOL is
+    accepted only within rounding_bound() (the bf16 rounding of P and of the output, which the
+    method prescribes); such elements are counted and printed."""
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     assert np.isfinite(ref).all(), f"{what}: oracle produced non-finite values"
     assert np.isfinite(gpu).all(), f"{what}: GPU produced non-finite values at {np.argwhere(~np.isfinite(gpu))[:5]}"
     err = np.abs(gpu - ref)
-    if _PEAKED_ATOL is not None:
-        bound = _PEAKED_ATOL + 2.0**-8 * np.abs(ref)
-        assert (err <= bound).all(), (
-            f"{what}: {int((err > bound).sum())} elements exceed the peaked-row bound; worst excess "
-            f"{(err - bound).max():.4g} at {np.unravel_index((err - bound).argmax(), err.shape)}"
-        )
-        rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
-        assert rel <= RTOL_L2, f"{what}: relative L2 {rel:.3g} > {RTOL_L2}"
-        return {"max_abs": float(err.max()) if err.size else 0.0, "rel_l2": rel, "peaked_atol": _PEAKED_ATOL}
     bad = err > ATOL
-    rounding_only = 0
+    exempt = 0
     if bad.any():
-        if bf16_out:
-            ok = err <= bf16_spacing(ref)
-            rounding_only = int(bad.sum())
-            assert ok[bad].all(), (
-                f"{what}: {int((bad & ~ok).sum())} elements exceed {ATOL} beyond bf16 rounding; "
-                f"worst {err.max():.4g} at {np.unravel_index(err.argmax(), err.shape)}"
-            )
-        else:
-            raise AssertionError(f"{what}: max abs err {err.max():.4g} > {ATOL}")
+        bound = rounding_bound(ref, gpu, bf16_out)
+        ok = err <= bound
+        exempt = int(bad.sum())
+        assert ok[bad].all(), (
+            f"{what}: {int((bad & ~ok).sum())} elements exceed {ATOL} beyond the rounding bound "
+            f"(vmax {_VMAX}); worst {err.max():.4g} at {np.unravel_index(err.argmax(), err.shape)}, worst excess "
+            f"{(err - bound).max():.4g}"
+        )
     rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
     assert rel <= RTOL_L2, f"{what}: relative L2 {rel:.3g} > {RTOL_L2}"
-    return {"max_abs": float(err.max()) if err.size else 0.0, "rel_l2": rel, "rounding_only": rounding_only}
+    res = {"max_abs": float(err.max()) if err.size else 0.0, "rel_l2": rel, "above_atol_within_rounding": exempt}
+    print(f"[parity] {what}: max_abs {res['max_abs']:.3g} rel_l2 {rel:.3g} above_1e-2_within_rounding {exempt}",
+          flush=True)
+    return res
 
 
 def check_lse(gpu: np.ndarray, ref: np.ndarray, what: str) -> float:
@@ -113,6 +132,7 @@ class DeviceWorkload:
 
     def __init__(self, wl, scale: float = 0.0):
         self.wl = wl
+        set_value_range(wl)
         self.k_cache = dev16(wl.k_cache)
         self.v_cache = dev16(wl.v_cache)
         self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride,
