@@ -8,11 +8,16 @@ reduce).  The 330 query tokens of the pass give the headline attention tokens/s 
 bf16) and resident in HBM before timing starts.
 
 Also reported: the dominant kernel's roofline (algorithmic bytes / HIP-event-timed launch
-duration against 8 TB/s; also with cold caches, a 1 GiB write before each launch evicting the
-L2s and the 256 MB MALL), the decode-only batch's HBM GB/s (warm and cold), and the CPU fp64
+duration against 8 TB/s).  Its headline is taken with cold caches: a 1 GiB write before each
+timed launch evicts the L2s and the 256 MB MALL; the warm figure (launches back to back) is
+context.  Every kernel time is given as mean, median and p10/p90 over at least 20 launches.
+Beside it: the decode-only batch's HBM GB/s (bf16 and fp8 pools), the speculative-verify batch,
+the tiny batched prefill, the graph-replayed decode step, the MFMA-bound passes (the cascade
+shared-prefix pass and the long chunked prefill, each as TFLOP/s against the 2.5 PFLOP/s bf16
+peak, with the cascade suffix pass, merge and the cascade-vs-single-pass ratio), and the CPU fp64
 oracle timed on a bounded sample of the same workload (``cpu_baseline``).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-graph] [--mfma]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-graph] [--no-mfma]
 """
 
 from __future__ import annotations
@@ -31,6 +36,30 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def stats(ms):
+    """mean, median and p10/p90 (ms) of per-launch durations."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {
+        "mean_ms": float(a.mean()),
+        "median_ms": float(np.median(a)),
+        "p10_ms": float(np.percentile(a, 10)),
+        "p90_ms": float(np.percentile(a, 90)),
+        "launches": int(a.size),
+    }
+
+
+def timed_launches(P, fn, reps, flush=None):
+    """Per-launch attention-kernel milliseconds (library HIP events on the launch's stream) over
+    `reps` calls of fn; with `flush`, a 1 GiB write precedes every call (outside the events)."""
+    P.timing_begin()
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        fn()
+    P.timing_end()
+    return P.timing_durations()
 
 
 def kv_bytes(seq_lens, num_kv_heads, head_dim):
@@ -111,8 +140,8 @@ def time_passes(runner, torch, steps, warmup):
     """Time `steps` passes bracketed by device syncs, then `steps` more with the library's
     launch timing on, which brackets each varlen attention kernel with a pair of HIP events on
     its stream.  The events add GPU time between launches (about 7 us per launch here), so the
-    step time comes from the first loop and the kernel time from the second.  Returns (total ms
-    of the first loop, kernel ms per launch, launches timed)."""
+    step time comes from the first loop and the kernel times from the second.  Returns (total ms
+    of the first loop, per-launch kernel ms of the second)."""
     import gc
 
     P = runner.P
@@ -132,9 +161,9 @@ def time_passes(runner, torch, steps, warmup):
     for _ in range(steps):
         runner.run_pass()
     torch.cuda.synchronize()
-    kern_total, launches = P.timing_end()
+    P.timing_end()
     gc.enable()
-    return start.elapsed_time(stop), kern_total / max(launches, 1), launches
+    return start.elapsed_time(stop), P.timing_durations()
 
 
 class Flusher:
@@ -150,8 +179,8 @@ class Flusher:
 
 
 def time_flushed(runner, torch, passes):
-    """Kernel ms per varlen launch when every launch starts with cold caches (a 1 GiB write
-    before it, outside the kernel's HIP events)."""
+    """Per-launch kernel ms of the varlen launches when every launch starts with cold caches (a
+    1 GiB write before it, outside the kernel's HIP events)."""
     P = runner.P
     fl = Flusher(torch)
     runner.run_pass(flush=fl)
@@ -159,10 +188,11 @@ def time_flushed(runner, torch, passes):
     P.timing_begin()
     for _ in range(passes):
         runner.run_pass(flush=fl)
-    total, n = P.timing_end()
+    P.timing_end()
+    d = P.timing_durations()
     del fl
     torch.cuda.empty_cache()
-    return total / max(n, 1)
+    return d
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -222,8 +252,9 @@ def cpu_baseline(wl, budget_s=10.0):
     }
 
 
-def decode_hbm(torch, P, steps=10, warmup=3):
-    """Decode-only batch (256 rows, context 1024..8192): varlen kernel GB/s against 8 TB/s."""
+def decode_hbm(torch, P, reps=20, warmup=5):
+    """Decode-only batch (256 rows, context 1024..8192): varlen kernel GB/s against 8 TB/s, with
+    cold caches (headline) and warm."""
     import workloads as W
 
     wl = W.decode_only(seed=0)
@@ -241,30 +272,21 @@ def decode_hbm(torch, P, steps=10, warmup=3):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    P.timing_begin()
-    for _ in range(steps):
-        call()
-    total, n = P.timing_end()
-    ms = total / n
+    warm = stats(timed_launches(P, call, reps))
     fl = Flusher(torch)
-    P.timing_begin()
-    for _ in range(5):
-        fl()
-        call()
-    total_f, n_f = P.timing_end()
+    cold = stats(timed_launches(P, call, reps, flush=fl))
     del fl
-    ms_f = total_f / n_f
     nbytes = step_bytes(st, wl)
-    gbs = nbytes / (ms * 1e-3) / 1e9
+    gbs = nbytes / (cold["mean_ms"] * 1e-3) / 1e9
     res = {
         "workload": "decode_only: 256 seqs, ctx U[1024,8192], 32q/8kv, D128, bs16",
-        "kernel_ms": ms,
         "algorithmic_bytes": nbytes,
         "GB/s": gbs,
         "frac_of_peak": gbs / HBM_PEAK_GBS,
-        "tokens/s/layer": st.num_tokens / (ms * 1e-3),
-        "flushed_kernel_ms": ms_f,
-        "flushed_frac_of_peak": nbytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "tokens/s/layer": st.num_tokens / (cold["mean_ms"] * 1e-3),
+        "kernel_ms_flushed": cold,
+        "kernel_ms_warm": warm,
+        "warm_frac_of_peak": nbytes / (warm["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "blocks_per_split": plan.blocks_per_split,
         "items": plan.num_items,
     }
@@ -273,9 +295,10 @@ def decode_hbm(torch, P, steps=10, warmup=3):
     return res
 
 
-def fp8_decode_hbm(torch, P, steps=10, warmup=3, bf16_ms=None):
+def fp8_decode_hbm(torch, P, reps=20, warmup=5, bf16_ms=None):
     """The decode-only batch over FP8 (e4m3) pools with per-(block, kv head) scales: varlen
-    kernel GB/s (K/V at one byte per element, plus the scales read) against 8 TB/s."""
+    kernel GB/s (K/V at one byte per element, plus the scales read) against 8 TB/s, cold caches
+    (headline) and warm."""
     import workloads as W
 
     wl = W.decode_only(seed=0)
@@ -300,25 +323,26 @@ def fp8_decode_hbm(torch, P, steps=10, warmup=3, bf16_ms=None):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    P.timing_begin()
-    for _ in range(steps):
-        call()
-    total, n = P.timing_end()
-    ms = total / n
+    warm = stats(timed_launches(P, call, reps))
+    fl = Flusher(torch)
+    cold = stats(timed_launches(P, call, reps, flush=fl))
+    del fl
     kvb = kv_bytes(st.seq_lens, wl.num_kv_heads, wl.head_dim) // 2
     blocks = int(np.sum(-(-st.seq_lens // wl.block_size)))
     nbytes = kvb + 2 * blocks * wl.num_kv_heads * 4 + 2 * st.num_tokens * wl.num_q_heads * wl.head_dim * 2 + blocks * 4
-    gbs = nbytes / (ms * 1e-3) / 1e9
+    gbs = nbytes / (cold["mean_ms"] * 1e-3) / 1e9
     res = {
         "workload": "decode_only over fp8 e4m3 pools: 256 seqs, ctx U[1024,8192], 32q/8kv, D128, bs16",
-        "kernel_ms": ms,
         "algorithmic_bytes": nbytes,
         "GB/s": gbs,
         "frac_of_peak": gbs / HBM_PEAK_GBS,
-        "tokens/s/layer": st.num_tokens / (ms * 1e-3),
+        "tokens/s/layer": st.num_tokens / (cold["mean_ms"] * 1e-3),
+        "kernel_ms_flushed": cold,
+        "kernel_ms_warm": warm,
+        "warm_frac_of_peak": nbytes / (warm["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
     }
     if bf16_ms:
-        res["speedup_vs_bf16_pools"] = bf16_ms / ms
+        res["speedup_vs_bf16_pools"] = bf16_ms / cold["mean_ms"]
     del kc, vc
     torch.cuda.empty_cache()
     return res
@@ -385,9 +409,10 @@ def decode_graph_step(torch, P, reps=50):
     return out
 
 
-def spec_verify_hbm(torch, P, reps=10):
+def spec_verify_hbm(torch, P, reps=20):
     """Speculative-verify batch (64 rows of 1 + 4 tokens, context 1024..4096): varlen launch
-    GB/s against 8 TB/s (the five query tokens of a row share every K/V byte)."""
+    GB/s against 8 TB/s (the five query tokens of a row share every K/V byte), cold caches
+    (headline) and warm."""
     import workloads as W
 
     wl = W.spec_verify(seed=0)
@@ -400,23 +425,23 @@ def spec_verify_hbm(torch, P, reps=10):
         P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"], s["seq"], r.shape, plan,
                                  r.ws, out=s["out"])
 
-    call()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
+    for _ in range(5):
         call()
-    b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
+    warm = stats(timed_launches(P, call, reps))
+    fl = Flusher(torch)
+    cold = stats(timed_launches(P, call, reps, flush=fl))
+    del fl
     byts = step_bytes(st, wl)
     out = {
         "workload": "spec_verify: 64 rows x (1 + 4 drafted) tokens, ctx U[1024,4096], 32q/8kv, D128",
-        "ms": ms,
         "algorithmic_bytes": byts,
-        "GB/s": byts / (ms * 1e-3) / 1e9,
-        "frac_of_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "tokens/s/layer": st.num_tokens / (ms * 1e-3),
+        "GB/s": byts / (cold["mean_ms"] * 1e-3) / 1e9,
+        "frac_of_peak": byts / (cold["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "warm_frac_of_peak": byts / (warm["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "tokens/s/layer": st.num_tokens / (cold["mean_ms"] * 1e-3),
+        "kernel_ms_flushed": cold,
+        "kernel_ms_warm": warm,
     }
     del r
     torch.cuda.empty_cache()
@@ -450,10 +475,29 @@ def tiny_prefill_latency(torch, P, reps=20):
             "tokens/s": st.num_tokens / (us * 1e-6)}
 
 
-def mfma_paths(torch, P, reps=5):
-    """MFMA-bound paths: the cascade shared-prefix pass (512 queries x 64 q heads over a
-    16384-token prefix) and the long chunked prefill (one 32768-token prompt in 16 chunks of
-    2048, no decode rows), as TFLOP/s against the 2.5 PFLOP/s bf16 dense peak."""
+def mfma_roofline(kernel, flops, cold, warm):
+    """Roofline block of an MFMA-bound pass: flops per launch over the mean cold-cache launch
+    time against the 2.5 PFLOP/s dense bf16 peak (warm launches as context)."""
+    tf = flops / (cold["mean_ms"] * 1e-3) / 1e12
+    return {
+        "kernel": kernel,
+        "bound": "mfma",
+        "achieved": tf,
+        "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+        "flops_per_launch": flops,
+        "kernel_ms_flushed": cold,
+        "kernel_ms_warm": warm,
+        "warm_frac": flops / (warm["mean_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+    }
+
+
+def mfma_paths(torch, P, reps=20):
+    """MFMA-bound passes: the cascade shared-prefix pass (512 queries x 64 q heads over a
+    16384-token prefix, with its suffix pass, merge and the cascade-vs-single-pass ratio) and
+    the long chunked prefill (one 32768-token prompt in 16 chunks of 2048, alone and beside 128
+    decode rows), as TFLOP/s against the 2.5 PFLOP/s dense bf16 peak."""
     import workloads as W
 
     out = {}
@@ -473,10 +517,16 @@ def mfma_paths(torch, P, reps=5):
     os_, ls_ = torch.empty_like(o), torch.empty_like(l)
     merged = torch.empty(st.q.shape, dtype=torch.bfloat16, device="cuda")
 
-    def cascade():
+    def prefix():
         P.cascade_prefix_attention(s["q"], r.k_cache, r.v_cache, pbt, cv.prefix_len, r.shape, cws, out=o, lse=l)
+
+    def suffix():
         P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, sbt, s["qsl"], sctx, sseq, sshape, splan, r.ws,
                                  out=os_, lse=ls_)
+
+    def cascade():
+        prefix()
+        suffix()
         P.merge_attn_states(o, l, os_, ls_, out=merged)
 
     def timed(fn, n):
@@ -490,49 +540,75 @@ def mfma_paths(torch, P, reps=5):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
-    prefix_ms = timed(lambda: P.cascade_prefix_attention(s["q"], r.k_cache, r.v_cache, pbt, cv.prefix_len,
-                                                         r.shape, cws, out=o, lse=l), reps)
-    cascade_ms = timed(cascade, reps)
-    suffix_ms = timed(lambda: P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, sbt, s["qsl"], sctx, sseq, sshape,
-                                                       splan, r.ws, out=os_, lse=ls_), reps)
-    merge_ms = timed(lambda: P.merge_attn_states(o, l, os_, ls_, out=merged), reps)
+    fl = Flusher(torch)
+    for _ in range(5):
+        prefix()
+    pre_warm = stats(timed_launches(P, prefix, reps))
+    pre_cold = stats(timed_launches(P, prefix, reps, flush=fl))
+    suffix()
+    suf_warm = stats(timed_launches(P, suffix, reps))
+    suf_cold = stats(timed_launches(P, suffix, reps, flush=fl))
+    cascade_ms = timed(cascade, 10)
+    merge_ms = timed(lambda: P.merge_attn_states(o, l, os_, ls_, out=merged), 10)
     # suffix keys once per kv head + bf16 Q + fp32 O and LSE + block-table entries
     suffix_bytes = (kv_bytes(cv.suffix_seq_lens, wl.num_kv_heads, wl.head_dim)
                     + st.num_tokens * wl.num_q_heads * (wl.head_dim * 2 + wl.head_dim * 4 + 4)
                     + int(np.sum(-(-cv.suffix_seq_lens // wl.block_size))) * 4)
     fplan = P.plan_varlen(r.ws, st.query_start_loc, st.context_lens, st.seq_lens, r.shape)
     single_ms = timed(lambda: P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"],
-                                                       s["seq"], r.shape, fplan, r.ws, out=s["out"]), reps)
+                                                       s["seq"], r.shape, fplan, r.ws, out=s["out"]), 5)
     flops = st.num_tokens * wl.num_q_heads * cv.prefix_len * 4 * wl.head_dim
-    out["cascade_prefix"] = {
-        "workload": "512 queries, 64 q / 8 kv heads, D128, shared 16384-token prefix",
-        "ms": prefix_ms,
-        "TFLOP/s": flops / (prefix_ms * 1e-3) / 1e12,
-        "frac_of_bf16_peak": flops / (prefix_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
-        "suffix_pass_ms": suffix_ms,
-        "suffix_pass_GB/s": suffix_bytes / (suffix_ms * 1e-3) / 1e9,
+    res = mfma_roofline("cascade_kernel (pkv_cascade_prefix_attention)", flops, pre_cold, pre_warm)
+    res.update({
+        "workload": "cascade_shared_prefix: 512 queries, 64 q / 8 kv heads, D128, shared 16384-token prefix",
+        "suffix_pass": {
+            "kernel_ms_flushed": suf_cold,
+            "kernel_ms_warm": suf_warm,
+            "algorithmic_bytes": suffix_bytes,
+            "GB/s": suffix_bytes / (suf_cold["mean_ms"] * 1e-3) / 1e9,
+            "frac_of_peak": suffix_bytes / (suf_cold["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        },
         "merge_ms": merge_ms,
         "cascade_total_ms": cascade_ms,
         "single_pass_ms": single_ms,
         "cascade_speedup": single_ms / cascade_ms,
-    }
+        "cascade_speedup_pages_h100_context": "up to 31x on H100 SXM 80GB, workload not stated",
+    })
+    out["cascade_prefix"] = res
     del r
     torch.cuda.empty_cache()
 
     wl = W.long_chunked_prefill(seed=0, num_decode=0)
     r = Runner(wl, torch, P)
-    tot_ms, tot_fl = 0.0, 0
+    warm_all, cold_all, tot_fl = [], [], 0
+    chunk_reps = 3
     for s in r.steps:
         st = s["st"]
         P.append_kv(s["k"], s["v"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"], r.shape)
         plan = P.plan_varlen(r.ws, st.query_start_loc, st.context_lens, st.seq_lens, r.shape)
-        tot_ms += timed(lambda: P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"],
-                                                         s["seq"], r.shape, plan, r.ws, out=s["out"]), 2)
+
+        def call():
+            P.paged_attention_varlen(s["q"], r.k_cache, r.v_cache, s["bt"], s["qsl"], s["ctx"], s["seq"], r.shape,
+                                     plan, r.ws, out=s["out"])
+
+        call()
+        warm_all.append(timed_launches(P, call, chunk_reps))
+        cold_all.append(timed_launches(P, call, chunk_reps, flush=fl))
         tot_fl += step_flops(st, wl)
-    # The same prompt beside 128 decode rows at context 2048 (+1 per chunk): whole steps.
-    wl2 = W.long_chunked_prefill(seed=0)
+    # Whole-prompt time: the 16 chunks' launches, each chunk's launch repeated chunk_reps times;
+    # stats over the chunk_reps sums of one launch per chunk.
+    warm_tot = stats(np.sum(np.stack(warm_all), axis=0))
+    cold_tot = stats(np.sum(np.stack(cold_all), axis=0))
+    res = mfma_roofline("prefill_wide_kernel (pkv_paged_attention_varlen, 16 launches)", tot_fl, cold_tot, warm_tot)
+    res["workload"] = ("long_chunked_prefill: one 32768-token prompt in 16 chunks of 2048 against its growing paged "
+                       "context, 32 q / 8 kv heads, D128; times are of all 16 chunk launches together")
+    res["last_chunk_ms_flushed"] = stats(cold_all[-1])
+    out["long_chunked_prefill"] = res
     del r
     torch.cuda.empty_cache()
+
+    # The same prompt beside 128 decode rows at context 2048 (+1 per chunk): whole steps.
+    wl2 = W.long_chunked_prefill(seed=0)
     r2 = Runner(wl2, torch, P)
     mixed_ms = 0.0
     for s2 in r2.steps:
@@ -547,14 +623,8 @@ def mfma_paths(torch, P, reps=5):
         "ms_all_steps": mixed_ms,
         "tokens/s/layer": sum(s2["st"].num_tokens for s2 in r2.steps) / (mixed_ms * 1e-3),
     }
-    del r2
+    del r2, fl
     torch.cuda.empty_cache()
-    out["long_chunked_prefill"] = {
-        "workload": "one 32768-token prompt in 16 chunks of 2048 against its growing paged context, 32 q / 8 kv heads",
-        "ms_all_chunks": tot_ms,
-        "TFLOP/s": tot_fl / (tot_ms * 1e-3) / 1e12,
-        "frac_of_bf16_peak": tot_fl / (tot_ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
-    }
     return out
 
 
@@ -566,7 +636,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed decode step")
-    ap.add_argument("--mfma", action="store_true", help="also time the MFMA-bound cascade prefix and long prefill")
+    ap.add_argument("--no-mfma", action="store_true", help="skip the MFMA-bound cascade prefix and long prefill")
     ap.add_argument(
         "--copy-calibration",
         type=int,
@@ -602,7 +672,7 @@ def main():
     wl = W.mixed_llama8b(seed=0)
     runner = Runner(wl, torch, P)
     log(f"bench: timing {args.steps} steps after {args.warmup} warmup")
-    total_ms, kern_ms, launches = time_passes(runner, torch, args.steps, args.warmup)
+    total_ms, warm_each = time_passes(runner, torch, args.steps, args.warmup)
     ms_per_step = total_ms / args.steps
     tokens = sum(st.num_tokens for st in wl.steps)
     value = tokens / (ms_per_step * 1e-3)
@@ -610,9 +680,10 @@ def main():
     bytes_per_launch = [step_bytes(st, wl) for st in wl.steps]
     flops_per_launch = [step_flops(st, wl) for st in wl.steps]
     mean_bytes = float(np.mean(bytes_per_launch))
-    achieved = mean_bytes / (kern_ms * 1e-3) / 1e9
     log("bench: the same launches with cold caches")
-    flushed_ms = time_flushed(runner, torch, passes=5)
+    cold_each = time_flushed(runner, torch, passes=max(7, -(-20 // len(wl.steps))))
+    warm, cold = stats(warm_each), stats(cold_each)
+    achieved = mean_bytes / (cold["mean_ms"] * 1e-3) / 1e9
     traffic = measured_traffic()
     line = {
         "metric": "paged-attn decode HBM GB/s (% peak) + mixed-batch attn tokens/s per layer",
@@ -642,26 +713,28 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
+            "timing": "achieved = algorithmic bytes / mean launch time with cold caches (1 GiB write before "
+                      "each launch); warm = the K timed steps' launches back to back",
             "algorithmic_bytes_per_launch": mean_bytes,
-            "avg_launch_ms": kern_ms,
-            "launches_timed": launches,
             "flops_per_launch": float(np.mean(flops_per_launch)),
-            "flushed_avg_launch_ms": flushed_ms,
-            "flushed_frac": mean_bytes / (flushed_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_ms_flushed": cold,
+            "kernel_ms_warm": warm,
+            "warm_achieved": mean_bytes / (warm["mean_ms"] * 1e-3) / 1e9,
+            "warm_frac": mean_bytes / (warm["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
     }
     if not args.no_decode:
         log("bench: decode-only batch")
         line["decode_hbm"] = decode_hbm(torch, P)
         log("bench: decode-only batch over fp8 pools")
-        line["fp8_decode_hbm"] = fp8_decode_hbm(torch, P, steps=20, warmup=5, bf16_ms=line["decode_hbm"]["kernel_ms"])
+        line["fp8_decode_hbm"] = fp8_decode_hbm(torch, P, bf16_ms=line["decode_hbm"]["kernel_ms_flushed"]["mean_ms"])
     if not args.no_decode:
         log("bench: speculative-verify batch, tiny prefill")
         line["spec_verify_hbm"] = spec_verify_hbm(torch, P)
         line["tiny_prefill"] = tiny_prefill_latency(torch, P)
         if not args.no_graph:
             line["decode_graph_step"] = decode_graph_step(torch, P)
-    if args.mfma:
+    if not args.no_mfma:
         log("bench: MFMA paths (cascade prefix, long chunked prefill)")
         line["mfma_paths"] = mfma_paths(torch, P)
     if not args.no_cpu:

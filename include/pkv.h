@@ -194,9 +194,12 @@ int pkv_plan_varlen_host(pkv_varlen_plan* plan, int32_t* items, int32_t max_item
 
 /* a3/a4/a5 — paged attention over a mixed continuous batch [Tencent Cloud article,
  * continuous batching, chunked prefill and prefix caching sections; "11. vLLM principles"
- * section 11.3, prefill vs decode]: one kernel launch serves decode rows (one query token;
- * VALU path with split-KV) and chunked-prefill / prefix-hit rows (MFMA tiles with the causal
- * mask offset by context_lens), followed by a split-KV reduce when any row was split.
+ * section 11.3, prefill vs decode]: decode rows (one query token; VALU path with split-KV) and
+ * chunked-prefill / prefix-hit rows (MFMA tiles with the causal mask offset by context_lens).
+ * Launches, by plan: a batch of decode rows and 128-row prefill tiles is one kernel; a batch
+ * with 256-row prefill tiles (at least 2048 packed prefill rows) runs them in one kernel and
+ * its decode rows in a second; rows of 2 .. 32 / G tokens (short items) add one more kernel;
+ * a split-KV reduce follows when any row was split.
  * out: [num_tokens, num_q_heads, head_dim], bf16 or fp32 (out_dtype); lse: nullable fp32
  * [num_tokens, num_q_heads].  The pools must already hold this step's new keys/values
  * (pkv_reshape_and_cache first).  `plan` must come from pkv_plan_varlen with the same
@@ -210,9 +213,9 @@ int pkv_paged_attention_varlen(void* out, int32_t out_dtype, float* lse, const v
                                size_t workspace_bytes, void* stream);
 
 /* a3/a4/a5 over fp8 pools: as pkv_paged_attention_varlen (same plan and workspace), reading
- * e4m3 codes with their per-(block, kv head) scales.  Decode rows convert codes to bf16
- * exactly and apply the key scale to the block's scores and the value scale to its
- * probabilities; prefill tiles stage code * scale rounded to bf16. */
+ * e4m3 codes with their per-(block, kv head) scales.  Every path converts codes to bf16
+ * exactly (prefill tiles stage the exact codes in LDS) and applies the key scale to the
+ * block's scores and the value scale to its probabilities, in fp32. */
 int pkv_paged_attention_varlen_fp8(void* out, int32_t out_dtype, float* lse, const void* q,
                                    const void* k_cache, const void* v_cache, const float* k_scale,
                                    const float* v_scale, const int32_t* block_tables,
@@ -237,8 +240,10 @@ int pkv_paged_attention_varlen_fp8(void* out, int32_t out_dtype, float* lse, con
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t max_seq_len, const pkv_shape* shape);
 
 /* Decode attention (a3) for num_seqs rows of one query token each: token query_start_loc[r] of
- * q attends to keys 0..seq_lens[r]-1 of row r.  out bf16 or fp32 [num_tokens, Hq, D], lse
- * nullable fp32 [num_tokens, Hq].  Errors as pkv_paged_attention_varlen. */
+ * q attends to keys 0..seq_lens[r]-1 of row r.  One token per row means query_start_loc must be
+ * 0, 1, ..., num_seqs (row r's token is token r; split rows' partial states are indexed by it),
+ * so q, out and lse have num_seqs rows: out bf16 or fp32 [num_seqs, Hq, D], lse nullable fp32
+ * [num_seqs, Hq].  Errors as pkv_paged_attention_varlen. */
 int pkv_paged_attention_decode(void* out, int32_t out_dtype, float* lse, const void* q,
                                const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                const int32_t* query_start_loc, const int32_t* seq_lens,
@@ -287,13 +292,20 @@ int pkv_merge_attn_states(void* out, int32_t out_dtype, float* lse_out, const fl
                           const float* lse_a, const float* out_b, const float* lse_b,
                           int32_t num_tokens, int32_t num_heads, int32_t head_dim, void* stream);
 
-/* Launch timing (measurement aid, per calling thread): after pkv_timing_begin(), every
- * varlen attention kernel launched by pkv_paged_attention_varlen is bracketed by two HIP
- * events recorded on its stream (the split-KV reduce falls outside them).  pkv_timing_end()
- * stops recording, waits for the last event and returns the summed kernel milliseconds and
- * the number of launches.  Creates HIP events on first use; not for graph capture. */
+/* Launch timing (measurement aid, per calling thread): after pkv_timing_begin(), the attention
+ * kernels launched by pkv_paged_attention_varlen(_fp8), pkv_paged_attention_decode(_fp8) and
+ * pkv_cascade_prefix_attention(_fp8) are bracketed by two HIP events recorded on their stream
+ * (the split-KV / segment reduce falls outside them; a varlen call whose plan needs more than
+ * one attention kernel counts as one launch).  pkv_timing_end() stops recording, waits for the
+ * last event and returns the summed kernel milliseconds and the number of launches.  Creates
+ * HIP events on first use; not for graph capture. */
 int pkv_timing_begin(void);
 int pkv_timing_end(double* total_ms, int32_t* launches);
+
+/* Per-launch milliseconds of the window the last pkv_timing_end() closed, in launch order:
+ * copies up to `capacity` of them into ms_each (host memory) and returns how many there were
+ * (negative PKV_E* code on a bad buffer). */
+int pkv_timing_durations(double* ms_each, int32_t capacity);
 
 /* Thread-local description of the last error returned on this thread ("" if none). */
 const char* pkv_last_error(void);

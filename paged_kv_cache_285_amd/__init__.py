@@ -27,6 +27,7 @@ from .ops import (  # noqa: F401
     reshape_and_cache,
     reshape_and_cache_fp8,
     timing_begin,
+    timing_durations,
     timing_end,
     varlen_workspace_size,
     version,

@@ -39,6 +39,7 @@ EXPORTS = (
     "pkv_merge_attn_states",
     "pkv_timing_begin",
     "pkv_timing_end",
+    "pkv_timing_durations",
     "pkv_last_error",
     "pkv_version",
 )
@@ -130,6 +131,7 @@ _SIGS = {
     "pkv_merge_attn_states": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
     "pkv_timing_begin": (ctypes.c_int, []),
     "pkv_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
+    "pkv_timing_durations": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }

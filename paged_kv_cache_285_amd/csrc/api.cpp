@@ -366,6 +366,7 @@ struct LaunchTiming {
   bool on = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
   size_t used = 0;
+  std::vector<double> last;  // per-launch milliseconds of the window pkv_timing_end closed
 };
 thread_local LaunchTiming g_timing;
 
@@ -434,6 +435,7 @@ int pkv_timing_end(double* total_ms, int32_t* launches) {
   if (!total_ms || !launches) return fail(PKV_EINVAL, "null pointer argument");
   g_timing.on = false;
   double sum = 0.0;
+  g_timing.last.clear();
   for (size_t i = 0; i < g_timing.used; ++i) {
     hipError_t e = hipEventSynchronize(g_timing.pool[i].second);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(timing)");
@@ -441,11 +443,20 @@ int pkv_timing_end(double* total_ms, int32_t* launches) {
     e = hipEventElapsedTime(&ms, g_timing.pool[i].first, g_timing.pool[i].second);
     if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime(timing)");
     sum += ms;
+    g_timing.last.push_back(ms);
   }
   *total_ms = sum;
   *launches = (int32_t)g_timing.used;
   g_timing.used = 0;
   return ok();
+}
+
+int pkv_timing_durations(double* ms_each, int32_t capacity) {
+  if (capacity < 0 || (capacity > 0 && !ms_each)) return fail(PKV_EINVAL, "bad duration buffer");
+  const size_t n = std::min<size_t>((size_t)capacity, g_timing.last.size());
+  for (size_t i = 0; i < n; ++i) ms_each[i] = g_timing.last[i];
+  g_error.clear();
+  return (int)g_timing.last.size();
 }
 
 size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
@@ -896,9 +907,11 @@ static int cascade_impl(float* out_prefix, float* lse_prefix, const void* q, con
   a.bt_shift = bt_shift(shape);
   a.scale_log2 = scale_log2(shape);
   const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (int rc = timing_mark((hipStream_t)stream, true)) return rc;
   hipError_t e = (fp8 ? pkv::launch_cascade_fp8 : pkv::launch_cascade)(a, shape->head_dim, G,
                                                                        (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "cascade prefix launch");
+  if (int rc = timing_mark((hipStream_t)stream, false)) return rc;
   if (cs.segs > 1) {
     pkv::ReduceArgs ra;
     ra.part_o = a.part_o;

@@ -7,7 +7,9 @@
 
 namespace pkv {
 
-constexpr int kBlockSize = 16;       // tokens per cache block (the only supported size)
+// Tokens per 16-token tile, the unit every kernel addresses.  A cache block of 16 R tokens
+// (block_size 16, 32, 64, 128 or 256) is R consecutive tiles, so "block" below means such a tile.
+constexpr int kBlockSize = 16;
 constexpr int kKvTile = 64;          // keys per MFMA KV tile (4 cache blocks)
 constexpr int kTileRows = 128;       // packed (token, q head) rows of a varlen prefill tile
 constexpr int kWideTileRows = 256;   // rows of a wide tile (prefill-heavy batches, cascade)

@@ -53,6 +53,45 @@ def _opt(t: Optional[torch.Tensor], name: str, dtypes=None) -> ctypes.c_void_p:
     return ctypes.c_void_p(0) if t is None else _dev(t, name, dtypes)
 
 
+def _need(t: Optional[torch.Tensor], n: int, name: str) -> None:
+    """Raise unless tensor ``t`` (if given) holds at least ``n`` elements: a buffer smaller than
+    the sizes passed to the library would be read or written out of bounds on the device."""
+    if t is not None and isinstance(t, torch.Tensor) and t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
+
+
+def _pool_elems(shape: PkvShape) -> int:
+    """Elements of one pool (keys or values) of this shape."""
+    return int(shape.num_blocks) * int(shape.num_kv_heads) * int(shape.block_size) * int(shape.head_dim)
+
+
+def _need_meta(block_tables, query_start_loc, context_lens, seq_lens, num_seqs: int, shape: PkvShape) -> None:
+    _need(block_tables, num_seqs * int(shape.bt_stride), "block_tables")
+    _need(query_start_loc, num_seqs + 1, "query_start_loc")
+    _need(context_lens, num_seqs, "context_lens")
+    _need(seq_lens, num_seqs, "seq_lens")
+
+
+def _need_pools(k_cache, v_cache, shape: PkvShape, k_scale=None, v_scale=None) -> None:
+    _need(k_cache, _pool_elems(shape), "k_cache")
+    _need(v_cache, _pool_elems(shape), "v_cache")
+    _need(k_scale, int(shape.num_blocks) * int(shape.num_kv_heads), "k_scale")
+    _need(v_scale, int(shape.num_blocks) * int(shape.num_kv_heads), "v_scale")
+
+
+def _need_new_kv(k, v, num_tokens: int, shape: PkvShape) -> None:
+    n = num_tokens * int(shape.num_kv_heads) * int(shape.head_dim)
+    _need(k, n, "k")
+    _need(v, n, "v")
+
+
+def _need_q_out(q, out, lse, num_tokens: int, shape: PkvShape) -> None:
+    n = num_tokens * int(shape.num_q_heads)
+    _need(q, n * int(shape.head_dim), "q")
+    _need(out, n * int(shape.head_dim), "out")
+    _need(lse, n, "lse")
+
+
 def _host_i32(x, name: str) -> np.ndarray:
     if isinstance(x, torch.Tensor):
         x = x.detach().cpu().numpy()
@@ -78,6 +117,8 @@ def compute_slot_mapping(
     num_seqs = int(context_lens.numel())
     if out is None:
         out = torch.empty(num_tokens, dtype=torch.int64, device=block_tables.device)
+    _need(out, num_tokens, "slot_mapping")
+    _need_meta(block_tables, query_start_loc, context_lens, None, num_seqs, shape)
     check(
         lib().pkv_compute_slot_mapping(
             _dev(out, "slot_mapping", (torch.int64,)),
@@ -103,6 +144,9 @@ def reshape_and_cache(
 ) -> None:
     """Write the new tokens' K/V bits into the paged pools at their slots (in place)."""
     num_tokens = int(k.shape[0])
+    _need_new_kv(k, v, num_tokens, shape)
+    _need_pools(k_cache, v_cache, shape)
+    _need(slot_mapping, num_tokens, "slot_mapping")
     check(
         lib().pkv_reshape_and_cache(
             _dev(k, "k", _16BIT),
@@ -119,6 +163,8 @@ def reshape_and_cache(
 
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: torch.Tensor, shape: PkvShape) -> None:
     """Copy physical blocks src -> dst in both pools (rows {src, dst} of int32 ``block_pairs``)."""
+    _need_pools(k_cache, v_cache, shape)
+    _need(block_pairs, 2 * int(block_pairs.shape[0]), "block_pairs")
     check(
         lib().pkv_copy_blocks(
             _dev(k_cache, "k_cache", _16BIT),
@@ -143,6 +189,10 @@ def append_kv(
     slot_mapping: Optional[torch.Tensor] = None,
 ) -> Optional[torch.Tensor]:
     """Slot mapping and cache write in one launch; also fills ``slot_mapping`` when given."""
+    _need_new_kv(k, v, int(k.shape[0]), shape)
+    _need_pools(k_cache, v_cache, shape)
+    _need_meta(block_tables, query_start_loc, context_lens, None, int(context_lens.numel()), shape)
+    _need(slot_mapping, int(k.shape[0]), "slot_mapping")
     check(
         lib().pkv_append_kv(
             _opt(slot_mapping, "slot_mapping", (torch.int64,)),
@@ -174,6 +224,9 @@ def reshape_and_cache_fp8(
 ) -> None:
     """Quantise the new tokens' bf16 K/V to e4m3 under their blocks' scales (fp32
     [num_blocks, Hkv]) and write them into the fp8 pools at their slots (in place)."""
+    _need_new_kv(k, v, int(k.shape[0]), shape)
+    _need_pools(k_cache, v_cache, shape, k_scale, v_scale)
+    _need(slot_mapping, int(k.shape[0]), "slot_mapping")
     check(
         lib().pkv_reshape_and_cache_fp8(
             _dev(k, "k", _16BIT),
@@ -204,6 +257,10 @@ def append_kv_fp8(
     slot_mapping: Optional[torch.Tensor] = None,
 ) -> Optional[torch.Tensor]:
     """append_kv into fp8 pools: slot mapping and quantising cache write in one launch."""
+    _need_new_kv(k, v, int(k.shape[0]), shape)
+    _need_pools(k_cache, v_cache, shape, k_scale, v_scale)
+    _need_meta(block_tables, query_start_loc, context_lens, None, int(context_lens.numel()), shape)
+    _need(slot_mapping, int(k.shape[0]), "slot_mapping")
     check(
         lib().pkv_append_kv_fp8(
             _opt(slot_mapping, "slot_mapping", (torch.int64,)),
@@ -234,6 +291,8 @@ def copy_blocks_fp8(
     shape: PkvShape,
 ) -> None:
     """copy_blocks for fp8 pools: the blocks' bytes and their per-kv-head scales."""
+    _need_pools(k_cache, v_cache, shape, k_scale, v_scale)
+    _need(block_pairs, 2 * int(block_pairs.shape[0]), "block_pairs")
     check(
         lib().pkv_copy_blocks_fp8(
             _dev(k_cache, "k_cache", _FP8),
@@ -324,6 +383,9 @@ def paged_attention_varlen(
     num_tokens = int(q.shape[0])
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _need_q_out(q, out, lse, num_tokens, shape)
+    _need_pools(k_cache, v_cache, shape)
+    _need_meta(block_tables, query_start_loc, context_lens, seq_lens, int(context_lens.numel()), shape)
     code = PKV_DTYPE_F32 if out.dtype == torch.float32 else PKV_DTYPE_BF16
     check(
         lib().pkv_paged_attention_varlen(
@@ -370,6 +432,9 @@ def paged_attention_varlen_fp8(
     num_tokens = int(q.shape[0])
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _need_q_out(q, out, lse, num_tokens, shape)
+    _need_pools(k_cache, v_cache, shape, k_scale, v_scale)
+    _need_meta(block_tables, query_start_loc, context_lens, seq_lens, int(context_lens.numel()), shape)
     code = PKV_DTYPE_F32 if out.dtype == torch.float32 else PKV_DTYPE_BF16
     check(
         lib().pkv_paged_attention_varlen_fp8(
@@ -424,6 +489,9 @@ def paged_attention_decode(
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     code = PKV_DTYPE_F32 if out.dtype == torch.float32 else PKV_DTYPE_BF16
+    _need_q_out(q, out, lse, num_seqs, shape)
+    _need_pools(k_cache, v_cache, shape, k_scale, v_scale)
+    _need_meta(block_tables, query_start_loc, None, seq_lens, num_seqs, shape)
     ws = workspace
     common = (
         _dev(block_tables, "block_tables", (torch.int32,)),
@@ -468,6 +536,9 @@ def cascade_prefix_attention(
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _need_q_out(q, out, lse, T, shape)
+    _need(prefix_block_table, int(prefix_len) // max(int(shape.block_size), 1), "prefix_block_table")
+    _need_pools(k_cache, v_cache, shape)
     ws = workspace
     check(
         lib().pkv_cascade_prefix_attention(
@@ -507,6 +578,9 @@ def cascade_prefix_attention_fp8(
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _need_q_out(q, out, lse, T, shape)
+    _need(prefix_block_table, int(prefix_len) // max(int(shape.block_size), 1), "prefix_block_table")
+    _need_pools(k_cache, v_cache, shape, k_scale, v_scale)
     ws = workspace
     check(
         lib().pkv_cascade_prefix_attention_fp8(
@@ -543,6 +617,9 @@ def merge_attn_states(
     if out is None:
         out = torch.empty((T, H, D), dtype=out_dtype, device=out_a.device)
     code = PKV_DTYPE_F32 if out.dtype == torch.float32 else PKV_DTYPE_BF16
+    for t, nm, n in ((out, "out", T * H * D), (out_b, "out_b", T * H * D), (lse_a, "lse_a", T * H),
+                     (lse_b, "lse_b", T * H), (lse_out, "lse_out", T * H)):
+        _need(t, n, nm)
     check(
         lib().pkv_merge_attn_states(
             _dev(out, "out", _16BIT + (torch.float32,)),
@@ -567,8 +644,18 @@ def timing_begin() -> None:
 
 
 def timing_end() -> Tuple[float, int]:
-    """Stop timing; return (summed kernel milliseconds, number of varlen launches)."""
+    """Stop timing; return (summed kernel milliseconds, number of timed launches)."""
     ms = ctypes.c_double()
     n = ctypes.c_int32()
     check(lib().pkv_timing_end(ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def timing_durations() -> np.ndarray:
+    """Per-launch kernel milliseconds of the window the last timing_end() closed."""
+    n = lib().pkv_timing_durations(None, 0)
+    check(min(n, 0))
+    buf = np.zeros(max(n, 1), dtype=np.float64)
+    got = lib().pkv_timing_durations(buf.ctypes.data_as(ctypes.c_void_p), n)
+    check(min(got, 0))
+    return buf[:n]

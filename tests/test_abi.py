@@ -231,3 +231,57 @@ def test_workspace_bound_holds_for_every_plan(P):
         plan, _ = P.plan_varlen_host(qsl, ctx, seq, s)
         bound = P.varlen_workspace_size(B, int(qsl[-1]), int(seq.max()), s)
         assert plan.workspace_used <= bound
+
+
+def test_binding_rejects_buffers_smaller_than_the_shape(P):
+    """The Python binding compares every buffer's size with the shape it passes and raises
+    before the library is called (on CPU tensors the size check comes first, so a correctly
+    sized CPU tensor fails only the device check)."""
+    import torch
+
+    s = P.make_shape(8, 2, 64, 10, 4)
+    pool = 10 * 2 * 16 * 64
+    T, B = 5, 2
+    good = dict(
+        q=torch.zeros(T * 8 * 64, dtype=torch.int16),
+        k_cache=torch.zeros(pool, dtype=torch.int16),
+        v_cache=torch.zeros(pool, dtype=torch.int16),
+        block_tables=torch.zeros(B * 4, dtype=torch.int32),
+        query_start_loc=torch.zeros(B + 1, dtype=torch.int32),
+        context_lens=torch.zeros(B, dtype=torch.int32),
+        seq_lens=torch.zeros(B, dtype=torch.int32),
+    )
+    plan = P.PkvVarlenPlan()
+    ws = torch.zeros(256, dtype=torch.uint8)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return P.paged_attention_varlen(a["q"].view(T, 8, 64) if a["q"].numel() == T * 512 else a["q"],
+                                        a["k_cache"], a["v_cache"], a["block_tables"], a["query_start_loc"],
+                                        a["context_lens"], a["seq_lens"], s, plan, ws,
+                                        out=torch.zeros(T * 8 * 64, dtype=torch.int16))
+
+    with pytest.raises(ValueError, match="device tensor"):
+        call()
+    for name, n in (("k_cache", pool - 1), ("v_cache", pool // 2), ("block_tables", B * 4 - 1),
+                    ("query_start_loc", B), ("seq_lens", B - 1)):
+        with pytest.raises(ValueError, match=f"{name} holds"):
+            call(**{name: torch.zeros(n, dtype=good[name].dtype)})
+    with pytest.raises(ValueError, match="lse holds"):
+        P.paged_attention_varlen(good["q"].view(T, 8, 64), good["k_cache"], good["v_cache"], good["block_tables"],
+                                 good["query_start_loc"], good["context_lens"], good["seq_lens"], s, plan, ws,
+                                 out=torch.zeros(T * 8 * 64, dtype=torch.int16), lse=torch.zeros(T * 8 - 1))
+    with pytest.raises(ValueError, match="v holds"):
+        P.reshape_and_cache(torch.zeros((T, 2, 64), dtype=torch.int16), torch.zeros((T, 2, 32), dtype=torch.int16),
+                            good["k_cache"], good["v_cache"], torch.zeros(T, dtype=torch.int64), s)
+    with pytest.raises(ValueError, match="k_scale holds"):
+        P.reshape_and_cache_fp8(torch.zeros((T, 2, 64), dtype=torch.int16), torch.zeros((T, 2, 64), dtype=torch.int16),
+                                torch.zeros(pool, dtype=torch.uint8), torch.zeros(pool, dtype=torch.uint8),
+                                torch.zeros(10 * 2 - 1), torch.zeros(10 * 2), torch.zeros(T, dtype=torch.int64), s)
+    with pytest.raises(ValueError, match="prefix_block_table holds"):
+        P.cascade_prefix_attention(good["q"].view(T, 8, 64), good["k_cache"], good["v_cache"],
+                                   torch.zeros(1, dtype=torch.int32), 32, s)
+    with pytest.raises(ValueError, match="out_b holds"):
+        P.merge_attn_states(torch.zeros((T, 8, 64)), torch.zeros((T, 8)), torch.zeros((T, 8, 63)),
+                            torch.zeros((T, 8)))
