@@ -250,6 +250,23 @@ int pkv_paged_attention_decode(void* out, int32_t out_dtype, float* lse, const v
                                int32_t num_seqs, int32_t max_seq_len, const pkv_shape* shape,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): pkv_paged_attention_decode with no workspace.  The
+ * split-KV partial states go to a device scratch array of PKV_DECODE_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends; the call allocates nothing.
+ * Same arguments, layouts, results (bit for bit) and errors as pkv_paged_attention_decode,
+ * plus PKV_EWORKSPACE when the batch's partial states exceed the scratch
+ * (pkv_decode_workspace_size(num_seqs, max_seq_len, shape) > PKV_DECODE_SCRATCH_BYTES; e.g.
+ * 512 rows of 32 q heads at D 128 up to 8192 keys fit).  Every call on one GPU shares that
+ * GPU's scratch: calls that may overlap on one GPU (other streams, other threads) race and
+ * must be serialised by the caller.  Not timed by pkv_timing_begin. */
+#define PKV_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+int pkv_paged_attention_decode_noalloc(void* out, int32_t out_dtype, float* lse, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* query_start_loc,
+                                       const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                       const pkv_shape* shape, void* stream);
+
 /* The same over fp8 (e4m3) pools with per-(block, kv head) scales. */
 int pkv_paged_attention_decode_fp8(void* out, int32_t out_dtype, float* lse, const void* q,
                                    const void* k_cache, const void* v_cache, const float* k_scale,

@@ -5,7 +5,15 @@ is its thin Python binding.  Importing it does not load the library; the first c
 raises if the library has not been built.
 """
 
-from ._lib import PKV_DTYPE_BF16, PKV_DTYPE_F32, PkvError, PkvShape, PkvVarlenPlan, lib  # noqa: F401
+from ._lib import (  # noqa: F401
+    PKV_DECODE_SCRATCH_BYTES,
+    PKV_DTYPE_BF16,
+    PKV_DTYPE_F32,
+    PkvError,
+    PkvShape,
+    PkvVarlenPlan,
+    lib,
+)
 from .ops import (  # noqa: F401
     alloc_workspace,
     append_kv,
@@ -20,6 +28,7 @@ from .ops import (  # noqa: F401
     make_shape,
     merge_attn_states,
     paged_attention_decode,
+    paged_attention_decode_noalloc,
     paged_attention_varlen,
     paged_attention_varlen_fp8,
     plan_varlen,

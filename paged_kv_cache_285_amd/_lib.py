@@ -17,6 +17,8 @@ PKV_DTYPE_BF16 = 0
 PKV_DTYPE_F32 = 1
 
 # Entry points declared in include/pkv.h (kept in sync by tests/test_abi.py).
+PKV_DECODE_SCRATCH_BYTES = 32 << 20  # device scratch of pkv_paged_attention_decode_noalloc
+
 EXPORTS = (
     "pkv_varlen_workspace_size",
     "pkv_compute_slot_mapping",
@@ -32,6 +34,7 @@ EXPORTS = (
     "pkv_paged_attention_varlen_fp8",
     "pkv_decode_workspace_size",
     "pkv_paged_attention_decode",
+    "pkv_paged_attention_decode_noalloc",
     "pkv_paged_attention_decode_fp8",
     "pkv_cascade_workspace_size",
     "pkv_cascade_prefix_attention",
@@ -114,6 +117,10 @@ _SIGS = {
     "pkv_paged_attention_decode": (
         ctypes.c_int,
         [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _P, _SZ, _P],
+    ),
+    "pkv_paged_attention_decode_noalloc": (
+        ctypes.c_int,
+        [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _SHAPE, _P],
     ),
     "pkv_paged_attention_decode_fp8": (
         ctypes.c_int,

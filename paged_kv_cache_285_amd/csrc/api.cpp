@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -742,6 +743,32 @@ int pkv_paged_attention_varlen_fp8(void* out, int32_t out_dtype, float* lse, con
                      shape, plan, workspace, workspace_bytes, stream);
 }
 
+// Device scratch of pkv_paged_attention_decode_noalloc: the split-KV partial states live in this
+// file-scope array instead of a caller workspace.  In host code `scratch` is only the host-side
+// handle of the symbol; its device address (one copy per GPU) comes from hipGetSymbolAddress,
+// taken once per device on the entry point's first call there with that device current.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_ptr;  // device ordinal -> device address of `scratch`
+
+static int scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    it = g_scratch_ptr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return PKV_OK;
+}
+
 // Work split of a graph-capturable decode batch: the split size the varlen planner would pick
 // if every row had max_seq_len keys (a power of two of 16 to 256 blocks of 16 keys), and the
 // number of splits of the longest row.
@@ -769,12 +796,14 @@ size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t max_seq_len, const pk
   return decode_bytes(num_seqs, decode_split(num_seqs, max_seq_len, shape), shape);
 }
 
+// use_scratch: the partial states go to the device scratch array (no workspace, no timing
+// events); the call then allocates nothing.
 static int decode_impl(void* out, int32_t out_dtype, float* lse, const void* q, const void* k_cache,
                        const void* v_cache, const float* k_scale, const float* v_scale, bool fp8,
                        const int32_t* block_tables, const int32_t* query_start_loc,
                        const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                        const pkv_shape* shape, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       void* stream, bool use_scratch = false) {
   if (int rc = check_shape(shape)) return rc;
   if (out_dtype != PKV_DTYPE_BF16 && out_dtype != PKV_DTYPE_F32)
     return fail(PKV_EINVAL, "out_dtype %d unsupported", out_dtype);
@@ -788,6 +817,17 @@ static int decode_impl(void* out, int32_t out_dtype, float* lse, const void* q, 
     return fail(PKV_EINVAL, "null pointer argument");
   const DecodeSplit d = decode_split(num_seqs, max_seq_len, shape);
   const size_t need = decode_bytes(num_seqs, d, shape);
+  if (use_scratch) {
+    if (need > kDecodeScratchBytes)
+      return fail(PKV_EWORKSPACE,
+                  "decode of %d rows up to %d keys needs %zu bytes of partial states, more than the %zu-byte "
+                  "device scratch of the allocation-free entry point",
+                  num_seqs, max_seq_len, need, kDecodeScratchBytes);
+    if (need > 0) {
+      if (int rc = scratch_address(&workspace)) return rc;
+      workspace_bytes = kDecodeScratchBytes;
+    }
+  }
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_EWORKSPACE, "decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
   pkv::VarlenArgs a{};
@@ -815,11 +855,13 @@ static int decode_impl(void* out, int32_t out_dtype, float* lse, const void* q, 
   a.bt_shift = bt_shift(shape);
   a.scale_log2 = scale_log2(shape);
   const int G = shape->num_q_heads / shape->num_kv_heads;
-  if (int rc = timing_mark((hipStream_t)stream, true)) return rc;
+  if (!use_scratch)
+    if (int rc = timing_mark((hipStream_t)stream, true)) return rc;
   hipError_t e = (fp8 ? pkv::launch_decode_graph_fp8 : pkv::launch_decode_graph)(
       a, shape->head_dim, G, num_seqs, d.splits, d.split_keys, num_seqs, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  if (int rc = timing_mark((hipStream_t)stream, false)) return rc;
+  if (!use_scratch)
+    if (int rc = timing_mark((hipStream_t)stream, false)) return rc;
   if (d.splits > 1) {
     pkv::ReduceArgs ra;
     ra.part_o = a.part_o;
@@ -845,6 +887,16 @@ int pkv_paged_attention_decode(void* out, int32_t out_dtype, float* lse, const v
   return decode_impl(out, out_dtype, lse, q, k_cache, v_cache, nullptr, nullptr, false, block_tables,
                      query_start_loc, seq_lens, num_seqs, max_seq_len, shape, workspace,
                      workspace_bytes, stream);
+}
+
+int pkv_paged_attention_decode_noalloc(void* out, int32_t out_dtype, float* lse, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* query_start_loc,
+                                       const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                       const pkv_shape* shape, void* stream) {
+  return decode_impl(out, out_dtype, lse, q, k_cache, v_cache, nullptr, nullptr, false, block_tables,
+                     query_start_loc, seq_lens, num_seqs, max_seq_len, shape, nullptr, 0, stream,
+                     /*use_scratch=*/true);
 }
 
 int pkv_paged_attention_decode_fp8(void* out, int32_t out_dtype, float* lse, const void* q,

@@ -515,6 +515,46 @@ def paged_attention_decode(
     return out
 
 
+def paged_attention_decode_noalloc(
+    q: torch.Tensor,
+    k_cache: torch.Tensor,
+    v_cache: torch.Tensor,
+    block_tables: torch.Tensor,
+    query_start_loc: torch.Tensor,
+    seq_lens: torch.Tensor,
+    shape: PkvShape,
+    max_seq_len: int,
+    out: torch.Tensor,
+    lse: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """paged_attention_decode with its partial states in the library's device scratch: no
+    workspace, and (with ``out`` given) nothing allocated, so it can be called where allocation
+    is not allowed.  Calls that may overlap on one GPU race on the shared scratch."""
+    num_seqs = int(seq_lens.numel())
+    code = PKV_DTYPE_F32 if out.dtype == torch.float32 else PKV_DTYPE_BF16
+    _need_q_out(q, out, lse, num_seqs, shape)
+    _need_pools(k_cache, v_cache, shape)
+    _need_meta(block_tables, query_start_loc, None, seq_lens, num_seqs, shape)
+    check(
+        lib().pkv_paged_attention_decode_noalloc(
+            _dev(out, "out", _16BIT + (torch.float32,)),
+            code,
+            _opt(lse, "lse", (torch.float32,)),
+            _dev(q, "q", _16BIT),
+            _dev(k_cache, "k_cache", _16BIT),
+            _dev(v_cache, "v_cache", _16BIT),
+            _dev(block_tables, "block_tables", (torch.int32,)),
+            _dev(query_start_loc, "query_start_loc", (torch.int32,)),
+            _dev(seq_lens, "seq_lens", (torch.int32,)),
+            num_seqs,
+            int(max_seq_len),
+            ctypes.byref(shape),
+            _stream(),
+        )
+    )
+    return out
+
+
 def cascade_workspace_size(num_tokens: int, prefix_len: int, shape: PkvShape) -> int:
     return int(lib().pkv_cascade_workspace_size(num_tokens, prefix_len, ctypes.byref(shape)))
 

@@ -285,3 +285,16 @@ def test_binding_rejects_buffers_smaller_than_the_shape(P):
     with pytest.raises(ValueError, match="out_b holds"):
         P.merge_attn_states(torch.zeros((T, 8, 64)), torch.zeros((T, 8)), torch.zeros((T, 8, 63)),
                             torch.zeros((T, 8)))
+
+
+def test_decode_noalloc_refuses_a_batch_beyond_its_scratch(P):
+    """The allocation-free decode checks the batch's partial-state bytes against its device
+    scratch before touching the device."""
+    lib = P.lib()
+    s = shape(P, num_blocks=1 << 20, bt_stride=4096)
+    assert P.decode_workspace_size(4096, 65536, s) > P.PKV_DECODE_SCRATCH_BYTES
+    rc = lib.pkv_paged_attention_decode_noalloc(ctypes.c_void_p(16), 0, None, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                                ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                                ctypes.c_void_p(16), 4096, 65536, ctypes.byref(s), None)
+    assert rc == -2
+    assert "scratch" in lib.pkv_last_error().decode()
