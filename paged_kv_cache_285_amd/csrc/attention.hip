@@ -1261,10 +1261,10 @@ __device__ void mfma_tile(const uint16_t* __restrict__ q, int Hq, const void* __
 // work: step t issues the MFMAs of S^T(t+1) = K(t+1) Q^T and O^T += V(t-1)^T P^T(t-1) while the
 // VALU computes the softmax of tile t (whose S^T the previous step produced).  Step t also
 // loads K(t+3) and V(t+1) at its start and stores them into LDS at its end (waves 0-3 copy K,
-// waves 4-7 copy V; a ring of four buffers each), with one barrier per two steps.  P^T is built
-// from the S^T accumulator with two lane-half swaps per K-step so that a lane holds 8
-// consecutive keys; the V^T operand is then one 16-byte read of the value tile in its natural
-// dim-major order.
+// waves 4-7 copy V; a ring of four buffers each), with one barrier per two steps.  P^T is the
+// S^T accumulator's p as they stand (a lane holds keys 4h..4h+3 and 8+4h..8+4h+3 of each 16-key
+// step), and the value tile is staged with its 4-key groups in that order, so the V^T operand is
+// one 16-byte read.  The softmax takes no tile maximum after the first tile (see pipe_step).
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct PipeRegs {
@@ -1310,32 +1310,84 @@ __device__ __forceinline__ void pipe_pv_step(PipeRegs<D>& R, const uint16_t* __r
   }
 }
 
+// Scores of the tile up to which p = exp2(s * scale - m) may grow before the tile is redone with
+// its own maximum: a tile's rounded weights summing past 2^32 (or not finite).
+constexpr float kPipeOverflow = 4294967296.0f;
+
+// Softmax of S^T set CUR into P^T and the tile's row sums, all at once (the first tile, and a tile
+// redone after an overflow): the running max becomes max(m, the tile's max), with the output and
+// row sums rescaled when m was finite (they hold the tiles before this one).
+template <int D, int CUR, bool FP8, bool LSE>
+__device__ __forceinline__ void pipe_softmax_with_max(PipeRegs<D>& R, int h, const float (&slk)[4],
+                                                      const float (&svb)[4], const float (&rsv)[4], float& ts,
+                                                      float& tr) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    float mb = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mb = fmaxf(mb, R.sacc[CUR][ks >> 1][8 * (ks & 1) + e]);
+    mx = fmaxf(mx, mb * slk[ks]);
+  }
+  mx = fmaxf(mx, other_half(mx, h));
+  const float mnew = fmaxf(R.m, mx);
+  if (R.m != -INFINITY) {
+    const float alpha = fast_exp2(R.m - mnew);
+    R.lsum *= alpha;
+    R.lr *= alpha;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) R.oacc[d][e] *= alpha;
+  }
+  R.m = mnew;
+  const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+  ts = 0.f;
+  tr = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 w;
+    float rb = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float p0 = fast_exp2(fmaf(R.sacc[CUR][ks >> 1][8 * (ks & 1) + 2 * u], slk[ks], -mref));
+      const float p1 = fast_exp2(fmaf(R.sacc[CUR][ks >> 1][8 * (ks & 1) + 2 * u + 1], slk[ks], -mref));
+      if constexpr (LSE) ts += p0 + p1;
+      w[u] = FP8 ? pack_bf16x2(p0 * svb[ks], p1 * svb[ks]) : pack_bf16x2(p0, p1);
+      rb = dot2(w[u], kBf16OnePair, rb);
+    }
+    tr = fmaf(rb, rsv[ks], tr);
+    R.pb[ks] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
 // One pipeline step.  CUR holds S^T(t) (already masked); the other set receives S^T(t+1) from
 // K buffer `kb`; P^T holds tile t-1 for the P.V over V buffer `vb` and is overwritten, 16-key
 // step by 16-key step after its last P.V use, with tile t.  The step is issued in a fixed
 // order, one slot per MFMA: slot i reads the operand of MFMA i + 2 from LDS, issues MFMA i
 // (first the P.V MFMAs, then the S MFMAs) and then a slice of the softmax of tile t, so that
-// every MFMA runs under VALU work and its operand has been in flight for two MFMAs.  The
-// softmax slices: the tile max and lazy max update over the first NMAX slots, then 16
-// pieces, each the p = exp2(s * scale - m) of 4 keys with their fp32 row sum and bf16 pairs,
-// the fourth piece of a 16-key step also swapping the pairs across the wave halves into the
-// new P^T step (a lane of half h holds keys 4h..4h+3 and 8+4h..8+4h+3 of the step as dwords
-// d0..d3; swapping d0<->d2 and d1<->d3 leaves it keys 8h..8h+7).  Returns in `need` whether
-// the running max moved, with the new max, the tile's fp32 row sum and the tile's sum of rounded
-// weights (v_dot2 of each bf16 pair against (1, 1); fp8: per key block, divided by its value scale).
-template <int D, int CUR, bool FP8>
+// every MFMA runs under VALU work and its operand has been in flight for two MFMAs.
+//
+// The softmax of tile t uses the running max m as it stands: p = exp2(s * scale - m), in 16
+// pieces of 4 keys (their bf16 pairs, the sum of the rounded weights as v_dot2 of each pair
+// against (1, 1), and with LSE the fp32 sum of p).  No tile maximum is taken; a tile whose
+// rounded weights sum past kPipeOverflow in some row (scores far above every earlier one) is
+// redone with its maximum after the step, which keeps p finite and exact.  S^T's accumulator
+// layout gives lane half h keys 4h..4h+3 and 8+4h..8+4h+3 of every 16-key step; those 8 p are the
+// lane's P^T operand as they stand, and the value tile is staged with the same key order.
+// FIRST (step 0, whose P.V is of the zeroed tile before the first): the slots carry no softmax
+// work; tile 0's softmax runs after them, with its own maximum.
+template <int D, int CUR, bool FP8, bool LSE, bool FIRST>
 __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __restrict__ kb,
                                           const uint16_t* __restrict__ vb, int n, int h, float sl,
-                                          const TileScales& tsc, bool& need, float& mnew, float& ts,
-                                          float& tr) {
+                                          const TileScales& tsc, float& ts, float& tr) {
   constexpr int NXT = 1 - CUR;
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
-  constexpr int NPV = 4 * DT;        // P.V MFMAs (16-key step ks, d tile d: index DT*ks + d)
+  constexpr int NPV = 4 * DT;           // P.V MFMAs (16-key step ks, d tile d: index DT*ks + d)
   constexpr int NM = NPV + 2 * KSTEPS;  // then S MFMAs (K-step s, key half mt: 2*s + mt)
-  constexpr int PF = 2;              // operand reads in flight
-  constexpr int NMAX = NM / 8;       // slots of the tile max
-  constexpr int SPAN = NM - NMAX - 2;  // slots over which the 16 exp pieces are spread
+  constexpr int PF = 2;                 // operand reads in flight
+  constexpr int SPAN = NM - 2;          // slots over which the 16 exp pieces are spread
   using S = TileSmem<D>;
   const floatx16 zero = {};
 
@@ -1348,24 +1400,21 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
     return *reinterpret_cast<const bf16x8*>(kb + (32 * mt + n) * S::KP + 16 * s + 8 * h);
   };
 
-  // Score scale and p multiplier of key block b of the tile (block b = 16-key step b).
-  float slk[4], svb[4];
+  // Score scale, p multiplier and rounded-weight divisor of key block b (16-key step b).
+  float slk[4], svb[4], rsv[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     slk[b] = FP8 ? sl * tsc.k[b] : sl;
     svb[b] = FP8 ? tsc.v[b] : 1.f;
+    rsv[b] = FP8 ? __builtin_amdgcn_rcpf(tsc.v[b]) : 1.f;
   }
   bf16x8 op[PF];
 #pragma unroll
   for (int i = 0; i < PF; ++i) op[i] = operand(i);
-  float mx = -INFINITY, mref = 0.f;
-  float mb[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // fp8: per-block raw maxima
+  const float mref = R.m;
   uint32_t pk[4][4];
-  float trb[4] = {0.f, 0.f, 0.f, 0.f};  // fp8: rounded-weight sums per key block
+  float trb[4] = {0.f, 0.f, 0.f, 0.f};  // rounded-weight sums per key block
   ts = 0.f;
-  tr = 0.f;
-  need = false;
-  mnew = R.m;
 #pragma unroll
   for (int i = 0; i < NM; ++i) {
     const bf16x8 a = op[i % PF];
@@ -1378,84 +1427,33 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
       R.sacc[NXT][mt] =
           __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, R.qb[s], s == 0 ? zero : R.sacc[NXT][mt], 0, 0, 0);
     }
-    // Softmax slices of this slot.
-    if (i < NMAX) {
-      constexpr int PER = 32 / NMAX;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int x = i * PER + e;  // element x of the tile's scores lies in key block x >> 3
-        if constexpr (FP8)
-          mb[x >> 3] = fmaxf(mb[x >> 3], R.sacc[CUR][x >> 4][x & 15]);
-        else
-          mx = fmaxf(mx, R.sacc[CUR][x >> 4][x & 15]);
-      }
-      if (i == NMAX - 1) {
-        // Lazy max: raised only past kLazy, for every lane of the wave at once, so that the
-        // output rescale stays rare.
-        if constexpr (FP8) {
-#pragma unroll
-          for (int b = 0; b < 4; ++b) mx = fmaxf(mx, mb[b] * slk[b]);
-          mx = fmaxf(mx, other_half(mx, h));
-        } else {
-          mx = fmaxf(mx, other_half(mx, h)) * sl;
-        }
-        need = __ballot(mx > R.m + kLazy) != 0;
-        mnew = need ? fmaxf(R.m, mx) : R.m;
-        mref = (mnew == -INFINITY) ? 0.f : mnew;
-      }
-    }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      if (NMAX + (q * SPAN) / 16 != i) continue;
+      if (FIRST || (q * SPAN) / 16 != i) continue;
       const int ks = q >> 2, u = q & 3, mt = ks >> 1, e0 = 8 * (ks & 1) + 2 * u;
       const float p0 = fast_exp2(fmaf(R.sacc[CUR][mt][e0], slk[ks], -mref));
       const float p1 = fast_exp2(fmaf(R.sacc[CUR][mt][e0 + 1], slk[ks], -mref));
-      ts += p0;
-      ts += p1;
+      if constexpr (LSE) ts += p0 + p1;
       pk[ks][u] = FP8 ? pack_bf16x2(p0 * svb[ks], p1 * svb[ks]) : pack_bf16x2(p0, p1);
-      if constexpr (FP8)
-        trb[ks] = dot2(pk[ks][u], kBf16OnePair, trb[ks]);
-      else
-        tr = dot2(pk[ks][u], kBf16OnePair, tr);
-      if (u == 3) {
-        // P^T(t-1) of this 16-key step had its last use in slot DT*ks + DT - 1 < i.
-        const auto s02 = __builtin_amdgcn_permlane32_swap(pk[ks][0], pk[ks][2], false, false);
-        const auto s13 = __builtin_amdgcn_permlane32_swap(pk[ks][1], pk[ks][3], false, false);
-        u32x4 w;
-        w[0] = s02[0];
-        w[1] = s13[0];
-        w[2] = s02[1];
-        w[3] = s13[1];
-        R.pb[ks] = __builtin_bit_cast(bf16x8, w);
-      }
+      trb[ks] = dot2(pk[ks][u], kBf16OnePair, trb[ks]);
+      // P^T(t-1) of this 16-key step had its last use in slot DT*ks + DT - 1 < i.
+      if (u == 3) R.pb[ks] = __builtin_bit_cast(bf16x8, u32x4{pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]});
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (FP8) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) tr = fmaf(trb[b], __builtin_amdgcn_rcpf(tsc.v[b]), tr);
+  if constexpr (FIRST) {
+    pipe_softmax_with_max<D, CUR, FP8, LSE>(R, h, slk, svb, rsv, ts, tr);
+    return;
   }
+  tr = 0.f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) tr = FP8 ? fmaf(trb[b], rsv[b], tr) : tr + trb[b];
+  // A row whose tile outgrew the running max (or whose max was -inf): redo the tile with its max.
+  if (__builtin_expect(__ballot(!(tr <= kPipeOverflow)) != 0, 0))
+    pipe_softmax_with_max<D, CUR, FP8, LSE>(R, h, slk, svb, rsv, ts, tr);
 }
 
-// After a step: apply a moved running max to the output (which now holds tiles up to t-1) and
-// the row sums, then add the tile's row sums.
-template <int D>
-__device__ __forceinline__ void pipe_commit(PipeRegs<D>& R, bool need, float mnew, float ts, float tr) {
-  if (need) {
-    const float alpha = fast_exp2(R.m - mnew);
-    R.lsum *= alpha;
-    R.lr *= alpha;
-#pragma unroll
-    for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) R.oacc[d][e] *= alpha;
-  }
-  R.m = mnew;
-  R.lsum += ts;
-  R.lr += tr;
-}
-
-template <int D, int G, bool CAUSAL, bool FP8>
+template <int D, int G, bool CAUSAL, bool FP8, bool LSE>
 __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __restrict__ k_cache,
                           const void* __restrict__ v_cache, const float* __restrict__ k_scale,
                           const float* __restrict__ v_scale, int Hkv, int g,
@@ -1507,9 +1505,11 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
   if (ntiles > 0) {
     // Staging: waves 0-3 copy the K rows (key KPI*i + lane/LPT, chunk lane % LPT) and waves 4-7
     // the V^T chunks (chunk lane + 64i of the dim-major block tile is dim (lane >> 1) + 32i,
-    // tokens 8*(lane & 1)..+7) of cache block (wave & 3) of a tile.  Loads are unconditional
-    // (past the end they re-read the last block); values of keys past the end are zeroed at
-    // store time.  The staging code is written per job (J = 1 job per wave).
+    // tokens 8*(lane & 1)..+7) of cache block (wave & 3) of a tile.  Within each block's 16 keys
+    // the V^T row holds the 4-key groups in the order 0, 2, 1, 3 (the key order of a lane's P^T
+    // operand), so a chunk is stored as two 8-byte halves.  Loads are unconditional (past the
+    // end they re-read the last block); values of keys past the end are zeroed at store time.
+    // The staging code is written per job (J = 1 job per wave).
     constexpr int J = 1;
     const int sblk = wave & 3;
     const int sc = lane % LPT;
@@ -1555,7 +1555,7 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       jv[j] = wave >= 4;
       jbase[j] = reinterpret_cast<const C8*>(jv[j] ? v_cache : k_cache) + (int64_t)g * tile_stride;
       // Chunk lane + 64i of the block tile: ((KPI*i + sr)*CH + sc) is that same index for K rows.
-      soff[j] = jv[j] ? PS::V_OFF + (lane >> 1) * S::VP + kBlockSize * sblk + 8 * (lane & 1)
+      soff[j] = jv[j] ? PS::V_OFF + (lane >> 1) * S::VP + kBlockSize * sblk + 4 * (lane & 1)
                       : (kBlockSize * sblk + sr) * S::KP + sc * 8;
       sstep[j] = jv[j] ? 32 * S::VP : KPI * S::KP;
     }
@@ -1581,17 +1581,25 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       u32x4 r[NI];
 #pragma unroll
       for (int i = 0; i < NI; ++i) r[i] = widen8(rc[i]);
-      if (nvalid >= kBlockSize) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + soff[j] + i * sstep[j]) = r[i];
-      } else {
+      if (nvalid < kBlockSize) {
         const int t0 = 8 * (lane & 1);
         u32x4 msk;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           msk[u] = (t0 + 2 * u < nvalid ? 0x0000ffffu : 0u) | (t0 + 2 * u + 1 < nvalid ? 0xffff0000u : 0u);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + soff[j] + i * sstep[j]) = r[i] & msk;
+        for (int i = 0; i < NI; ++i) r[i] &= msk;
+      }
+      if (jv[j]) {
+        // Tokens 8 th .. 8 th + 3 go to group slot th, tokens 8 th + 4 .. + 7 to slot 2 + th.
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          *reinterpret_cast<u32x2*>(dst + soff[j] + i * sstep[j]) = u32x2{r[i][0], r[i][1]};
+          *reinterpret_cast<u32x2*>(dst + soff[j] + i * sstep[j] + 8) = u32x2{r[i][2], r[i][3]};
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + soff[j] + i * sstep[j]) = r[i];
       }
     };
 
@@ -1636,8 +1644,10 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
     // loaded tiles, so the whole step covers the load.  A tile staged in step t is first read in
     // step t+2, and its buffer was last read in step t-2, so one barrier before every even step
     // orders both (the steps alternate the S^T sets, so even steps are the CUR == 0 ones).
-    auto step = [&](auto cur, int t) __attribute__((always_inline)) {
+    // Step 0 takes tile 0's softmax with its maximum (FIRST).
+    auto step = [&](auto cur, auto first, int t) __attribute__((always_inline)) {
       constexpr int CUR = decltype(cur)::value;
+      constexpr bool FIRST = decltype(first)::value;
       if constexpr (CUR == 0) __syncthreads();
 #pragma unroll
       for (int j = 0; j < J; ++j) nv[j] = load(j, jv[j] ? t + 1 : t + 3, st[j], ksv[j], vsv[j]);
@@ -1646,25 +1656,30 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       const int k0 = kv_begin + t * kKvTile;
       if ((k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > pos0))
         pipe_mask<D, CUR, CAUSAL>(R, h, k0, kv_end);
-      bool need;
-      float mnew, ts, tr;
+      float ts, tr;
       // A wave in its matrix/softmax block issues ahead of the other wave on its SIMD while that
       // one runs its commit, LDS stores and barrier wait (1-3 % faster than equal priority).
       __builtin_amdgcn_s_setprio(1);
-      pipe_step<D, CUR, FP8>(R, kbuf0 + ((t + 1) & (NB - 1)) * S::K_ELEMS,
-                             vbuf0 + ((t - 1) & (NB - 1)) * S::V_ELEMS, n, h, sl, tsc, need, mnew, ts, tr);
+      pipe_step<D, CUR, FP8, LSE, FIRST>(R, kbuf0 + ((t + 1) & (NB - 1)) * S::K_ELEMS,
+                                         vbuf0 + ((t - 1) & (NB - 1)) * S::V_ELEMS, n, h, sl, tsc, ts, tr);
       __builtin_amdgcn_s_setprio(0);
-      pipe_commit<D>(R, need, mnew, ts, tr);
+      if constexpr (LSE) R.lsum += ts;
+      R.lr += tr;
 #pragma unroll
       for (int j = 0; j < J; ++j)
         store(j, (jv[j] ? t + 1 : t + 3) & (NB - 1), st[j], nv[j], ksv[j], vsv[j], (t + 3) % PS::SC_SLOTS);
     };
-    int t = 0;
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using First = std::true_type;
+    using Next = std::false_type;
+    step(C0(), First(), 0);
+    int t = 1;
     for (; t + 1 < ntiles; t += 2) {
-      step(std::integral_constant<int, 0>(), t);
-      step(std::integral_constant<int, 1>(), t + 1);
+      step(C1(), Next(), t);
+      step(C0(), Next(), t + 1);
     }
-    if (t < ntiles) step(std::integral_constant<int, 0>(), t);
+    if (t < ntiles) step(C1(), Next(), t);
     // The last P.V (tile ntiles - 1, stored by the last step).
     __syncthreads();
     const uint16_t* vlast = vbuf0 + ((ntiles - 1) & (NB - 1)) * S::V_ELEMS;
@@ -1694,7 +1709,7 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       }
     }
   }
-  if (lse_out && h == 0) lse_out[orow] = (lsum > 0.f) ? (R.m + __log2f(lsum)) * kLn2 : -INFINITY;
+  if (LSE && lse_out && h == 0) lse_out[orow] = (lsum > 0.f) ? (R.m + __log2f(lsum)) * kLn2 : -INFINITY;
 }
 
 // DECODE_ONLY instantiations carry no MFMA path, so they need far fewer registers and run
@@ -1764,8 +1779,9 @@ void decode_graph_kernel(VarlenArgs a, int32_t splits, int32_t split_keys, int32
   decode_item<D, G, 4, FP8, FP8 ? 2 : 1>(a, it, g, smem);
 }
 
-// Wide-tile kernels: 256-row pipelined tiles on 8 waves (two per SIMD).
-template <int D, int G, bool FP8>
+// Wide-tile kernels: 256-row pipelined tiles on 8 waves (two per SIMD).  LSE: the call asks for
+// the LSE (the fp32 row sums are only kept then).
+template <int D, int G, bool FP8, bool LSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void prefill_wide_kernel(VarlenArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -1776,7 +1792,7 @@ void prefill_wide_kernel(VarlenArgs a) {
   const int ctx = a.context_lens[r];
   const int tok0 = a.query_start_loc[r] + it.q_begin;
   const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
-  pipe_tile<D, G, true, FP8>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
+  pipe_tile<D, G, true, FP8, LSE>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
                              g, bt, a.bt_shift, tok0, it.q_count, ctx + it.q_begin, it.kv_begin, it.kv_end, a.scale_log2,
                              a.out, a.out_f32, a.lse, smem);
 }
@@ -1801,7 +1817,7 @@ void cascade_kernel(CascadeArgs a) {
     out = a.part_o + (int64_t)seg * a.num_tokens * a.num_q_heads * D;
     lse = a.part_lse + (int64_t)seg * a.num_tokens * a.num_q_heads;
   }
-  pipe_tile<D, G, false, FP8>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
+  pipe_tile<D, G, false, FP8, true>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
                               g, a.prefix_bt, a.bt_shift, tok0, ntok, 0, kv_begin, kv_end, a.scale_log2, out, 1,
                               lse, smem);
 }
@@ -1886,7 +1902,7 @@ hipError_t launch_varlen_t(const VarlenArgs& a, int n_prefill, int n_decode, int
     } else if (tile_rows == kWideTileRows) {
       // Wide prefill tiles, then the decode items in a kernel of their own (the wide tile's
       // register budget allows two waves per SIMD, too few for the decode path).
-      auto kern = prefill_wide_kernel<D, G, kFp8>;
+      auto kern = a.lse ? prefill_wide_kernel<D, G, kFp8, true> : prefill_wide_kernel<D, G, kFp8, false>;
       hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_prefill * Hkv)), dim3(512),
                          (size_t)PipeSmem<D>::BYTES, stream, a);
       if (n_decode > 0) {
