@@ -177,7 +177,10 @@ int pkv_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_s
  * 128 or 256 packed (token, q head) rows (256 once the batch holds at least 2048 prefill
  * rows), orders them heaviest first, and enqueues a host-to-device copy of the list into
  * `workspace` on `stream`.  Fills *plan.  The workspace must stay untouched until the
- * attention call that uses the plan has run. */
+ * attention call that uses the plan has run.  The copy goes through a ring of 32 pinned host
+ * buffers of 256 KB per device and calling thread, allocated on the thread's first plan on the
+ * device (a plan of more than 8192 work items grows its buffer once); the call waits only when
+ * 32 earlier uploads of the thread have not yet been read by the device. */
 int pkv_plan_varlen(pkv_varlen_plan* plan, void* workspace, size_t workspace_bytes,
                     const int32_t* h_query_start_loc, const int32_t* h_context_lens,
                     const int32_t* h_seq_lens, int32_t num_seqs, int32_t num_tokens,

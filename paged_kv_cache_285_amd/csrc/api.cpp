@@ -307,8 +307,12 @@ void fill_plan_struct(pkv_varlen_plan* out, const Plan& P, int32_t num_seqs, int
   out->workspace_used = (int64_t)L.total;
 }
 
-// Pinned host staging for the plan upload: a small ring per device and thread, so a buffer is
-// only refilled after the copy that last read it has completed.
+// Pinned host staging for the plan upload: a ring of kStagingSlots buffers per device and thread,
+// so a buffer is only refilled after the copy that last read it has completed.  The whole ring
+// (kStagingSlots x kStagingSlotBytes of pinned memory) is allocated on the first upload of a
+// thread on a device; after that an upload allocates nothing unless a plan is larger than a slot
+// (more than kStagingSlotBytes / 32 work items), when that slot grows once.  An upload waits
+// only when the host has enqueued kStagingSlots uploads that the device has not yet read.
 struct StagingSlot {
   void* host = nullptr;
   size_t cap = 0;
@@ -316,11 +320,23 @@ struct StagingSlot {
   bool pending = false;
 };
 constexpr int kStagingSlots = 32;
+constexpr size_t kStagingSlotBytes = size_t(256) << 10;
 struct StagingRing {
   StagingSlot slot[kStagingSlots];
   int next = 0;
+  bool ready = false;
 };
 thread_local std::unordered_map<int, StagingRing> g_rings;
+
+int grow_slot(StagingSlot& sl, size_t bytes) {
+  if (sl.host) (void)hipHostFree(sl.host);
+  sl.host = nullptr;
+  sl.cap = 0;
+  hipError_t e = hipHostMalloc(&sl.host, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
+  sl.cap = bytes;
+  return PKV_OK;
+}
 
 int stage_and_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return PKV_OK;
@@ -328,29 +344,24 @@ int stage_and_copy(void* dst, const void* src, size_t bytes, hipStream_t stream)
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   StagingRing& ring = g_rings[dev];
+  if (!ring.ready) {
+    for (StagingSlot& s0 : ring.slot) {
+      if (int rc = grow_slot(s0, kStagingSlotBytes)) return rc;
+      e = hipEventCreateWithFlags(&s0.ev, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate(staging)");
+    }
+    ring.ready = true;
+  }
   StagingSlot& sl = ring.slot[ring.next];
   ring.next = (ring.next + 1) % kStagingSlots;
   if (sl.pending) {
-    // The copy that last read this buffer was enqueued kStagingSlots uploads ago; poll rather
-    // than sleep so a host running ahead of the device resumes as soon as it completes.
-    while ((e = hipEventQuery(sl.ev)) == hipErrorNotReady) {
-    }
-    if (e != hipSuccess) return hip_fail(e, "hipEventQuery(staging)");
+    // The copy that last read this buffer was enqueued kStagingSlots uploads ago.
+    e = hipEventSynchronize(sl.ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
     sl.pending = false;
   }
-  if (!sl.ev) {
-    e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreate(staging)");
-  }
-  if (sl.cap < bytes) {
-    if (sl.host) (void)hipHostFree(sl.host);
-    sl.host = nullptr;
-    sl.cap = 0;
-    const size_t cap = std::max<size_t>(bytes, 64 << 10);
-    e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
-    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
-    sl.cap = cap;
-  }
+  if (sl.cap < bytes)
+    if (int rc = grow_slot(sl, bytes)) return rc;
   std::memcpy(sl.host, src, bytes);
   e = hipMemcpyAsync(dst, sl.host, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");

@@ -1274,8 +1274,10 @@ struct PipeRegs {
   floatx16 oacc[DT];    // O^T accumulators
   floatx16 sacc[2][2];  // two S^T sets (tile t and t+1), each two 32-key halves
   bf16x8 pb[4];         // P^T (four 16-key steps): tile t-1 until its P.V step, then tile t
-  float m, lsum;        // running max (log2 units of scaled scores) and fp32 row sum (LSE)
-  float lr;             // sum of the bf16-rounded weights P.V applied (normalises the output)
+  float m;             // running max (log2 units of scaled scores)
+  float lr;            // sum of the bf16-rounded weights P.V applied: normalises the output and
+                       // gives the LSE (within ln(1 + 2^-9) of the fp32 sum's, and consistent
+                       // with the output when states are merged)
   int qpos;             // position of the lane's query row
 };
 
@@ -1317,10 +1319,9 @@ constexpr float kPipeOverflow = 4294967296.0f;
 // Softmax of S^T set CUR into P^T and the tile's row sums, all at once (the first tile, and a tile
 // redone after an overflow): the running max becomes max(m, the tile's max), with the output and
 // row sums rescaled when m was finite (they hold the tiles before this one).
-template <int D, int CUR, bool FP8, bool LSE>
+template <int D, int CUR, bool FP8>
 __device__ __forceinline__ void pipe_softmax_with_max(PipeRegs<D>& R, int h, const float (&slk)[4],
-                                                      const float (&svb)[4], const float (&rsv)[4], float& ts,
-                                                      float& tr) {
+                                                      const float (&svb)[4], const float (&rsv)[4], float& tr) {
   float mx = -INFINITY;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -1333,7 +1334,6 @@ __device__ __forceinline__ void pipe_softmax_with_max(PipeRegs<D>& R, int h, con
   const float mnew = fmaxf(R.m, mx);
   if (R.m != -INFINITY) {
     const float alpha = fast_exp2(R.m - mnew);
-    R.lsum *= alpha;
     R.lr *= alpha;
 #pragma unroll
     for (int d = 0; d < D / 32; ++d)
@@ -1342,7 +1342,6 @@ __device__ __forceinline__ void pipe_softmax_with_max(PipeRegs<D>& R, int h, con
   }
   R.m = mnew;
   const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-  ts = 0.f;
   tr = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -1352,7 +1351,6 @@ __device__ __forceinline__ void pipe_softmax_with_max(PipeRegs<D>& R, int h, con
     for (int u = 0; u < 4; ++u) {
       const float p0 = fast_exp2(fmaf(R.sacc[CUR][ks >> 1][8 * (ks & 1) + 2 * u], slk[ks], -mref));
       const float p1 = fast_exp2(fmaf(R.sacc[CUR][ks >> 1][8 * (ks & 1) + 2 * u + 1], slk[ks], -mref));
-      if constexpr (LSE) ts += p0 + p1;
       w[u] = FP8 ? pack_bf16x2(p0 * svb[ks], p1 * svb[ks]) : pack_bf16x2(p0, p1);
       rb = dot2(w[u], kBf16OnePair, rb);
     }
@@ -1377,10 +1375,12 @@ __device__ __forceinline__ void pipe_softmax_with_max(PipeRegs<D>& R, int h, con
 // lane's P^T operand as they stand, and the value tile is staged with the same key order.
 // FIRST (step 0, whose P.V is of the zeroed tile before the first): the slots carry no softmax
 // work; tile 0's softmax runs after them, with its own maximum.
-template <int D, int CUR, bool FP8, bool LSE, bool FIRST>
+// Stage(i) runs after MFMA slot i: the staging of a later tile (LDS stores of the tile loaded in
+// the previous step, then the loads of the next one) spread over the slots.
+template <int D, int CUR, bool FP8, bool FIRST, typename Stage>
 __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __restrict__ kb,
                                           const uint16_t* __restrict__ vb, int n, int h, float sl,
-                                          const TileScales& tsc, float& ts, float& tr) {
+                                          const TileScales& tsc, float& tr, Stage&& stage) {
   constexpr int NXT = 1 - CUR;
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
@@ -1414,7 +1414,6 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
   const float mref = R.m;
   uint32_t pk[4][4];
   float trb[4] = {0.f, 0.f, 0.f, 0.f};  // rounded-weight sums per key block
-  ts = 0.f;
 #pragma unroll
   for (int i = 0; i < NM; ++i) {
     const bf16x8 a = op[i % PF];
@@ -1433,16 +1432,16 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
       const int ks = q >> 2, u = q & 3, mt = ks >> 1, e0 = 8 * (ks & 1) + 2 * u;
       const float p0 = fast_exp2(fmaf(R.sacc[CUR][mt][e0], slk[ks], -mref));
       const float p1 = fast_exp2(fmaf(R.sacc[CUR][mt][e0 + 1], slk[ks], -mref));
-      if constexpr (LSE) ts += p0 + p1;
       pk[ks][u] = FP8 ? pack_bf16x2(p0 * svb[ks], p1 * svb[ks]) : pack_bf16x2(p0, p1);
       trb[ks] = dot2(pk[ks][u], kBf16OnePair, trb[ks]);
       // P^T(t-1) of this 16-key step had its last use in slot DT*ks + DT - 1 < i.
       if (u == 3) R.pb[ks] = __builtin_bit_cast(bf16x8, u32x4{pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]});
     }
+    stage(i);
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (FIRST) {
-    pipe_softmax_with_max<D, CUR, FP8, LSE>(R, h, slk, svb, rsv, ts, tr);
+    pipe_softmax_with_max<D, CUR, FP8>(R, h, slk, svb, rsv, tr);
     return;
   }
   tr = 0.f;
@@ -1450,10 +1449,10 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
   for (int b = 0; b < 4; ++b) tr = FP8 ? fmaf(trb[b], rsv[b], tr) : tr + trb[b];
   // A row whose tile outgrew the running max (or whose max was -inf): redo the tile with its max.
   if (__builtin_expect(__ballot(!(tr <= kPipeOverflow)) != 0, 0))
-    pipe_softmax_with_max<D, CUR, FP8, LSE>(R, h, slk, svb, rsv, ts, tr);
+    pipe_softmax_with_max<D, CUR, FP8>(R, h, slk, svb, rsv, tr);
 }
 
-template <int D, int G, bool CAUSAL, bool FP8, bool LSE>
+template <int D, int G, bool CAUSAL, bool FP8>
 __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __restrict__ k_cache,
                           const void* __restrict__ v_cache, const float* __restrict__ k_scale,
                           const float* __restrict__ v_scale, int Hkv, int g,
@@ -1498,7 +1497,6 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
 #pragma unroll
     for (int e = 0; e < 16; ++e) R.oacc[d][e] = 0.f;
   R.m = -INFINITY;
-  R.lsum = 0.f;
   R.lr = 0.f;
 
   const int ntiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
@@ -1567,44 +1565,42 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       for (int i = 0; i < NI; ++i) r[i] = p[lane + 64 * i];
       return jv[j] ? kv_end - lb * kBlockSize : kBlockSize;
     };
-    // Stores a loaded tile into LDS buffer `buf`; a K job also stores its block's scales into
-    // scale slot `slot`.
-    auto store = [&](int j, int buf, const C8 (&rc)[NI], int nvalid, float ks, float vs, int slot)
+    // Stores chunk i of a loaded tile into LDS buffer `buf` (chunk 0 of a K job also stores the
+    // block's scales into scale slot `slot`).  Values of keys past the end are zeroed.
+    auto store_chunk = [&](int j, int i, int buf, const C8 (&rc)[NI], int nvalid, float ks, float vs, int slot)
         __attribute__((always_inline)) {
       uint16_t* dst = smem + buf * (jv[j] ? S::V_ELEMS : S::K_ELEMS);
       if constexpr (FP8) {
-        if (!jv[j] && lane == 0) {
+        if (i == 0 && !jv[j] && lane == 0) {
           scl[8 * slot + sblk] = ks;
           scl[8 * slot + 4 + sblk] = vs;
         }
       }
-      u32x4 r[NI];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) r[i] = widen8(rc[i]);
+      u32x4 r = widen8(rc[i]);
       if (nvalid < kBlockSize) {
         const int t0 = 8 * (lane & 1);
         u32x4 msk;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           msk[u] = (t0 + 2 * u < nvalid ? 0x0000ffffu : 0u) | (t0 + 2 * u + 1 < nvalid ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) r[i] &= msk;
+        r &= msk;
       }
       if (jv[j]) {
         // Tokens 8 th .. 8 th + 3 go to group slot th, tokens 8 th + 4 .. + 7 to slot 2 + th.
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          *reinterpret_cast<u32x2*>(dst + soff[j] + i * sstep[j]) = u32x2{r[i][0], r[i][1]};
-          *reinterpret_cast<u32x2*>(dst + soff[j] + i * sstep[j] + 8) = u32x2{r[i][2], r[i][3]};
-        }
+        *reinterpret_cast<u32x2*>(dst + soff[j] + i * sstep[j]) = u32x2{r[0], r[1]};
+        *reinterpret_cast<u32x2*>(dst + soff[j] + i * sstep[j] + 8) = u32x2{r[2], r[3]};
       } else {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + soff[j] + i * sstep[j]) = r[i];
+        *reinterpret_cast<u32x4*>(dst + soff[j] + i * sstep[j]) = r;
       }
     };
+    auto store = [&](int j, int buf, const C8 (&rc)[NI], int nvalid, float ks, float vs, int slot)
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) store_chunk(j, i, buf, rc, nvalid, ks, vs, slot);
+    };
 
-    // Prologue: K(0), K(1), K(2) and V(0) in LDS, V(-1) = 0 (no tile before the first),
-    // S^T(0) computed.
+    // Prologue: K(0), K(1), K(2) and V(0) in LDS and the loads of K(3) and V(1) in flight,
+    // V(-1) = 0 (no tile before the first), S^T(0) computed.
     C8 st[J][NI];
     int nv[J];
     float ksv[J], vsv[J];
@@ -1616,9 +1612,11 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
           nv[j] = load(j, x, st[j], ksv[j], vsv[j]);
           store(j, x, st[j], nv[j], ksv[j], vsv[j], x);
         }
+        nv[j] = load(j, 3, st[j], ksv[j], vsv[j]);
       } else {
         nv[j] = load(j, 0, st[j], ksv[j], vsv[j]);
         store(j, 0, st[j], nv[j], ksv[j], vsv[j], 0);
+        nv[j] = load(j, 1, st[j], ksv[j], vsv[j]);
       }
     }
     {
@@ -1640,34 +1638,37 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) R.pb[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 
-    // Step t: load K(t+3) / V(t+1), compute S^T(t+1), P.V(t-1) and softmax(t), then store the
-    // loaded tiles, so the whole step covers the load.  A tile staged in step t is first read in
-    // step t+2, and its buffer was last read in step t-2, so one barrier before every even step
-    // orders both (the steps alternate the S^T sets, so even steps are the CUR == 0 ones).
-    // Step 0 takes tile 0's softmax with its maximum (FIRST).
+    // Step t: compute S^T(t+1), P.V(t-1) and softmax(t); spread over its MFMA slots, store the
+    // tile loaded in step t-1 (K(t+3) / V(t+1)) into LDS and then load the next one (K(t+4) /
+    // V(t+2)), so each load has a whole step to arrive.  K(x) is stored in step x-3 and first
+    // read in step x-1; V(x) is stored in step x-1 and first read in step x+1; each buffer's
+    // previous tile was last read four steps before the store.  So one barrier before every even
+    // step orders every store against its reads (the steps alternate the S^T sets, so even steps
+    // are the CUR == 0 ones).  Step 0 takes tile 0's softmax with its maximum.
+    constexpr int ST0 = 2;  // first slot with a staging store
     auto step = [&](auto cur, auto first, int t) __attribute__((always_inline)) {
       constexpr int CUR = decltype(cur)::value;
       constexpr bool FIRST = decltype(first)::value;
       if constexpr (CUR == 0) __syncthreads();
-#pragma unroll
-      for (int j = 0; j < J; ++j) nv[j] = load(j, jv[j] ? t + 1 : t + 3, st[j], ksv[j], vsv[j]);
       TileScales tsc;
       if constexpr (FP8) tsc = read_scales(scl + 8 * (t % PS::SC_SLOTS));
       const int k0 = kv_begin + t * kKvTile;
       if ((k0 + kKvTile > kv_end) || (CAUSAL && k0 + kKvTile - 1 > pos0))
         pipe_mask<D, CUR, CAUSAL>(R, h, k0, kv_end);
-      float ts, tr;
+      const int sbuf = (jv[0] ? t + 1 : t + 3) & (NB - 1);
+      auto stage = [&](int i) __attribute__((always_inline)) {
+        if (i >= ST0 && i < ST0 + NI)
+          store_chunk(0, i - ST0, sbuf, st[0], nv[0], ksv[0], vsv[0], (t + 3) % PS::SC_SLOTS);
+        if (i == ST0 + NI) nv[0] = load(0, jv[0] ? t + 2 : t + 4, st[0], ksv[0], vsv[0]);
+      };
+      float tr;
       // A wave in its matrix/softmax block issues ahead of the other wave on its SIMD while that
-      // one runs its commit, LDS stores and barrier wait (1-3 % faster than equal priority).
+      // one waits at the barrier (equal priority measured 1-3 % slower).
       __builtin_amdgcn_s_setprio(1);
-      pipe_step<D, CUR, FP8, LSE, FIRST>(R, kbuf0 + ((t + 1) & (NB - 1)) * S::K_ELEMS,
-                                         vbuf0 + ((t - 1) & (NB - 1)) * S::V_ELEMS, n, h, sl, tsc, ts, tr);
+      pipe_step<D, CUR, FP8, FIRST>(R, kbuf0 + ((t + 1) & (NB - 1)) * S::K_ELEMS,
+                                    vbuf0 + ((t - 1) & (NB - 1)) * S::V_ELEMS, n, h, sl, tsc, tr, stage);
       __builtin_amdgcn_s_setprio(0);
-      if constexpr (LSE) R.lsum += ts;
       R.lr += tr;
-#pragma unroll
-      for (int j = 0; j < J; ++j)
-        store(j, (jv[j] ? t + 1 : t + 3) & (NB - 1), st[j], nv[j], ksv[j], vsv[j], (t + 3) % PS::SC_SLOTS);
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
@@ -1687,7 +1688,6 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
     for (int ks = 0; ks < 4; ++ks) pipe_pv_step<D>(R, vlast, n, h, ks);
   }
 
-  const float lsum = R.lsum + other_half(R.lsum, h);
   const float lr = R.lr + other_half(R.lr, h);
   if (!row_valid) return;
   const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
@@ -1709,7 +1709,7 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       }
     }
   }
-  if (LSE && lse_out && h == 0) lse_out[orow] = (lsum > 0.f) ? (R.m + __log2f(lsum)) * kLn2 : -INFINITY;
+  if (lse_out && h == 0) lse_out[orow] = (lr > 0.f) ? (R.m + __log2f(lr)) * kLn2 : -INFINITY;
 }
 
 // DECODE_ONLY instantiations carry no MFMA path, so they need far fewer registers and run
@@ -1779,9 +1779,8 @@ void decode_graph_kernel(VarlenArgs a, int32_t splits, int32_t split_keys, int32
   decode_item<D, G, 4, FP8, FP8 ? 2 : 1>(a, it, g, smem);
 }
 
-// Wide-tile kernels: 256-row pipelined tiles on 8 waves (two per SIMD).  LSE: the call asks for
-// the LSE (the fp32 row sums are only kept then).
-template <int D, int G, bool FP8, bool LSE>
+// Wide-tile kernels: 256-row pipelined tiles on 8 waves (two per SIMD).
+template <int D, int G, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void prefill_wide_kernel(VarlenArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -1792,7 +1791,7 @@ void prefill_wide_kernel(VarlenArgs a) {
   const int ctx = a.context_lens[r];
   const int tok0 = a.query_start_loc[r] + it.q_begin;
   const int32_t* bt = a.block_tables + (int64_t)r * a.bt_stride;
-  pipe_tile<D, G, true, FP8, LSE>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
+  pipe_tile<D, G, true, FP8>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
                              g, bt, a.bt_shift, tok0, it.q_count, ctx + it.q_begin, it.kv_begin, it.kv_end, a.scale_log2,
                              a.out, a.out_f32, a.lse, smem);
 }
@@ -1817,7 +1816,7 @@ void cascade_kernel(CascadeArgs a) {
     out = a.part_o + (int64_t)seg * a.num_tokens * a.num_q_heads * D;
     lse = a.part_lse + (int64_t)seg * a.num_tokens * a.num_q_heads;
   }
-  pipe_tile<D, G, false, FP8, true>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
+  pipe_tile<D, G, false, FP8>(a.q, a.num_q_heads, a.k_cache, a.v_cache, a.k_scale, a.v_scale, a.num_kv_heads,
                               g, a.prefix_bt, a.bt_shift, tok0, ntok, 0, kv_begin, kv_end, a.scale_log2, out, 1,
                               lse, smem);
 }
@@ -1902,7 +1901,7 @@ hipError_t launch_varlen_t(const VarlenArgs& a, int n_prefill, int n_decode, int
     } else if (tile_rows == kWideTileRows) {
       // Wide prefill tiles, then the decode items in a kernel of their own (the wide tile's
       // register budget allows two waves per SIMD, too few for the decode path).
-      auto kern = a.lse ? prefill_wide_kernel<D, G, kFp8, true> : prefill_wide_kernel<D, G, kFp8, false>;
+      auto kern = prefill_wide_kernel<D, G, kFp8>;
       hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_prefill * Hkv)), dim3(512),
                          (size_t)PipeSmem<D>::BYTES, stream, a);
       if (n_decode > 0) {

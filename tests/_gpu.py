@@ -3,6 +3,7 @@
 from __future__ import annotations
 
 import contextlib
+import math
 
 import numpy as np
 import torch
@@ -77,16 +78,16 @@ peaked_tolerance = value_range
 def rounding_bound(ref: np.ndarray, gpu: np.ndarray, bf16_out: bool) -> np.ndarray:
     """Per-element error the method's two prescribed roundings can produce.
 
-    * P to bf16 before P.V: each weight p_j carries a relative error up to 2^-9 (round to
-      nearest even, 8 significant bits); the output is normalised by the sum of those same
-      rounded weights, so it is a convex combination whose weights moved by
-      w_j (e_j - e_mean) / (1 + e_mean), and |o_gpu - o| <= 2^-8 (1 + 2^-8) max_j |v_j - o|
-      <= 2^-8 (1 + 2^-8) (max|v| + |o|).
+    * P to bf16 before P.V: each weight p_j carries a relative error e_j up to the bf16 unit
+      roundoff u = 2^-8 (8 significant bits, round to nearest even); the output is normalised by
+      the sum of those same rounded weights, so it is a convex combination whose weights moved
+      by w_j (e_j - e_mean) / (1 + e_mean), and |o_gpu - o| <= 2u / (1 - u) max_j |v_j - o|
+      <= 2^-7 (1 + 2^-7) (max|v| + |o|).
     * The output to bf16: half a bf16 spacing at its magnitude.
     Plus 1e-5 of fp32 accumulation."""
     b = np.full(ref.shape, 1e-5)
     if _VMAX is not None:
-        b = b + 2.0**-8 * (1.0 + 2.0**-8) * (_VMAX + np.abs(ref))
+        b = b + 2.0**-7 * (1.0 + 2.0**-7) * (_VMAX + np.abs(ref))
     if bf16_out:
         b = b + 0.5 * bf16_spacing(np.maximum(np.abs(ref), np.abs(gpu)))
     return b
@@ -119,11 +120,26 @@ def check_attention(gpu: np.ndarray, ref: np.ndarray, what: str, bf16_out: bool 
     return res
 
 
+# Largest LSE error the bf16 rounding of the weights can cause in a path whose LSE is taken from
+# the sum of its rounded weights (the pipelined 256-row tiles and the cascade prefix pass): each
+# weight carries a relative error up to the bf16 unit roundoff 2^-8 (8 significant bits, round to
+# nearest even), so the sum does too and ln of it moves by at most ln(1 + 2^-8); plus fp32
+# accumulation.
+LSE_ROUNDING = math.log1p(2.0**-8) + 2e-5
+
+
 def check_lse(gpu: np.ndarray, ref: np.ndarray, what: str) -> float:
+    """LSE max abs error <= LSE_ATOL; elements above it are accepted only within LSE_ROUNDING
+    (counted and printed)."""
     fin = np.isfinite(ref)
     assert np.array_equal(fin, np.isfinite(gpu)), f"{what}: LSE finiteness differs"
-    d = float(np.max(np.abs(gpu[fin] - ref[fin]))) if fin.any() else 0.0
-    assert d <= LSE_ATOL, f"{what}: LSE max abs err {d:.3g} > {LSE_ATOL}"
+    err = np.abs(gpu[fin] - ref[fin])
+    d = float(err.max()) if err.size else 0.0
+    above = int((err > LSE_ATOL).sum())
+    assert d <= LSE_ROUNDING, f"{what}: LSE max abs err {d:.3g} > {LSE_ROUNDING:.3g}"
+    if above:
+        print(f"[parity] {what}: LSE max abs {d:.3g}, {above} above {LSE_ATOL} within the weight rounding",
+              flush=True)
     return d
 
 
