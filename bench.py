@@ -638,6 +638,12 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed decode step")
     ap.add_argument("--no-mfma", action="store_true", help="skip the MFMA-bound cascade prefix and long prefill")
     ap.add_argument(
+        "--only",
+        choices=["decode", "fp8_decode", "spec_verify", "mfma"],
+        help="run just one measured section (e.g. under a profiler) and print its JSON",
+    )
+    ap.add_argument("--reps", type=int, default=20, help="timed repetitions per section")
+    ap.add_argument(
         "--copy-calibration",
         type=int,
         default=0,
@@ -667,6 +673,17 @@ def main():
 
     import paged_kv_cache_285_amd as P
     import workloads as W
+
+    if args.only:
+        sections = {
+            "decode": lambda: decode_hbm(torch, P, reps=args.reps),
+            "fp8_decode": lambda: fp8_decode_hbm(torch, P, reps=args.reps),
+            "spec_verify": lambda: spec_verify_hbm(torch, P, reps=args.reps),
+            "mfma": lambda: mfma_paths(torch, P, reps=args.reps),
+        }
+        log(f"bench: section {args.only} only, {args.reps} reps")
+        print(json.dumps({"only": args.only, args.only: sections[args.only]()}), flush=True)
+        return
 
     log("bench: building mixed_llama8b workload (seed 0)")
     wl = W.mixed_llama8b(seed=0)

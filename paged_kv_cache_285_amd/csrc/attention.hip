@@ -1413,7 +1413,9 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
   for (int i = 0; i < PF; ++i) op[i] = operand(i);
   const float mref = R.m;
   uint32_t pk[4][4];
-  float trb[4] = {0.f, 0.f, 0.f, 0.f};  // rounded-weight sums per key block
+  // Rounded-weight sums: per key block over fp8 pools (each block divides by its value scale),
+  // one sum over bf16 pools.
+  float trb[FP8 ? 4 : 1] = {};
 #pragma unroll
   for (int i = 0; i < NM; ++i) {
     const bf16x8 a = op[i % PF];
@@ -1433,7 +1435,7 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
       const float p0 = fast_exp2(fmaf(R.sacc[CUR][mt][e0], slk[ks], -mref));
       const float p1 = fast_exp2(fmaf(R.sacc[CUR][mt][e0 + 1], slk[ks], -mref));
       pk[ks][u] = FP8 ? pack_bf16x2(p0 * svb[ks], p1 * svb[ks]) : pack_bf16x2(p0, p1);
-      trb[ks] = dot2(pk[ks][u], kBf16OnePair, trb[ks]);
+      trb[FP8 ? ks : 0] = dot2(pk[ks][u], kBf16OnePair, trb[FP8 ? ks : 0]);
       // P^T(t-1) of this 16-key step had its last use in slot DT*ks + DT - 1 < i.
       if (u == 3) R.pb[ks] = __builtin_bit_cast(bf16x8, u32x4{pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]});
     }
@@ -1444,9 +1446,13 @@ __device__ __forceinline__ void pipe_step(PipeRegs<D>& R, const uint16_t* __rest
     pipe_softmax_with_max<D, CUR, FP8>(R, h, slk, svb, rsv, tr);
     return;
   }
-  tr = 0.f;
+  if constexpr (FP8) {
+    tr = 0.f;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) tr = FP8 ? fmaf(trb[b], rsv[b], tr) : tr + trb[b];
+    for (int b = 0; b < 4; ++b) tr = fmaf(trb[b], rsv[b], tr);
+  } else {
+    tr = trb[0];
+  }
   // A row whose tile outgrew the running max (or whose max was -inf): redo the tile with its max.
   if (__builtin_expect(__ballot(!(tr <= kPipeOverflow)) != 0, 0))
     pipe_softmax_with_max<D, CUR, FP8>(R, h, slk, svb, rsv, tr);
@@ -1578,11 +1584,15 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
       }
       u32x4 r = widen8(rc[i]);
       if (nvalid < kBlockSize) {
+        // Only the last tile takes this branch; the empty asm keeps the compiler from computing
+        // the mask (8 compares) ahead of the branch on every step.
+        int nv = nvalid;
+        asm volatile("" : "+s"(nv));
         const int t0 = 8 * (lane & 1);
         u32x4 msk;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          msk[u] = (t0 + 2 * u < nvalid ? 0x0000ffffu : 0u) | (t0 + 2 * u + 1 < nvalid ? 0xffff0000u : 0u);
+          msk[u] = (t0 + 2 * u < nv ? 0x0000ffffu : 0u) | (t0 + 2 * u + 1 < nv ? 0xffff0000u : 0u);
         r &= msk;
       }
       if (jv[j]) {
