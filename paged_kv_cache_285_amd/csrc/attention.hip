@@ -637,6 +637,13 @@ struct ShortSmem {
   static constexpr int BYTES = (COLS * DP + 3 * NW * COLS) * 4;
 };
 
+// Waves of a short item's workgroup: one workgroup fills a CU at two waves per SIMD, so the
+// items (longest first) are taken by CUs as they free up.
+#ifndef PKV_SHORT_WAVES
+#define PKV_SHORT_WAVES 8
+#endif
+constexpr int kShortWaves = PKV_SHORT_WAVES;
+
 // bf16 pair (1, 1): v_dot2 against it sums a packed pair of bf16 weights exactly in fp32.
 constexpr uint32_t kBf16OnePair = 0x3f803f80u;
 
@@ -1755,12 +1762,12 @@ void varlen_kernel(VarlenArgs a) {
 // two-column-group MFMA path needs a register budget of two waves per SIMD, which the decode
 // kernels must not inherit.
 template <int D, int G, bool FP8>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kShortWaves, 64 * kShortWaves), amdgpu_waves_per_eu(2, 2)))
 void short_kernel(VarlenArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int x = blockIdx.x;
   const int g = x % a.num_kv_heads;
-  short_item<D, G, 4, FP8>(a, a.items[x / a.num_kv_heads], g, smem);
+  short_item<D, G, kShortWaves, FP8>(a, a.items[x / a.num_kv_heads], g, smem);
 }
 
 // Decode batch with a device-side work split, for graph capture: the grid depends only on
@@ -1933,8 +1940,8 @@ hipError_t launch_varlen_t(const VarlenArgs& a, int n_prefill, int n_decode, int
     VarlenArgs b = a;
     b.items = a.items + n_prefill + n_decode;
     b.num_items = n_short;
-    const size_t smem = (size_t)ShortSmem<D, 4>::BYTES;
-    hipLaunchKernelGGL((short_kernel<D, G, kFp8>), dim3((unsigned)((int64_t)n_short * Hkv)), dim3(256), smem,
+    const size_t smem = (size_t)ShortSmem<D, kShortWaves>::BYTES;
+    hipLaunchKernelGGL((short_kernel<D, G, kFp8>), dim3((unsigned)((int64_t)n_short * Hkv)), dim3(64 * kShortWaves), smem,
                        stream, b);
   }
   return hipGetLastError();
