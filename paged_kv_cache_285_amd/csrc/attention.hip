@@ -1819,9 +1819,11 @@ template <int D, int G, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void prefill_wide_kernel(VarlenArgs a) {
   extern __shared__ __align__(16) char smem[];
-  int item, g;
-  xcd_item(a.num_kv_heads, item, g);
-  const WorkItem it = a.items[item];
+  // Item-major order here: the tiles of one request read the same keys per kv head, and with
+  // 8 kv heads each XCD then holds one head's tiles, whose key and value reads its L2 shares.
+  const int x = blockIdx.x;
+  const int g = x % a.num_kv_heads;
+  const WorkItem it = a.items[x / a.num_kv_heads];
   const int r = it.seq;
   const int ctx = a.context_lens[r];
   const int tok0 = a.query_start_loc[r] + it.q_begin;
