@@ -352,15 +352,15 @@ def _fp8_cascade_check(wl, rows=None):
     say(f"    fp8 cascade merged {r}")
 
 
-def test_fp8_decode_full_size_sampled():
-    """The full decode-only batch (256 rows, context 1024..8192) over fp8 pools, sampled rows."""
-    say("fp8 decode_only full size, sampled rows")
-    run_and_check_fp8(W.decode_only(seed=0), rows_per_step=48, seed=0, check_pools=False)
+def test_fp8_decode_full_size_every_row():
+    """The full decode-only batch (256 rows, context 1024..8192) over fp8 pools, every row."""
+    say("fp8 decode_only full size, every row")
+    run_and_check_fp8(W.decode_only(seed=0), seed=0, check_pools=False)
 
 
-def test_fp8_mixed_full_size_sampled():
-    say("fp8 mixed batch full size (64 decode rows, ctx 128..4096), sampled rows")
-    run_and_check_fp8(W.mixed_llama8b(seed=0), rows_per_step=64, seed=0, check_pools=False)
+def test_fp8_mixed_full_size_every_row():
+    say("fp8 mixed batch full size (64 decode rows, ctx 128..4096), every row")
+    run_and_check_fp8(W.mixed_llama8b(seed=0), seed=0, check_pools=False)
 
 
 @pytest.mark.parametrize("case", ["mixed", "decode"])
