@@ -639,7 +639,7 @@ def main():
     ap.add_argument("--no-mfma", action="store_true", help="skip the MFMA-bound cascade prefix and long prefill")
     ap.add_argument(
         "--only",
-        choices=["decode", "fp8_decode", "spec_verify", "mfma"],
+        choices=["decode", "fp8_decode", "spec_verify", "mfma", "graph"],
         help="run just one measured section (e.g. under a profiler) and print its JSON",
     )
     ap.add_argument("--reps", type=int, default=20, help="timed repetitions per section")
@@ -680,6 +680,7 @@ def main():
             "fp8_decode": lambda: fp8_decode_hbm(torch, P, reps=args.reps),
             "spec_verify": lambda: spec_verify_hbm(torch, P, reps=args.reps),
             "mfma": lambda: mfma_paths(torch, P, reps=args.reps),
+            "graph": lambda: decode_graph_step(torch, P, reps=args.reps),
         }
         log(f"bench: section {args.only} only, {args.reps} reps")
         print(json.dumps({"only": args.only, args.only: sections[args.only]()}), flush=True)

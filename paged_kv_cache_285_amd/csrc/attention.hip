@@ -1729,24 +1729,6 @@ __device__ void pipe_tile(const uint16_t* __restrict__ q, int Hq, const void* __
   if (lse_out && h == 0) lse_out[orow] = (lr > 0.f) ? (R.m + __log2f(lr)) * kLn2 : -INFINITY;
 }
 
-// Workgroup -> (work item, kv head) for a grid of n_items x Hkv workgroups.  Workgroups go to
-// the 8 XCDs round robin, so with the plain item-major order the kv heads of one item land on
-// 8 different XCDs and each XCD's L2 fetches the block-table and fp8-scale lines they share.
-// Here groups of 8 items take 8 * Hkv consecutive workgroups, workgroup 8 * Hkv * grp + 8 * g + i
-// running kv head g of item 8 * grp + i: every kv head of an item runs on one XCD (a last group
-// of fewer than 8 items is laid out the same way over its size).  Items keep their order in
-// groups of 8, so the heaviest-first plan order still holds.
-__device__ __forceinline__ void xcd_item(int Hkv, int& item, int& g) {
-  const int x = blockIdx.x;
-  const int n_items = (int)gridDim.x / Hkv;
-  const int per = 8 * Hkv;
-  const int grp = x / per;
-  const int r = x - grp * per;
-  const int gs = min(8, n_items - 8 * grp);
-  g = r / gs;
-  item = 8 * grp + (r - g * gs);
-}
-
 // DECODE_ONLY instantiations carry no MFMA path, so they need far fewer registers and run
 // more waves per SIMD; a plan with any prefill tile uses the full kernel, with 4 or 8 waves
 // per workgroup (8 when the batch carries enough prefill rows to fill 256-row tiles).
@@ -1755,9 +1737,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu(DECODE_ONLY ? (G >= 8 ? PKV_DECODE_WAVES_G8 : PKV_DECODE_WAVES) : 2)))
 void varlen_kernel(VarlenArgs a) {
   extern __shared__ __align__(16) char smem[];
-  int item, g;
-  xcd_item(a.num_kv_heads, item, g);
-  const WorkItem it = a.items[item];
+  const int x = blockIdx.x;
+  const int g = x % a.num_kv_heads;
+  const WorkItem it = a.items[x / a.num_kv_heads];
   if (DECODE_ONLY || it.kind == kDecode) {
     decode_item<D, G, NW, FP8, FP8 ? 2 : 1>(a, it, g, smem);
   } else {
@@ -1783,9 +1765,9 @@ template <int D, int G, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kShortWaves, 64 * kShortWaves), amdgpu_waves_per_eu(2, 2)))
 void short_kernel(VarlenArgs a) {
   extern __shared__ __align__(16) char smem[];
-  int item, g;
-  xcd_item(a.num_kv_heads, item, g);
-  short_item<D, G, kShortWaves, FP8>(a, a.items[item], g, smem);
+  const int x = blockIdx.x;
+  const int g = x % a.num_kv_heads;
+  short_item<D, G, kShortWaves, FP8>(a, a.items[x / a.num_kv_heads], g, smem);
 }
 
 // Decode batch with a device-side work split, for graph capture: the grid depends only on
@@ -1798,10 +1780,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(G >= 8 ? PKV_DECODE_WAVES_G8 : PKV_DECODE_WAVES)))
 void decode_graph_kernel(VarlenArgs a, int32_t splits, int32_t split_keys, int32_t num_tokens) {
   extern __shared__ __align__(16) char smem[];
-  int item, g;
-  xcd_item(a.num_kv_heads, item, g);
-  const int s = item % splits;
-  const int r = item / splits;
+  const int x = blockIdx.x;
+  const int g = x % a.num_kv_heads;
+  const int s = (x / a.num_kv_heads) % splits;
+  const int r = x / (a.num_kv_heads * splits);
   WorkItem it;
   it.seq = r;
   it.kind = kDecode;
@@ -1819,8 +1801,6 @@ template <int D, int G, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void prefill_wide_kernel(VarlenArgs a) {
   extern __shared__ __align__(16) char smem[];
-  // Item-major order here: the tiles of one request read the same keys per kv head, and with
-  // 8 kv heads each XCD then holds one head's tiles, whose key and value reads its L2 shares.
   const int x = blockIdx.x;
   const int g = x % a.num_kv_heads;
   const WorkItem it = a.items[x / a.num_kv_heads];
