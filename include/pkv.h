@@ -82,8 +82,11 @@ typedef struct pkv_varlen_plan {
   int32_t num_prefill_items;
   int32_t num_decode_items;
   int32_t num_partials;    /* split-KV partial states per q head */
-  int32_t blocks_per_split; /* 16-token blocks per split of a decode row (short rows choose
-                              their own, usually longer, split) */
+  int32_t blocks_per_split; /* most 16-token blocks per split of a decode row: a row of n
+                              blocks is cut into ceil(n / blocks_per_split) splits of that size,
+                              except that a last split under a quarter of it is evened out with
+                              the one before (short rows choose their own, usually longer,
+                              split) */
   int32_t has_splits;
   int64_t workspace_used;  /* bytes of the workspace the plan occupies */
   int32_t head_dim, num_q_heads, num_kv_heads, block_size; /* shape the plan was made for */

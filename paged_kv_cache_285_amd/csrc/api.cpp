@@ -105,6 +105,18 @@ struct Plan {
   int32_t n_prefill = 0, n_decode = 0, n_short = 0;
 };
 
+// First block of key split k (0 <= k <= splits) of a row of nblk blocks cut into splits of at
+// most bps blocks: full splits of bps blocks, except that a last split under bps / 4 blocks is
+// evened out with the one before it, so that no item is a sliver (a row of 1030 keys with 64-block
+// splits is two items of 33 and 32 blocks, not 64 and 1).  Splits keep their order; the last one
+// ends at nblk.
+int32_t split_start(int32_t nblk, int32_t bps, int32_t splits, int32_t k) {
+  if (k >= splits) return nblk;
+  const int32_t rem = nblk - (splits - 1) * bps;
+  if (splits > 1 && rem < bps / 4 && k == splits - 1) return (splits - 2) * bps + (bps + rem + 1) / 2;
+  return k * bps;
+}
+
 int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* seq,
                int32_t num_seqs, int32_t num_tokens, const pkv_shape* s) {
   if (num_seqs < 0 || num_tokens < 0) return fail(PKV_EINVAL, "negative num_seqs/num_tokens");
@@ -190,8 +202,8 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
         it.kind = pkv::kDecode;
         it.q_begin = 0;
         it.q_count = splits;
-        it.kv_begin = sidx * bps * pkv::kBlockSize;
-        it.kv_end = std::min<int32_t>(seq[r], (sidx + 1) * bps * pkv::kBlockSize);
+        it.kv_begin = split_start(nblk, bps, splits, sidx) * pkv::kBlockSize;
+        it.kv_end = std::min<int32_t>(seq[r], split_start(nblk, bps, splits, sidx + 1) * pkv::kBlockSize);
         it.partial_base = splits > 1 ? partials : -1;
         it.split = sidx;
         dec.push_back(it);
@@ -216,8 +228,8 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
         it.kind = pkv::kShort;
         it.q_begin = 0;
         it.q_count = ql;
-        it.kv_begin = sidx * bps_short * pkv::kBlockSize;
-        it.kv_end = std::min<int32_t>(seq[r], (sidx + 1) * bps_short * pkv::kBlockSize);
+        it.kv_begin = split_start(nblk, bps_short, splits, sidx) * pkv::kBlockSize;
+        it.kv_end = std::min<int32_t>(seq[r], split_start(nblk, bps_short, splits, sidx + 1) * pkv::kBlockSize);
         it.partial_base = splits > 1 ? partials + sidx * ql : -1;
         it.split = sidx;
         shrt.push_back(it);

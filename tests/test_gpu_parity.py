@@ -131,19 +131,25 @@ def test_spec_verify_small_parity():
 
 
 def test_short_rows_split_at_key_boundaries():
-    """Short rows cut into key splits (512 keys for this batch), with contexts placed so that
-    a split starts before, at, and after the first query's position (a token can see no key of
-    a split)."""
-    say("short rows over long contexts: split boundaries")
-    ctxs = [1019, 1020, 1023, 1024, 1025, 2043, 2047, 2048, 3071, 1100]
-    reqs = [W.RequestSpec(c, [5]) for c in ctxs] + [W.RequestSpec(1500, [16]), W.RequestSpec(1030, [2])]
-    wl = W.build("short_rows", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=13)
+    """Rows split by keys with a split starting before, at and after the first query token's
+    position, so that some tokens see no key of a split (an empty state the reduce must weigh by
+    zero): rows of 12 tokens (48 packed rows at G 4) over contexts around 1024 and 2048 are cut
+    tiles with 1024-key splits; rows of 2, 5 and 16 tokens over long contexts are split too
+    (short items: equal pieces)."""
+    say("rows split by keys around the query tokens' positions")
+    ctxs = [1019, 1020, 1023, 1024, 1025, 2043, 2047, 2048]
+    reqs = [W.RequestSpec(c, [12]) for c in ctxs] + [W.RequestSpec(c, [5]) for c in (3071, 1100, 2500)]
+    reqs += [W.RequestSpec(1500, [16]), W.RequestSpec(1030, [2])]
+    wl = W.build("split_edges", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=13)
     st = wl.steps[0]
     shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride)
     _, items = P.plan_varlen_host(st.query_start_loc, st.context_lens, st.seq_lens, shape)
-    short = items[items[:, 1] == 2]
-    # the rows at context 1020 .. 1025 have a split starting at key 1024, as the cases need
-    assert all(1024 in short[short[:, 0] == r, 4] for r in range(1, 5))
+    cut = items[(items[:, 1] == 1) & (items[:, 6] >= 0)]
+    # every row around 1024 / 2048 has a split starting inside its query tokens' positions
+    for r, c in enumerate(ctxs):
+        starts = cut[cut[:, 0] == r, 4]
+        assert any(c - 5 <= b <= c + 11 for b in starts if b > 0), (c, starts)
+    assert (items[:, 1] == 2).sum() > 3  # short rows split as well
     run_and_check(wl)
 
 
