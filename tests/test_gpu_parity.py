@@ -38,9 +38,10 @@ def say(*a):
 
 
 def run_and_check(wl, rows_per_step=None, check_pools=True, want_lse=True, out_dtype=torch.bfloat16, seed=0,
-                  expect_tile_rows=None, scale=None):
+                  expect_tile_rows=None, scale=None, check_steps=None):
     """Run every step of ``wl`` on the GPU and compare with the oracle (optionally on sampled rows);
-    ``scale``: a softmax scale other than 1/sqrt(head_dim), for both."""
+    ``check_steps``: compare only those steps (every step by default); ``scale``: a softmax scale
+    other than 1/sqrt(head_dim), for both."""
     bs = wl.block_size
     dw = DeviceWorkload(wl, scale=scale or 0.0)
     kp, vp = wl.k_cache, wl.v_cache
@@ -63,6 +64,8 @@ def run_and_check(wl, rows_per_step=None, check_pools=True, want_lse=True, out_d
             assert np.array_equal(host16(dw.k_cache[touched]), kp[touched]), "k_cache bits differ"
             assert np.array_equal(host16(dw.v_cache[touched]), vp[touched]), "v_cache bits differ"
         rows = None
+        if check_steps is not None and si not in check_steps:
+            continue
         if rows_per_step is not None and st.num_tokens > rows_per_step:
             rows = np.sort(rng.choice(st.num_tokens, size=rows_per_step, replace=False))
             # always include the first and last token of every prefill row and the longest decode row
@@ -529,7 +532,13 @@ def test_cascade_small_parity():
     _cascade_check(wl)
 
 
-def _cascade_check(wl, rows=None, scale=None):
+def _cascade_check(wl, rows=None, scale=None, every_row=False):
+    """GPU prefix pass, suffix pass and merge against the oracle.  With rows, the prefix pass and
+    the merged output are compared on those rows only (the merged output against single-pass
+    attention).  With every_row, the prefix and suffix passes and the merged output are compared
+    on every row against the oracle's own prefix pass, suffix pass and merge (which the CPU pins
+    tie to single-pass attention), and rows still picks the rows checked against single-pass
+    attention."""
     bs = wl.block_size
     st = wl.steps[0]
     cv = wl.cascade
@@ -558,6 +567,20 @@ def _cascade_check(wl, rows=None, scale=None):
     torch.cuda.synchronize()
     slots_o = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, bs)
     kp, vp = O.reshape_and_cache(st.k, st.v, wl.k_cache, wl.v_cache, slots_o, bs)
+    if every_row:
+        po, pl = O.cascade_prefix_attention(st.q, kp, vp, cv.prefix_block_table, cv.prefix_len, bs, scale=scale)
+        check_attention(o_p.cpu().numpy().astype(np.float64), po, "cascade prefix, every row", bf16_out=False)
+        check_lse(l_p.cpu().numpy(), pl, "cascade prefix lse, every row")
+        so, sl = O.paged_attention(st.q, kp, vp, sbt_np, st.query_start_loc, cv.suffix_context_lens,
+                                   cv.suffix_seq_lens, bs, scale=scale)
+        check_attention(o_s.cpu().numpy().astype(np.float64), so, "cascade suffix, every row", bf16_out=False)
+        check_lse(l_s.cpu().numpy(), sl, "cascade suffix lse, every row")
+        mo, ml = O.merge_attn_states(po, pl, so, sl)
+        r = check_attention(bf16_out_to_f64(out), mo, "cascade merged vs oracle merge, every row")
+        check_lse(lse_m.cpu().numpy(), ml, "cascade merged lse, every row")
+        say(f"    cascade merged, every row {r}")
+        if rows is None:
+            return
     sel = slice(None) if rows is None else rows
     qs = st.q if rows is None else st.q[rows]
     po, pl = O.cascade_prefix_attention(qs, kp, vp, cv.prefix_block_table, cv.prefix_len, bs, scale=scale)
@@ -625,16 +648,25 @@ def test_decode_full_size_every_row():
     run_and_check(W.decode_only(seed=0), check_pools=False)
 
 
-def test_cascade_full_size_sampled():
-    say("cascade full size (512 queries, 16384-token prefix), sampled rows")
+def test_cascade_full_size_every_row():
+    """Full cascade size (512 queries x 64 heads, 16384-token prefix, suffixes 64..1024) in the
+    launch configuration bench times: every row of the three passes against the oracle's, and
+    24 sampled rows of the merged output against single-pass attention."""
+    say("cascade full size (512 queries, 16384-token prefix), every row")
     wl = W.cascade_shared_prefix(seed=0)
     rows = np.sort(np.random.default_rng(3).choice(wl.steps[0].num_tokens, 24, replace=False))
-    _cascade_check(wl, rows=rows)
+    _cascade_check(wl, rows=rows, every_row=True)
 
 
-def test_long_chunked_prefill_full_size_sampled():
-    say("long_chunked_prefill full size (32768-token prompt in 16 chunks + 128 decode rows), sampled")
-    run_and_check(W.long_chunked_prefill(seed=0), rows_per_step=24, check_pools=False, want_lse=False)
+@pytest.mark.parametrize("chunks", [(0, 8), (8, 11), (11, 13), (13, 15), (15, 16)])
+def test_long_chunked_prefill_full_size_every_row(chunks):
+    """Full long-prefill size (a 32768-token prompt in 16 chunks of 2048 beside 128 decode rows)
+    in the launch configuration bench times, every row: each case runs all 16 steps and compares
+    every row of the steps in [chunks) (2048 prompt rows over up to 32768 keys and the 128 decode
+    rows each); the cases split the oracle's work, which grows with the chunk index."""
+    say(f"long_chunked_prefill full size (32768-token prompt in 16 chunks + 128 decode rows), steps {chunks}")
+    wl = W.long_chunked_prefill(seed=0)
+    run_and_check(wl, check_pools=False, want_lse=False, check_steps=range(*chunks))
 
 
 # ---------------------------------------------------------------------------
