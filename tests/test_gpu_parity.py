@@ -704,9 +704,9 @@ def test_block_size_256_copy_blocks_bitwise():
     assert np.array_equal(host16(dw.k_cache), kc) and np.array_equal(host16(dw.v_cache), vc)
 
 
-def test_block_size_256_full_size_decode_sampled():
-    say("256-token blocks: decode_only full size, sampled rows")
-    run_and_check(W.decode_only(seed=0, block_size=256), rows_per_step=48, check_pools=False)
+def test_block_size_256_full_size_decode_every_row():
+    say("256-token blocks: decode_only full size, every row")
+    run_and_check(W.decode_only(seed=0, block_size=256), check_pools=False)
 
 
 # ---------------------------------------------------------------------------
