@@ -1839,6 +1839,7 @@ void cascade_kernel(CascadeArgs a) {
 }
 
 // One wave per (token, head) row; lane holds D/64 consecutive dims.
+constexpr int kReduceBatch = 8;  // splits a row's states are loaded for at once
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   constexpr int V = D / 64;
@@ -1860,21 +1861,56 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
     count = a.uniform_count;
     stride = a.num_tokens;
   }
+  // One wave per row: the split layout is the same for every lane.
+  count = __builtin_amdgcn_readfirstlane(count);
   float mx = -INFINITY;
-  for (int s = 0; s < count; ++s) mx = fmaxf(mx, a.part_lse[(base + s * stride) * Hq + head]);
   float acc[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) acc[e] = 0.f;
   float z = 0.f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < count; ++s) {
-      const int64_t prow = (base + s * stride) * Hq + head;
-      const float ls = a.part_lse[prow];
-      const float w = (ls == -INFINITY) ? 0.f : __expf(ls - mx);
-      z += w;
-      const float* src = a.part_o + prow * D + lane * V;
+  if (count <= kReduceBatch) {
+    // Every split's (lse, o) loads are issued before the first is used, so the partial states,
+    // which the attention launch just wrote, arrive in one memory round trip; the arithmetic
+    // and its order are those of the loops for more splits.
+    float ls[kReduceBatch], po[kReduceBatch][V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+    for (int s = 0; s < kReduceBatch; ++s) {
+      ls[s] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < V; ++e) po[s][e] = 0.f;
+      if (s < count) {
+        const int64_t prow = (base + s * stride) * Hq + head;
+        ls[s] = a.part_lse[prow];
+        const float* src = a.part_o + prow * D + lane * V;
+#pragma unroll
+        for (int e = 0; e < V; ++e) po[s][e] = src[e];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kReduceBatch; ++s) mx = fmaxf(mx, ls[s]);
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int s = 0; s < kReduceBatch; ++s) {
+        if (s < count) {
+          const float w = (ls[s] == -INFINITY) ? 0.f : __expf(ls[s] - mx);
+          z += w;
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc[e] = fmaf(w, po[s][e], acc[e]);
+        }
+      }
+    }
+  } else {
+    for (int s = 0; s < count; ++s) mx = fmaxf(mx, a.part_lse[(base + s * stride) * Hq + head]);
+    if (mx != -INFINITY) {
+      for (int s = 0; s < count; ++s) {
+        const int64_t prow = (base + s * stride) * Hq + head;
+        const float ls = a.part_lse[prow];
+        const float w = (ls == -INFINITY) ? 0.f : __expf(ls - mx);
+        z += w;
+        const float* src = a.part_o + prow * D + lane * V;
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+      }
     }
   }
   const float inv = (z > 0.f) ? 1.f / z : 0.f;
