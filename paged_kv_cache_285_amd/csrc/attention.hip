@@ -603,8 +603,8 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
 // ------------------------------------------------------------------------------------------
 // Short item: a row of a few query tokens (at most 32 packed (token, q head) rows, such as a
 // speculative-verify row of 1 + k tokens) over a key range, on the matrix cores, with the
-// decode item's work split (4 waves, whole 16-key blocks per wave, block ids and scales
-// fetched once per lane) and two blocks in flight per wave.  The packed rows are the columns
+// decode item's work split (whole 16-key blocks per wave, block ids and scales fetched once per
+// lane) and two blocks in flight per wave.  The packed rows are the columns
 // of two 16-column groups:
 //  * S^T = K Q^T per group: v_mfma_f32_16x16x32_bf16 over D/32 K-steps.  A = the block's 16
 //    key rows: lane (i = lane % 16, q = lane / 16) holds dims 32s + 8q .. +7 of key i, one
@@ -614,8 +614,9 @@ __device__ void decode_item(const VarlenArgs& a, const WorkItem& it, int g, char
 //    reduction), and those 4 p are exactly the B operand (keys 4q .. 4q+3, column n) of
 //  * O^T += V^T P^T per group: v_mfma_f32_16x16x16_bf16 per 16 dims.  A = V^T: lane (d, q)
 //    holds keys 4q .. 4q+3 of dim 16 dg + d, one 8-byte load (4 of fp8) shared by both groups.
-// The 4 waves' states are merged in LDS one wave after another (fixed order: the result does
-// not depend on timing).
+// The waves' states are merged in LDS: each wave writes its sums, rescaled to the common max, to
+// a slot of its own, and the slots are added in wave order (the result does not depend on
+// timing).
 // ------------------------------------------------------------------------------------------
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -626,15 +627,17 @@ __device__ __forceinline__ uint2 widen4(uint32_t c) {
 }
 __device__ __forceinline__ uint2 widen4(uint2 c) { return c; }
 
-// LDS of a short item: the packed query rows (bf16, pitch QP) while the blocks stream, then, in
-// the same bytes, the waves' output sums (fp32, pitch DP); the per-wave m, l and r after them.
+// LDS of a short item: the packed query rows (bf16, pitch QP) while the blocks stream, then, from
+// the same bytes on, one slot of output sums per wave (fp32, pitch DP); the per-wave m, l and r
+// after them.
 template <int D, int NW>
 struct ShortSmem {
   static constexpr int COLS = 32;
   static constexpr int DP = D + 4;  // row pitch (floats): 16 columns' float4 stores hit distinct banks
   static constexpr int QP = D + 8;  // query row pitch (bf16): conflict-free 16-byte operand reads
-  static_assert(COLS * QP * 2 <= COLS * DP * 4, "query rows fit the output rows");
-  static constexpr int BYTES = (COLS * DP + 3 * NW * COLS) * 4;
+  static_assert(COLS * QP * 2 <= COLS * DP * 4, "query rows fit the first output slot");
+  static constexpr int BYTES = (NW * COLS * DP + 3 * NW * COLS) * 4;
+  static_assert(BYTES <= 160 * 1024, "fits the LDS of a CU");
 };
 
 // Waves of a short item's workgroup: one workgroup fills a CU at two waves per SIMD, so the
@@ -820,9 +823,10 @@ __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char*
   }
 
   // Merge the waves: every wave publishes (m, l) per column; each lane rescales its o to the
-  // columns' common max; the waves then add their o into one LDS buffer in wave order.
-  float* s_o = reinterpret_cast<float*>(smem_raw);  // [COLS][DP], over the query rows
-  float* s_m = s_o + SM::COLS * SM::DP;              // [NW][COLS]
+  // columns' common max into an LDS slot of its wave; the store below adds the slots in wave
+  // order (one barrier, rather than one per wave for a running sum).
+  float* s_o = reinterpret_cast<float*>(smem_raw);  // [NW][COLS][DP], the first slot over the query rows
+  float* s_m = s_o + NW * SM::COLS * SM::DP;         // [NW][COLS]
   float* s_l = s_m + NW * SM::COLS;                  // [NW][COLS]
   float* s_r = s_l + NW * SM::COLS;                  // [NW][COLS]
 #pragma unroll
@@ -848,27 +852,12 @@ __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char*
     fac[cg] = (mx == -INFINITY) ? 0.f : fast_exp2(m[cg] - mx);
   }
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    if (wave == w) {
+  for (int cg = 0; cg < NC; ++cg)
 #pragma unroll
-      for (int cg = 0; cg < NC; ++cg)
-#pragma unroll
-        for (int d = 0; d < DG; ++d) {
-          float4* dst = reinterpret_cast<float4*>(s_o + (16 * cg + n16) * SM::DP + 16 * d + 4 * q);
-          float4 x = make_float4(o[cg][d][0] * fac[cg], o[cg][d][1] * fac[cg], o[cg][d][2] * fac[cg],
-                                 o[cg][d][3] * fac[cg]);
-          if (w > 0) {
-            const float4 y = *dst;
-            x.x += y.x;
-            x.y += y.y;
-            x.z += y.z;
-            x.w += y.w;
-          }
-          *dst = x;
-        }
-    }
-    __syncthreads();
-  }
+    for (int d = 0; d < DG; ++d)
+      *reinterpret_cast<float4*>(s_o + (wave * SM::COLS + 16 * cg + n16) * SM::DP + 16 * d + 4 * q) =
+          make_float4(o[cg][d][0] * fac[cg], o[cg][d][1] * fac[cg], o[cg][d][2] * fac[cg], o[cg][d][3] * fac[cg]);
+  __syncthreads();
   // Store: thread per 8 output values of a valid column.
   for (int idx = threadIdx.x; idx < ncols * CH; idx += 64 * NW) {
     const int n = idx / CH, cc = idx % CH;
@@ -887,7 +876,13 @@ __device__ void short_item(const VarlenArgs& a, const WorkItem& it, int g, char*
     const float inv = (rr > 0.f) ? 1.f / rr : 0.f;
     float oo[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) oo[e] = s_o[n * SM::DP + 8 * cc + e] * inv;
+    for (int e = 0; e < 8; ++e) oo[e] = s_o[n * SM::DP + 8 * cc + e];
+#pragma unroll
+    for (int w = 1; w < NW; ++w)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) oo[e] += s_o[(w * SM::COLS + n) * SM::DP + 8 * cc + e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oo[e] *= inv;
     const float lse = (ll > 0.f) ? (mx + __log2f(ll)) * kLn2 : -INFINITY;
     const int t = n / G, head = g * G + n % G;
     if (it.partial_base < 0) {
