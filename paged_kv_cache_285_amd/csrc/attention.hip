@@ -7,10 +7,10 @@
 // j = 0..p of the request, read through its block table, weighting the values v_j.
 //
 // Kernel design (MI355X-first, not a translation of any printed kernel):
-//  * varlen_kernel: one launch serves the whole batch.  The host plan lists work items; each
-//    is run once per kv head (grid = items * Hkv, kv head fastest so that all tiles of one kv
-//    head fall on the same XCD under round-robin dispatch and share its L2).  Each workgroup
-//    branches uniformly on the item kind:
+//  * varlen_kernel: one launch serves the batch's decode items and 128-row prefill tiles.  The
+//    host plan lists work items; each is run once per kv head (grid = items * Hkv, kv head
+//    fastest so that all tiles of one kv head fall on the same XCD under round-robin dispatch
+//    and share its L2).  Each workgroup branches uniformly on the item kind:
 //      - decode item (query length 1): VALU path.  4 waves stream disjoint 16-token blocks of
 //        the item's key range straight from HBM with 16-byte coalesced loads (one wave load
 //        covers 1 KB of a 4 KB block tile), software-pipelined one block ahead.  All G q heads
@@ -27,6 +27,10 @@
 //        row-major, V^T tiles key-permuted so every MFMA operand is one conflict-free 16-byte
 //        read, both double-buffered; the causal mask (offset by the cached length) is only
 //        evaluated on tiles that straddle the diagonal or the sequence end.
+//    A batch with enough prompt rows runs its prefill tiles as 256-row tiles of 8 waves in
+//    prefill_wide_kernel and its decode items in a varlen launch of their own; rows of
+//    2 .. 32/G tokens (speculative verification) run as short items in short_kernel, a launch
+//    of its own.
 //  * cascade_kernel: the shared-prefix pass, the same 8-wave MFMA tile with no mask over the
 //    prefix block table, cut into key segments when there are too few query tiles to fill
 //    the chip; the segment states are merged afterwards.
