@@ -741,6 +741,14 @@ def main():
             "warm_frac": mean_bytes / (warm["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
     }
+    props = torch.cuda.get_device_properties(0)
+    line["device"] = {
+        "name": props.name,
+        "arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count,
+        "memory_GiB": round(props.total_memory / 2**30, 1),
+        "peaks": "published MI355X figures: HBM 8 TB/s; dense bf16 MFMA 2.5 PFLOP/s (256 CUs at 2.4 GHz)",
+    }
     if not args.no_decode:
         log("bench: decode-only batch")
         line["decode_hbm"] = decode_hbm(torch, P)
