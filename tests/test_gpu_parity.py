@@ -197,6 +197,23 @@ def test_lengths_at_block_tile_and_split_edges():
     run_and_check(wl)
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_split_counts_around_the_reduce_batch(out_dtype):
+    """Decode rows cut into 7, 8, 9, 10 and 17 key splits beside unsplit rows: the split-KV
+    reduce loads up to 8 splits' states in one round and takes more in a loop; both against
+    the oracle."""
+    say(f"split counts 7..17 around the reduce's batch of 8 ({out_dtype})")
+    reqs = [W.RequestSpec(c, [1]) for c in (1791, 2047, 2048, 2303, 2559, 4351, 100, 0)]
+    wl = W.build("reduce_batch_edges", reqs, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=44)
+    st = wl.steps[0]
+    shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride,
+                         block_size=wl.block_size)
+    _, items = P.plan_varlen_host(st.query_start_loc, st.context_lens, st.seq_lens, shape)
+    splits = np.bincount(items[:, 0], minlength=len(reqs))
+    assert {7, 8, 9, 10, 17} <= set(splits.tolist()) and 1 in splits, splits
+    run_and_check(wl, out_dtype=out_dtype)
+
+
 def test_spec_verify_full_size_every_row():
     say("spec_verify full: 64 rows of 5 tokens, ctx U[1024, 4096], every row")
     run_and_check(W.spec_verify(seed=0), check_pools=False)
