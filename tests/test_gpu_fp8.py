@@ -167,7 +167,8 @@ def test_fp8_copy_blocks_copies_bytes_and_scales():
 
 
 def run_and_check_fp8(wl, rows_per_step=None, want_lse=True, out_dtype=torch.bfloat16, seed=0, expect_tile_rows=None,
-                      check_pools=True, scale=None):
+                      check_pools=True, scale=None, check_steps=None):
+    """As run_and_check over fp8 pools; ``check_steps``: compare only those steps (all by default)."""
     bs = wl.block_size
     d = DeviceFp8(wl, seed=seed, scale=scale or 0.0)
     kp, vp = d.c.k_cache, d.c.v_cache
@@ -192,6 +193,8 @@ def run_and_check_fp8(wl, rows_per_step=None, want_lse=True, out_dtype=torch.bfl
         if check_pools:
             gk, gv = d.host_pools()
             assert np.array_equal(gk, kp) and np.array_equal(gv, vp), "fp8 pool bytes differ"
+        if check_steps is not None and si not in check_steps:
+            continue
         rows = None
         if rows_per_step is not None and st.num_tokens > rows_per_step:
             rows = np.sort(rng.choice(st.num_tokens, size=rows_per_step, replace=False))
@@ -315,7 +318,10 @@ def test_fp8_cascade_small_parity():
     _fp8_cascade_check(wl)
 
 
-def _fp8_cascade_check(wl, rows=None):
+def _fp8_cascade_check(wl, rows=None, every_row=False):
+    """As the bf16 cascade check: with every_row, the three passes on every row against the
+    oracle's prefix pass, suffix pass and merge; rows picks the rows checked against single-pass
+    attention."""
     bs = wl.block_size
     st = wl.steps[0]
     cv = wl.cascade
@@ -339,6 +345,21 @@ def _fp8_cascade_check(wl, rows=None):
     torch.cuda.synchronize()
     slots = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, bs)
     kp, vp = O.reshape_and_cache_fp8(st.k, st.v, d.c.k_cache, d.c.v_cache, slots, d.c.k_scale, d.c.v_scale, bs)
+    if every_row:
+        po, pl = O.cascade_prefix_attention_fp8(st.q, kp, vp, d.c.k_scale, d.c.v_scale, cv.prefix_block_table,
+                                                cv.prefix_len, bs)
+        check_attention(o_p.cpu().numpy().astype(np.float64), po, "fp8 cascade prefix, every row", bf16_out=False)
+        check_lse(l_p.cpu().numpy(), pl, "fp8 cascade prefix lse, every row")
+        so, sl = O.paged_attention_fp8(st.q, kp, vp, d.c.k_scale, d.c.v_scale, sbt, st.query_start_loc,
+                                       cv.suffix_context_lens, cv.suffix_seq_lens, bs)
+        check_attention(o_s.cpu().numpy().astype(np.float64), so, "fp8 cascade suffix, every row", bf16_out=False)
+        check_lse(l_s.cpu().numpy(), sl, "fp8 cascade suffix lse, every row")
+        mo, ml = O.merge_attn_states(po, pl, so, sl)
+        r = check_attention(bf16_out_to_f64(out), mo, "fp8 cascade merged vs oracle merge, every row")
+        check_lse(lse_m.cpu().numpy(), ml, "fp8 cascade merged lse, every row")
+        say(f"    fp8 cascade merged, every row {r}")
+        if rows is None:
+            return
     sel = slice(None) if rows is None else rows
     qs = st.q if rows is None else st.q[rows]
     po, pl = O.cascade_prefix_attention_fp8(qs, kp, vp, d.c.k_scale, d.c.v_scale, cv.prefix_block_table,
@@ -350,6 +371,26 @@ def _fp8_cascade_check(wl, rows=None):
     r = check_attention(bf16_out_to_f64(out)[sel], fo[sel], "fp8 cascade merged vs single pass")
     check_lse(lse_m.cpu().numpy()[sel], fl[sel], "fp8 cascade merged lse")
     say(f"    fp8 cascade merged {r}")
+
+
+def test_fp8_cascade_full_size_every_row():
+    """The full cascade (512 queries x 64 heads, 16384-token prefix, suffixes 64..1024) over fp8
+    pools: every row of the three passes against the oracle's, 24 sampled rows of the merged
+    output against single-pass attention over the dequantised pools."""
+    say("fp8 cascade full size, every row")
+    wl = W.cascade_shared_prefix(seed=0)
+    rows = np.sort(np.random.default_rng(3).choice(wl.steps[0].num_tokens, 24, replace=False))
+    _fp8_cascade_check(wl, rows=rows, every_row=True)
+
+
+def test_fp8_long_chunked_prefill_full_size_last_chunk_every_row():
+    """The full long prefill (a 32768-token prompt in 16 chunks of 2048 beside 128 decode rows)
+    over fp8 pools: every step runs; every row of the last (2048 prompt rows over 32768 keys on
+    256-row tiles, and the 128 decode rows) is compared."""
+    say("fp8 long_chunked_prefill full size, last chunk every row")
+    wl = W.long_chunked_prefill(seed=0)
+    run_and_check_fp8(wl, seed=0, want_lse=False, check_pools=False, expect_tile_rows=256,
+                      check_steps=(len(wl.steps) - 1,))
 
 
 def test_fp8_decode_full_size_every_row():
