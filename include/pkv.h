@@ -92,6 +92,9 @@ typedef struct pkv_varlen_plan {
   int32_t head_dim, num_q_heads, num_kv_heads, block_size; /* shape the plan was made for */
   int32_t tile_rows;       /* packed (token, q head) rows per prefill tile: 128 or 256 */
   int32_t num_short_items; /* items of rows of 2 .. 32 / G query tokens (short items) */
+  int32_t decode_waves;    /* waves per workgroup of decode items launched on their own: 4, or 1
+                              when every decode item has at most 64 16-token blocks, G >= 8 and
+                              there are at least 4096 (item, kv head) workgroups */
 } pkv_varlen_plan;
 
 /* Size in bytes of a workspace that fits any plan with at most these sizes. */

@@ -77,6 +77,7 @@ class PkvVarlenPlan(ctypes.Structure):
         ("block_size", ctypes.c_int32),
         ("tile_rows", ctypes.c_int32),
         ("num_short_items", ctypes.c_int32),
+        ("decode_waves", ctypes.c_int32),
     ]
 
 

@@ -103,6 +103,7 @@ struct Plan {
   int32_t bps = 0;
   int32_t tile_rows = pkv::kTileRows;
   int32_t n_prefill = 0, n_decode = 0, n_short = 0;
+  int32_t decode_waves = 4;
 };
 
 // First block of key split k (0 <= k <= splits) of a row of nblk blocks cut into splits of at
@@ -116,6 +117,8 @@ int32_t split_start(int32_t nblk, int32_t bps, int32_t splits, int32_t k) {
   if (splits > 1 && rem < bps / 4 && k == splits - 1) return (splits - 2) * bps + (bps + rem + 1) / 2;
   return k * bps;
 }
+
+constexpr int64_t kOneWaveDecodeItems = 4096;  // decode workgroups from which one-wave ones pay
 
 int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* seq,
                int32_t num_seqs, int32_t num_tokens, const pkv_shape* s) {
@@ -295,6 +298,21 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
   P.num_partials = partials;
   P.n_prefill = (int32_t)pre.size();
   P.n_decode = (int32_t)dec.size();
+  // Decode items in a launch of their own (no 128-row tiles beside them) run one wave per
+  // workgroup when every item fits one wave (one block id per lane: at most 64 blocks), q heads
+  // share a kv head eight at a time, and there are at least kOneWaveDecodeItems of them (two
+  // rounds of the one-wave workgroups the chip holds at two waves per SIMD).  Short rows cut
+  // from a long shared prefix (a cascade's suffix pass) are the case: the 4-wave item's start
+  // and cross-wave merge are then a large part of its time.
+  int32_t max_blocks = 0;
+  for (const pkv::WorkItem& it : dec)
+    max_blocks = std::max<int32_t>(max_blocks, (int32_t)ceil_div(it.kv_end, pkv::kBlockSize) -
+                                                   it.kv_begin / pkv::kBlockSize);
+  const bool decode_alone = P.n_prefill == 0 || P.tile_rows == pkv::kWideTileRows;
+  P.decode_waves = decode_alone && G >= 8 && max_blocks <= 64 &&
+                           (int64_t)P.n_decode * s->num_kv_heads >= kOneWaveDecodeItems
+                       ? 1
+                       : 4;
   return PKV_OK;
 }
 
@@ -314,6 +332,7 @@ void fill_plan_struct(pkv_varlen_plan* out, const Plan& P, int32_t num_seqs, int
   out->num_kv_heads = s->num_kv_heads;
   out->block_size = s->block_size;
   out->tile_rows = P.tile_rows;
+  out->decode_waves = P.decode_waves;
   const VarlenLayout L =
       varlen_layout(out->num_items, num_tokens, P.num_partials, s->num_q_heads, s->head_dim);
   out->workspace_used = (int64_t)L.total;
@@ -686,6 +705,8 @@ static int varlen_impl(void* out, int32_t out_dtype, float* lse, const void* q,
       plan->head_dim != shape->head_dim || plan->num_q_heads != shape->num_q_heads ||
       plan->num_kv_heads != shape->num_kv_heads)
     return fail(PKV_EINVAL, "plan was made for different metadata or shape");
+  if (plan->decode_waves != 1 && plan->decode_waves != 4)
+    return fail(PKV_EINVAL, "plan decode_waves %d invalid (1 or 4)", plan->decode_waves);
   if (num_tokens == 0 || plan->num_items == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens ||
       !seq_lens || !workspace || (fp8 && (!k_scale || !v_scale)))
@@ -722,7 +743,7 @@ static int varlen_impl(void* out, int32_t out_dtype, float* lse, const void* q,
   if (int rc = timing_mark((hipStream_t)stream, true)) return rc;
   hipError_t e = (fp8 ? pkv::launch_varlen_fp8 : pkv::launch_varlen)(
       a, shape->head_dim, G, plan->num_prefill_items, plan->num_decode_items, plan->num_short_items,
-      plan->tile_rows, (hipStream_t)stream);
+      plan->tile_rows, plan->decode_waves, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "varlen attention launch");
   if (int rc = timing_mark((hipStream_t)stream, false)) return rc;
   if (plan->num_partials > 0) {

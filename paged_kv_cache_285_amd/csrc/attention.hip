@@ -19,7 +19,8 @@
 //        dim-major value tile with v_dot2_f32_bf16 against bf16 p pairs.  Waves are merged
 //        with the (o, lse) merge in LDS; long rows are cut into split-KV items whose partial
 //        states reduce_kernel merges.  A decode-only batch uses a specialisation with no
-//        prefill branch and a tighter register budget.
+//        prefill branch and a tighter register budget, with one-wave workgroups when the plan
+//        asks for them (many short items at G = 8).
 //      - prefill tile (query length > 1): 32 packed (token, q head) rows per wave (4 or 8
 //        waves) x 64-key tiles on bf16 MFMA 32x32x16.  S^T = K Q^T puts one query per lane
 //        column so the row max and row sum stay inside a lane (plus one cross-half exchange);
@@ -251,8 +252,7 @@ __device__ __forceinline__ void decode_merge(const VarlenArgs& a, const WorkItem
   const float* s_r = s_l + NW * G;
   const int Hq = a.num_q_heads;
   __syncthreads();
-  const int t = threadIdx.x;
-  if (t < G * CH) {
+  for (int t = threadIdx.x; t < G * CH; t += 64 * NW) {
     const int hh = t / CH, cc = t % CH;
     float mm = -INFINITY, ll = 0.f, rr = 0.f, oo[8];
 #pragma unroll
@@ -1941,15 +1941,30 @@ size_t varlen_smem(bool has_prefill) {
 
 constexpr bool kFp8 = PKV_KV_FP8 != 0;
 
+
+// Decode items in a launch of their own: 4-wave workgroups, or one-wave ones (decode_waves == 1,
+// which the plan picks only when every decode item fits one wave).
+template <int D, int G>
+void launch_decode_only(const VarlenArgs& a, int n_decode, int decode_waves, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)n_decode * a.num_kv_heads));
+  if constexpr (G >= 8) {
+    if (decode_waves == 1) {
+      const size_t smem = varlen_smem<D, G, 1>(false);
+      hipLaunchKernelGGL((varlen_kernel<D, G, true, 1, kFp8>), grid, dim3(64), smem, stream, a);
+      return;
+    }
+  }
+  const size_t smem = varlen_smem<D, G, 4>(false);
+  hipLaunchKernelGGL((varlen_kernel<D, G, true, 4, kFp8>), grid, dim3(256), smem, stream, a);
+}
+
 template <int D, int G>
 hipError_t launch_varlen_t(const VarlenArgs& a, int n_prefill, int n_decode, int n_short, int tile_rows,
-                           hipStream_t stream) {
+                           int decode_waves, hipStream_t stream) {
   const int Hkv = a.num_kv_heads;
   if (n_prefill + n_decode > 0) {
     if (n_prefill == 0) {
-      auto kern = varlen_kernel<D, G, true, 4, kFp8>;
-      const size_t smem = varlen_smem<D, G, 4>(false);
-      hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)n_decode * Hkv)), dim3(256), smem, stream, a);
+      launch_decode_only<D, G>(a, n_decode, decode_waves, stream);
     } else if (tile_rows == kWideTileRows) {
       // Wide prefill tiles, then the decode items in a kernel of their own (the wide tile's
       // register budget allows two waves per SIMD, too few for the decode path).
@@ -1960,9 +1975,7 @@ hipError_t launch_varlen_t(const VarlenArgs& a, int n_prefill, int n_decode, int
         VarlenArgs b = a;
         b.items = a.items + n_prefill;
         b.num_items = n_decode;
-        auto dk = varlen_kernel<D, G, true, 4, kFp8>;
-        const size_t smem = varlen_smem<D, G, 4>(false);
-        hipLaunchKernelGGL(dk, dim3((unsigned)((int64_t)n_decode * Hkv)), dim3(256), smem, stream, b);
+        launch_decode_only<D, G>(b, n_decode, decode_waves, stream);
       }
     } else {
       auto kern = varlen_kernel<D, G, false, 4, kFp8>;
@@ -2032,8 +2045,9 @@ hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
 #endif
 
 hipError_t PKV_KV_NAME(launch_varlen)(const VarlenArgs& a, int head_dim, int group, int n_prefill,
-                                      int n_decode, int n_short, int tile_rows, hipStream_t stream) {
-#define CALL_V(D, G) launch_varlen_t<D, G>(a, n_prefill, n_decode, n_short, tile_rows, stream)
+                                      int n_decode, int n_short, int tile_rows, int decode_waves,
+                                      hipStream_t stream) {
+#define CALL_V(D, G) launch_varlen_t<D, G>(a, n_prefill, n_decode, n_short, tile_rows, decode_waves, stream)
   PKV_DISPATCH_DG(head_dim, group, CALL_V)
 #undef CALL_V
 }

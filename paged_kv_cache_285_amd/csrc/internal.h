@@ -135,14 +135,16 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
                               int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                               int32_t elem_bytes, hipStream_t stream);
 // Launches the attention kernels of a varlen plan whose items list n_prefill prefill tiles of
-// tile_rows rows first, then n_decode decode items, then n_short short items.
+// tile_rows rows first, then n_decode decode items, then n_short short items; decode items in a
+// launch of their own run decode_waves (4, or 1) waves per workgroup.
 hipError_t launch_varlen(const VarlenArgs& a, int head_dim, int group, int n_prefill, int n_decode,
-                         int n_short, int tile_rows, hipStream_t stream);
+                         int n_short, int tile_rows, int decode_waves, hipStream_t stream);
 hipError_t launch_cascade(const CascadeArgs& a, int head_dim, int group, hipStream_t stream);
 // The same over fp8 (e4m3) pools with per-(block, kv head) scales (attention.hip built with
 // PKV_KV_FP8=1).
 hipError_t launch_varlen_fp8(const VarlenArgs& a, int head_dim, int group, int n_prefill,
-                             int n_decode, int n_short, int tile_rows, hipStream_t stream);
+                             int n_decode, int n_short, int tile_rows, int decode_waves,
+                             hipStream_t stream);
 hipError_t launch_cascade_fp8(const CascadeArgs& a, int head_dim, int group, hipStream_t stream);
 // Decode batch (one query token per row) split into `splits` key ranges of split_keys keys per
 // row, with the split computed on the device (graph-capturable); num_tokens = rows of the

@@ -217,6 +217,29 @@ def test_plan_covers_every_row_exactly_once(P, lengths):
     assert (np.diff(dec[:, 5] - dec[:, 4]) <= 0).all()
 
 
+def test_decode_waves_one_only_for_many_short_g8_items(P):
+    """A decode-only plan asks for one-wave workgroups only when every item has at most 64
+    blocks, q heads share a kv head eight at a time and there are at least 4096 (item, kv head)
+    workgroups; otherwise four waves."""
+    rng = np.random.default_rng(3)
+
+    def plan(B, lo, hi, Hq, Hkv=8, extra_ql=()):
+        ql = np.array([1] * B + list(extra_ql))
+        ctx = rng.integers(lo, hi + 1, size=len(ql))
+        qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+        s = shape(P, num_q_heads=Hq, num_kv_heads=Hkv, bt_stride=600, num_blocks=60000)
+        p, items = P.plan_varlen_host(qsl, ctx, (ctx + ql).astype(np.int32), s)
+        return p, items
+
+    p, items = plan(512, 63, 1023, 64)  # the cascade suffix pass's shape
+    assert p.decode_waves == 1
+    assert ((items[:, 5] + 15) // 16 - items[:, 4] // 16).max() <= 64
+    assert plan(512, 63, 1023, 32)[0].decode_waves == 4  # G = 4
+    assert plan(400, 63, 1023, 64)[0].decode_waves == 4  # 3200 workgroups
+    assert plan(512, 63, 2000, 64)[0].decode_waves == 4  # items over 64 blocks
+    assert plan(512, 63, 1023, 64, extra_ql=(40,))[0].decode_waves == 4  # 128-row tiles beside
+
+
 def test_workspace_bound_holds_for_every_plan(P):
     rng = np.random.default_rng(1)
     for trial in range(40):

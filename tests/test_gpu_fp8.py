@@ -393,6 +393,17 @@ def test_fp8_long_chunked_prefill_full_size_last_chunk_every_row():
                       check_steps=(len(wl.steps) - 1,))
 
 
+def test_fp8_one_wave_decode_items():
+    """Many short G = 8 decode rows over fp8 pools, run as one-wave workgroups."""
+    say("fp8 one-wave decode items")
+    wl = W.decode_only(seed=46, num_seqs=520, ctx_range=(1, 1000), num_q_heads=64)
+    st = wl.steps[0]
+    shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride,
+                         block_size=wl.block_size)
+    assert P.plan_varlen_host(st.query_start_loc, st.context_lens, st.seq_lens, shape)[0].decode_waves == 1
+    run_and_check_fp8(wl, seed=46, out_dtype=torch.float32)
+
+
 def test_fp8_decode_full_size_every_row():
     """The full decode-only batch (256 rows, context 1024..8192) over fp8 pools, every row."""
     say("fp8 decode_only full size, every row")

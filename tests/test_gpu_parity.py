@@ -198,6 +198,20 @@ def test_lengths_at_block_tile_and_split_edges():
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_one_wave_decode_items(out_dtype):
+    """Many short G = 8 decode rows (520 rows of 1..1000 keys, 64 q / 8 kv heads): the plan runs
+    them as one-wave workgroups; every row against the oracle."""
+    say(f"one-wave decode items ({out_dtype})")
+    wl = W.decode_only(seed=45, num_seqs=520, ctx_range=(1, 1000), num_q_heads=64)
+    st = wl.steps[0]
+    shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride,
+                         block_size=wl.block_size)
+    plan, _ = P.plan_varlen_host(st.query_start_loc, st.context_lens, st.seq_lens, shape)
+    assert plan.decode_waves == 1
+    run_and_check(wl, out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_split_counts_around_the_reduce_batch(out_dtype):
     """Decode rows cut into 7, 8, 9, 10 and 17 key splits beside unsplit rows: the split-KV
     reduce loads up to 8 splits' states in one round and takes more in a loop; both against
