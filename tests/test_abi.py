@@ -240,6 +240,24 @@ def test_decode_waves_one_only_for_many_short_g8_items(P):
     assert plan(512, 63, 1023, 64, extra_ql=(40,))[0].decode_waves == 4  # 128-row tiles beside
 
 
+def test_one_wave_decode_items_always_fit_one_wave(P):
+    """Over random G = 8 decode-only batches (300..1200 rows, contexts up to 100..3000 keys),
+    a plan that asks for one-wave workgroups never holds a decode item over 64 blocks (one
+    block id per lane), and some of them ask for it."""
+    rng = np.random.default_rng(7)
+    s = shape(P, num_q_heads=64, num_kv_heads=8, bt_stride=200, num_blocks=200000)
+    ones = 0
+    for _ in range(100):
+        B = int(rng.integers(300, 1200))
+        ctx = rng.integers(0, int(rng.integers(100, 3000)), size=B)
+        qsl = np.arange(B + 1, dtype=np.int32)
+        plan, items = P.plan_varlen_host(qsl, ctx, (ctx + 1).astype(np.int32), s)
+        if plan.decode_waves == 1:
+            ones += 1
+            assert ((items[:, 5] + 15) // 16 - items[:, 4] // 16).max() <= 64
+    assert ones > 0
+
+
 def test_workspace_bound_holds_for_every_plan(P):
     rng = np.random.default_rng(1)
     for trial in range(40):
@@ -251,9 +269,14 @@ def test_workspace_bound_holds_for_every_plan(P):
         ctx = rng.integers(0, 10000, size=B)
         qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
         seq = (ctx + ql).astype(np.int32)
-        plan, _ = P.plan_varlen_host(qsl, ctx, seq, s)
+        plan, items = P.plan_varlen_host(qsl, ctx, seq, s)
         bound = P.varlen_workspace_size(B, int(qsl[-1]), int(seq.max()), s)
         assert plan.workspace_used <= bound
+        # one-wave decode workgroups hold one block id per lane: every decode item <= 64 blocks
+        assert plan.decode_waves in (1, 4)
+        if plan.decode_waves == 1:
+            dec = items[items[:, 1] == 0]
+            assert ((dec[:, 5] + 15) // 16 - dec[:, 4] // 16).max() <= 64
 
 
 def test_binding_rejects_buffers_smaller_than_the_shape(P):
