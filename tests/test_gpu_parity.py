@@ -307,6 +307,32 @@ def test_decode_device_split_matches_oracle(out_dtype):
     assert not bf16_out_to_f64(out0)[3].any() and bool(torch.isneginf(lse[3]).all())
 
 
+@pytest.mark.parametrize("head_dim,group", [(64, 1), (64, 2), (128, 8)])
+def test_decode_device_split_every_shape(head_dim, group):
+    """The device-split decode at the head sizes and groupings the varlen tests cover apart from
+    D 128 / G 4: 12 rows of 1..3000 keys against the oracle."""
+    say(f"device-split decode D={head_dim} G={group}")
+    reqs = [W.RequestSpec(int(c), [1]) for c in np.random.default_rng(47).integers(0, 3000, size=12)]
+    wl = W.build("dsplit_shapes", reqs, num_q_heads=2 * group, num_kv_heads=2, head_dim=head_dim, seed=47)
+    st = wl.steps[0]
+    dw = DeviceWorkload(wl)
+    t = dw.step_tensors(st)
+    P.append_kv(t["k"], t["v"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], t["ctx"], dw.shape)
+    max_seq = wl.bt_stride * wl.block_size
+    ws = P.alloc_workspace(P.decode_workspace_size(st.num_seqs, max_seq, dw.shape))
+    lse = torch.empty(st.q.shape[:2], dtype=torch.float32, device="cuda")
+    out = P.paged_attention_decode(t["q"], dw.k_cache, dw.v_cache, t["bt"], t["qsl"], t["seq"], dw.shape, max_seq,
+                                   workspace=ws, lse=lse)
+    torch.cuda.synchronize()
+    slots = O.slot_mapping(st.block_tables, st.query_start_loc, st.context_lens, wl.block_size)
+    kp, vp = O.reshape_and_cache(st.k, st.v, wl.k_cache, wl.v_cache, slots, wl.block_size)
+    ref, lref = O.paged_attention(st.q, kp, vp, st.block_tables, st.query_start_loc, st.context_lens, st.seq_lens,
+                                  wl.block_size)
+    r = check_attention(bf16_out_to_f64(out), ref, f"device-split decode D={head_dim} G={group}")
+    check_lse(lse.cpu().numpy(), lref, "device-split decode lse")
+    say(f"    {r}")
+
+
 def test_decode_step_graph_replays_with_new_metadata():
     """A decode step (fused cache write + device-split decode) for a padded bucket of 8 rows is
     captured once in a HIP graph, then replayed for three different batches written into the
