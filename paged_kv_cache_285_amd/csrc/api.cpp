@@ -89,12 +89,9 @@ VarlenLayout varlen_layout(int64_t items, int64_t tokens, int64_t partials, int6
   return L;
 }
 
-// Workgroups the decode split size aims for; PKV_DECODE_TARGET_WGS overrides it (tuning).
-int decode_target_wgs() {
-  const char* e = std::getenv("PKV_DECODE_TARGET_WGS");
-  const int x = e ? std::atoi(e) : 0;
-  return x > 0 ? x : 2048;
-}
+// Workgroups the decode split size aims for (about two and a half rounds of the decode
+// workgroups 256 CUs hold; 1024, 4096 and 8192 measured slower on the bench batch).
+constexpr int64_t kDecodeTargetWorkgroups = 2048;
 
 struct Plan {
   std::vector<pkv::WorkItem> items;
@@ -177,7 +174,7 @@ int build_plan(Plan& P, const int32_t* qsl, const int32_t* ctx, const int32_t* s
   const int64_t short_wgs = count_items(true, bps_short) * s->num_kv_heads;
   int bps = pkv::kMinBlocksPerSplit;
   for (; bps < 256; bps *= 2)
-    if (count_items(false, bps) * s->num_kv_heads + short_wgs <= decode_target_wgs()) break;
+    if (count_items(false, bps) * s->num_kv_heads + short_wgs <= kDecodeTargetWorkgroups) break;
   P.bps = bps;
   P.items.clear();
   P.token_split.assign((size_t)num_tokens * 3, 0);
@@ -822,7 +819,7 @@ struct DecodeSplit {
 static DecodeSplit decode_split(int32_t num_seqs, int32_t max_seq_len, const pkv_shape* s) {
   const int64_t blocks = ceil_div(std::max(max_seq_len, 1), pkv::kBlockSize);
   int64_t bps = pkv::kMinBlocksPerSplit;
-  while (bps < 256 && (int64_t)num_seqs * ceil_div(blocks, bps) * s->num_kv_heads > decode_target_wgs()) bps *= 2;
+  while (bps < 256 && (int64_t)num_seqs * ceil_div(blocks, bps) * s->num_kv_heads > kDecodeTargetWorkgroups) bps *= 2;
   DecodeSplit d;
   d.split_keys = (int32_t)(bps * pkv::kBlockSize);
   d.splits = (int32_t)ceil_div(std::max(max_seq_len, 1), d.split_keys);
