@@ -2,7 +2,6 @@
 
 from __future__ import annotations
 
-import contextlib
 import math
 
 import numpy as np
@@ -42,81 +41,30 @@ def bf16_spacing(x: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
-# Largest |value| the rows under test attend over (None: unknown).  Set for every workload that
-# DeviceWorkload / the fp8 helpers upload, and by value_range() around other checks.
-_VMAX = None
-
-
-def workload_vmax(wl, fp8: bool = False) -> float:
-    """max |v| over a workload's pools and new values (fp8 pools: e4m3 rounding adds up to 2^-4)."""
-    arrs = [wl.v_cache] + [st.v for st in wl.steps]
-    vmax = max(float(np.nanmax(np.abs((a.astype(np.uint32) << 16).view(np.float32)))) for a in arrs)
-    return vmax * (1.0 + 2.0**-4 if fp8 else 1.0)
-
-
-def set_value_range(wl, fp8: bool = False, vmax=None) -> None:
-    global _VMAX
-    _VMAX = workload_vmax(wl, fp8) if vmax is None else float(vmax)
-
-
-@contextlib.contextmanager
-def value_range(wl, fp8: bool = False):
-    """Checks inside this context use the value range of ``wl``."""
-    global _VMAX
-    old = _VMAX
-    _VMAX = workload_vmax(wl, fp8)
-    try:
-        yield _VMAX
-    finally:
-        _VMAX = old
-
-
-# Inputs whose softmax rows one key dominates (queries 16x N(0,1)) are checked under the same rule.
-peaked_tolerance = value_range
-
-
-def rounding_bound(ref: np.ndarray, gpu: np.ndarray, bf16_out: bool) -> np.ndarray:
-    """Per-element error the method's two prescribed roundings can produce.
-
-    * P to bf16 before P.V: each weight p_j carries a relative error e_j up to the bf16 unit
-      roundoff u = 2^-8 (8 significant bits, round to nearest even); the output is normalised by
-      the sum of those same rounded weights, so it is a convex combination whose weights moved
-      by w_j (e_j - e_mean) / (1 + e_mean), and |o_gpu - o| <= 2u / (1 - u) max_j |v_j - o|
-      <= 2^-7 (1 + 2^-7) (max|v| + |o|).
-    * The output to bf16: half a bf16 spacing at its magnitude.
-    Plus 1e-5 of fp32 accumulation."""
-    b = np.full(ref.shape, 1e-5)
-    if _VMAX is not None:
-        b = b + 2.0**-7 * (1.0 + 2.0**-7) * (_VMAX + np.abs(ref))
-    if bf16_out:
-        b = b + 0.5 * bf16_spacing(np.maximum(np.abs(ref), np.abs(gpu)))
-    return b
-
-
 def check_attention(gpu: np.ndarray, ref: np.ndarray, what: str, bf16_out: bool = True) -> dict:
-    """Assert max |gpu - ref| <= ATOL and relative L2 <= RTOL_L2.  An element above ATOL is
-    accepted only within rounding_bound() (the bf16 rounding of P and of the output, which the
-    method prescribes); such elements are counted and printed."""
+    """Assert max |gpu - ref| <= ATOL before the output's own rounding, and relative L2 <= RTOL_L2.
+
+    A bf16 output is the kernel's fp32 result rounded to bf16, which moves it by up to half a
+    bf16 spacing of the stored value (more than 1e-2 once |o| >= 4); so an element passes when
+    |gpu - ref| - half that spacing <= ATOL.  fp32 outputs are held to ATOL as they stand.
+    Elements above ATOL only through the output rounding are counted and printed."""
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     assert np.isfinite(ref).all(), f"{what}: oracle produced non-finite values"
     assert np.isfinite(gpu).all(), f"{what}: GPU produced non-finite values at {np.argwhere(~np.isfinite(gpu))[:5]}"
     err = np.abs(gpu - ref)
-    bad = err > ATOL
-    exempt = 0
-    if bad.any():
-        bound = rounding_bound(ref, gpu, bf16_out)
-        ok = err <= bound
-        exempt = int(bad.sum())
-        assert ok[bad].all(), (
-            f"{what}: {int((bad & ~ok).sum())} elements exceed {ATOL} beyond the rounding bound "
-            f"(vmax {_VMAX}); worst {err.max():.4g} at {np.unravel_index(err.argmax(), err.shape)}, worst excess "
-            f"{(err - bound).max():.4g}"
-        )
+    pre = err - 0.5 * bf16_spacing(np.abs(gpu)) if bf16_out else err
+    worst = float(pre.max()) if pre.size else 0.0
+    assert worst <= ATOL, (
+        f"{what}: max abs error before the output rounding {worst:.4g} > {ATOL} at "
+        f"{np.unravel_index(pre.argmax(), pre.shape)} (max abs {err.max():.4g})"
+    )
+    above = int((err > ATOL).sum())
     rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
     assert rel <= RTOL_L2, f"{what}: relative L2 {rel:.3g} > {RTOL_L2}"
-    res = {"max_abs": float(err.max()) if err.size else 0.0, "rel_l2": rel, "above_atol_within_rounding": exempt}
-    print(f"[parity] {what}: max_abs {res['max_abs']:.3g} rel_l2 {rel:.3g} above_1e-2_within_rounding {exempt}",
-          flush=True)
+    res = {"max_abs": float(err.max()) if err.size else 0.0, "rel_l2": rel,
+           "max_abs_before_output_rounding": worst, "above_atol_by_output_rounding": above}
+    print(f"[parity] {what}: max_abs {res['max_abs']:.3g} (before output rounding {worst:.3g}) rel_l2 {rel:.3g}"
+          f" above_1e-2_by_output_rounding {above}", flush=True)
     return res
 
 
@@ -128,15 +76,27 @@ def check_attention(gpu: np.ndarray, ref: np.ndarray, what: str, bf16_out: bool 
 LSE_ROUNDING = math.log1p(2.0**-8) + 2e-5
 
 
-def check_lse(gpu: np.ndarray, ref: np.ndarray, what: str) -> float:
-    """LSE max abs error <= LSE_ATOL; elements above it are accepted only within LSE_ROUNDING
-    (counted and printed)."""
+def lse_rows_from_rounded_weights(st, group: int, tile_rows: int) -> np.ndarray:
+    """Token rows whose LSE a varlen call takes from the sum of rounded weights: the rows of
+    requests on 256-row pipelined tiles (more than 32 packed rows, in a plan of 256-row tiles)."""
+    ql = np.diff(st.query_start_loc)
+    on_tiles = (ql > 1) & (ql * group > 32) & (tile_rows == 256)
+    return np.repeat(on_tiles, ql)
+
+
+def check_lse(gpu: np.ndarray, ref: np.ndarray, what: str, rounded=False) -> float:
+    """LSE max abs error <= LSE_ATOL.  On rows whose LSE comes from the sum of the rounded weights
+    (``rounded``: True for every row, or a boolean mask over the first axis) an element above it
+    is accepted within LSE_ROUNDING and counted and printed."""
     fin = np.isfinite(ref)
     assert np.array_equal(fin, np.isfinite(gpu)), f"{what}: LSE finiteness differs"
-    err = np.abs(gpu[fin] - ref[fin])
+    loose = np.broadcast_to(np.asarray(rounded, dtype=bool).reshape((-1,) + (1,) * (gpu.ndim - 1)), gpu.shape)
+    err = np.where(fin, np.abs(np.where(fin, gpu, 0.0) - np.where(fin, ref, 0.0)), 0.0)
     d = float(err.max()) if err.size else 0.0
-    above = int((err > LSE_ATOL).sum())
+    strict = float(err[~loose].max()) if (~loose).any() else 0.0
+    assert strict <= LSE_ATOL, f"{what}: LSE max abs err {strict:.3g} > {LSE_ATOL} on rows with an fp32 sum"
     assert d <= LSE_ROUNDING, f"{what}: LSE max abs err {d:.3g} > {LSE_ROUNDING:.3g}"
+    above = int((err > LSE_ATOL).sum())
     if above:
         print(f"[parity] {what}: LSE max abs {d:.3g}, {above} above {LSE_ATOL} within the weight rounding",
               flush=True)
@@ -148,7 +108,6 @@ class DeviceWorkload:
 
     def __init__(self, wl, scale: float = 0.0):
         self.wl = wl
-        set_value_range(wl)
         self.k_cache = dev16(wl.k_cache)
         self.v_cache = dev16(wl.v_cache)
         self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride,

@@ -25,11 +25,10 @@ from _gpu import (  # noqa: E402
     bf16_out_to_f64,
     check_attention,
     check_lse,
+    lse_rows_from_rounded_weights,
     dev16,
     dev32,
     many_requests,
-    peaked_tolerance,
-    set_value_range,
 )
 
 
@@ -46,18 +45,6 @@ def devf(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
-def fp8_value_max(c, wl) -> float:
-    """Largest |dequantised value| the rows can attend over: the pool's largest code magnitude per
-    (block, kv head) times its value scale, and the new tokens' values after their quantisation
-    (at most 2^-4 larger, or 448 times the largest scale when they saturate)."""
-    nb, hkv = c.v_scale.shape
-    mag = np.ascontiguousarray(c.v_cache).reshape(nb, -1, hkv, wl.head_dim * 16) & 0x7F
-    mag[mag == 0x7F] = 0  # NaN codes hold no value
-    pool = float(np.max(O.e4m3_decode(mag.max(axis=(1, 3)).astype(np.uint8)) * c.v_scale))
-    new = max(float(np.nanmax(np.abs((st.v.astype(np.uint32) << 16).view(np.float32)))) for st in wl.steps)
-    return max(pool, min(new * (1.0 + 2.0**-4), 448.0 * float(c.v_scale.max())))
-
-
 class DeviceFp8:
     """A workload's fp8 pools and scales on the device (scales uniform, or powers of two)."""
 
@@ -70,7 +57,6 @@ class DeviceFp8:
             c.k_scale = np.exp2(rng.integers(-6, -2, shape)).astype(np.float32)
             c.v_scale = np.exp2(rng.integers(-6, -2, shape)).astype(np.float32)
         self.c = c
-        set_value_range(wl, fp8=True, vmax=fp8_value_max(c, wl))
         self.k_cache, self.v_cache = dev8(c.k_cache), dev8(c.v_cache)
         self.k_scale, self.v_scale = devf(c.k_scale), devf(c.v_scale)
         self.shape = P.make_shape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks, wl.bt_stride,
@@ -209,7 +195,9 @@ def run_and_check_fp8(wl, rows_per_step=None, want_lse=True, out_dtype=torch.bfl
         r = check_attention(bf16_out_to_f64(out)[sel], o_ref[sel], f"fp8 {wl.name} step {si}",
                             bf16_out=out_dtype != torch.float32)
         if want_lse:
-            r["lse_max_abs"] = check_lse(lse.cpu().numpy()[sel], l_ref[sel], f"fp8 {wl.name} step {si} lse")
+            loose = lse_rows_from_rounded_weights(st, wl.num_q_heads // wl.num_kv_heads, plan.tile_rows)
+            r["lse_max_abs"] = check_lse(lse.cpu().numpy()[sel], l_ref[sel], f"fp8 {wl.name} step {si} lse",
+                                         rounded=loose[sel])
         stats.append(r)
         say(f"    plan items={plan.num_items} tile_rows={plan.tile_rows} partials={plan.num_partials} {r}")
     return stats
@@ -291,16 +279,13 @@ def test_fp8_large_scores_take_the_rescale_paths():
     reqs = [W.RequestSpec(c, [1]) for c in (3000, 1500, 700, 40)]
     reqs += [W.RequestSpec(2000, [5]), W.RequestSpec(300, [200])]
     wl = W.build("fp8_large_mixed", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=31)
-    with peaked_tolerance(wl, fp8=True):
-        run_and_check_fp8(_large_scores(wl), seed=31)
+    run_and_check_fp8(_large_scores(wl), seed=31)
     reqs = [W.RequestSpec(300, [2048 // 4 + 37]), W.RequestSpec(2500, [1])]
     wl = W.build("fp8_large_wide", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=32)
-    with peaked_tolerance(wl, fp8=True):
-        run_and_check_fp8(_large_scores(wl), seed=32, expect_tile_rows=256)
+    run_and_check_fp8(_large_scores(wl), seed=32, expect_tile_rows=256)
     wl = W.cascade_shared_prefix(seed=33, num_queries=70, prefix=1040, suffix_range=(1, 200),
                                  num_q_heads=16, num_kv_heads=2, head_dim=128)
-    with peaked_tolerance(wl, fp8=True):
-        _fp8_cascade_check(_large_scores(wl))
+    _fp8_cascade_check(_large_scores(wl))
 
 
 def test_fp8_cascade_prefix_cut_into_segments():
@@ -349,14 +334,14 @@ def _fp8_cascade_check(wl, rows=None, every_row=False):
         po, pl = O.cascade_prefix_attention_fp8(st.q, kp, vp, d.c.k_scale, d.c.v_scale, cv.prefix_block_table,
                                                 cv.prefix_len, bs)
         check_attention(o_p.cpu().numpy().astype(np.float64), po, "fp8 cascade prefix, every row", bf16_out=False)
-        check_lse(l_p.cpu().numpy(), pl, "fp8 cascade prefix lse, every row")
+        check_lse(l_p.cpu().numpy(), pl, "fp8 cascade prefix lse, every row", rounded=True)
         so, sl = O.paged_attention_fp8(st.q, kp, vp, d.c.k_scale, d.c.v_scale, sbt, st.query_start_loc,
                                        cv.suffix_context_lens, cv.suffix_seq_lens, bs)
         check_attention(o_s.cpu().numpy().astype(np.float64), so, "fp8 cascade suffix, every row", bf16_out=False)
         check_lse(l_s.cpu().numpy(), sl, "fp8 cascade suffix lse, every row")
         mo, ml = O.merge_attn_states(po, pl, so, sl)
         r = check_attention(bf16_out_to_f64(out), mo, "fp8 cascade merged vs oracle merge, every row")
-        check_lse(lse_m.cpu().numpy(), ml, "fp8 cascade merged lse, every row")
+        check_lse(lse_m.cpu().numpy(), ml, "fp8 cascade merged lse, every row", rounded=True)
         say(f"    fp8 cascade merged, every row {r}")
         if rows is None:
             return
@@ -365,11 +350,11 @@ def _fp8_cascade_check(wl, rows=None, every_row=False):
     po, pl = O.cascade_prefix_attention_fp8(qs, kp, vp, d.c.k_scale, d.c.v_scale, cv.prefix_block_table,
                                             cv.prefix_len, bs)
     check_attention(o_p.cpu().numpy().astype(np.float64)[sel], po, "fp8 cascade prefix", bf16_out=False)
-    check_lse(l_p.cpu().numpy()[sel], pl, "fp8 cascade prefix lse")
+    check_lse(l_p.cpu().numpy()[sel], pl, "fp8 cascade prefix lse", rounded=True)
     fo, fl = O.paged_attention_fp8(st.q, kp, vp, d.c.k_scale, d.c.v_scale, st.block_tables, st.query_start_loc,
                                    st.context_lens, st.seq_lens, bs, rows=rows)
     r = check_attention(bf16_out_to_f64(out)[sel], fo[sel], "fp8 cascade merged vs single pass")
-    check_lse(lse_m.cpu().numpy()[sel], fl[sel], "fp8 cascade merged lse")
+    check_lse(lse_m.cpu().numpy()[sel], fl[sel], "fp8 cascade merged lse", rounded=True)
     say(f"    fp8 cascade merged {r}")
 
 

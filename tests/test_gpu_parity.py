@@ -25,10 +25,10 @@ from _gpu import (  # noqa: E402
     bf16_out_to_f64,
     check_attention,
     check_lse,
+    lse_rows_from_rounded_weights,
     dev16,
     dev32,
     host16,
-    peaked_tolerance,
 )
 
 
@@ -80,7 +80,9 @@ def run_and_check(wl, rows_per_step=None, check_pools=True, want_lse=True, out_d
         sel = slice(None) if rows is None else rows
         r = check_attention(o_gpu[sel], o_ref[sel], f"{wl.name} step {si}", bf16_out=out_dtype != torch.float32)
         if want_lse:
-            r["lse_max_abs"] = check_lse(lse_g.cpu().numpy()[sel], l_ref[sel], f"{wl.name} step {si} lse")
+            loose = lse_rows_from_rounded_weights(st, wl.num_q_heads // wl.num_kv_heads, plan.tile_rows)
+            r["lse_max_abs"] = check_lse(lse_g.cpu().numpy()[sel], l_ref[sel], f"{wl.name} step {si} lse",
+                                         rounded=loose[sel])
         stats.append(r)
         say(f"    plan items={plan.num_items} tile_rows={plan.tile_rows} partials={plan.num_partials} bps={plan.blocks_per_split} {r}")
     return stats
@@ -551,27 +553,24 @@ def _large_scores(wl, factor=16.0):
 def test_large_scores_take_the_rescale_paths(case):
     """Decode rows (split and unsplit), a speculative-verify row (short item), a chunk over a
     cached context (128-row tiles) and, for "wide", a long chunk on 256-row pipelined tiles, all
-    with queries 16x N(0, 1); the element bound is the peaked-row one (p rounding)."""
+    with queries 16x N(0, 1), so that one key dominates many rows."""
     say(f"large scores: {case}")
     if case == "mixed":
         reqs = [W.RequestSpec(c, [1]) for c in (3000, 1500, 700, 40)]
         reqs += [W.RequestSpec(2000, [5]), W.RequestSpec(300, [200])]
         wl = W.build("large_mixed", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=21)
-        with peaked_tolerance(wl):
-            run_and_check(_large_scores(wl))
+        run_and_check(_large_scores(wl))
     else:
         reqs = [W.RequestSpec(300, [2048 // 4 + 37]), W.RequestSpec(2500, [1])]
         wl = W.build("large_wide", reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, seed=22)
-        with peaked_tolerance(wl):
-            run_and_check(_large_scores(wl), expect_tile_rows=256)
+        run_and_check(_large_scores(wl), expect_tile_rows=256)
 
 
 def test_large_scores_cascade():
     say("large scores: cascade")
     wl = W.cascade_shared_prefix(seed=23, num_queries=70, prefix=1040, suffix_range=(1, 200),
                                  num_q_heads=16, num_kv_heads=2, head_dim=128)
-    with peaked_tolerance(wl):
-        _cascade_check(_large_scores(wl))
+    _cascade_check(_large_scores(wl))
 
 
 def test_cascade_prefix_cut_into_segments():
@@ -627,14 +626,14 @@ def _cascade_check(wl, rows=None, scale=None, every_row=False):
     if every_row:
         po, pl = O.cascade_prefix_attention(st.q, kp, vp, cv.prefix_block_table, cv.prefix_len, bs, scale=scale)
         check_attention(o_p.cpu().numpy().astype(np.float64), po, "cascade prefix, every row", bf16_out=False)
-        check_lse(l_p.cpu().numpy(), pl, "cascade prefix lse, every row")
+        check_lse(l_p.cpu().numpy(), pl, "cascade prefix lse, every row", rounded=True)
         so, sl = O.paged_attention(st.q, kp, vp, sbt_np, st.query_start_loc, cv.suffix_context_lens,
                                    cv.suffix_seq_lens, bs, scale=scale)
         check_attention(o_s.cpu().numpy().astype(np.float64), so, "cascade suffix, every row", bf16_out=False)
         check_lse(l_s.cpu().numpy(), sl, "cascade suffix lse, every row")
         mo, ml = O.merge_attn_states(po, pl, so, sl)
         r = check_attention(bf16_out_to_f64(out), mo, "cascade merged vs oracle merge, every row")
-        check_lse(lse_m.cpu().numpy(), ml, "cascade merged lse, every row")
+        check_lse(lse_m.cpu().numpy(), ml, "cascade merged lse, every row", rounded=True)
         say(f"    cascade merged, every row {r}")
         if rows is None:
             return
@@ -642,11 +641,11 @@ def _cascade_check(wl, rows=None, scale=None, every_row=False):
     qs = st.q if rows is None else st.q[rows]
     po, pl = O.cascade_prefix_attention(qs, kp, vp, cv.prefix_block_table, cv.prefix_len, bs, scale=scale)
     check_attention(o_p.cpu().numpy().astype(np.float64)[sel], po, "cascade prefix", bf16_out=False)
-    check_lse(l_p.cpu().numpy()[sel], pl, "cascade prefix lse")
+    check_lse(l_p.cpu().numpy()[sel], pl, "cascade prefix lse", rounded=True)
     fo, fl = O.paged_attention(st.q, kp, vp, st.block_tables, st.query_start_loc, st.context_lens, st.seq_lens, bs, rows=rows,
                                scale=scale)
     r = check_attention(bf16_out_to_f64(out)[sel], fo[sel], "cascade merged vs single pass")
-    check_lse(lse_m.cpu().numpy()[sel], fl[sel], "cascade merged lse")
+    check_lse(lse_m.cpu().numpy()[sel], fl[sel], "cascade merged lse", rounded=True)
     say(f"    cascade merged {r}")
 
 
