@@ -99,9 +99,10 @@ def test_mixed_batch_small_parity():
     run_and_check(W.mixed_llama8b(seed=1, num_decode=12, ctx_range=(17, 700)))
 
 
-def test_mixed_batch_full_parity():
-    say("mixed_llama8b full (64 decode rows, ctx 128..4096)")
-    run_and_check(W.mixed_llama8b(seed=0))
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_mixed_batch_full_parity(seed):
+    say(f"mixed_llama8b full (64 decode rows, ctx 128..4096), seed {seed}")
+    run_and_check(W.mixed_llama8b(seed=seed))
 
 
 def test_decode_small_parity_fp32_out():
@@ -697,21 +698,32 @@ def test_empty_and_zero_length_rows():
     assert plan0.num_items == 0
 
 
-def test_decode_full_size_every_row():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_full_size_every_row(seed):
     """Full decode-only size (256 rows, ctx 1024..8192) in the launch configuration bench times,
     every row against the oracle."""
-    say("decode_only full size, every row")
-    run_and_check(W.decode_only(seed=0), check_pools=False)
+    say(f"decode_only full size, every row, seed {seed}")
+    run_and_check(W.decode_only(seed=seed), check_pools=False)
 
 
-def test_cascade_full_size_every_row():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_cascade_full_size_every_row(seed):
     """Full cascade size (512 queries x 64 heads, 16384-token prefix, suffixes 64..1024) in the
     launch configuration bench times: every row of the three passes against the oracle's, and
     24 sampled rows of the merged output against single-pass attention."""
-    say("cascade full size (512 queries, 16384-token prefix), every row")
-    wl = W.cascade_shared_prefix(seed=0)
+    say(f"cascade full size (512 queries, 16384-token prefix), every row, seed {seed}")
+    wl = W.cascade_shared_prefix(seed=seed)
     rows = np.sort(np.random.default_rng(3).choice(wl.steps[0].num_tokens, 24, replace=False))
     _cascade_check(wl, rows=rows, every_row=True)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_long_chunked_prefill_full_size_last_chunk_other_seeds(seed):
+    """The full long prefill with the other correctness seeds: every step runs, every row of the
+    last (2048 prompt rows over 32768 keys and the 128 decode rows) is compared."""
+    say(f"long_chunked_prefill full size, last chunk every row, seed {seed}")
+    wl = W.long_chunked_prefill(seed=seed)
+    run_and_check(wl, check_pools=False, want_lse=False, check_steps=(len(wl.steps) - 1,))
 
 
 @pytest.mark.parametrize("chunks", [(0, 8), (8, 11), (11, 13), (13, 15), (15, 16)])
