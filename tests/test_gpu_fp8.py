@@ -395,9 +395,10 @@ def test_fp8_decode_full_size_every_row():
     run_and_check_fp8(W.decode_only(seed=0), seed=0, check_pools=False)
 
 
-def test_fp8_mixed_full_size_every_row():
-    say("fp8 mixed batch full size (64 decode rows, ctx 128..4096), every row")
-    run_and_check_fp8(W.mixed_llama8b(seed=0), seed=0, check_pools=False)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_fp8_mixed_full_size_every_row(seed):
+    say(f"fp8 mixed batch full size (64 decode rows, ctx 128..4096), every row, seed {seed}")
+    run_and_check_fp8(W.mixed_llama8b(seed=seed), seed=seed, check_pools=False)
 
 
 @pytest.mark.parametrize("case", ["mixed", "decode"])
